@@ -1,0 +1,96 @@
+"""libkda Python binding: Kimi Delta Attention kernels for MI355X (gfx950).
+
+``chunk_fwd`` (chunkwise prefill) and ``recurrent_step`` (decode) take torch
+tensors on the GPU and call the C ABI of ``libkda.so`` on the current stream.
+torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+from ._binding import (KDA_BF16, KDA_F32, KDAError, lib, status_string,  # noqa: F401
+                       version, _check)
+
+__all__ = ["chunk_fwd", "recurrent_step", "status_string", "version", "KDAError",
+           "KDA_F32", "KDA_BF16", "lib"]
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.float32 or torch.bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, shape, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out=None, S_T=None,
+              return_state: bool = True):
+    """Chunked KDA prefill.  q, k, v: [B, T, H, 128] (fp32 or bf16); log_alpha:
+    [B, T, H, 128] fp32; beta: [B, T, H] (same dtype as q); S0: [B, H, 128, 128]
+    fp32 or None.  Returns ``(o, S_T)`` (``S_T`` is None if not requested)."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for t, n, shp in ((k, "k", q.shape), (v, "v", (B, T, H, dv)), (beta, "beta", (B, T, H))):
+        _need(t, n, dt, shp, dev)
+    _need(log_alpha, "log_alpha", torch.float32, q.shape, dev)
+    _need(q, "q", dt, q.shape, dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, T, H, dv), dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _need(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
+    st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(S0), _ptr(out), _ptr(S_T), B, T, H, dk, dv, code,
+                             _stream(dev))
+    _check("kda_chunk_fwd", st)
+    return out, S_T
+
+
+def recurrent_step(q, k, v, log_alpha, beta, S, *, out=None):
+    """One KDA decode step, state updated in place.  q, k, v: [N, H, 128];
+    log_alpha: [N, H, 128] fp32; beta: [N, H]; S: [N, H, 128, 128] fp32.
+    Returns o [N, H, 128]."""
+    import torch
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for t, n, shp in ((k, "k", q.shape), (v, "v", (N, H, dv)), (beta, "beta", (N, H))):
+        _need(t, n, dt, shp, dev)
+    _need(log_alpha, "log_alpha", torch.float32, q.shape, dev)
+    _need(S, "S", torch.float32, (N, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (N, H, dv), dev)
+    st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  _ptr(S), _ptr(out), N, H, dk, dv, code, _stream(dev))
+    _check("kda_recurrent_step", st)
+    return out

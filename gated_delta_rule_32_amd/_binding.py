@@ -1,0 +1,67 @@
+"""ctypes binding of libkda (argument marshalling only).
+
+Every compute step runs in the HIP kernels of ``libkda.so``; this module only
+checks tensor metadata, allocates outputs with torch (device memory plumbing)
+and passes raw device pointers and the current HIP stream to the C ABI.  If the
+library is missing, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_OK = 0
+STATUS_NAMES = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
+                -3: "KDA_ERR_ALIGNMENT", -4: "KDA_ERR_HIP"}
+
+# name -> (restype, argtypes) for every symbol declared in include/kda.h
+_VP, _I = ctypes.c_void_p, ctypes.c_int
+SIGNATURES = {
+    "kda_chunk_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                           _I, _I, _I, _I, _I, _I, _VP]),
+    "kda_recurrent_step": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                _I, _I, _I, _I, _I, _VP]),
+    "kda_status_string": (ctypes.c_char_p, [_I]),
+    "kda_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().kda_status_string(status).decode()
+        super().__init__(f"{fn} returned {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def lib():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not found: build it with "
+                               "`python -m gated_delta_rule_32_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().kda_version().decode()
+
+
+def _check(fn: str, status: int):
+    if status != KDA_OK:
+        raise KDAError(fn, status)

@@ -1,0 +1,147 @@
+// kda_api.cpp -- the C ABI of libkda: argument validation and dispatch.
+//
+// Validation is pure host code that runs before any HIP call, so every error
+// path can be exercised on a machine without a GPU.
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+#include <limits.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kHeadDim = 128;
+
+struct Range {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+int check_ptr(const void* p, size_t align) {
+    if (!p) return KDA_ERR_INVALID_ARG;
+    if ((uintptr_t)p % align) return KDA_ERR_ALIGNMENT;
+    return KDA_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == KDA_BF16 ? 2 : 4; }
+
+// Product of non-negative ints as size_t, or 0 with *ok = false on overflow
+// past 2^62 (far beyond any device memory).
+size_t mul3(long long a, long long b, long long c, bool* ok) {
+    const long long lim = (long long)1 << 62;
+    long long r = a;
+    if (b && r > lim / b) { *ok = false; return 0; }
+    r *= b;
+    if (c && r > lim / c) { *ok = false; return 0; }
+    return (size_t)(r * c);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument (NULL pointer, negative size or overlapping buffers)";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k and d_v must be 128; dtype must be KDA_F32 or KDA_BF16)";
+        case KDA_ERR_ALIGNMENT: return "misaligned pointer (data pointers need 16-byte alignment, beta its element size)";
+        case KDA_ERR_HIP: return "HIP runtime or launch error";
+        default: return "unknown status";
+    }
+}
+
+const char* kda_version(void) { return "0.1.0"; }
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v,
+                  const float* log_alpha, const void* beta, const float* S0,
+                  void* o, float* S_T,
+                  int B, int T, int H, int dk, int dv, int dtype, void* stream)
+{
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return KDA_OK;
+
+    bool ok = true;
+    const size_t es = elem_size(dtype);
+    const size_t tok = mul3(B, T, H, &ok);            // tokens x heads
+    const size_t heads = mul3(B, H, 1, &ok);
+    const size_t n_qk = mul3((long long)tok, kHeadDim, 1, &ok);
+    const size_t n_state = mul3((long long)heads, kHeadDim, kHeadDim, &ok);
+    if (!ok) return KDA_ERR_UNSUPPORTED;
+    if (heads * 64 > (size_t)INT_MAX) return KDA_ERR_UNSUPPORTED;  // grid size
+
+    int rc;
+    if (S0 && (rc = check_ptr(S0, 16)) != KDA_OK) return rc;
+    if (S_T && (rc = check_ptr(S_T, 16)) != KDA_OK) return rc;
+    const Range rS0{S0, S0 ? n_state * 4 : 0}, rST{S_T, S_T ? n_state * 4 : 0};
+    if (T > 0) {
+        if ((rc = check_ptr(q, 16)) || (rc = check_ptr(k, 16)) || (rc = check_ptr(v, 16)) ||
+            (rc = check_ptr(log_alpha, 16)) || (rc = check_ptr(beta, es)) ||
+            (rc = check_ptr(o, 16)))
+            return rc;
+        const Range in[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es},
+                            {log_alpha, n_qk * 4}, {beta, tok * es}, rS0};
+        const Range ro{o, n_qk * es};
+        for (const Range& r : in)
+            if (overlap(ro, r)) return KDA_ERR_INVALID_ARG;
+        if (overlap(ro, rST)) return KDA_ERR_INVALID_ARG;
+        for (int i = 0; i < 5; ++i)
+            if (overlap(rST, in[i])) return KDA_ERR_INVALID_ARG;
+    }
+    // S_T may coincide with S0 exactly (in-place update), never partially.
+    if (overlap(rS0, rST) && (const void*)S0 != (const void*)S_T) return KDA_ERR_INVALID_ARG;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (T == 0) {
+        if (!S_T || (const void*)S0 == (const void*)S_T) return KDA_OK;
+        e = kda::launch_state_copy(S0, S_T, (long long)heads, s);
+    } else {
+        e = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dtype, s);
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_recurrent_step(const void* q, const void* k, const void* v,
+                       const float* log_alpha, const void* beta, float* S,
+                       void* o, int N, int H, int dk, int dv, int dtype,
+                       void* stream)
+{
+    if (N < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if ((long long)N * H == 0) return KDA_OK;
+
+    bool ok = true;
+    const size_t es = elem_size(dtype);
+    const size_t heads = mul3(N, H, 1, &ok);
+    const size_t n_vec = mul3((long long)heads, kHeadDim, 1, &ok);
+    const size_t n_state = mul3((long long)heads, kHeadDim, kHeadDim, &ok);
+    if (!ok || heads > (size_t)INT_MAX) return KDA_ERR_UNSUPPORTED;
+
+    int rc;
+    if ((rc = check_ptr(q, 16)) || (rc = check_ptr(k, 16)) || (rc = check_ptr(v, 16)) ||
+        (rc = check_ptr(log_alpha, 16)) || (rc = check_ptr(beta, es)) ||
+        (rc = check_ptr(S, 16)) || (rc = check_ptr(o, 16)))
+        return rc;
+    const Range in[] = {{q, n_vec * es}, {k, n_vec * es}, {v, n_vec * es},
+                        {log_alpha, n_vec * 4}, {beta, heads * es}};
+    const Range rS{S, n_state * 4}, ro{o, n_vec * es};
+    for (const Range& r : in)
+        if (overlap(rS, r) || overlap(ro, r)) return KDA_ERR_INVALID_ARG;
+    if (overlap(rS, ro)) return KDA_ERR_INVALID_ARG;
+
+    hipError_t e = kda::launch_decode_step(q, k, v, log_alpha, beta, S, o,
+                                           (long long)heads, dtype, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

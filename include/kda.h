@@ -1,0 +1,117 @@
+/*
+ * kda.h -- C ABI of libkda, Kimi Delta Attention (KDA) kernels for AMD MI355X
+ * (gfx950).
+ *
+ * KDA is the gated delta rule with a per-channel forget gate, eq. (1) on page
+ * "Kimi K3论文：Kimi Linear", section 3:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,
+ *
+ * with S_t a d_k x d_v fp32 state, alpha_t = exp(g_t) in (0,1]^{d_k} and
+ * beta_t in [0,1].  The same page (section 4) splits the work into a
+ * chunkwise-parallel prefill and a cheaper recurrent decode step; this library
+ * exports one entry point for each.
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are DEVICE pointers (HIP global memory) owned by the
+ *    caller.  The library allocates nothing, frees nothing and keeps no pointer
+ *    after it returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*, NULL = the default stream).  No call synchronises the host; buffers
+ *    must stay alive until the stream work has finished.
+ *  - Layouts are dense, row-major (C order), no padding.  Every data pointer
+ *    must be 16-byte aligned, except `beta`, which needs its element size.
+ *  - Only d_k = d_v = 128 is supported; other sizes return KDA_ERR_UNSUPPORTED.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    failed check returns a negative status and touches no memory.  Values
+ *    are not inspected: NaN and Inf pass through.
+ *  - Calls keep no state between them and are safe from several host threads.
+ *
+ * Numeric range of the gate: g (= log alpha) must be finite and <= 0.  The
+ * chunked prefill factorises exp(G_r - G_i) over 64-token chunks, so it needs
+ * the cumulative log-decay of every channel over one chunk to stay above -80
+ * (alpha products above e^-80); gates stronger than that are outside the
+ * supported range.  The decode step has no such limit.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, beta and o.  g and the state are always fp32. */
+typedef enum {
+    KDA_F32 = 0,  /* IEEE fp32 */
+    KDA_BF16 = 1  /* bfloat16 (upper half of an fp32) */
+} kda_dtype_t;
+
+/* Status codes. */
+enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, overlapping buffers */
+    KDA_ERR_UNSUPPORTED = -2, /* d_k or d_v != 128, unknown dtype, size overflow */
+    KDA_ERR_ALIGNMENT = -3,   /* pointer not aligned as documented above */
+    KDA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/*
+ * Chunkwise prefill: runs eq. (1) over T tokens of B x H independent heads, in
+ * chunks of 64 tokens (page "Kimi Linear：高效注意力机制在长序列处理中的创新应用",
+ * sections 2.1-2.3, and page "Kimi K3论文：Kimi Linear", section 4: in-chunk
+ * cumulative decay, masked intra-chunk matrices Aqk and Akk, inversion of the
+ * unit-lower-triangular I + Akk by forward substitution, WY factors, and a
+ * sequential chunk-to-chunk pass of the state).
+ *
+ *   q, k      [B, T, H, dk]  dtype          queries, keys (L2-normalised by the caller)
+ *   v         [B, T, H, dv]  dtype          values
+ *   log_alpha [B, T, H, dk]  fp32           g_t = log(alpha_t), finite, <= 0
+ *   beta      [B, T, H]      dtype          write strength
+ *   S0        [B, H, dk, dv] fp32           initial state; NULL means zeros
+ *   o         [B, T, H, dv]  dtype   out    o_t = S_t^T q_t
+ *   S_T       [B, H, dk, dv] fp32    out    final state; NULL means not written.
+ *                                           S_T may equal S0 (updated in place);
+ *                                           any other overlap is rejected.
+ * T may be any value >= 0 (a partial last chunk is handled exactly); T = 0
+ * copies S0 (or zeros) to S_T.  B*H = 0 is a no-op.  `o` must not overlap any
+ * input.  Returns KDA_OK or a negative status.
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v,
+                  const float* log_alpha, const void* beta, const float* S0,
+                  void* o, float* S_T,
+                  int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * Recurrent decode step: applies eq. (1) once (one token) to each of N x H
+ * independent heads, updating the state in place, and returns o = S^T q
+ * (page "Kimi K3论文：Kimi Linear", section 3 eq. (1) and section 4, the
+ * recurrent kernel used for decoding).
+ *
+ *   q, k      [N, H, dk]      dtype
+ *   v         [N, H, dv]      dtype
+ *   log_alpha [N, H, dk]      fp32
+ *   beta      [N, H]          dtype
+ *   S         [N, H, dk, dv]  fp32   in/out  read, then overwritten with S_t
+ *   o         [N, H, dv]      dtype  out
+ * N*H = 0 is a no-op.  `S` and `o` must not overlap each other or any input.
+ */
+int kda_recurrent_step(const void* q, const void* k, const void* v,
+                       const float* log_alpha, const void* beta, float* S,
+                       void* o, int N, int H, int dk, int dv, int dtype,
+                       void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* kda_status_string(int status);
+
+/* Library version as "major.minor.patch" (static string). */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,28 @@
+"""Helpers shared by the tests: the error metric and oracle calls on the
+input dicts produced by gated_delta_rule_32_amd.inputs."""
+import numpy as np
+
+from oracle import kda_ref
+
+TOL = {"float32": 1e-4, "bfloat16": 2e-2}
+
+
+def max_rel_err(x, ref):
+    """max |x - ref| / max |ref| over one output tensor, in fp64."""
+    x = x.detach().cpu().double().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(x - ref)) / den) if den > 0 else float(np.max(np.abs(x)))
+
+
+def oracle_prefill(inp, heads=None):
+    """Oracle on a prefill input dict; ``heads`` = list of (b, h) to restrict to."""
+    q, k, v, g, beta, S0 = (inp[n] for n in ("q", "k", "v", "g", "beta", "S0"))
+    if heads is None:
+        return kda_ref.recurrent(q, k, v, g, beta, S0)
+    outs = []
+    for b, h in heads:
+        sl = lambda t: t[b:b + 1, :, h:h + 1]
+        s0 = None if S0 is None else S0[b:b + 1, h:h + 1]
+        outs.append(kda_ref.recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), s0))
+    return outs

@@ -1,0 +1,155 @@
+"""GPU parity of the chunked prefill (kda_chunk_fwd through the C ABI) against
+the fp64 oracle, element by element on every output and final-state entry, at
+sizes the oracle finishes in seconds (several chunks, ragged tails), and on
+sampled heads at the full workload sizes in the launch configuration the
+benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_32_amd as kda
+from gated_delta_rule_32_amd import inputs
+from tests.kda_testutil import TOL, max_rel_err, oracle_prefill
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def to_dev(inp):
+    return {n: (x.to(DEV) if x is not None else None) for n, x in inp.items()}
+
+
+def run(d, S0="inp", **kw):
+    s0 = d["S0"] if S0 == "inp" else S0
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], s0, **kw)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def check(inp, o, S, tol, heads=None):
+    if heads is None:
+        o_ref, S_ref = oracle_prefill(inp)
+        eo, es = max_rel_err(o, o_ref), max_rel_err(S, S_ref)
+    else:
+        refs = oracle_prefill(inp, heads)
+        eo = max(max_rel_err(o[b, :, h], r[0][0, :, 0]) for (b, h), r in zip(heads, refs))
+        es = max(max_rel_err(S[b, h], r[1][0, 0]) for (b, h), r in zip(heads, refs))
+    print(f"  o err {eo:.3e}  S err {es:.3e}  (tol {tol})", flush=True)
+    assert eo <= tol and es <= tol
+    return eo, es
+
+
+def test_config1_fp32_full():
+    """1 head, T = 256, fp32 everywhere, S0 = 0: max relative error <= 1e-4."""
+    print("prefill c1 fp32 T=256", flush=True)
+    inp = inputs.prefill_config("c1_fp32_T256")
+    o, S = run(to_dev(inp))
+    check(inp, o, S, TOL["float32"])
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 200])
+def test_ragged_lengths_with_initial_state(dtype, T):
+    print(f"prefill ragged dtype={dtype} T={T}", flush=True)
+    inp = inputs.prefill_inputs(2, T, 3, dtype=dtype, g_scale=0.1, s0_std=0.05, seed=T)
+    o, S = run(to_dev(inp))
+    check(inp, o, S, TOL[dtype])
+
+
+@pytest.mark.parametrize("H", [1, 40, 100])
+def test_bf16_slice_widths(H):
+    """Head counts that select each value-slice width (16, 32, 64 columns)."""
+    print(f"prefill slice widths H={H}", flush=True)
+    inp = inputs.prefill_inputs(1, 150, H, dtype="bfloat16", g_scale=0.05, s0_std=0.02, seed=H)
+    o, S = run(to_dev(inp))
+    heads = [(0, 0), (0, H - 1), (0, H // 2)]
+    check(inp, o, S, TOL["bfloat16"], heads=heads)
+
+
+def test_config2_reduced_all_elements():
+    print("prefill c2 reduced B=2 H=4 T=1000", flush=True)
+    inp = inputs.prefill_config("c2_bf16_B8_H16_T4096", B=2, H=4, T=1000)
+    o, S = run(to_dev(inp))
+    check(inp, o, S, TOL["bfloat16"])
+
+
+def test_config2_full_size_sampled_heads():
+    """B = 8, H = 16, T = 4096 bf16: every token and state entry of 6 heads."""
+    print("prefill c2 full", flush=True)
+    inp = inputs.prefill_config("c2_bf16_B8_H16_T4096")
+    o, S = run(to_dev(inp))
+    heads = [(0, 0), (7, 15), (3, 9), (5, 2), (1, 14), (6, 7)]
+    check(inp, o, S, TOL["bfloat16"], heads=heads)
+
+
+def test_config3_full_size_sampled_heads():
+    """B = 1, H = 32, T = 65536 bf16, S0 ~ N(0, 0.02^2): 2 heads end to end."""
+    print("prefill c3 full", flush=True)
+    inp = inputs.prefill_config("c3_bf16_B1_H32_T65536")
+    o, S = run(to_dev(inp))
+    check(inp, o, S, TOL["bfloat16"], heads=[(0, 0), (0, 31)])
+
+
+def test_strong_decay_near_range_limit():
+    """Per-channel log-decay of about -0.8 per token: chunk sums down to about -65."""
+    print("prefill strong decay", flush=True)
+    inp = inputs.prefill_inputs(1, 200, 2, dtype="bfloat16", g_scale=1.0, s0_std=0.05, seed=8)
+    o, S = run(to_dev(inp))
+    check(inp, o, S, TOL["bfloat16"])
+    inp32 = inputs.prefill_inputs(1, 200, 2, dtype="float32", g_scale=1.0, s0_std=0.05, seed=8)
+    o, S = run(to_dev(inp32))
+    check(inp32, o, S, TOL["float32"])
+
+
+def test_state_options_and_edge_cases():
+    inp = inputs.prefill_inputs(2, 77, 2, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=5)
+    d = to_dev(inp)
+    o_ref, S_ref = run(d)
+    # S_T not requested
+    o2, S2 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], return_state=False)
+    torch.cuda.synchronize()
+    assert S2 is None and torch.equal(o2, o_ref)
+    # in place: S_T == S0
+    S_io = d["S0"].clone()
+    o3, S3 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S_io, S_T=S_io)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o_ref) and torch.equal(S_io, S_ref)
+    # S0 = None equals an explicit zero state
+    oz, Sz = run(d, S0=None)
+    oz2, Sz2 = run(d, S0=torch.zeros_like(d["S0"]))
+    assert torch.equal(oz, oz2) and torch.equal(Sz, Sz2)
+    # T = 0 copies the initial state (or zeros)
+    e = lambda x: x[:, :0].contiguous()
+    _, S0c = kda.chunk_fwd(e(d["q"]), e(d["k"]), e(d["v"]), e(d["g"]), e(d["beta"]), d["S0"])
+    _, Sze = kda.chunk_fwd(e(d["q"]), e(d["k"]), e(d["v"]), e(d["g"]), e(d["beta"]), None)
+    torch.cuda.synchronize()
+    assert torch.equal(S0c, d["S0"]) and torch.count_nonzero(Sze) == 0
+    # deterministic: bitwise equal reruns
+    o4, S4 = run(d)
+    assert torch.equal(o4, o_ref) and torch.equal(S4, S_ref)
+
+
+def test_split_and_resume_matches_single_call():
+    inp = inputs.prefill_inputs(1, 300, 4, dtype="bfloat16", g_scale=0.05, s0_std=0.02, seed=6)
+    d = to_dev(inp)
+    o, S = run(d)
+    a = {n: (x[:, :128].contiguous() if x is not None and x.dim() >= 3 else x) for n, x in d.items()}
+    bb = {n: (x[:, 128:].contiguous() if x is not None and x.dim() >= 3 else x) for n, x in d.items()}
+    a["S0"] = d["S0"]
+    oa, Sa = run(a)
+    bb["S0"] = Sa
+    ob, Sb = run(bb)
+    o_ref, S_ref = oracle_prefill(inp)
+    eo, es = max_rel_err(torch.cat([oa, ob], 1), o_ref), max_rel_err(Sb, S_ref)
+    print(f"  o err {eo:.3e}  S err {es:.3e}", flush=True)
+    assert eo <= TOL["bfloat16"] and es <= TOL["bfloat16"]
+
+
+def test_nan_propagates():
+    """NaN inputs are not masked: a NaN value in chunk 1 reaches the outputs of
+    that chunk onward and the final state; chunk 0 stays finite."""
+    inp = inputs.prefill_inputs(1, 150, 1, dtype="float32", seed=9)
+    inp["v"][0, 70, 0, 5] = float("nan")
+    o, S = run(to_dev(inp))
+    assert torch.isnan(o[0, 70:]).any() and torch.isnan(S).any()
+    assert not torch.isnan(o[0, :64]).any()
