@@ -1,0 +1,254 @@
+"""KDA benchmark on one MI355X.
+
+One step = one kda_chunk_fwd call over the prefill workload B = 8, H = 16,
+T = 4096, d_k = d_v = 128, C = 64, bf16 q/k/v/beta, fp32 log-decay, S0 = 0,
+returning o and S_T (inputs already resident in HBM).  The headline value is
+head-tokens per second (B*T*H / time).  The JSON line also carries:
+  * roofline: the fused prefill kernel against HBM bandwidth (the pages' cost
+    model puts the workload below the bf16 ridge point), its measured average
+    launch time from HIP events on the launch stream, and the HBM traffic
+    measured with rocprofv3 counters (stored under profiles/);
+  * mfma: the pages' cost-model FLOPs as a fraction of the bf16 MFMA peak;
+  * decode: the recurrent decode step over 256 x 32 heads, state GB/s and %
+    of HBM peak;
+  * cpu_baseline: the fp64 oracle timed on the host cores on the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --workload c3|c1|decode  (single-workload lines, for profiling)
+       python bench.py --copy-calibration       (plain copy kernel for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz)
+D, C = 128, 64
+# Pages' cost model per head and token (page "Kimi K3论文：Kimi Linear", section 4):
+# 6 T d^2 + 3 T C d + T C^2 FLOPs per head -> per head-token:
+FLOP_PER_HEAD_TOKEN = 6 * D * D + 3 * C * D + C * C          # 126,976
+# Compulsory HBM bytes per head-token for bf16 prefill: q, k, v (3 x 256),
+# log-decay fp32 (512), beta bf16 (2), o bf16 (256).
+BYTES_PER_HEAD_TOKEN_BF16 = 3 * 2 * D + 4 * D + 2 + 2 * D     # 1,538
+BYTES_PER_HEAD_TOKEN_F32 = 3 * 4 * D + 4 * D + 4 + 4 * D      # 2,564
+STATE_BYTES = 4 * D * D                                        # 65,536 per head
+# Decode: per head and step the state is read and written once, plus q, k, v
+# (bf16), log-decay (fp32), beta (bf16) and o (bf16).
+DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + 3 * 2 * D + 4 * D + 2 + 2 * D   # 132,610
+
+PREFILL_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_prefill.hip")
+DECODE_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+WORKLOADS = {
+    "c2": "c2_bf16_B8_H16_T4096",
+    "c3": "c3_bf16_B1_H32_T65536",
+    "c1": "c1_fp32_T256",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, src_path):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    absent or taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("src_sha256_16") != src_hash(src_path):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup):
+    """Average time of fn() over `steps` back-to-back calls, from HIP events
+    recorded on the current stream (the stream the kernels are launched on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3 / steps, wall
+
+
+def prefill_line(name, steps, warmup):
+    import torch
+    import gated_delta_rule_32_amd as kda
+    from gated_delta_rule_32_amd import inputs
+
+    cfg = inputs.PREFILL_CONFIGS[name]
+    B, T, H = cfg["B"], cfg["T"], cfg["H"]
+    log(f"[bench] generating inputs for {name}")
+    inp = inputs.prefill_config(name)
+    d = {n: (x.to("cuda:0") if x is not None else None) for n, x in inp.items()}
+    o = torch.empty_like(d["v"])
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda:0")
+
+    def step():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], out=o, S_T=S_T)
+
+    log(f"[bench] timing {steps} steps after {warmup} warmup")
+    t_kernel, wall = time_launches(step, steps, warmup)
+    head_tokens = B * T * H
+    per_ht = BYTES_PER_HEAD_TOKEN_BF16 if cfg["dtype"] == "bfloat16" else BYTES_PER_HEAD_TOKEN_F32
+    s0_bytes = STATE_BYTES * B * H if d["S0"] is not None else 0
+    alg_bytes = head_tokens * per_ht + STATE_BYTES * B * H + s0_bytes
+    flops = head_tokens * FLOP_PER_HEAD_TOKEN
+    t_floor = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+    traffic = measured_traffic(f"chunk_fwd_{name}", PREFILL_KERNEL_SRC)
+    achieved = alg_bytes / t_kernel / 1e9
+    return dict(
+        inp=inp, t=t_kernel, wall=wall, head_tokens=head_tokens,
+        value=head_tokens / t_kernel,
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                  "traffic": traffic,
+                  "kernel": "chunk_fwd_kernel<bf16,64>" if cfg["dtype"] == "bfloat16" else "chunk_fwd_kernel<f32,16>",
+                  "alg_bytes_per_launch": alg_bytes,
+                  "avg_launch_us": round(t_kernel * 1e6, 2)},
+        mfma={"model_flops_per_launch": flops,
+              "achieved_tflops": round(flops / t_kernel / 1e12, 2),
+              "peak_tflops": BF16_PEAK_TFLOPS,
+              "frac_of_bf16_peak": round(flops / t_kernel / 1e12 / BF16_PEAK_TFLOPS, 4),
+              "frac_of_roofline": round(t_floor / t_kernel, 4)},
+        config={"workload": f"kda_chunk_fwd {name}", "B": B, "T": T, "H": H, "d_k": D, "d_v": D,
+                "chunk": C, "dtype": cfg["dtype"], "S0": "N(0,%g)" % cfg["s0_std"] if d["S0"] is not None else "zero",
+                "log_decay": "-%g*softplus(N(0,1))" % cfg["g_scale"]},
+    )
+
+
+def decode_line(steps, warmup):
+    import torch
+    import gated_delta_rule_32_amd as kda
+    from gated_delta_rule_32_amd import inputs
+
+    cfg = inputs.DECODE_CONFIG
+    N, H = cfg["N"], cfg["H"]
+    nsteps = steps + warmup
+    log(f"[bench] decode: {N}x{H} heads, {nsteps} steps of tokens")
+    S = inputs.decode_state(N, H, s_std=cfg["s_std"], seed=cfg["seed"], device="cuda:0")
+    toks = inputs.decode_tokens(N, H, nsteps, dtype=cfg["dtype"], seed=cfg["seed"], device="cuda:0")
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda:0")
+    i = [0]
+
+    def step():
+        s = i[0] % nsteps
+        kda.recurrent_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["g"][s],
+                           toks["beta"][s], S, out=o)
+        i[0] += 1
+
+    t, _ = time_launches(step, steps, warmup)
+    alg = N * H * DECODE_BYTES_PER_HEAD
+    gbs = alg / t / 1e9
+    return {"workload": f"kda_recurrent_step {N}x{H} heads, fp32 128x128 state, bf16 tokens",
+            "us_per_step": round(t * 1e6, 2), "state_gb_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "alg_bytes_per_step": alg,
+            "traffic": measured_traffic("recurrent_step_decode", DECODE_KERNEL_SRC)}
+
+
+def cpu_baseline(inp):
+    """The fp64 oracle as it stands, on the host cores, on the whole workload."""
+    import numpy as np
+    from oracle import kda_ref
+    B, T, H, _ = inp["q"].shape
+    arrs = [kda_ref._f64(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+    S0 = kda_ref._f64(inp["S0"])
+    threads = kda_ref.max_threads()
+    log(f"[bench] cpu baseline: oracle on {B}x{H} heads x {T} tokens, {threads} threads")
+    t0 = time.perf_counter()
+    kda_ref.recurrent(*arrs, S0, nthreads=threads)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": round(B * T * H / dt, 1), "unit": "head-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole workload: {B}x{H} heads x {T} tokens, fp64 sequential recurrence "
+                      f"(C, -O2, OpenMP over heads), {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode"], default=None,
+                    help="time one workload only (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (for HBM counter scaling) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the KDA heads shard across GPUs with no communication, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.init()
+
+    if args.copy_calibration:
+        n = 1 << 28   # 256 Mi floats = 1 GiB
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+        return
+
+    if args.workload == "decode":
+        dec = decode_line(args.steps, args.warmup)
+        print(json.dumps({"metric": "KDA decode state GB/s", **dec}))
+        return
+
+    name = WORKLOADS[args.workload or "c2"]
+    pre = prefill_line(name, args.steps, args.warmup)
+    line = {
+        "metric": "KDA prefill tokens/s/head-layer (% MFMA peak); decode state GB/s (% HBM)",
+        "value": round(pre["value"], 1),
+        "unit": "head-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(pre["t"] * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if pre["config"]["dtype"] == "bfloat16" else "f32",
+        "data": "synthetic",
+        "config": pre["config"],
+        "roofline": pre["roofline"],
+        "mfma": pre["mfma"],
+    }
+    if args.workload is None and not args.no_decode:
+        line["decode"] = decode_line(max(args.steps, 20), args.warmup)
+    if not args.no_cpu and args.workload is None:
+        line["cpu_baseline"] = cpu_baseline(pre["inp"])
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

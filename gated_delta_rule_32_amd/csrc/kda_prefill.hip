@@ -1,38 +1,45 @@
 // kda_prefill.hip -- chunkwise KDA prefill for gfx950 (one fused kernel).
 //
 // Method: page "Kimi Linear：高效注意力机制在长序列处理中的创新应用", sections
-// 2.1-2.3 (Proposition S_r = P_r S_0 + H_r, WY representation, chunk size 64,
+// 2.1-2.3 (Proposition S_r = P_r S_0 + H_r, WY representation, chunks of 64,
 // forward substitution) and page "Kimi K3论文：Kimi Linear", section 4 (intra-
 // chunk matrix products, UT transform, chunk-to-chunk state recurrence).
-// For a chunk of C = 64 tokens with entry state S (d_k x d_v, fp32):
+// For a chunk of C = 64 tokens with entry state S (d_k x d_v, fp32), and
+// G = in-chunk cumulative sum of g = log(alpha):
 //
-//   G       = in-chunk cumulative sum of g = log(alpha)            [64 x 128]
-//   Aqk     = (e^{G} * Q)(e^{-G} * K)^T, kept for i <= r            [64 x 64]
-//   Akk     = (beta e^{G} * K)(e^{-G} * K)^T, kept for i < r        [64 x 64]
-//   Tm      = (I + Akk)^{-1}                 (forward substitution)
-//   W       = Tm (beta e^{G} * K),   U = Tm (beta * V)              (WY factors)
-//   Vn      = U - W S
-//   O       = (e^{G} * Q) S + Aqk Vn
-//   S      <- Diag(e^{G_64}) S + (e^{G_64 - G} * K)^T Vn
+//   Qt = e^{G} * Q,  Kh = e^{G} * K,  Kb = e^{-G} * K                  [64 x 128]
+//   Aqk = Qt Kb^T   (kept for i <= r)                                  [64 x 64]
+//   Akk = Diag(beta) Kh Kb^T   (kept for i < r)
+//   Tm  = (I + Akk)^{-1}                         (UT transform)
+//   Vn  = Tm Diag(beta) (V - Kh S)               (= U - W S with the WY factors
+//                                                  W = Tm Diag(beta) Kh, U = Tm Diag(beta) V)
+//   O   = Qt S + Aqk Vn
+//   S  <- Diag(e^{G_64}) (S + Kb^T Vn)           (= Diag(e^{G_64}) S + (e^{G_64 - G} * K)^T Vn)
 //
 // The decay e^{G_r - G_i} is split into a row factor e^{G_r} and a column
-// factor e^{-G_i} (reference point: the chunk start), which is exact up to
-// rounding while every |G| in a chunk stays below ~80.
+// factor e^{-G_i} (reference point: the chunk start); this is exact up to
+// rounding while every |G| in a chunk stays below ~80.  The WY factor W is
+// never formed: Tm is applied to the residual V - Kh S instead, which is the
+// same product reassociated and saves one 64x64x128 product and its buffer.
+//
+// Tm is built blockwise: the four 16x16 diagonal blocks by forward
+// substitution in registers (one column per lane), then the off-diagonal
+// blocks X_RI = -X_RR sum_J Akk_RJ X_JI column by column.
 //
 // Work decomposition.  The state recurrence is sequential over chunks, so one
-// workgroup (4 waves) owns one head and walks its chunks in order with the
-// fp32 state resident in MFMA accumulators.  Everything after W and U is
-// independent per value column, so the d_v = 128 columns are split into
-// NSPLIT slices of DV columns; each slice is its own workgroup (the d_k-side
-// work -- G, Aqk, Akk, Tm, W -- is recomputed per slice).  Slices of one head
-// are placed on one XCD so that their reads of q, k, g hit the same L2.
-// All operands live in LDS in the layout their MFMA fetch wants (contraction
-// index contiguous, rows padded by 16 B against bank conflicts); nothing but
-// the inputs, o and the final state touches HBM.
+// workgroup (8 waves) owns one head and walks its chunks in order with the
+// fp32 state resident in MFMA accumulators.  Everything after Tm is
+// independent per value column, so the 128 value columns are split into
+// slices of DV columns, each its own workgroup (the key-side work -- G, Aqk,
+// Akk, Tm -- is recomputed per slice).  Slices of one head are placed on one
+// XCD so that their reads of q, k, g share an L2.  All operands live in LDS in
+// the layout their MFMA fetch wants (contraction index contiguous, rows padded
+// by 16 B against bank conflicts); nothing but the inputs, o and the final
+// state touches HBM.
 //
 // Two instantiations: bf16 inputs use v_mfma_f32_16x16x32_bf16 (fp32
-// accumulate); fp32 inputs use v_mfma_f32_16x16x4_f32 so that fp32 workloads
-// keep fp32 products.  The element type of the LDS operands follows the input.
+// accumulate) with bf16 LDS operands; fp32 inputs use v_mfma_f32_16x16x4_f32
+// with fp32 LDS operands, so fp32 workloads keep fp32 products.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -41,7 +48,9 @@ namespace {
 
 constexpr int C = 64;     // chunk length
 constexpr int DK = 128;   // key / value head dimension
-constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int NW = 8;     // waves per workgroup
+constexpr int NT = 64 * NW;
+constexpr int RPT = C / NW;   // rows per thread in the elementwise phase (8)
 
 // Barrier that orders LDS traffic only: global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -49,17 +58,18 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---- MFMA wrappers -------------------------------------------------------
-// Operand fetch for a 16 x 16 output tile: `p` points at a row-major LDS
-// matrix with pitch `ld` whose rows are the tile's M (or N) index and whose
-// columns are the contraction index.  The two operands of one product use the
-// same per-lane contraction slots, so the product is a plain sum over k.
+// A 16 x 16 output tile D = A B.  `frag_kc` fetches an operand from a row-major
+// LDS matrix whose rows are the tile's M (or N) index and whose columns are the
+// contraction index (pitch `ld`); `frag_mc` (fp32 only) fetches it from the
+// transposed layout.  Both operands of one product use the same per-lane
+// contraction slots, so the product is a plain sum over k.
 // Output: acc[e] holds D[4 * (lane / 16) + e][lane % 16].
 template <typename E> struct Mma;
 
 template <> struct Mma<bf16_t> {
     static constexpr int KS = 32;
     typedef bf16x8 frag_t;
-    __device__ static frag_t frag(const bf16_t* p, int ld, int row0, int k0, int lane) {
+    __device__ static frag_t frag_kc(const bf16_t* p, int ld, int row0, int k0, int lane) {
         return *reinterpret_cast<const bf16x8*>(p + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
     }
     __device__ static f32x4 mma(frag_t a, frag_t b, f32x4 c) {
@@ -70,32 +80,32 @@ template <> struct Mma<bf16_t> {
 template <> struct Mma<float> {
     static constexpr int KS = 4;
     typedef float frag_t;
-    __device__ static frag_t frag(const float* p, int ld, int row0, int k0, int lane) {
+    __device__ static frag_t frag_kc(const float* p, int ld, int row0, int k0, int lane) {
         return p[(row0 + (lane & 15)) * ld + k0 + (lane >> 4)];
+    }
+    __device__ static frag_t frag_mc(const float* p, int ld, int row0, int k0, int lane) {
+        return p[(k0 + (lane >> 4)) * ld + row0 + (lane & 15)];
     }
     __device__ static f32x4 mma(frag_t a, frag_t b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
 };
 
-template <typename E>
-__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const E* A, int lda, int arow0,
-                                          const E* B, int ldb, int brow0, int k0, int k1,
-                                          int lane) {
-    for (int k = k0; k < k1; k += Mma<E>::KS)
-        acc = Mma<E>::mma(Mma<E>::frag(A, lda, arow0, k, lane),
-                          Mma<E>::frag(B, ldb, brow0, k, lane), acc);
-    return acc;
+// acc[t] += A[arow0.., K] * B[brow[t].., K]^T over k in [0, K); A fragments are
+// loaded once and reused for the NB output tiles.
+template <typename E, int K, int NB>
+__device__ __forceinline__ void mma_rows(f32x4 (&acc)[NB], const E* A, int lda, int arow0,
+                                         const E* B, int ldb, const int (&brow)[NB], int lane) {
+    constexpr int UNR = (K / Mma<E>::KS) < 8 ? (K / Mma<E>::KS) : 8;
+#pragma unroll UNR
+    for (int k = 0; k < K; k += Mma<E>::KS) {
+        const auto a = Mma<E>::frag_kc(A, lda, arow0, k, lane);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) acc[t] = Mma<E>::mma(a, Mma<E>::frag_kc(B, ldb, brow[t], k, lane), acc[t]);
+    }
 }
 
-// End of the contraction range over tokens i <= 16R+15, rounded up to the
-// instruction's K (the entries past 16R+15 are zero).
-template <typename E> __device__ __forceinline__ int kend_tri(int R) {
-    const int e = 16 * R + 16;
-    return (e + Mma<E>::KS - 1) / Mma<E>::KS * Mma<E>::KS;
-}
-
-// ---- element pairs ---------------------------------------------------------
+// ---- element pairs and runs ------------------------------------------------
 template <typename E> struct Pair;
 template <> struct Pair<bf16_t> { typedef bf16x2 type; };
 template <> struct Pair<float> { typedef float2 type; };
@@ -116,20 +126,60 @@ template <> __device__ __forceinline__ void store_vec4<bf16_t>(bf16_t* p, f32x4 
 template <> __device__ __forceinline__ void store_vec4<float>(float* p, f32x4 x) {
     *reinterpret_cast<f32x4*>(p) = x;
 }
+template <typename E> __device__ __forceinline__ f32x4 load_vec4(const E* p);
+template <> __device__ __forceinline__ f32x4 load_vec4<bf16_t>(const bf16_t* p) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <> __device__ __forceinline__ f32x4 load_vec4<float>(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
 
-// Store n (multiple of 4) contiguous values.
+// Store N contiguous values (N = 1, 2, 4, 8, ...).
 template <typename E, int N>
 __device__ __forceinline__ void store_run(E* p, const float* x) {
-#pragma unroll
-    for (int i = 0; i < N; i += 4) store_vec4<E>(p + i, f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]});
-}
-template <typename E, int N>
-__device__ __forceinline__ void store_run_small(E* p, const float* x) {
-    if constexpr (N % 4 == 0) {
-        store_run<E, N>(p, x);
-    } else {
-        static_assert(N == 2, "run length");
+    if constexpr (N == 1) {
+        *p = (E)x[0];
+    } else if constexpr (N == 2) {
         *reinterpret_cast<typename Pair<E>::type*>(p) = pack<E>(x[0], x[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) store_vec4<E>(p + i, f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]});
+    }
+}
+
+// ---- UT transform, off-diagonal blocks of one block column -------------------
+// Column I of X = (I + A)^{-1} (A strictly lower, 4x4 blocks of 16, diagonal
+// blocks X_RR already inverted in place in RA):  X_RI = -X_RR sum_{J=I}^{R-1}
+// A_RJ X_JI.  The products are 16x16x16 bf16 MFMAs chained through registers:
+// the D layout of one product (lane holds rows 4*(lane/16)+e of column
+// lane%16) is exactly the B-operand layout of the next.  Each X_RI is written
+// to RT scaled by beta of its column.
+__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
+    bf16x4 r; r[0] = (bf16_t)x[0]; r[1] = (bf16_t)x[1]; r[2] = (bf16_t)x[2]; r[3] = (bf16_t)x[3];
+    return r;
+}
+
+template <int I, int PA, int PT>
+__device__ __forceinline__ void ut_offdiag_column(const float* RA, bf16_t* RT, const float* s_beta, int lane) {
+    const int ln = lane & 15, lg = lane >> 4;
+    auto a_op = [&](int R, int J) {   // A operand: block (R, J) of RA, row-major
+        return to_bf16x4(*reinterpret_cast<const f32x4*>(RA + (16 * R + ln) * PA + 16 * J + 4 * lg));
+    };
+    f32x4 X[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[I][e] = RA[(16 * I + 4 * lg + e) * PA + 16 * I + ln];
+    const float bcol = s_beta[16 * I + ln];
+#pragma unroll
+    for (int R = I + 1; R < 4; ++R) {
+        f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = I; J < R; ++J)
+            Y = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_op(R, J), to_bf16x4(X[J]), Y, 0, 0, 0);
+        X[R] = -__builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_op(R, R), to_bf16x4(Y),
+                                                          f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) RT[(16 * R + 4 * lg + e) * PT + 16 * I + ln] = (bf16_t)(bcol * X[R][e]);
     }
 }
 
@@ -142,41 +192,34 @@ struct Layout {
     static constexpr int P128 = DK + PAD;   // token-major [64][128] rows
     static constexpr int P64 = C + PAD;     // channel-major [*][64] rows
     static constexpr int PA = C + 4;        // fp32 [64][64] rows (== P64 when E is fp32)
-    static constexpr int PZ = 48 + 4;       // fp32 [16][48] scratch rows
     static constexpr int SZ_TOK = C * P128 * ES;
-    static constexpr int SZ_CH = DK * P64 * ES;
-    static constexpr int OFF_R1 = 0;                                  // Qt = e^G q
-    static constexpr int OFF_R2 = OFF_R1 + SZ_TOK;                    // Kbar = e^-G k, then -W
-    static constexpr int OFF_R3 = OFF_R2 + SZ_TOK;                    // Kg, Kg^T, Kt^T
-    static constexpr int OFF_RA = OFF_R3 + (SZ_TOK > SZ_CH ? SZ_TOK : SZ_CH);  // Akk -> Tm (fp32)
-    static constexpr int OFF_RT = OFF_RA + C * PA * 4;               // Tm in E (bf16 only)
-    static constexpr int OFF_RQK = OFF_RT + (kF32 ? 0 : C * P64 * ES);   // Aqk
-    static constexpr int OFF_RV = OFF_RQK + C * P64 * ES;            // (beta v)^T slice
-    static constexpr int OFF_RS = OFF_RV + DV * P64 * ES;            // S^T slice in E
-    static constexpr int OFF_RVN = OFF_RS + DV * P128 * ES;          // Vn^T slice
-    static constexpr int OFF_GAM = OFF_RVN + DV * P64 * ES;          // e^{G_64}
+    static constexpr int OFF_QT = 0;                                  // Qt = e^G q
+    static constexpr int OFF_KH = OFF_QT + SZ_TOK;                    // Kh = e^G k
+    static constexpr int OFF_KB = OFF_KH + SZ_TOK;                    // Kb = e^-G k
+    static constexpr int OFF_KBT = OFF_KB + SZ_TOK;                   // Kb^T (bf16 only)
+    static constexpr int OFF_RA = OFF_KBT + (kF32 ? 0 : DK * P64 * ES);   // Akk -> Tm (fp32)
+    static constexpr int OFF_RT = OFF_RA + C * PA * 4;               // Tm Diag(beta) in E (bf16 only)
+    static constexpr int OFF_QK = OFF_RT + (kF32 ? 0 : C * P64 * ES);    // Aqk
+    static constexpr int OFF_VT = OFF_QK + C * P64 * ES;             // V^T slice
+    static constexpr int OFF_ST = OFF_VT + DV * P64 * ES;            // S^T slice in E
+    static constexpr int OFF_ZT = OFF_ST + DV * P128 * ES;           // (V - Kh S)^T
+    static constexpr int OFF_VN = OFF_ZT + DV * P64 * ES;            // Vn^T
+    static constexpr int OFF_GAM = OFF_VN + DV * P64 * ES;           // e^{G_64}
     static constexpr int OFF_BETA = OFF_GAM + DK * 4;
     static constexpr int OFF_TOT = OFF_BETA + C * 4;                 // per-wave column sums of g
-    static constexpr int OFF_Z = OFF_TOT + 4 * DK * 4;
-    static constexpr int TOTAL = OFF_Z + 16 * PZ * 4;
+    static constexpr int TOTAL = OFF_TOT + NW * DK * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static_assert(!kF32 || P64 == PA, "fp32 Tm aliases Akk");
 };
 
-// Lower-triangular 16x16 tiles (I <= R) of a 64x64 matrix, balanced order.
-__constant__ int kTriI[10] = {0, 1, 2, 3, 0, 1, 2, 0, 1, 0};
-__constant__ int kTriR[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
-__constant__ int kUpI[6] = {1, 2, 3, 2, 3, 3};
-__constant__ int kUpR[6] = {0, 0, 0, 1, 1, 2};
-
 // Per-thread registers of one chunk's inputs (prefetched one chunk ahead).
-//   q/k/g: channels 2cp, 2cp+1, rows 16*wave .. 16*wave+15
+//   q/k/g: channels 2cp, 2cp+1, rows RPT*wave .. RPT*wave + RPT-1
 //   v    : channels 2jp, 2jp+1 of the slice, rows RVR*rgv .. +RVR-1
 template <typename E, int DV>
 struct ChunkIn {
-    static constexpr int RVR = DV / 8;
-    float2 g[16];
-    typename Pair<E>::type q[16], k[16];
+    static constexpr int RVR = DV / 16;
+    float2 g[RPT];
+    typename Pair<E>::type q[RPT], k[RPT];
     typename Pair<E>::type v[RVR];
     float beta;
 };
@@ -191,30 +234,31 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
     using L = Layout<E, DV>;
     using In = ChunkIn<E, DV>;
     using PairT = typename Pair<E>::type;
+    using M = Mma<E>;
     constexpr int NJ = DV / 16;             // value-column tiles in the slice
-    constexpr int NU = 4 * NJ;              // (token-block, column-block) tiles
-    constexpr int NS = 8 * NJ;              // state tiles (128 x DV)
     constexpr int RVR = In::RVR;
     constexpr int VP = DV / 2;              // value channel pairs
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-    E* R1 = reinterpret_cast<E*>(smem + L::OFF_R1);
-    E* R2 = reinterpret_cast<E*>(smem + L::OFF_R2);
-    E* R3 = reinterpret_cast<E*>(smem + L::OFF_R3);
+    E* sQt = reinterpret_cast<E*>(smem + L::OFF_QT);
+    E* sKh = reinterpret_cast<E*>(smem + L::OFF_KH);
+    E* sKb = reinterpret_cast<E*>(smem + L::OFF_KB);
+    E* sKbT = reinterpret_cast<E*>(smem + L::OFF_KBT);
     float* RA = reinterpret_cast<float*>(smem + L::OFF_RA);
     E* RT = reinterpret_cast<E*>(smem + (L::kF32 ? L::OFF_RA : L::OFF_RT));
-    E* RQK = reinterpret_cast<E*>(smem + L::OFF_RQK);
-    E* RV = reinterpret_cast<E*>(smem + L::OFF_RV);
-    E* RS = reinterpret_cast<E*>(smem + L::OFF_RS);
-    E* RVN = reinterpret_cast<E*>(smem + L::OFF_RVN);
+    E* sQK = reinterpret_cast<E*>(smem + L::OFF_QK);
+    E* sVT = reinterpret_cast<E*>(smem + L::OFF_VT);
+    E* sST = reinterpret_cast<E*>(smem + L::OFF_ST);
+    E* sZT = reinterpret_cast<E*>(smem + L::OFF_ZT);
+    E* sVN = reinterpret_cast<E*>(smem + L::OFF_VN);
     float* s_gam = reinterpret_cast<float*>(smem + L::OFF_GAM);
     float* s_beta = reinterpret_cast<float*>(smem + L::OFF_BETA);
     float* s_tot = reinterpret_cast<float*>(smem + L::OFF_TOT);
-    float* s_z = reinterpret_cast<float*>(smem + L::OFF_Z);
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int cp = t & 63;                  // channel pair for q/k/g work
     const int jp = t % VP, rgv = t / VP;    // value pair / row group for v
+    const int ln = lane & 15, lg = lane >> 4;
 
     // Workgroup -> (head, slice), keeping the slices of a head on one XCD
     // (workgroups are dealt to the 8 XCDs round-robin).
@@ -232,8 +276,8 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
     auto load_chunk = [&](int n, In& in) {
         const int tok0 = n * C;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tok = tok0 + 16 * wave + i;
+        for (int i = 0; i < RPT; ++i) {
+            const int tok = tok0 + RPT * wave + i;
             if (tok < T) {
                 const size_t off = hbase + (size_t)tok * tokstride + 2 * cp;
                 in.g[i] = *reinterpret_cast<const float2*>(g + off);
@@ -257,28 +301,18 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
         }
     };
 
-    // ---- state slice in accumulators: tile s = wave + 4m -> (Cb, jb) --------
-    constexpr int MS = (NS + 3) / 4;
-    f32x4 acc_s[MS];
+    // ---- state slice in accumulators: wave w owns rows 16w..16w+15 ------------
+    f32x4 acc_s[NJ];
 #pragma unroll
-    for (int m = 0; m < MS; ++m) {
-        const int s = wave + 4 * m;
-        const int Cb = s / NJ, jb = s % NJ;
-        const int c = 16 * Cb + 4 * (lane >> 4), j = j0 + 16 * jb + (lane & 15);
+    for (int jb = 0; jb < NJ; ++jb) {
+        const int c = 16 * wave + 4 * lg, j = j0 + 16 * jb + ln;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            acc_s[m][e] = (s < NS && S0) ? S0[sbase + (size_t)(c + e) * DK + j] : 0.f;
+        for (int e = 0; e < 4; ++e) acc_s[jb][e] = S0 ? S0[sbase + (size_t)(c + e) * DK + j] : 0.f;
     }
     auto write_state_lds = [&]() {
 #pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int s = wave + 4 * m;
-            if (s < NS) {
-                const int Cb = s / NJ, jb = s % NJ;
-                const int c = 16 * Cb + 4 * (lane >> 4), j = 16 * jb + (lane & 15);
-                store_vec4<E>(RS + j * L::P128 + c, acc_s[m]);
-            }
-        }
+        for (int jb = 0; jb < NJ; ++jb)
+            store_vec4<E>(sST + (16 * jb + ln) * L::P128 + 16 * wave + 4 * lg, acc_s[jb]);
     };
     write_state_lds();
 
@@ -286,212 +320,274 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
     load_chunk(0, in);
 
     for (int n = 0; n < nchunks; ++n) {
-        // ===== E1: cumulative log-decay and the decay-scaled operands =====
-        float G0[16], G1[16];
-        PairT kraw[16];
+        // ===== E: cumulative log-decay and the decay-scaled operands =====
+        float G0[RPT], G1[RPT];
         {
             float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < RPT; ++i) {
                 r0 += in.g[i].x; r1 += in.g[i].y;
                 G0[i] = r0; G1[i] = r1;
-                kraw[i] = in.k[i];
             }
             s_tot[wave * DK + 2 * cp] = r0;
             s_tot[wave * DK + 2 * cp + 1] = r1;
             if (t < C) s_beta[t] = in.beta;
         }
         lds_barrier();
-        float tot0 = 0.f, tot1 = 0.f;
         {
-            float off0 = 0.f, off1 = 0.f;
+            float off0 = 0.f, off1 = 0.f, tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
+            for (int w2 = 0; w2 < NW; ++w2) {
                 const float a0 = s_tot[w2 * DK + 2 * cp], a1 = s_tot[w2 * DK + 2 * cp + 1];
                 if (w2 < wave) { off0 += a0; off1 += a1; }
                 tot0 += a0; tot1 += a1;
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) { G0[i] += off0; G1[i] += off1; }
             if (wave == 0) { s_gam[2 * cp] = exp_fast(tot0); s_gam[2 * cp + 1] = exp_fast(tot1); }
+            float kb0[RPT], kb1[RPT];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 16 * wave + i;
-                const float bt = s_beta[r];
-                const float e0 = exp_fast(G0[i]), e1 = exp_fast(G1[i]);
-                const float n0 = exp_fast(-G0[i]), n1 = exp_fast(-G1[i]);
+            for (int i = 0; i < RPT; ++i) {
+                const int r = RPT * wave + i;
+                const float Ga = G0[i] + off0, Gb = G1[i] + off1;
+                const float e0 = exp_fast(Ga), e1 = exp_fast(Gb);
+                const float n0 = exp_fast(-Ga), n1 = exp_fast(-Gb);
                 const float2 qf = unpack(in.q[i]), kf = unpack(in.k[i]);
-                *reinterpret_cast<PairT*>(R1 + r * L::P128 + 2 * cp) = pack<E>(qf.x * e0, qf.y * e1);
-                *reinterpret_cast<PairT*>(R2 + r * L::P128 + 2 * cp) = pack<E>(kf.x * n0, kf.y * n1);
-                *reinterpret_cast<PairT*>(R3 + r * L::P128 + 2 * cp) = pack<E>(bt * kf.x * e0, bt * kf.y * e1);
+                kb0[i] = kf.x * n0; kb1[i] = kf.y * n1;
+                *reinterpret_cast<PairT*>(sQt + r * L::P128 + 2 * cp) = pack<E>(qf.x * e0, qf.y * e1);
+                *reinterpret_cast<PairT*>(sKh + r * L::P128 + 2 * cp) = pack<E>(kf.x * e0, kf.y * e1);
+                *reinterpret_cast<PairT*>(sKb + r * L::P128 + 2 * cp) = pack<E>(kb0[i], kb1[i]);
             }
-            // (beta v)^T: rows = value channels of the slice, columns = tokens
+            if constexpr (!L::kF32) {
+                store_run<E, RPT>(sKbT + (2 * cp) * L::P64 + RPT * wave, kb0);
+                store_run<E, RPT>(sKbT + (2 * cp + 1) * L::P64 + RPT * wave, kb1);
+            }
             float va[RVR], vb[RVR];
 #pragma unroll
             for (int i = 0; i < RVR; ++i) {
-                const float bt = s_beta[RVR * rgv + i];
                 const float2 vf = unpack(in.v[i]);
-                va[i] = bt * vf.x; vb[i] = bt * vf.y;
+                va[i] = vf.x; vb[i] = vf.y;
             }
-            store_run_small<E, RVR>(RV + (2 * jp) * L::P64 + RVR * rgv, va);
-            store_run_small<E, RVR>(RV + (2 * jp + 1) * L::P64 + RVR * rgv, vb);
+            store_run<E, RVR>(sVT + (2 * jp) * L::P64 + RVR * rgv, va);
+            store_run<E, RVR>(sVT + (2 * jp + 1) * L::P64 + RVR * rgv, vb);
         }
         lds_barrier();
 
         // prefetch the next chunk while this one is computed
         if (n + 1 < nchunks) load_chunk(n + 1, in);
 
-        // ===== M1: Aqk (i <= r) and Akk (i < r), stored row-major [r][i] =====
-        for (int job = wave; job < 20; job += 4) {
-            const bool kk = job >= 10;
-            const int p = kk ? job - 10 : job;
-            const int I = kTriI[p], R = kTriR[p];
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mma<E>(acc, R2, L::P128, 16 * I, kk ? R3 : R1, L::P128, 16 * R, 0, DK, lane);
-            const int r = 16 * R + (lane & 15), i0 = 16 * I + 4 * (lane >> 4);
-            f32x4 val;
+        // ===== M1 (waves 0-3): Aqk, Akk.  P (waves 4-7): Kh S, then Z = V - Kh S =====
+        if (wave < 4) {
+            // Aqk^T / Akk^T tiles (rows i in block I, columns r in block R >= I);
+            // the A operand (Kb rows of block I) is shared by the wave's tiles.
+            auto epilogue = [&](const f32x4& acc, int I, int R, bool kk) {
+                const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
+                f32x4 val;
+                const float bt = kk ? s_beta[r] : 1.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) val[e] = (kk ? (i0 + e < r) : (i0 + e <= r)) ? acc[e] : 0.f;
-            if (kk) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = val;
-            else store_vec4<E>(RQK + r * L::P64 + i0, val);
+                for (int e = 0; e < 4; ++e) val[e] = (kk ? (i0 + e < r) : (i0 + e <= r)) ? bt * acc[e] : 0.f;
+                if (kk) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = val;
+                else store_vec4<E>(sQK + r * L::P64 + i0, val);
+            };
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            if (wave < 2) {               // I = 0, R = 0..3, one matrix per wave
+                const bool kk = wave == 1;
+                f32x4 acc[4] = {z4, z4, z4, z4};
+                const int br[4] = {0, 16, 32, 48};
+                mma_rows<E, DK, 4>(acc, sKb, L::P128, 0, kk ? sKh : sQt, L::P128, br, lane);
+#pragma unroll
+                for (int R = 0; R < 4; ++R) epilogue(acc[R], 0, R, kk);
+            } else if (wave == 2) {       // I = 1, R = 1..3, both matrices
+                f32x4 acc[6] = {z4, z4, z4, z4, z4, z4};
+                {
+                    f32x4 a3[3] = {z4, z4, z4};
+                    const int br[3] = {16, 32, 48};
+                    mma_rows<E, DK, 3>(a3, sKb, L::P128, 16, sQt, L::P128, br, lane);
+                    acc[0] = a3[0]; acc[1] = a3[1]; acc[2] = a3[2];
+                    f32x4 b3[3] = {z4, z4, z4};
+                    mma_rows<E, DK, 3>(b3, sKb, L::P128, 16, sKh, L::P128, br, lane);
+                    acc[3] = b3[0]; acc[4] = b3[1]; acc[5] = b3[2];
+                }
+#pragma unroll
+                for (int R = 1; R < 4; ++R) { epilogue(acc[R - 1], 1, R, false); epilogue(acc[R + 2], 1, R, true); }
+            } else {                      // I = 2 (R = 2, 3) and I = 3 (R = 3), both matrices
+                f32x4 a2[2] = {z4, z4}, b2[2] = {z4, z4};
+                const int br[2] = {32, 48};
+                mma_rows<E, DK, 2>(a2, sKb, L::P128, 32, sQt, L::P128, br, lane);
+                mma_rows<E, DK, 2>(b2, sKb, L::P128, 32, sKh, L::P128, br, lane);
+                f32x4 a1[1] = {z4}, b1[1] = {z4};
+                const int br1[1] = {48};
+                mma_rows<E, DK, 1>(a1, sKb, L::P128, 48, sQt, L::P128, br1, lane);
+                mma_rows<E, DK, 1>(b1, sKb, L::P128, 48, sKh, L::P128, br1, lane);
+                epilogue(a2[0], 2, 2, false); epilogue(a2[1], 2, 3, false);
+                epilogue(b2[0], 2, 2, true); epilogue(b2[1], 2, 3, true);
+                epilogue(a1[0], 3, 3, false); epilogue(b1[0], 3, 3, true);
+                // zero the upper tiles (I > R) of Aqk and Akk
+                for (int u = 0; u < 6; ++u) {
+                    const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
+                    const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
+                    const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
+                    *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = z4;
+                    store_vec4<E>(sQK + r * L::P64 + i0, z4);
+                }
+            }
         }
-        for (int job = wave; job < 12; job += 4) {   // zero upper tiles
-            const bool kk = job >= 6;
-            const int p = kk ? job - 6 : job;
-            const int I = kUpI[p], R = kUpR[p];
-            const int r = 16 * R + (lane & 15), i0 = 16 * I + 4 * (lane >> 4);
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            if (kk) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = z;
-            else store_vec4<E>(RQK + r * L::P64 + i0, z);
+        f32x4 pacc[NJ];
+        if (wave >= 4) {                  // P tiles (R = wave - 4, all column blocks)
+            const int R = wave - 4;
+            int br[NJ];
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) { pacc[jb] = f32x4{0.f, 0.f, 0.f, 0.f}; br[jb] = 16 * jb; }
+            mma_rows<E, DK, NJ>(pacc, sKh, L::P128, 16 * R, sST, L::P128, br, lane);
         }
         lds_barrier();
 
-        // ===== E2: (beta e^G k)^T, channel-major, over the dead Kg =====
-        {
-            float t0[16], t1[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float bt = s_beta[16 * wave + i];
-                const float2 kf = unpack(kraw[i]);
-                t0[i] = bt * kf.x * exp_fast(G0[i]);
-                t1[i] = bt * kf.y * exp_fast(G1[i]);
-            }
-            store_run<E, 16>(R3 + (2 * cp) * L::P64 + 16 * wave, t0);
-            store_run<E, 16>(R3 + (2 * cp + 1) * L::P64 + 16 * wave, t1);
-        }
-
-        // ===== UT transform: Tm = (I + Akk)^{-1}, in place in RA (fp32) =====
-        // (a) the four 16x16 diagonal blocks, one column per lane of wave 0
+        // ===== UT transform, diagonal blocks (wave 0) | Z = V - Kh S (waves 4-7) =====
         if (wave == 0) {
-            const int blk = lane >> 4, m = lane & 15;
-            float* A = RA + 16 * blk * L::PA + 16 * blk;
+            // column m of X = (I + A_bb)^{-1} for block bb, right-looking substitution
+            const int bb = lane >> 4, m = lane & 15;
+            float* A = RA + 16 * bb * L::PA + 16 * bb;
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = (i == m) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 1; i < 16; ++i) {
-                float s = 0.f;
+            for (int j = 0; j < 15; ++j) {
 #pragma unroll
-                for (int j = 0; j < i; ++j) s += A[i * L::PA + j] * x[j];
-                if (i > m) x[i] = -s;
+                for (int i = j + 1; i < 16; ++i) x[i] -= A[i * L::PA + j] * x[j];
+                __builtin_amdgcn_sched_barrier(0);   // keep one column of loads in flight
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) A[i * L::PA + m] = x[i];
+        } else if (wave >= 4) {
+            const int R = wave - 4;
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) {
+                const int j = 16 * jb + ln, r = 16 * R + 4 * lg;
+                const f32x4 vv = load_vec4<E>(sVT + j * L::P64 + r);
+                store_vec4<E>(sZT + j * L::P64 + r, vv - pacc[jb]);
+            }
         }
         lds_barrier();
-        // (b) block rows R = 1..3: X_RI = X_RR * Z, Z = -sum_J Akk_RJ X_JI
-        for (int R = 1; R < 4; ++R) {
-            const int w16 = 16 * R;
-            for (int e = t; e < 16 * w16; e += NT) {
-                const int r = e / w16, i = e % w16;
-                const float* arow = RA + (w16 + r) * L::PA;
-                float s = 0.f;
-                for (int j = i; j < w16; ++j) s += arow[j] * RA[j * L::PA + i];
-                s_z[r * L::PZ + i] = -s;
-            }
-            lds_barrier();
-            for (int e = t; e < 16 * w16; e += NT) {
-                const int r = e / w16, i = e % w16;
-                const float* xrow = RA + (w16 + r) * L::PA + w16;
-                float s = 0.f;
-                for (int rp = 0; rp <= r; ++rp) s += xrow[rp] * s_z[rp * L::PZ + i];
-                RA[(w16 + r) * L::PA + i] = s;
-            }
-            lds_barrier();
-        }
+
+        // ===== UT transform, off-diagonal blocks; then Tm Diag(beta) in E =====
         if constexpr (!L::kF32) {
-            for (int e = t; e < C * 16; e += NT) {
-                const int r = e >> 4, c4 = (e & 15) * 4;
-                store_vec4<E>(RT + r * L::P64 + c4, *reinterpret_cast<const f32x4*>(RA + r * L::PA + c4));
+            // Column I = wave (0..2): X_RI = -X_RR sum_{J=I}^{R-1} A_RJ X_JI, chained
+            // through registers with 16x16x16 bf16 MFMAs (the D layout of one
+            // product is the B layout of the next).  Results go straight to RT,
+            // scaled by beta of their column.  Wave 3 writes the diagonal blocks,
+            // waves 4-7 clear the upper blocks of RT.
+            if (wave == 0) ut_offdiag_column<0, L::PA, L::P64>(RA, RT, s_beta, lane);
+            else if (wave == 1) ut_offdiag_column<1, L::PA, L::P64>(RA, RT, s_beta, lane);
+            else if (wave == 2) ut_offdiag_column<2, L::PA, L::P64>(RA, RT, s_beta, lane);
+            else if (wave == 3) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int r = 16 * bb + 4 * lg;
+                    const float bcol = s_beta[16 * bb + ln];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        RT[(r + e) * L::P64 + 16 * bb + ln] = (E)(bcol * RA[(r + e) * L::PA + 16 * bb + ln]);
+                }
+            } else {
+                for (int u = wave - 4; u < 6; u += 4) {
+                    const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
+                    const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
+                    store_vec4<E>(RT + (16 * R + ln) * L::P64 + 16 * I + 4 * lg, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+            }
+            lds_barrier();
+        } else {
+            // fp32: block rows R = 1..3 by plain dot products, in place in RA,
+            // then scale the columns by beta.
+            float* s_z = reinterpret_cast<float*>(sVN);   // Vn^T is not in use yet
+            static_assert(16 * 48 * 4 <= DV * L::P64 * L::ES, "scratch fits in the Vn^T buffer");
+            for (int R = 1; R < 4; ++R) {
+                const int w16 = 16 * R;
+                for (int e = t; e < 16 * w16; e += NT) {   // Z = -sum_J A_RJ X_J.
+                    const int r = e / w16, i = e % w16;
+                    const float* arow = RA + (w16 + r) * L::PA;
+                    float s = 0.f;
+                    for (int j = i; j < w16; ++j) s += arow[j] * RA[j * L::PA + i];
+                    s_z[e] = -s;
+                }
+                lds_barrier();
+                for (int e = t; e < 16 * w16; e += NT) {   // X_R. = X_RR Z
+                    const int r = e / w16, i = e % w16;
+                    const float* xrow = RA + (w16 + r) * L::PA + w16;
+                    float s = 0.f;
+                    for (int rp = 0; rp <= r; ++rp) s += xrow[rp] * s_z[rp * w16 + i];
+                    RA[(w16 + r) * L::PA + i] = s;
+                }
+                lds_barrier();
+            }
+            for (int e = t; e < C * C; e += NT) {
+                const int r = e >> 6, i = e & 63;
+                RA[r * L::PA + i] *= s_beta[i];
             }
             lds_barrier();
         }
 
-        // ===== M2: -W = -(Tm Kg) token-major over Kbar; U = Tm (beta v) =====
-        for (int job = wave; job < 32; job += 4) {
-            const int Cb = job & 7, R = job >> 3;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mma<E>(acc, R3, L::P64, 16 * Cb, RT, L::P64, 16 * R, 0, kend_tri<E>(R), lane);
-            const int c = 16 * Cb + 4 * (lane >> 4), r = 16 * R + (lane & 15);
-            store_vec4<E>(R2 + r * L::P128 + c, -acc);
-        }
-        constexpr int MU = (NU + 3) / 4;
-        f32x4 uacc[MU];
-#pragma unroll
-        for (int m = 0; m < MU; ++m) {
-            const int u = wave + 4 * m;
-            uacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (u < NU) {
-                const int R = u / NJ, jb = u % NJ;
-                uacc[m] = tile_mma<E>(uacc[m], RT, L::P64, 16 * R, RV, L::P64, 16 * jb, 0, kend_tri<E>(R), lane);
-            }
-        }
-        lds_barrier();
-
-        // ===== E3: (e^{G_64 - G} k)^T over the dead Kg^T; M3a: Vn = U - W S =====
+        // ===== Vn = Tm Diag(beta) Z; tiles (R, jb), A operand shared per wave =====
         {
-            float t0[16], t1[16];
+            constexpr int NVT = 4 * NJ;            // tiles
+            constexpr int PER = (NVT + NW - 1) / NW;
+            if (wave < NVT) {
+                const int R = wave % 4;
+                f32x4 acc[PER];
+                int br[PER];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float2 kf = unpack(kraw[i]);
-                t0[i] = kf.x * exp_fast(tot0 - G0[i]);
-                t1[i] = kf.y * exp_fast(tot1 - G1[i]);
-            }
-            store_run<E, 16>(R3 + (2 * cp) * L::P64 + 16 * wave, t0);
-            store_run<E, 16>(R3 + (2 * cp + 1) * L::P64 + 16 * wave, t1);
-        }
+                for (int u = 0; u < PER; ++u) {
+                    acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const int jb = (wave / 4) + 2 * u;
+                    br[u] = 16 * (jb < NJ ? jb : 0);
+                }
+                mma_rows<E, C, PER>(acc, RT, L::P64, 16 * R, sZT, L::P64, br, lane);
 #pragma unroll
-        for (int m = 0; m < MU; ++m) {
-            const int u = wave + 4 * m;
-            if (u < NU) {
-                const int R = u / NJ, jb = u % NJ;
-                f32x4 acc = tile_mma<E>(uacc[m], R2, L::P128, 16 * R, RS, L::P128, 16 * jb, 0, DK, lane);
-                const int r = 16 * R + 4 * (lane >> 4), j = 16 * jb + (lane & 15);
-                store_vec4<E>(RVN + j * L::P64 + r, acc);
+                for (int u = 0; u < PER; ++u) {
+                    const int jb = (wave / 4) + 2 * u;
+                    if (jb < NJ) store_vec4<E>(sVN + (16 * jb + ln) * L::P64 + 16 * R + 4 * lg, acc[u]);
+                }
             }
         }
         lds_barrier();
 
-        // ===== M3b: O = Qt S + Aqk Vn (written to HBM); S update =====
-        for (int u = wave; u < NU; u += 4) {
-            const int R = u / NJ, jb = u % NJ;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mma<E>(acc, RS, L::P128, 16 * jb, R1, L::P128, 16 * R, 0, DK, lane);
-            acc = tile_mma<E>(acc, RVN, L::P64, 16 * jb, RQK, L::P64, 16 * R, 0, kend_tri<E>(R), lane);
-            const int j = 16 * jb + 4 * (lane >> 4), r = 16 * R + (lane & 15);
-            const int tok = n * C + r;
-            if (tok < T) store_vec4<E>(o + hbase + (size_t)tok * tokstride + j0 + j, acc);
-        }
+        // ===== O = Qt S + Aqk Vn (to HBM) | S <- Diag(gamma) (S + Kb^T Vn) =====
+        {
+            constexpr int NOT = 4 * NJ;
+            constexpr int PER = (NOT + NW - 1) / NW;
+            const int ot0 = PER * wave;
+            if (ot0 < NOT) {
+                const int jb = ot0 / 4;
+                f32x4 acc[PER];
+                int br[PER];
 #pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int s = wave + 4 * m;
-            if (s < NS) {
-                const int Cb = s / NJ, jb = s % NJ;
-                const int c = 16 * Cb + 4 * (lane >> 4);
+                for (int u = 0; u < PER; ++u) { acc[u] = f32x4{0.f, 0.f, 0.f, 0.f}; br[u] = 16 * ((ot0 + u) % 4); }
+                mma_rows<E, DK, PER>(acc, sST, L::P128, 16 * jb, sQt, L::P128, br, lane);
+                mma_rows<E, C, PER>(acc, sVN, L::P64, 16 * jb, sQK, L::P64, br, lane);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc_s[m][e] *= s_gam[c + e];
-                acc_s[m] = tile_mma<E>(acc_s[m], R3, L::P64, 16 * Cb, RVN, L::P64, 16 * jb, 0, C, lane);
+                for (int u = 0; u < PER; ++u) {
+                    const int r = br[u] + ln, tok = n * C + r;
+                    if (tok < T) store_vec4<E>(o + hbase + (size_t)tok * tokstride + j0 + 16 * jb + 4 * lg, acc[u]);
+                }
             }
+            int br[NJ];
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) br[jb] = 16 * jb;
+            if constexpr (L::kF32) {
+                // A operand Kb^T read from the token-major Kb
+#pragma unroll
+                for (int kk = 0; kk < C; kk += M::KS) {
+                    const float a = M::frag_mc(sKb, L::P128, 16 * wave, kk, lane);
+#pragma unroll
+                    for (int jb = 0; jb < NJ; ++jb)
+                        acc_s[jb] = M::mma(a, M::frag_kc(sVN, L::P64, br[jb], kk, lane), acc_s[jb]);
+                }
+            } else {
+                mma_rows<E, C, NJ>(acc_s, sKbT, L::P64, 16 * wave, sVN, L::P64, br, lane);
+            }
+            const int c = 16 * wave + 4 * lg;
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc_s[jb][e] *= s_gam[c + e];
         }
         lds_barrier();
         write_state_lds();
@@ -499,14 +595,10 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
 
     if (S_T) {
 #pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int s = wave + 4 * m;
-            if (s < NS) {
-                const int Cb = s / NJ, jb = s % NJ;
-                const int c = 16 * Cb + 4 * (lane >> 4), j = j0 + 16 * jb + (lane & 15);
+        for (int jb = 0; jb < NJ; ++jb) {
+            const int c = 16 * wave + 4 * lg, j = j0 + 16 * jb + ln;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S_T[sbase + (size_t)(c + e) * DK + j] = acc_s[m][e];
-            }
+            for (int e = 0; e < 4; ++e) S_T[sbase + (size_t)(c + e) * DK + j] = acc_s[jb][e];
         }
     }
 }
