@@ -43,14 +43,18 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <type_traits>
+
 namespace kda {
 namespace {
 
 constexpr int C = 64;     // chunk length
 constexpr int DK = 128;   // key / value head dimension
-constexpr int NW = 8;     // waves per workgroup
+constexpr int NW = 8;     // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;
-constexpr int RPT = C / NW;   // rows per thread in the elementwise phase (8)
+constexpr int RPT = C / NW;   // rows per wave in the elementwise phase (8)
+constexpr int RPL = RPT / 4;  // rows per lane in the elementwise phase (2)
+constexpr float LOG2E = 1.4426950408889634f;
 
 // Barrier that orders LDS traffic only: global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -96,7 +100,7 @@ template <> struct Mma<float> {
 template <typename E, int K, int NB>
 __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NB], const E* A, int lda, int arow0,
                                          const E* B, int ldb, const int (&brow)[NB], int lane) {
-    constexpr int UNR = (K / Mma<E>::KS) < 8 ? (K / Mma<E>::KS) : 8;
+    constexpr int UNR = (K / Mma<E>::KS) < 2 ? (K / Mma<E>::KS) : 2;
 #pragma unroll UNR
     for (int k = 0; k < K; k += Mma<E>::KS) {
         const auto a = Mma<E>::frag_kc(A, lda, arow0, k, lane);
@@ -183,6 +187,41 @@ __device__ __forceinline__ void ut_offdiag_column(const float* RA, bf16_t* RT, c
     }
 }
 
+// Eight consecutive elements (one 16-byte load for bf16, two for fp32).
+template <typename E> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    bf16x8 x;
+    __device__ __forceinline__ void load(const bf16_t* p) { x = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ float operator[](int i) const { return (float)x[i]; }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const f32x4*>(p)[0];
+        b = reinterpret_cast<const f32x4*>(p)[1];
+    }
+    __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+struct Raw8f {   // eight fp32 values (the log-decay)
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const f32x4*>(p)[0];
+        b = reinterpret_cast<const f32x4*>(p)[1];
+    }
+    __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+template <typename E> __device__ __forceinline__ void store8(E* p, const float* x);
+template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* x) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16_t)x[i];
+    *reinterpret_cast<bf16x8*>(p) = v;
+}
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* x) {
+    reinterpret_cast<f32x4*>(p)[0] = f32x4{x[0], x[1], x[2], x[3]};
+    reinterpret_cast<f32x4*>(p)[1] = f32x4{x[4], x[5], x[6], x[7]};
+}
+
 // ---- LDS layout -------------------------------------------------------------
 template <typename E, int DV>
 struct Layout {
@@ -194,14 +233,15 @@ struct Layout {
     static constexpr int PA = C + 4;        // fp32 [64][64] rows (== P64 when E is fp32)
     static constexpr int SZ_TOK = C * P128 * ES;
     static constexpr int OFF_QT = 0;                                  // Qt = e^G q
-    static constexpr int OFF_KH = OFF_QT + SZ_TOK;                    // Kh = e^G k
+    static constexpr int OFF_KH = OFF_QT + SZ_TOK;                    // Kh = e^G k (right after Qt)
     static constexpr int OFF_KB = OFF_KH + SZ_TOK;                    // Kb = e^-G k
     static constexpr int OFF_KBT = OFF_KB + SZ_TOK;                   // Kb^T (bf16 only)
     static constexpr int OFF_RA = OFF_KBT + (kF32 ? 0 : DK * P64 * ES);   // Akk -> Tm (fp32)
     static constexpr int OFF_RT = OFF_RA + C * PA * 4;               // Tm Diag(beta) in E (bf16 only)
     static constexpr int OFF_QK = OFF_RT + (kF32 ? 0 : C * P64 * ES);    // Aqk
-    static constexpr int OFF_VT = OFF_QK + C * P64 * ES;             // V^T slice
-    static constexpr int OFF_ST = OFF_VT + DV * P64 * ES;            // S^T slice in E
+    static constexpr int PV = DV + PAD;     // token-major [64][DV] rows
+    static constexpr int OFF_V = OFF_QK + C * P64 * ES;              // V slice, token-major
+    static constexpr int OFF_ST = OFF_V + C * PV * ES;               // S^T slice in E
     static constexpr int OFF_ZT = OFF_ST + DV * P128 * ES;           // (V - Kh S)^T
     static constexpr int OFF_VN = OFF_ZT + DV * P64 * ES;            // Vn^T
     static constexpr int OFF_GAM = OFF_VN + DV * P64 * ES;           // e^{G_64}
@@ -210,34 +250,48 @@ struct Layout {
     static constexpr int TOTAL = OFF_TOT + NW * DK * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static_assert(!kF32 || P64 == PA, "fp32 Tm aliases Akk");
+    // Kb^T (channel-major, 64 tokens per row) is stored with its 8-token
+    // blocks XOR-swizzled by bits 3..5 of the channel, so that the elementwise
+    // phase (lanes 8 channels apart) writes it without bank conflicts while the
+    // MFMA fetch (8 consecutive channels, one 8-token block) stays conflict-free.
+    static constexpr int PDT = 16 + 4;      // fp32 rows of the transposed diagonal blocks
+    static_assert(4 * (DV / 16) * 64 * 16 <= SZ_TOK, "parked output tiles fit in the Kh buffer");
+    static_assert(kF32 || C * PDT * 4 <= C * P64 * ES, "transposed blocks fit in the Tm buffer");
+    __device__ static constexpr int kbt(int c, int i) {
+        return c * P64 + ((((i >> 3) ^ ((c >> 3) & 7)) << 3) | (i & 7));
+    }
 };
 
-// Per-thread registers of one chunk's inputs (prefetched one chunk ahead).
-//   q/k/g: channels 2cp, 2cp+1, rows RPT*wave .. RPT*wave + RPT-1
-//   v    : channels 2jp, 2jp+1 of the slice, rows RVR*rgv .. +RVR-1
+// Per-thread registers of one chunk's inputs (prefetched one chunk ahead),
+// all fetched with 16-byte loads:
+//   q/k/g: channels 8cg .. 8cg+7, rows RPT*wave + RPL*rq + i (i < RPL)
+//   v    : channels 8vg .. 8vg+7 of the slice, rows RVR*vr + i (i < RVR)
 template <typename E, int DV>
 struct ChunkIn {
-    static constexpr int RVR = DV / 16;
-    float2 g[RPT];
-    typename Pair<E>::type q[RPT], k[RPT];
-    typename Pair<E>::type v[RVR];
-    float beta;
+    static constexpr int VL = DV / 8;                   // lanes per value row
+    static constexpr int RVR = (64 * VL + NT - 1) / NT; // value rows per thread
+    Raw8f g[RPL];
+    Raw8<E> q[RPL], k[RPL];
+    Raw8<E> v[RVR];
+    E beta;
 };
 
 template <typename E, int DV>
 __global__ void __launch_bounds__(NT)
-chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-                 const float* __restrict__ g, const E* __restrict__ beta,
-                 const float* __restrict__ S0, E* __restrict__ o, float* __restrict__ S_T,
-                 int T, int H, int nsplit)
+chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* beta,
+                 const float* S0, E* o, float* S_T, int T, int H, int nsplit)
 {
+    // (No __restrict__ on the inputs: the LDS barriers are asm statements with
+    // a memory clobber, and without restrict the compiler keeps the prefetch
+    // loads where they are written instead of sinking them towards their use.)
     using L = Layout<E, DV>;
     using In = ChunkIn<E, DV>;
     using PairT = typename Pair<E>::type;
     using M = Mma<E>;
     constexpr int NJ = DV / 16;             // value-column tiles in the slice
     constexpr int RVR = In::RVR;
-    constexpr int VP = DV / 2;              // value channel pairs
+    constexpr int NO = 4 * NJ;              // output tiles (jb, R)
+    constexpr int MO = (NO + NW - 2) / (NW - 1);   // output tiles per wave (waves 1..NW-1)
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
     E* sQt = reinterpret_cast<E*>(smem + L::OFF_QT);
@@ -246,8 +300,14 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
     E* sKbT = reinterpret_cast<E*>(smem + L::OFF_KBT);
     float* RA = reinterpret_cast<float*>(smem + L::OFF_RA);
     E* RT = reinterpret_cast<E*>(smem + (L::kF32 ? L::OFF_RA : L::OFF_RT));
+    // transposed diagonal blocks of Akk, [block][j][i] = Akk_block[i][j]; lives
+    // in the Tm buffer, which is only written after the substitution
+    float* sDT = reinterpret_cast<float*>(smem + L::OFF_RT);
+    // inter-chunk output tiles Qt S (fp32, one f32x4 per lane per tile), parked
+    // in the Kh buffer, which is dead once Akk and Kh S are formed
+    float* sOI = reinterpret_cast<float*>(smem + L::OFF_KH);
     E* sQK = reinterpret_cast<E*>(smem + L::OFF_QK);
-    E* sVT = reinterpret_cast<E*>(smem + L::OFF_VT);
+    E* sV = reinterpret_cast<E*>(smem + L::OFF_V);
     E* sST = reinterpret_cast<E*>(smem + L::OFF_ST);
     E* sZT = reinterpret_cast<E*>(smem + L::OFF_ZT);
     E* sVN = reinterpret_cast<E*>(smem + L::OFF_VN);
@@ -255,9 +315,10 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
     float* s_beta = reinterpret_cast<float*>(smem + L::OFF_BETA);
     float* s_tot = reinterpret_cast<float*>(smem + L::OFF_TOT);
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int cp = t & 63;                  // channel pair for q/k/g work
-    const int jp = t % VP, rgv = t / VP;    // value pair / row group for v
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform per wave
+    const int cg = lane & 15, rq = lane >> 4;   // 8-channel group and row quad for q/k/g
+    const int vg = t % In::VL, vr = t / In::VL; // 8-channel group and row group for v
     const int ln = lane & 15, lg = lane >> 4;
 
     // Workgroup -> (head, slice), keeping the slices of a head on one XCD
@@ -273,35 +334,30 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
     const size_t sbase = (size_t)head * DK * DK;                   // state of this head
     const int nchunks = (T + C - 1) / C;
 
+    // Prefetch of one chunk into registers.  Branch-free: rows past T read the
+    // last valid token (always in bounds) and are zeroed when consumed, so no
+    // load result is needed before the next chunk starts.
+    const E* betap = beta + (size_t)b * T * H + h;
     auto load_chunk = [&](int n, In& in) {
         const int tok0 = n * C;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int tok = tok0 + RPT * wave + i;
-            if (tok < T) {
-                const size_t off = hbase + (size_t)tok * tokstride + 2 * cp;
-                in.g[i] = *reinterpret_cast<const float2*>(g + off);
-                in.q[i] = *reinterpret_cast<const PairT*>(q + off);
-                in.k[i] = *reinterpret_cast<const PairT*>(k + off);
-            } else {
-                in.g[i] = make_float2(0.f, 0.f);
-                in.q[i] = pack<E>(0.f, 0.f);
-                in.k[i] = pack<E>(0.f, 0.f);
-            }
+        for (int i = 0; i < RPL; ++i) {
+            const int tok = min(tok0 + RPT * wave + RPL * rq + i, T - 1);
+            const size_t off = hbase + (size_t)tok * tokstride + 8 * cg;
+            in.g[i].load(g + off);
+            in.q[i].load(q + off);
+            in.k[i].load(k + off);
         }
 #pragma unroll
         for (int i = 0; i < RVR; ++i) {
-            const int tok = tok0 + RVR * rgv + i;
-            in.v[i] = tok < T ? *reinterpret_cast<const PairT*>(v + hbase + (size_t)tok * tokstride + j0 + 2 * jp)
-                              : pack<E>(0.f, 0.f);
+            const int tok = min(tok0 + RVR * vr + i, T - 1);
+            if (RVR * vr + i < C)
+                in.v[i].load(v + hbase + (size_t)tok * tokstride + j0 + 8 * vg);
         }
-        if (t < C) {
-            const int tok = tok0 + t;
-            in.beta = tok < T ? to_f32(beta[((size_t)b * T + tok) * H + h]) : 0.f;
-        }
+        in.beta = betap[(size_t)min(tok0 + lane, T - 1) * H];
     };
 
-    // ---- state slice in accumulators: wave w owns rows 16w..16w+15 ------------
+    // ---- state slice in accumulators: wave w owns rows 16w .. 16w+15 ----------
     f32x4 acc_s[NJ];
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
@@ -318,66 +374,107 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
 
     In in;
     load_chunk(0, in);
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
     for (int n = 0; n < nchunks; ++n) {
-        // ===== E: cumulative log-decay and the decay-scaled operands =====
-        float G0[RPT], G1[RPT];
-        {
-            float r0 = 0.f, r1 = 0.f;
+        const bool full = (n + 1) * C <= T;     // uniform: no row of this chunk is past T
+
+        // ===== E: cumulative log2-decay and the decay-scaled operands =====
+        // G is kept in log2 units so that 2^G = e^{sum g}.  Each lane owns
+        // 8 channels x 4 consecutive rows; the prefix over rows is local, then
+        // across the 4 row quads of a wave (shuffles), then across waves (LDS).
+        // Full chunks take a path without per-row masking.
+        auto ephase = [&](auto masked_t) {
+            constexpr bool MASKED = decltype(masked_t)::value;
+            auto row_ok = [&](int r) { return !MASKED || n * C + r < T; };
+            const int r0 = RPT * wave + RPL * rq;
+            float G[RPL][8];
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                r0 += in.g[i].x; r1 += in.g[i].y;
-                G0[i] = r0; G1[i] = r1;
+            for (int c = 0; c < 8; ++c) {
+                float run = 0.f;
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) {
+                    const float gi = in.g[i][c] * LOG2E;
+                    run += row_ok(r0 + i) ? gi : 0.f;
+                    G[i][c] = run;
+                }
+                float inc = run;                       // inclusive scan over rq
+                float up = __shfl_up(inc, 16);
+                inc += rq >= 1 ? up : 0.f;
+                up = __shfl_up(inc, 32);
+                inc += rq >= 2 ? up : 0.f;
+                const float excl = inc - run;
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) G[i][c] += excl;
+                if (rq == 3) s_tot[wave * DK + 8 * cg + c] = inc;
             }
-            s_tot[wave * DK + 2 * cp] = r0;
-            s_tot[wave * DK + 2 * cp + 1] = r1;
-            if (t < C) s_beta[t] = in.beta;
-        }
-        lds_barrier();
-        {
-            float off0 = 0.f, off1 = 0.f, tot0 = 0.f, tot1 = 0.f;
+            if (wave == 0) s_beta[lane] = row_ok(lane) ? to_f32(in.beta) : 0.f;
+            lds_barrier();
+            // per channel: exclusive prefix of the wave totals, in place, and e^{G_64}
+            if (t < DK) {
+                float acc = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) {
-                const float a0 = s_tot[w2 * DK + 2 * cp], a1 = s_tot[w2 * DK + 2 * cp + 1];
-                if (w2 < wave) { off0 += a0; off1 += a1; }
-                tot0 += a0; tot1 += a1;
+                for (int w2 = 0; w2 < NW; ++w2) {
+                    const float a = s_tot[w2 * DK + t];
+                    s_tot[w2 * DK + t] = acc;
+                    acc += a;
+                }
+                s_gam[t] = __builtin_amdgcn_exp2f(acc);
             }
-            if (wave == 0) { s_gam[2 * cp] = exp_fast(tot0); s_gam[2 * cp + 1] = exp_fast(tot1); }
-            float kb0[RPT], kb1[RPT];
+            lds_barrier();
+            {
+                const f32x4 o0 = *reinterpret_cast<const f32x4*>(s_tot + wave * DK + 8 * cg);
+                const f32x4 o1 = *reinterpret_cast<const f32x4*>(s_tot + wave * DK + 8 * cg + 4);
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int r = RPT * wave + i;
-                const float Ga = G0[i] + off0, Gb = G1[i] + off1;
-                const float e0 = exp_fast(Ga), e1 = exp_fast(Gb);
-                const float n0 = exp_fast(-Ga), n1 = exp_fast(-Gb);
-                const float2 qf = unpack(in.q[i]), kf = unpack(in.k[i]);
-                kb0[i] = kf.x * n0; kb1[i] = kf.y * n1;
-                *reinterpret_cast<PairT*>(sQt + r * L::P128 + 2 * cp) = pack<E>(qf.x * e0, qf.y * e1);
-                *reinterpret_cast<PairT*>(sKh + r * L::P128 + 2 * cp) = pack<E>(kf.x * e0, kf.y * e1);
-                *reinterpret_cast<PairT*>(sKb + r * L::P128 + 2 * cp) = pack<E>(kb0[i], kb1[i]);
+                for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) { G[i][c] += o0[c]; G[i][c + 4] += o1[c]; }
+            }
+            float kb[RPL][8];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const int r = r0 + i;
+                const bool ok = row_ok(r);
+                float qe[8], ke[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float e = __builtin_amdgcn_exp2f(G[i][c]), ne = __builtin_amdgcn_exp2f(-G[i][c]);
+                    const float qv = ok ? in.q[i][c] : 0.f, kv = ok ? in.k[i][c] : 0.f;
+                    qe[c] = qv * e; ke[c] = kv * e; kb[i][c] = kv * ne;
+                }
+                store8<E>(sQt + r * L::P128 + 8 * cg, qe);
+                store8<E>(sKh + r * L::P128 + 8 * cg, ke);
+                store8<E>(sKb + r * L::P128 + 8 * cg, kb[i]);
             }
             if constexpr (!L::kF32) {
-                store_run<E, RPT>(sKbT + (2 * cp) * L::P64 + RPT * wave, kb0);
-                store_run<E, RPT>(sKbT + (2 * cp + 1) * L::P64 + RPT * wave, kb1);
-            }
-            float va[RVR], vb[RVR];
 #pragma unroll
-            for (int i = 0; i < RVR; ++i) {
-                const float2 vf = unpack(in.v[i]);
-                va[i] = vf.x; vb[i] = vf.y;
+                for (int c = 0; c < 8; ++c) {
+                    float col[RPL];
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) col[i] = kb[i][c];
+                    store_run<E, RPL>(sKbT + L::kbt(8 * cg + c, r0), col);
+                }
             }
-            store_run<E, RVR>(sVT + (2 * jp) * L::P64 + RVR * rgv, va);
-            store_run<E, RVR>(sVT + (2 * jp + 1) * L::P64 + RVR * rgv, vb);
-        }
+            if (RVR * vr < C) {
+#pragma unroll
+                for (int i = 0; i < RVR; ++i) {
+                    const bool ok = row_ok(RVR * vr + i);
+                    float row[8];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) row[c] = ok ? in.v[i][c] : 0.f;
+                    store8<E>(sV + (RVR * vr + i) * L::PV + 8 * vg, row);
+                }
+            }
+        };
+        if (full) ephase(std::false_type{});
+        else ephase(std::true_type{});
         lds_barrier();
 
-        // prefetch the next chunk while this one is computed
-        if (n + 1 < nchunks) load_chunk(n + 1, in);
-
-        // ===== M1 (waves 0-3): Aqk, Akk.  P (waves 4-7): Kh S, then Z = V - Kh S =====
-        if (wave < 4) {
-            // Aqk^T / Akk^T tiles (rows i in block I, columns r in block R >= I);
-            // the A operand (Kb rows of block I) is shared by the wave's tiles.
+        // ===== M1: Aqk, Akk (waves 0-3) | P = Kh S, Z = V - P (waves 4-7) =====
+        {
+            // Aqk^T / Akk^T tiles: rows i in block I (A operand = Kb rows, shared
+            // by the wave's tiles), columns r in block R >= I.  Kh sits right
+            // after Qt in LDS, so Kh row r is row 64 + r of the Qt base.
             auto epilogue = [&](const f32x4& acc, int I, int R, bool kk) {
                 const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
                 f32x4 val;
@@ -386,42 +483,51 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
                 for (int e = 0; e < 4; ++e) val[e] = (kk ? (i0 + e < r) : (i0 + e <= r)) ? bt * acc[e] : 0.f;
                 if (kk) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = val;
                 else store_vec4<E>(sQK + r * L::P64 + i0, val);
-            };
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            if (wave < 2) {               // I = 0, R = 0..3, one matrix per wave
-                const bool kk = wave == 1;
-                f32x4 acc[4] = {z4, z4, z4, z4};
-                const int br[4] = {0, 16, 32, 48};
-                mma_rows<E, DK, 4>(acc, sKb, L::P128, 0, kk ? sKh : sQt, L::P128, br, lane);
+                if constexpr (!L::kF32) {
+                    // diagonal Akk blocks again, transposed, for the substitution
+                    if (kk && I == R) {
 #pragma unroll
-                for (int R = 0; R < 4; ++R) epilogue(acc[R], 0, R, kk);
-            } else if (wave == 2) {       // I = 1, R = 1..3, both matrices
-                f32x4 acc[6] = {z4, z4, z4, z4, z4, z4};
-                {
-                    f32x4 a3[3] = {z4, z4, z4};
-                    const int br[3] = {16, 32, 48};
-                    mma_rows<E, DK, 3>(a3, sKb, L::P128, 16, sQt, L::P128, br, lane);
-                    acc[0] = a3[0]; acc[1] = a3[1]; acc[2] = a3[2];
-                    f32x4 b3[3] = {z4, z4, z4};
-                    mma_rows<E, DK, 3>(b3, sKb, L::P128, 16, sKh, L::P128, br, lane);
-                    acc[3] = b3[0]; acc[4] = b3[1]; acc[5] = b3[2];
+                        for (int e = 0; e < 4; ++e) sDT[(16 * R + 4 * lg + e) * L::PDT + ln] = val[e];
+                    }
                 }
+            };
+            // 20 tiles over waves 0-3 (Kh row r is row 64 + r of the Qt base).
+            if (wave == 0) {          // I = 0: Aqk R = 0..3, Akk R = 0
+                f32x4 acc[5] = {z4, z4, z4, z4, z4};
+                const int br[5] = {0, 16, 32, 48, 64};
+                mma_rows<E, DK, 5>(acc, sKb, L::P128, 0, sQt, L::P128, br, lane);
 #pragma unroll
-                for (int R = 1; R < 4; ++R) { epilogue(acc[R - 1], 1, R, false); epilogue(acc[R + 2], 1, R, true); }
-            } else {                      // I = 2 (R = 2, 3) and I = 3 (R = 3), both matrices
-                f32x4 a2[2] = {z4, z4}, b2[2] = {z4, z4};
-                const int br[2] = {32, 48};
-                mma_rows<E, DK, 2>(a2, sKb, L::P128, 32, sQt, L::P128, br, lane);
-                mma_rows<E, DK, 2>(b2, sKb, L::P128, 32, sKh, L::P128, br, lane);
-                f32x4 a1[1] = {z4}, b1[1] = {z4};
-                const int br1[1] = {48};
-                mma_rows<E, DK, 1>(a1, sKb, L::P128, 48, sQt, L::P128, br1, lane);
-                mma_rows<E, DK, 1>(b1, sKb, L::P128, 48, sKh, L::P128, br1, lane);
-                epilogue(a2[0], 2, 2, false); epilogue(a2[1], 2, 3, false);
-                epilogue(b2[0], 2, 2, true); epilogue(b2[1], 2, 3, true);
-                epilogue(a1[0], 3, 3, false); epilogue(b1[0], 3, 3, true);
-                // zero the upper tiles (I > R) of Aqk and Akk
-                for (int u = 0; u < 6; ++u) {
+                for (int R = 0; R < 4; ++R) epilogue(acc[R], 0, R, false);
+                epilogue(acc[4], 0, 0, true);
+            } else if (wave == 1) {   // I = 0: Akk R = 1..3;  I = 1: Aqk R = 1, 2
+                f32x4 acc[3] = {z4, z4, z4};
+                const int br[3] = {80, 96, 112};
+                mma_rows<E, DK, 3>(acc, sKb, L::P128, 0, sQt, L::P128, br, lane);
+                f32x4 acc2[2] = {z4, z4};
+                const int br2[2] = {16, 32};
+                mma_rows<E, DK, 2>(acc2, sKb, L::P128, 16, sQt, L::P128, br2, lane);
+#pragma unroll
+                for (int R = 1; R < 4; ++R) epilogue(acc[R - 1], 0, R, true);
+                epilogue(acc2[0], 1, 1, false); epilogue(acc2[1], 1, 2, false);
+            } else if (wave == 2) {   // I = 1: Aqk R = 3, Akk R = 1..3
+                f32x4 acc[4] = {z4, z4, z4, z4};
+                const int br[4] = {48, 80, 96, 112};
+                mma_rows<E, DK, 4>(acc, sKb, L::P128, 16, sQt, L::P128, br, lane);
+                epilogue(acc[0], 1, 3, false);
+#pragma unroll
+                for (int R = 1; R < 4; ++R) epilogue(acc[R], 1, R, true);
+            } else if (wave == 3) {   // I = 2, 3 for both, and the zero upper tiles
+                f32x4 acc[4] = {z4, z4, z4, z4};
+                const int br[4] = {32, 48, 96, 112};
+                mma_rows<E, DK, 4>(acc, sKb, L::P128, 32, sQt, L::P128, br, lane);
+                f32x4 acc3[2] = {z4, z4};
+                const int br3[2] = {48, 112};
+                mma_rows<E, DK, 2>(acc3, sKb, L::P128, 48, sQt, L::P128, br3, lane);
+                epilogue(acc[0], 2, 2, false); epilogue(acc[1], 2, 3, false);
+                epilogue(acc[2], 2, 2, true); epilogue(acc[3], 2, 3, true);
+                epilogue(acc3[0], 3, 3, false); epilogue(acc3[1], 3, 3, true);
+#pragma unroll
+                for (int u = 0; u < 6; ++u) {       // zero the upper tiles (I > R)
                     const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
                     const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
                     const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
@@ -429,18 +535,27 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
                     store_vec4<E>(sQK + r * L::P64 + i0, z4);
                 }
             }
-        }
-        f32x4 pacc[NJ];
-        if (wave >= 4) {                  // P tiles (R = wave - 4, all column blocks)
-            const int R = wave - 4;
-            int br[NJ];
+            // P tiles for token block R = wave - 4 (waves 4-7)
+            auto p_block = [&](int R) {
+                f32x4 pacc[NJ];
+                int br[NJ];
 #pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) { pacc[jb] = f32x4{0.f, 0.f, 0.f, 0.f}; br[jb] = 16 * jb; }
-            mma_rows<E, DK, NJ>(pacc, sKh, L::P128, 16 * R, sST, L::P128, br, lane);
+                for (int jb = 0; jb < NJ; ++jb) { pacc[jb] = z4; br[jb] = 16 * jb; }
+                mma_rows<E, DK, NJ>(pacc, sKh, L::P128, 16 * R, sST, L::P128, br, lane);
+#pragma unroll
+                for (int jb = 0; jb < NJ; ++jb) {
+                    const int j = 16 * jb + ln, r = 16 * R + 4 * lg;
+                    f32x4 vv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vv[e] = to_f32(sV[(r + e) * L::PV + j]);
+                    store_vec4<E>(sZT + j * L::P64 + r, vv - pacc[jb]);
+                }
+            };
+            if (wave >= 4) p_block(wave - 4);
         }
         lds_barrier();
 
-        // ===== UT transform, diagonal blocks (wave 0) | Z = V - Kh S (waves 4-7) =====
+        // ===== UT diagonal blocks (wave 0) | inter-chunk output Qt S (waves 1-7) =====
         if (wave == 0) {
             // column m of X = (I + A_bb)^{-1} for block bb, right-looking substitution
             const int bb = lane >> 4, m = lane & 15;
@@ -448,36 +563,62 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = (i == m) ? 1.f : 0.f;
+            // right-looking: once x[j] is final, column j of the block updates x[i > j]
+            if constexpr (!L::kF32) {
+                // column j is row j of the transposed block: four 16-byte loads,
+                // fetched one step ahead
+                const float* D = sDT + 16 * bb * L::PDT;
+                f32x4 col[2][4];
 #pragma unroll
-            for (int j = 0; j < 15; ++j) {
+                for (int q4 = 0; q4 < 4; ++q4) col[0][q4] = *reinterpret_cast<const f32x4*>(D + 4 * q4);
 #pragma unroll
-                for (int i = j + 1; i < 16; ++i) x[i] -= A[i * L::PA + j] * x[j];
-                __builtin_amdgcn_sched_barrier(0);   // keep one column of loads in flight
+                for (int j = 0; j < 15; ++j) {
+                    if (j + 1 < 15) {
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            col[(j + 1) & 1][q4] = *reinterpret_cast<const f32x4*>(D + (j + 1) * L::PDT + 4 * q4);
+                    }
+#pragma unroll
+                    for (int i = j + 1; i < 16; ++i) x[i] -= col[j & 1][i >> 2][i & 3] * x[j];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 15; ++j) {
+#pragma unroll
+                    for (int i = j + 1; i < 16; ++i) x[i] -= A[i * L::PA + j] * x[j];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) A[i * L::PA + m] = x[i];
-        } else if (wave >= 4) {
-            const int R = wave - 4;
+        } else {
+            // output tiles t = (wave - 1) + (NW - 1) m: (jb = t / 4, R = t % 4)
 #pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) {
-                const int j = 16 * jb + ln, r = 16 * R + 4 * lg;
-                const f32x4 vv = load_vec4<E>(sVT + j * L::P64 + r);
-                store_vec4<E>(sZT + j * L::P64 + r, vv - pacc[jb]);
+            for (int m = 0; m < MO; ++m) {
+                const int tt = (wave - 1) + (NW - 1) * m;
+                if (tt < NO) {
+                    f32x4 one[1] = {z4};
+                    const int br[1] = {16 * (tt % 4)};
+                    mma_rows<E, DK, 1>(one, sST, L::P128, 16 * (tt / 4), sQt, L::P128, br, lane);
+                    *reinterpret_cast<f32x4*>(sOI + (tt * 64 + lane) * 4) = one[0];
+                }
             }
         }
         lds_barrier();
 
-        // ===== UT transform, off-diagonal blocks; then Tm Diag(beta) in E =====
+        // Prefetch the next chunk while the rest of this one is computed.  It is
+        // issued here, not earlier, so that its registers are free during the
+        // register-heavy Akk/Aqk products and diagonal-block substitution.
+        if (n + 1 < nchunks) load_chunk(n + 1, in);
+
+        // ===== UT off-diagonal blocks; Tm Diag(beta) in E =====
         if constexpr (!L::kF32) {
-            // Column I = wave (0..2): X_RI = -X_RR sum_{J=I}^{R-1} A_RJ X_JI, chained
-            // through registers with 16x16x16 bf16 MFMAs (the D layout of one
-            // product is the B layout of the next).  Results go straight to RT,
-            // scaled by beta of their column.  Wave 3 writes the diagonal blocks,
-            // waves 4-7 clear the upper blocks of RT.
             if (wave == 0) ut_offdiag_column<0, L::PA, L::P64>(RA, RT, s_beta, lane);
             else if (wave == 1) ut_offdiag_column<1, L::PA, L::P64>(RA, RT, s_beta, lane);
             else if (wave == 2) ut_offdiag_column<2, L::PA, L::P64>(RA, RT, s_beta, lane);
             else if (wave == 3) {
+                // diagonal blocks, scaled by beta of their column
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
                     const int r = 16 * bb + 4 * lg;
@@ -487,10 +628,10 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
                         RT[(r + e) * L::P64 + 16 * bb + ln] = (E)(bcol * RA[(r + e) * L::PA + 16 * bb + ln]);
                 }
             } else {
-                for (int u = wave - 4; u < 6; u += 4) {
+                for (int u = wave - 4; u < 6; u += 4) {   // zero upper blocks of RT
                     const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
                     const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
-                    store_vec4<E>(RT + (16 * R + ln) * L::P64 + 16 * I + 4 * lg, f32x4{0.f, 0.f, 0.f, 0.f});
+                    store_vec4<E>(RT + (16 * R + ln) * L::P64 + 16 * I + 4 * lg, z4);
                 }
             }
             lds_barrier();
@@ -525,71 +666,78 @@ chunk_fwd_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __re
             lds_barrier();
         }
 
-        // ===== Vn = Tm Diag(beta) Z; tiles (R, jb), A operand shared per wave =====
+        // ===== Vn = Tm Diag(beta) Z: wave w -> token block R = w % 4, column blocks w / 4 + 2u =====
         {
-            constexpr int NVT = 4 * NJ;            // tiles
-            constexpr int PER = (NVT + NW - 1) / NW;
-            if (wave < NVT) {
-                const int R = wave % 4;
+            constexpr int PER = (NJ + 1) / 2;
+            const int R = wave % 4;
+            if (wave / 4 < NJ) {
                 f32x4 acc[PER];
                 int br[PER];
 #pragma unroll
                 for (int u = 0; u < PER; ++u) {
-                    acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const int jb = (wave / 4) + 2 * u;
+                    acc[u] = z4;
+                    const int jb = wave / 4 + 2 * u;
                     br[u] = 16 * (jb < NJ ? jb : 0);
                 }
                 mma_rows<E, C, PER>(acc, RT, L::P64, 16 * R, sZT, L::P64, br, lane);
 #pragma unroll
                 for (int u = 0; u < PER; ++u) {
-                    const int jb = (wave / 4) + 2 * u;
+                    const int jb = wave / 4 + 2 * u;
                     if (jb < NJ) store_vec4<E>(sVN + (16 * jb + ln) * L::P64 + 16 * R + 4 * lg, acc[u]);
                 }
             }
         }
         lds_barrier();
 
-        // ===== O = Qt S + Aqk Vn (to HBM) | S <- Diag(gamma) (S + Kb^T Vn) =====
-        {
-            constexpr int NOT = 4 * NJ;
-            constexpr int PER = (NOT + NW - 1) / NW;
-            const int ot0 = PER * wave;
-            if (ot0 < NOT) {
-                const int jb = ot0 / 4;
-                f32x4 acc[PER];
-                int br[PER];
+        // ===== O += Aqk Vn (to HBM, waves 1-3) | S <- Diag(gamma) (S + Kb^T Vn) =====
+        if (wave > 0) {
 #pragma unroll
-                for (int u = 0; u < PER; ++u) { acc[u] = f32x4{0.f, 0.f, 0.f, 0.f}; br[u] = 16 * ((ot0 + u) % 4); }
-                mma_rows<E, DK, PER>(acc, sST, L::P128, 16 * jb, sQt, L::P128, br, lane);
-                mma_rows<E, C, PER>(acc, sVN, L::P64, 16 * jb, sQK, L::P64, br, lane);
-#pragma unroll
-                for (int u = 0; u < PER; ++u) {
-                    const int r = br[u] + ln, tok = n * C + r;
-                    if (tok < T) store_vec4<E>(o + hbase + (size_t)tok * tokstride + j0 + 16 * jb + 4 * lg, acc[u]);
+            for (int m = 0; m < MO; ++m) {
+                const int tt = (wave - 1) + (NW - 1) * m;
+                if (tt < NO) {
+                    const int jb = tt / 4, R = tt % 4;
+                    f32x4 one[1] = {*reinterpret_cast<const f32x4*>(sOI + (tt * 64 + lane) * 4)};
+                    const int br[1] = {16 * R};
+                    mma_rows<E, C, 1>(one, sVN, L::P64, 16 * jb, sQK, L::P64, br, lane);
+                    const int tok = n * C + 16 * R + ln;
+                    if (full || tok < T)
+                        store_vec4<E>(o + hbase + (size_t)tok * tokstride + j0 + 16 * jb + 4 * lg, one[0]);
                 }
             }
+        }
+        {
             int br[NJ];
 #pragma unroll
             for (int jb = 0; jb < NJ; ++jb) br[jb] = 16 * jb;
+            const int Cb = wave;
             if constexpr (L::kF32) {
                 // A operand Kb^T read from the token-major Kb
-#pragma unroll
+#pragma unroll 4
                 for (int kk = 0; kk < C; kk += M::KS) {
-                    const float a = M::frag_mc(sKb, L::P128, 16 * wave, kk, lane);
+                    const float a = M::frag_mc(sKb, L::P128, 16 * Cb, kk, lane);
 #pragma unroll
                     for (int jb = 0; jb < NJ; ++jb)
                         acc_s[jb] = M::mma(a, M::frag_kc(sVN, L::P64, br[jb], kk, lane), acc_s[jb]);
                 }
             } else {
-                mma_rows<E, C, NJ>(acc_s, sKbT, L::P64, 16 * wave, sVN, L::P64, br, lane);
+                const int row = 16 * Cb + ln;
+#pragma unroll
+                for (int kk = 0; kk < C; kk += M::KS) {
+                    const int blk = ((kk >> 3) + lg) ^ ((row >> 3) & 7);
+                    const auto a = *reinterpret_cast<const bf16x8*>(sKbT + row * L::P64 + (blk << 3));
+#pragma unroll
+                    for (int jb = 0; jb < NJ; ++jb)
+                        acc_s[jb] = M::mma(a, M::frag_kc(sVN, L::P64, br[jb], kk, lane), acc_s[jb]);
+                }
             }
-            const int c = 16 * wave + 4 * lg;
+            const int c = 16 * Cb + 4 * lg;
 #pragma unroll
             for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc_s[jb][e] *= s_gam[c + e];
         }
-        lds_barrier();
+        // S^T for the next chunk: nobody reads S^T in this phase, and the next
+        // chunk's first barrier orders these writes before its readers.
         write_state_lds();
     }
 
