@@ -1,0 +1,133 @@
+"""Summarise rocprofv3 CSV output for libkda kernels.
+
+Usage:
+  python -m gated_delta_rule_32_amd.rocprof_summary trace  DIR [--match SUBSTR]
+      per-kernel duration statistics from a `--kernel-trace --stats
+      --output-format csv` run (reads *_kernel_stats.csv / *_kernel_trace.csv)
+  python -m gated_delta_rule_32_amd.rocprof_summary counters DIR [--match SUBSTR]
+      per-kernel mean of every counter from a `--pmc ... --output-format csv`
+      run (reads *_counter_collection.csv)
+  python -m gated_delta_rule_32_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
+      --match SUBSTR --copy-fetch CF_DIR --copy-write CW_DIR --copy-bytes N
+      HBM bytes per launch of the matching kernel: FETCH_SIZE and WRITE_SIZE
+      (KiB per dispatch) scaled by what the same counters read for a plain
+      copy kernel that reads and writes N bytes.
+Output is Markdown on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import os
+import statistics
+import sys
+from collections import defaultdict
+
+
+def _rows(d, pattern):
+    files = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def trace(d, match=None):
+    rows = _rows(d, "*kernel_trace.csv")
+    per = defaultdict(list)
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        if match and match not in name:
+            continue
+        try:
+            per[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        except (KeyError, ValueError):
+            continue
+    print("| kernel | calls | mean us | median us | min us | max us | total ms |")
+    print("|---|---|---|---|---|---|---|")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) < 90 else name[:87] + "..."
+        print(f"| `{short}` | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} "
+              f"| {min(v):.2f} | {max(v):.2f} | {sum(v) / 1e3:.3f} |")
+    return per
+
+
+def counters(d, match=None):
+    rows = _rows(d, "*counter_collection.csv")
+    per = defaultdict(lambda: defaultdict(list))
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        if match and match not in name:
+            continue
+        per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = {}
+    for name, cs in per.items():
+        print(f"### `{name[:100]}`\n")
+        print("| counter | dispatches | mean per dispatch |")
+        print("|---|---|---|")
+        out[name] = {}
+        for c, v in sorted(cs.items()):
+            m = statistics.mean(v)
+            out[name][c] = m
+            print(f"| {c} | {len(v)} | {m:.1f} |")
+        print()
+    return out
+
+
+def _mean_counter(d, counter, match):
+    vals = []
+    for r in _rows(d, "*counter_collection.csv"):
+        if match in r.get("Kernel_Name", "") and r["Counter_Name"] == counter:
+            vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {match!r} in {d}")
+    return statistics.mean(vals), len(vals)
+
+
+def traffic(fetch_dir, write_dir, match, cf_dir, cw_dir, copy_bytes, copy_match):
+    f_kib, nf = _mean_counter(fetch_dir, "FETCH_SIZE", match)
+    w_kib, nw = _mean_counter(write_dir, "WRITE_SIZE", match)
+    cf_kib, _ = _mean_counter(cf_dir, "FETCH_SIZE", copy_match)
+    cw_kib, _ = _mean_counter(cw_dir, "WRITE_SIZE", copy_match)
+    sf = copy_bytes / (cf_kib * 1024.0)
+    sw = copy_bytes / (cw_kib * 1024.0)
+    fetch_b = f_kib * 1024.0 * sf
+    write_b = w_kib * 1024.0 * sw
+    print(f"| quantity | value |\n|---|---|")
+    print(f"| kernel match | `{match}` ({nf} / {nw} dispatches) |")
+    print(f"| FETCH_SIZE raw (KiB/dispatch) | {f_kib:.1f} |")
+    print(f"| WRITE_SIZE raw (KiB/dispatch) | {w_kib:.1f} |")
+    print(f"| copy kernel FETCH_SIZE / WRITE_SIZE (KiB) for {copy_bytes} B each way | {cf_kib:.1f} / {cw_kib:.1f} |")
+    print(f"| scale factors fetch / write | {sf:.4f} / {sw:.4f} |")
+    print(f"| HBM read bytes per launch | {fetch_b:.4e} |")
+    print(f"| HBM write bytes per launch | {write_b:.4e} |")
+    print(f"| HBM bytes per launch (read + write) | {fetch_b + write_b:.4e} |")
+    return fetch_b + write_b
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace"); t.add_argument("dir"); t.add_argument("--match")
+    c = sub.add_parser("counters"); c.add_argument("dir"); c.add_argument("--match")
+    x = sub.add_parser("traffic")
+    x.add_argument("fetch_dir"); x.add_argument("write_dir")
+    x.add_argument("--match", required=True)
+    x.add_argument("--copy-fetch", required=True); x.add_argument("--copy-write", required=True)
+    x.add_argument("--copy-bytes", type=float, required=True)
+    x.add_argument("--copy-match", default="copy")
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        trace(a.dir, a.match)
+    elif a.cmd == "counters":
+        counters(a.dir, a.match)
+    else:
+        traffic(a.fetch_dir, a.write_dir, a.match, a.copy_fetch, a.copy_write, a.copy_bytes,
+                a.copy_match)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
