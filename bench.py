@@ -96,7 +96,7 @@ def time_launches(fn, steps, warmup):
     return start.elapsed_time(end) / 1e3 / steps, wall
 
 
-def prefill_line(name, steps, warmup):
+def prefill_line(name, steps, warmup, schedule="auto"):
     import torch
     import gated_delta_rule_32_amd as kda
     from gated_delta_rule_32_amd import inputs
@@ -108,9 +108,16 @@ def prefill_line(name, steps, warmup):
     d = {n: (x.to("cuda:0") if x is not None else None) for n, x in inp.items()}
     o = torch.empty_like(d["v"])
     S_T = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda:0")
+    if schedule == "auto":
+        nbytes = kda.workspace_size(B, T, H, kda.KDA_BF16 if cfg["dtype"] == "bfloat16" else kda.KDA_F32)
+    else:
+        nbytes = kda.scan_workspace_bytes(B, T, H) if schedule == "two_kernel" else 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0") if nbytes else None
+    sched = "two_kernel" if ws is not None and cfg["dtype"] == "bfloat16" else "fused"
 
     def step():
-        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], out=o, S_T=S_T)
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], out=o, S_T=S_T,
+                      workspace=ws)
 
     log(f"[bench] timing {steps} steps after {warmup} warmup")
     t_kernel, wall = time_launches(step, steps, warmup)
@@ -128,7 +135,8 @@ def prefill_line(name, steps, warmup):
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": traffic,
-                  "kernel": "chunk_fwd_kernel<bf16,64>" if cfg["dtype"] == "bfloat16" else "chunk_fwd_kernel<f32,16>",
+                  "kernel": ("chunk_fwd_kernel (fused)" if sched == "fused"
+                             else "chunk_fwd_kernel (prep) + chunk_scan_kernel"),
                   "alg_bytes_per_launch": alg_bytes,
                   "avg_launch_us": round(t_kernel * 1e6, 2)},
         mfma={"model_flops_per_launch": flops,
@@ -136,7 +144,8 @@ def prefill_line(name, steps, warmup):
               "peak_tflops": BF16_PEAK_TFLOPS,
               "frac_of_bf16_peak": round(flops / t_kernel / 1e12 / BF16_PEAK_TFLOPS, 4),
               "frac_of_roofline": round(t_floor / t_kernel, 4)},
-        config={"workload": f"kda_chunk_fwd {name}", "B": B, "T": T, "H": H, "d_k": D, "d_v": D,
+        config={"workload": f"kda_chunk_fwd {name}", "schedule": sched,
+                "B": B, "T": T, "H": H, "d_k": D, "d_v": D,
                 "chunk": C, "dtype": cfg["dtype"], "S0": "N(0,%g)" % cfg["s0_std"] if d["S0"] is not None else "zero",
                 "log_decay": "-%g*softplus(N(0,1))" % cfg["g_scale"]},
     )
@@ -200,6 +209,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode"], default=None,
                     help="time one workload only (profiling runs)")
+    ap.add_argument("--schedule", choices=["auto", "fused", "two_kernel"], default="auto",
+                    help="prefill schedule (auto: the library's preferred one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for HBM counter scaling) and exit")
     args = ap.parse_args()
@@ -229,7 +240,7 @@ def main():
         return
 
     name = WORKLOADS[args.workload or "c2"]
-    pre = prefill_line(name, args.steps, args.warmup)
+    pre = prefill_line(name, args.steps, args.warmup, args.schedule)
     line = {
         "metric": "KDA prefill tokens/s/head-layer (% MFMA peak); decode state GB/s (% HBM)",
         "value": round(pre["value"], 1),

@@ -9,7 +9,8 @@ from __future__ import annotations
 from ._binding import (KDA_BF16, KDA_F32, KDAError, lib, status_string,  # noqa: F401
                        version, _check)
 
-__all__ = ["chunk_fwd", "recurrent_step", "status_string", "version", "KDAError",
+__all__ = ["chunk_fwd", "recurrent_step", "workspace_size", "scan_workspace_bytes",
+           "status_string", "version", "KDAError",
            "KDA_F32", "KDA_BF16", "lib"]
 
 
@@ -42,11 +43,37 @@ def _need(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+_ws_cache = {}
+
+
+def workspace_size(B, T, H, dtype_code, d=128):
+    """Workspace bytes kda_chunk_fwd wants for its fastest schedule (0: none)."""
+    return int(lib().kda_chunk_fwd_workspace_size(B, T, H, d, d, dtype_code))
+
+
+def scan_workspace_bytes(B, T, H):
+    """Workspace that selects the two-kernel schedule for any bf16 shape."""
+    return B * H * ((T + 63) // 64) * 66048
+
+
+def _workspace(device, nbytes):
+    import torch
+    if nbytes <= 0:
+        return None
+    buf = _ws_cache.get(device)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[device] = buf
+    return buf
+
+
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out=None, S_T=None,
-              return_state: bool = True):
+              return_state: bool = True, workspace="auto"):
     """Chunked KDA prefill.  q, k, v: [B, T, H, 128] (fp32 or bf16); log_alpha:
     [B, T, H, 128] fp32; beta: [B, T, H] (same dtype as q); S0: [B, H, 128, 128]
-    fp32 or None.  Returns ``(o, S_T)`` (``S_T`` is None if not requested)."""
+    fp32 or None.  ``workspace``: "auto" (the size the library asks for, cached
+    per device), None (fused single-kernel schedule) or a uint8 device tensor.
+    Returns ``(o, S_T)`` (``S_T`` is None if not requested)."""
     import torch
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -66,9 +93,18 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out=None, S_T=None,
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif S_T is not None:
         _need(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        workspace = _workspace(dev, workspace_size(B, T, H, code, dk))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device != dev or workspace.dtype != torch.uint8:
+            raise ValueError("workspace must be a uint8 tensor on the same device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                              _ptr(S0), _ptr(out), _ptr(S_T), B, T, H, dk, dv, code,
-                             _stream(dev))
+                             ws_ptr, ws_bytes, _stream(dev))
     _check("kda_chunk_fwd", st)
     return out, S_T
 

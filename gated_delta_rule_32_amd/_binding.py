@@ -19,10 +19,11 @@ STATUS_NAMES = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED
                 -3: "KDA_ERR_ALIGNMENT", -4: "KDA_ERR_HIP"}
 
 # name -> (restype, argtypes) for every symbol declared in include/kda.h
-_VP, _I = ctypes.c_void_p, ctypes.c_int
+_VP, _I, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
     "kda_chunk_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                           _I, _I, _I, _I, _I, _I, _VP]),
+                           _I, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
+    "kda_chunk_fwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "kda_recurrent_step": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                 _I, _I, _I, _I, _I, _VP]),
     "kda_status_string": (ctypes.c_char_p, [_I]),

@@ -59,10 +59,18 @@ const char* kda_status_string(int status) {
 
 const char* kda_version(void) { return "0.1.0"; }
 
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || dk != kHeadDim || dv != kHeadDim || dtype != KDA_BF16) return 0;
+    if (!kda::chunk_prefers_two_kernel(B, T, H, dtype)) return 0;
+    return kda::chunk_ws_bytes(B, T, H);
+}
+
 int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* log_alpha, const void* beta, const float* S0,
                   void* o, float* S_T,
-                  int B, int T, int H, int dk, int dv, int dtype, void* stream)
+                  int B, int T, int H, int dk, int dv, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream)
 {
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -99,13 +107,27 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
     // S_T may coincide with S0 exactly (in-place update), never partially.
     if (overlap(rS0, rST) && (const void*)S0 != (const void*)S_T) return KDA_ERR_INVALID_ARG;
 
+    // two-kernel schedule when a large enough workspace is supplied (bf16)
+    void* ws = nullptr;
+    const long long grid_prep = (long long)heads * ((T + 63) / 64);
+    if (T > 0 && workspace && dtype == KDA_BF16 && grid_prep <= INT_MAX &&
+        workspace_bytes >= kda::chunk_ws_bytes(B, T, H)) {
+        if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
+        const Range rw{workspace, kda::chunk_ws_bytes(B, T, H)};
+        const Range all[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, n_qk * 4},
+                             {beta, tok * es}, rS0, rST, {o, n_qk * es}};
+        for (const Range& r : all)
+            if (overlap(rw, r)) return KDA_ERR_INVALID_ARG;
+        ws = workspace;
+    }
+
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (T == 0) {
         if (!S_T || (const void*)S0 == (const void*)S_T) return KDA_OK;
         e = kda::launch_state_copy(S0, S_T, (long long)heads, s);
     } else {
-        e = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dtype, s);
+        e = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dtype, ws, s);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

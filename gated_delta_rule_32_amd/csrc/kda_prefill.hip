@@ -276,10 +276,24 @@ struct ChunkIn {
     E beta;
 };
 
-template <typename E, int DV>
+// Workspace block of one chunk, written by the prep instantiation of the
+// kernel below and read by chunk_scan_kernel (bf16 only).  Byte offsets:
+constexpr int WS_QT = 0;                       // Qt   [64][128] bf16, token-major
+constexpr int WS_KH = WS_QT + C * DK * 2;      // Kh   [64][128] bf16, token-major
+constexpr int WS_KBT = WS_KH + C * DK * 2;     // Kb^T [128][64] bf16, channel-major
+constexpr int WS_TM = WS_KBT + DK * C * 2;     // Tm Diag(beta) [64][64] bf16
+constexpr int WS_QK = WS_TM + C * C * 2;       // Aqk  [64][64] bf16
+constexpr int WS_GAM = WS_QK + C * C * 2;      // e^{G_64} [128] fp32
+constexpr int WS_CHUNK = WS_GAM + DK * 4;      // 66,048 bytes
+
+// The fused kernel (PREP = false): one workgroup per (head, value slice)
+// walks all chunks of its head.  The prep instantiation (PREP = true): one
+// workgroup per (head, chunk) runs only the key-side work -- decay, Aqk, Akk,
+// Tm -- and exports it to the workspace for chunk_scan_kernel.
+template <typename E, int DV, bool PREP>
 __global__ void __launch_bounds__(NT)
 chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* beta,
-                 const float* S0, E* o, float* S_T, int T, int H, int nsplit)
+                 const float* S0, E* o, float* S_T, int T, int H, int nsplit, char* ws)
 {
     // (No __restrict__ on the inputs: the LDS barriers are asm statements with
     // a memory clobber, and without restrict the compiler keeps the prefetch
@@ -321,18 +335,21 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     const int vg = t % In::VL, vr = t / In::VL; // 8-channel group and row group for v
     const int ln = lane & 15, lg = lane >> 4;
 
+    const int nchunks = (T + C - 1) / C;
     // Workgroup -> (head, slice), keeping the slices of a head on one XCD
-    // (workgroups are dealt to the 8 XCDs round-robin).
+    // (workgroups are dealt to the 8 XCDs round-robin); prep: (head, chunk).
     const int nwg = gridDim.x, w = blockIdx.x;
-    const int lid = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
-    const int head = lid / nsplit, slice = lid % nsplit;
+    const int lid = (!PREP && nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
+    const int head = PREP ? lid / nchunks : lid / nsplit;
+    const int slice = PREP ? 0 : lid % nsplit;
     const int b = head / H, h = head % H;
     const int j0 = slice * DV;
+    const int n_first = PREP ? lid % nchunks : 0;
+    const int n_end = PREP ? n_first + 1 : nchunks;
 
     const size_t tokstride = (size_t)H * DK;                       // one token, all heads
     const size_t hbase = ((size_t)b * T * H + h) * DK;             // (b, t=0, h, 0)
     const size_t sbase = (size_t)head * DK * DK;                   // state of this head
-    const int nchunks = (T + C - 1) / C;
 
     // Prefetch of one chunk into registers.  Branch-free: rows past T read the
     // last valid token (always in bounds) and are zeroed when consumed, so no
@@ -348,17 +365,20 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
             in.q[i].load(q + off);
             in.k[i].load(k + off);
         }
+        if constexpr (!PREP) {
 #pragma unroll
-        for (int i = 0; i < RVR; ++i) {
-            const int tok = min(tok0 + RVR * vr + i, T - 1);
-            if (RVR * vr + i < C)
-                in.v[i].load(v + hbase + (size_t)tok * tokstride + j0 + 8 * vg);
+            for (int i = 0; i < RVR; ++i) {
+                const int tok = min(tok0 + RVR * vr + i, T - 1);
+                if (RVR * vr + i < C)
+                    in.v[i].load(v + hbase + (size_t)tok * tokstride + j0 + 8 * vg);
+            }
         }
         in.beta = betap[(size_t)min(tok0 + lane, T - 1) * H];
     };
 
     // ---- state slice in accumulators: wave w owns rows 16w .. 16w+15 ----------
     f32x4 acc_s[NJ];
+    if constexpr (!PREP)
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
         const int c = 16 * wave + 4 * lg, j = j0 + 16 * jb + ln;
@@ -370,13 +390,13 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         for (int jb = 0; jb < NJ; ++jb)
             store_vec4<E>(sST + (16 * jb + ln) * L::P128 + 16 * wave + 4 * lg, acc_s[jb]);
     };
-    write_state_lds();
+    if constexpr (!PREP) write_state_lds();
 
     In in;
-    load_chunk(0, in);
+    load_chunk(n_first, in);
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
-    for (int n = 0; n < nchunks; ++n) {
+    for (int n = n_first; n < n_end; ++n) {
         const bool full = (n + 1) * C <= T;     // uniform: no row of this chunk is past T
 
         // ===== E: cumulative log2-decay and the decay-scaled operands =====
@@ -455,7 +475,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     store_run<E, RPL>(sKbT + L::kbt(8 * cg + c, r0), col);
                 }
             }
-            if (RVR * vr < C) {
+            if (!PREP && RVR * vr < C) {
 #pragma unroll
                 for (int i = 0; i < RVR; ++i) {
                     const bool ok = row_ok(RVR * vr + i);
@@ -551,7 +571,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     store_vec4<E>(sZT + j * L::P64 + r, vv - pacc[jb]);
                 }
             };
-            if (wave >= 4) p_block(wave - 4);
+            if (!PREP && wave >= 4) p_block(wave - 4);
         }
         lds_barrier();
 
@@ -592,7 +612,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) A[i * L::PA + m] = x[i];
-        } else {
+        } else if constexpr (!PREP) {
             // output tiles t = (wave - 1) + (NW - 1) m: (jb = t / 4, R = t % 4)
 #pragma unroll
             for (int m = 0; m < MO; ++m) {
@@ -610,7 +630,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         // Prefetch the next chunk while the rest of this one is computed.  It is
         // issued here, not earlier, so that its registers are free during the
         // register-heavy Akk/Aqk products and diagonal-block substitution.
-        if (n + 1 < nchunks) load_chunk(n + 1, in);
+        if (!PREP && n + 1 < nchunks) load_chunk(n + 1, in);
 
         // ===== UT off-diagonal blocks; Tm Diag(beta) in E =====
         if constexpr (!L::kF32) {
@@ -664,6 +684,29 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                 RA[r * L::PA + i] *= s_beta[i];
             }
             lds_barrier();
+        }
+
+        if constexpr (PREP) {
+            // ===== export the key-side operands of this chunk =====
+            char* blk = ws + ((size_t)head * nchunks + n) * WS_CHUNK;
+            typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+            for (int u = t; u < C * DK / 8; u += NT) {            // Qt, Kh: [64][128]
+                const int r = u >> 4, cb = u & 15;
+                reinterpret_cast<i32x4*>(blk + WS_QT)[u] = *reinterpret_cast<const i32x4*>(sQt + r * L::P128 + 8 * cb);
+                reinterpret_cast<i32x4*>(blk + WS_KH)[u] = *reinterpret_cast<const i32x4*>(sKh + r * L::P128 + 8 * cb);
+            }
+            for (int u = t; u < DK * C / 8; u += NT) {            // Kb^T: [128][64], unswizzled
+                const int c = u >> 3, b8 = u & 7;
+                reinterpret_cast<i32x4*>(blk + WS_KBT)[u] = *reinterpret_cast<const i32x4*>(sKbT + L::kbt(c, 8 * b8));
+            }
+            for (int u = t; u < C * C / 8; u += NT) {             // Tm Diag(beta), Aqk: [64][64]
+                const int r = u >> 3, b8 = u & 7;
+                reinterpret_cast<i32x4*>(blk + WS_TM)[u] = *reinterpret_cast<const i32x4*>(RT + r * L::P64 + 8 * b8);
+                reinterpret_cast<i32x4*>(blk + WS_QK)[u] = *reinterpret_cast<const i32x4*>(sQK + r * L::P64 + 8 * b8);
+            }
+            if (t < DK / 4)
+                reinterpret_cast<f32x4*>(blk + WS_GAM)[t] = reinterpret_cast<const f32x4*>(s_gam)[t];
+            continue;
         }
 
         // ===== Vn = Tm Diag(beta) Z: wave w -> token block R = w % 4, column blocks w / 4 + 2u =====
@@ -741,6 +784,230 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         write_state_lds();
     }
 
+    if (!PREP && S_T) {
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+            const int c = 16 * wave + 4 * lg, j = j0 + 16 * jb + ln;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S_T[sbase + (size_t)(c + e) * DK + j] = acc_s[jb][e];
+        }
+    }
+}
+
+
+// ---- serial scan over chunks from the workspace (bf16) --------------------
+// One workgroup per (head, value slice), 8 waves.  For every chunk it loads
+// the key-side operands that chunk_fwd_kernel<.., PREP = true> exported (the
+// slices of one head read the same bytes, shared through L2) and the V slice,
+// and runs only the state-dependent products:
+//   Z = V - Kh S;  Vn = Tm Diag(beta) Z;  O = Qt S + Aqk Vn;
+//   S <- Diag(gamma) (S + Kb^T Vn).
+// The next chunk's operands are fetched into registers while the current one
+// is computed.
+template <int DV>
+struct ScanLayout {
+    typedef bf16_t E;
+    static constexpr int ES = 2, PAD = 8;
+    static constexpr int P128 = DK + PAD, P64 = C + PAD, PV = DV + PAD;
+    static constexpr int OFF_QT = 0;
+    static constexpr int OFF_KH = OFF_QT + C * P128 * ES;
+    static constexpr int OFF_KBT = OFF_KH + C * P128 * ES;
+    static constexpr int OFF_TM = OFF_KBT + DK * P64 * ES;
+    static constexpr int OFF_QK = OFF_TM + C * P64 * ES;
+    static constexpr int OFF_V = OFF_QK + C * P64 * ES;
+    static constexpr int OFF_ST = OFF_V + C * PV * ES;
+    static constexpr int OFF_ZT = OFF_ST + DV * P128 * ES;
+    static constexpr int OFF_VN = OFF_ZT + DV * P64 * ES;
+    static constexpr int OFF_GAM = OFF_VN + DV * P64 * ES;
+    static constexpr int TOTAL = OFF_GAM + DK * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    __device__ static constexpr int kbt(int c, int i) {
+        return c * P64 + ((((i >> 3) ^ ((c >> 3) & 7)) << 3) | (i & 7));
+    }
+};
+
+template <int DV>
+__global__ void __launch_bounds__(NT)
+chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
+                  int T, int H, int nsplit)
+{
+    typedef bf16_t E;
+    using L = ScanLayout<DV>;
+    using M = Mma<E>;
+    typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+    constexpr int NJ = DV / 16;
+    constexpr int VL = DV / 8;              // lanes per value row (16 bytes each)
+
+    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    E* sQt = reinterpret_cast<E*>(smem + L::OFF_QT);
+    E* sKh = reinterpret_cast<E*>(smem + L::OFF_KH);
+    E* sKbT = reinterpret_cast<E*>(smem + L::OFF_KBT);
+    E* sTM = reinterpret_cast<E*>(smem + L::OFF_TM);
+    E* sQK = reinterpret_cast<E*>(smem + L::OFF_QK);
+    E* sV = reinterpret_cast<E*>(smem + L::OFF_V);
+    E* sST = reinterpret_cast<E*>(smem + L::OFF_ST);
+    E* sZT = reinterpret_cast<E*>(smem + L::OFF_ZT);
+    E* sVN = reinterpret_cast<E*>(smem + L::OFF_VN);
+    float* s_gam = reinterpret_cast<float*>(smem + L::OFF_GAM);
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int ln = lane & 15, lg = lane >> 4;
+    const int nchunks = (T + C - 1) / C;
+    const int nwg = gridDim.x, w = blockIdx.x;
+    const int lid = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
+    const int head = lid / nsplit, slice = lid % nsplit;
+    const int b = head / H, h = head % H;
+    const int j0 = slice * DV;
+    const size_t tokstride = (size_t)H * DK;
+    const size_t hbase = ((size_t)b * T * H + h) * DK;
+    const size_t sbase = (size_t)head * DK * DK;
+    const char* wsh = ws + (size_t)head * nchunks * WS_CHUNK;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+    // registers of one chunk: 8 x 16 bytes of the workspace block per thread
+    // (the first 64 KiB), e^{G_64} (threads 0-31) and one value row segment
+    struct Pre { i32x4 blk[8]; f32x4 gam; Raw8<E> v; };
+    const int vg = t % VL, vr = t / VL;
+    auto load = [&](int n, Pre& pr) {
+        const char* src = wsh + (size_t)n * WS_CHUNK;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) pr.blk[m] = reinterpret_cast<const i32x4*>(src)[t + NT * m];
+        if (t < DK / 4) pr.gam = reinterpret_cast<const f32x4*>(src + WS_GAM)[t];
+        if (vr < C) pr.v.load(v + hbase + (size_t)min(n * C + vr, T - 1) * tokstride + j0 + 8 * vg);
+    };
+    auto store = [&](int n, const Pre& pr) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int u = t + NT * m;                       // 16-byte unit in the block
+            i32x4* dst;
+            if (m < 2) dst = reinterpret_cast<i32x4*>(sQt + (u >> 4) * L::P128 + 8 * (u & 15));
+            else if (m < 4) { const int x = u - 1024; dst = reinterpret_cast<i32x4*>(sKh + (x >> 4) * L::P128 + 8 * (x & 15)); }
+            else if (m < 6) { const int x = u - 2048; dst = reinterpret_cast<i32x4*>(sKbT + L::kbt(x >> 3, 8 * (x & 7))); }
+            else if (m < 7) { const int x = u - 3072; dst = reinterpret_cast<i32x4*>(sTM + (x >> 3) * L::P64 + 8 * (x & 7)); }
+            else { const int x = u - 3584; dst = reinterpret_cast<i32x4*>(sQK + (x >> 3) * L::P64 + 8 * (x & 7)); }
+            *dst = pr.blk[m];
+        }
+        if (t < DK / 4) reinterpret_cast<f32x4*>(s_gam)[t] = pr.gam;
+        if (vr < C) {
+            const bool ok = n * C + vr < T;
+            float row[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) row[c] = ok ? pr.v[c] : 0.f;
+            store8<E>(sV + vr * L::PV + 8 * vg, row);
+        }
+    };
+
+    // state rows 16w .. 16w+15 of the slice in accumulators
+    f32x4 acc_s[NJ];
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) {
+        const int c = 16 * wave + 4 * lg, j = j0 + 16 * jb + ln;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc_s[jb][e] = S0 ? S0[sbase + (size_t)(c + e) * DK + j] : 0.f;
+    }
+    auto write_state_lds = [&]() {
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb)
+            store_vec4<E>(sST + (16 * jb + ln) * L::P128 + 16 * wave + 4 * lg, acc_s[jb]);
+    };
+    write_state_lds();
+
+    Pre pre;
+    load(0, pre);
+    for (int n = 0; n < nchunks; ++n) {
+        store(n, pre);
+        if (n + 1 < nchunks) load(n + 1, pre);
+        lds_barrier();
+
+        // ---- waves 0-3: Z = V - Kh S for token block R = wave | waves 4-7: Qt S
+        f32x4 oacc[NJ];
+        if (wave < 4) {
+            const int R = wave;
+            f32x4 pacc[NJ];
+            int br[NJ];
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) { pacc[jb] = z4; br[jb] = 16 * jb; }
+            mma_rows<E, DK, NJ>(pacc, sKh, L::P128, 16 * R, sST, L::P128, br, lane);
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) {
+                const int j = 16 * jb + ln, r = 16 * R + 4 * lg;
+                f32x4 vv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vv[e] = (float)sV[(r + e) * L::PV + j];
+                store_vec4<E>(sZT + j * L::P64 + r, vv - pacc[jb]);
+            }
+        } else {
+            // output tiles (jb, R = wave - 4): A = S^T rows jb, B = Qt rows R
+            const int R = wave - 4;
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) {
+                f32x4 one[1] = {z4};
+                const int br[1] = {16 * R};
+                mma_rows<E, DK, 1>(one, sST, L::P128, 16 * jb, sQt, L::P128, br, lane);
+                oacc[jb] = one[0];
+            }
+        }
+        lds_barrier();
+
+        // ---- Vn = Tm Diag(beta) Z: wave -> token block R = wave % 4, column blocks wave / 4 + 2u
+        {
+            constexpr int PER = (NJ + 1) / 2;
+            const int R = wave % 4;
+            if (wave / 4 < NJ) {
+                f32x4 acc[PER];
+                int br[PER];
+#pragma unroll
+                for (int u = 0; u < PER; ++u) {
+                    acc[u] = z4;
+                    const int jb = wave / 4 + 2 * u;
+                    br[u] = 16 * (jb < NJ ? jb : 0);
+                }
+                mma_rows<E, C, PER>(acc, sTM, L::P64, 16 * R, sZT, L::P64, br, lane);
+#pragma unroll
+                for (int u = 0; u < PER; ++u) {
+                    const int jb = wave / 4 + 2 * u;
+                    if (jb < NJ) store_vec4<E>(sVN + (16 * jb + ln) * L::P64 + 16 * R + 4 * lg, acc[u]);
+                }
+            }
+        }
+        lds_barrier();
+
+        // ---- O = Qt S + Aqk Vn (waves 4-7) | S <- Diag(gamma) (S + Kb^T Vn) (all)
+        if (wave >= 4) {
+            const int R = wave - 4;
+            const int tok = n * C + 16 * R + ln;
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) {
+                f32x4 one[1] = {oacc[jb]};
+                const int br[1] = {16 * R};
+                mma_rows<E, C, 1>(one, sVN, L::P64, 16 * jb, sQK, L::P64, br, lane);
+                if (tok < T) store_vec4<E>(o + hbase + (size_t)tok * tokstride + j0 + 16 * jb + 4 * lg, one[0]);
+            }
+        }
+        {
+            int br[NJ];
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) br[jb] = 16 * jb;
+            const int row = 16 * wave + ln;
+#pragma unroll
+            for (int kk = 0; kk < C; kk += M::KS) {
+                const int blk = ((kk >> 3) + lg) ^ ((row >> 3) & 7);
+                const auto a = *reinterpret_cast<const bf16x8*>(sKbT + row * L::P64 + (blk << 3));
+#pragma unroll
+                for (int jb = 0; jb < NJ; ++jb)
+                    acc_s[jb] = M::mma(a, M::frag_kc(sVN, L::P64, br[jb], kk, lane), acc_s[jb]);
+            }
+            const int c = 16 * wave + 4 * lg;
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc_s[jb][e] *= s_gam[c + e];
+        }
+        lds_barrier();      // everyone is done with this chunk's operands and S^T
+        write_state_lds();
+    }
+
     if (S_T) {
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) {
@@ -757,21 +1024,52 @@ void launch_one(const void* q, const void* k, const void* v, const float* g, con
 {
     const int nsplit = DK / DV;
     const unsigned nwg = (unsigned)((long long)B * H * nsplit);
-    hipLaunchKernelGGL((chunk_fwd_kernel<E, DV>), dim3(nwg), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((chunk_fwd_kernel<E, DV, false>), dim3(nwg), dim3(NT), 0, stream,
                        (const E*)q, (const E*)k, (const E*)v, g, (const E*)beta, S0, (E*)o, S_T,
-                       T, H, nsplit);
+                       T, H, nsplit, (char*)nullptr);
 }
 
 }  // namespace
 
+size_t chunk_ws_bytes(long long B, long long T, long long H)
+{
+    return (size_t)B * (size_t)H * (size_t)((T + C - 1) / C) * (size_t)WS_CHUNK;
+}
+
+bool chunk_prefers_two_kernel(long long B, long long T, long long H, int dtype)
+{
+    // The fused kernel recomputes the key-side work once per value slice; with
+    // fewer than 128 heads it needs 4 or 8 slices to fill the machine, and the
+    // precomputed operands (about 1 KiB per token) cost less than the recompute.
+    return dtype == 1 && B * H < 128 && T > C;
+}
+
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                             const void* beta, const float* S0, void* o, float* S_T,
-                            int B, int T, int H, int dtype, hipStream_t stream)
+                            int B, int T, int H, int dtype, void* ws, hipStream_t stream)
 {
     const long long heads = (long long)B * H;
     if (dtype == 0) {
         // fp32 operands need the narrowest slice to fit the LDS budget
         launch_one<float, 16>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+    } else if (ws) {
+        const int nchunks = (T + C - 1) / C;
+        hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true>), dim3((unsigned)(heads * nchunks)), dim3(NT),
+                           0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
+                           (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws);
+        // value slices: enough workgroups to cover the machine
+        const int dv = heads * 2 >= 256 ? 64 : (heads * 4 >= 256 ? 32 : 16);
+        const int nsplit = DK / dv;
+        const dim3 grid((unsigned)(heads * nsplit));
+        if (dv == 64)
+            hipLaunchKernelGGL(chunk_scan_kernel<64>, grid, dim3(NT), 0, stream, (const char*)ws,
+                               (const bf16_t*)v, S0, (bf16_t*)o, S_T, T, H, nsplit);
+        else if (dv == 32)
+            hipLaunchKernelGGL(chunk_scan_kernel<32>, grid, dim3(NT), 0, stream, (const char*)ws,
+                               (const bf16_t*)v, S0, (bf16_t*)o, S_T, T, H, nsplit);
+        else
+            hipLaunchKernelGGL(chunk_scan_kernel<16>, grid, dim3(NT), 0, stream, (const char*)ws,
+                               (const bf16_t*)v, S0, (bf16_t*)o, S_T, T, H, nsplit);
     } else if (heads * 2 >= 256) {
         launch_one<bf16_t, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
     } else if (heads * 4 >= 256) {

@@ -76,6 +76,16 @@ enum {
  *   S_T       [B, H, dk, dv] fp32    out    final state; NULL means not written.
  *                                           S_T may equal S0 (updated in place);
  *                                           any other overlap is rejected.
+ *   workspace                 device scratch, owned by the caller, or NULL.
+ *                             With dtype == KDA_BF16 and workspace_bytes >=
+ *                             B * H * ceil(T / 64) * 66048, the call runs two
+ *                             kernels: the key-side operands of every chunk
+ *                             are computed in parallel into the workspace,
+ *                             then a serial scan applies them to the state.
+ *                             Otherwise one fused kernel does both (no
+ *                             workspace is touched).  The workspace must be
+ *                             256-byte aligned and overlap no other buffer;
+ *                             its contents on entry and exit are unspecified.
  * T may be any value >= 0 (a partial last chunk is handled exactly); T = 0
  * copies S0 (or zeros) to S_T.  B*H = 0 is a no-op.  `o` must not overlap any
  * input.  Returns KDA_OK or a negative status.
@@ -83,7 +93,16 @@ enum {
 int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* log_alpha, const void* beta, const float* S0,
                   void* o, float* S_T,
-                  int B, int T, int H, int dk, int dv, int dtype, void* stream);
+                  int B, int T, int H, int dk, int dv, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes that kda_chunk_fwd should be given for the fastest schedule
+ * on this shape: B * H * ceil(T / 64) * 66048 when the two-kernel schedule is
+ * expected to win (bf16 with fewer than 128 heads in total), else 0 (the fused
+ * kernel is used and no workspace is needed).  Invalid arguments return 0.
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
 
 /*
  * Recurrent decode step: applies eq. (1) once (one token) to each of N x H

@@ -33,7 +33,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_recurrent_step", "kda_status_string", "kda_version"}
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_recurrent_step",
+                          "kda_status_string", "kda_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_binding.SIGNATURES) == set(names)
@@ -46,8 +47,8 @@ def test_status_strings(lib):
 
 
 def chunk(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S0=None,
-          o=P + 2**28, ST=P + 2**29, B=1, T=64, H=1, dk=128, dv=128, dt=BF16):
-    return lib.kda_chunk_fwd(q, k, v, g, beta, S0, o, ST, B, T, H, dk, dv, dt, None)
+          o=P + 2**28, ST=P + 2**29, B=1, T=64, H=1, dk=128, dv=128, dt=BF16, ws=None, wsb=0):
+    return lib.kda_chunk_fwd(q, k, v, g, beta, S0, o, ST, B, T, H, dk, dv, dt, ws, wsb, None)
 
 
 def step(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S=P + 2**28,
@@ -66,6 +67,8 @@ def step(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S=P + 
     (dict(ST=P + 2**26 + 64), INVALID),         # S_T overlaps g
     (dict(S0=P + 2**30, ST=P + 2**30 + 16), INVALID),  # partial S0/S_T overlap
     (dict(B=2**30, H=2**30), UNSUP),            # size overflow
+    (dict(ws=P + 2**31 + 16, wsb=66048), ALIGN),           # workspace needs 256-byte alignment
+    (dict(ws=P + 2**24, wsb=66048), INVALID),               # workspace overlaps k
 ])
 def test_chunk_fwd_rejects(lib, kw, code):
     assert chunk(lib, **kw) == code
@@ -74,9 +77,9 @@ def test_chunk_fwd_rejects(lib, kw, code):
 def test_chunk_fwd_noop_and_in_place_accepted_shapes(lib):
     # B*H == 0 returns before any launch, even with NULL pointers
     assert lib.kda_chunk_fwd(None, None, None, None, None, None, None, None,
-                             0, 64, 4, 128, 128, BF16, None) == OK
+                             0, 64, 4, 128, 128, BF16, None, 0, None) == OK
     assert lib.kda_chunk_fwd(None, None, None, None, None, None, None, None,
-                             3, 64, 0, 128, 128, F32, None) == OK
+                             3, 64, 0, 128, 128, F32, None, 0, None) == OK
     # T == 0 with S_T == NULL: nothing to do
     assert chunk(lib, q=None, k=None, v=None, g=None, beta=None, o=None, ST=None, T=0) == OK
 
@@ -91,6 +94,22 @@ def test_chunk_fwd_noop_and_in_place_accepted_shapes(lib):
 ])
 def test_recurrent_step_rejects(lib, kw, code):
     assert step(lib, **kw) == code
+
+
+def test_workspace_size_query(lib):
+    f = lib.kda_chunk_fwd_workspace_size
+    # few heads, bf16: two-kernel schedule, one 66,048-byte block per chunk
+    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 66048
+    assert f(1, 32768, 16, 128, 128, BF16) == 16 * 512 * 66048
+    assert f(1, 100, 3, 128, 128, BF16) == 3 * 2 * 66048
+    # many heads, fp32, tiny T or bad arguments: fused kernel, no workspace
+    assert f(8, 4096, 16, 128, 128, BF16) == 0
+    assert f(1, 256, 1, 128, 128, F32) == 0
+    assert f(1, 64, 1, 128, 128, BF16) == 0
+    assert f(1, 100, 3, 64, 128, BF16) == 0 and f(-1, 100, 3, 128, 128, BF16) == 0
+    # a workspace too small is simply not used (fused kernel): no error
+    assert chunk(lib, ws=P + 2**31, wsb=100, T=0, q=None, k=None, v=None, g=None, beta=None,
+                 o=None, ST=None) == OK
 
 
 def test_recurrent_step_empty_is_noop(lib):

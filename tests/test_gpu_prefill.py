@@ -19,8 +19,16 @@ def to_dev(inp):
     return {n: (x.to(DEV) if x is not None else None) for n, x in inp.items()}
 
 
-def run(d, S0="inp", **kw):
+def run(d, S0="inp", schedule="auto", **kw):
+    """schedule: "auto" (library's choice), "fused" (no workspace) or
+    "two_kernel" (a workspace large enough for the prep + scan kernels)."""
     s0 = d["S0"] if S0 == "inp" else S0
+    if schedule == "fused":
+        kw["workspace"] = None
+    elif schedule == "two_kernel":
+        B, T, H, _ = d["q"].shape
+        kw["workspace"] = torch.empty(kda.scan_workspace_bytes(B, T, H), dtype=torch.uint8,
+                                      device=d["q"].device)
     o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], s0, **kw)
     torch.cuda.synchronize()
     return o, S
@@ -47,46 +55,51 @@ def test_config1_fp32_full():
     check(inp, o, S, TOL["float32"])
 
 
-@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("dtype,schedule", [("float32", "fused"), ("bfloat16", "fused"),
+                                            ("bfloat16", "two_kernel")])
 @pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 200])
-def test_ragged_lengths_with_initial_state(dtype, T):
-    print(f"prefill ragged dtype={dtype} T={T}", flush=True)
+def test_ragged_lengths_with_initial_state(dtype, schedule, T):
+    print(f"prefill ragged dtype={dtype} schedule={schedule} T={T}", flush=True)
     inp = inputs.prefill_inputs(2, T, 3, dtype=dtype, g_scale=0.1, s0_std=0.05, seed=T)
-    o, S = run(to_dev(inp))
+    o, S = run(to_dev(inp), schedule=schedule)
     check(inp, o, S, TOL[dtype])
 
 
+@pytest.mark.parametrize("schedule", ["fused", "two_kernel"])
 @pytest.mark.parametrize("H", [1, 40, 100])
-def test_bf16_slice_widths(H):
+def test_bf16_slice_widths(H, schedule):
     """Head counts that select each value-slice width (16, 32, 64 columns)."""
-    print(f"prefill slice widths H={H}", flush=True)
+    print(f"prefill slice widths H={H} schedule={schedule}", flush=True)
     inp = inputs.prefill_inputs(1, 150, H, dtype="bfloat16", g_scale=0.05, s0_std=0.02, seed=H)
-    o, S = run(to_dev(inp))
+    o, S = run(to_dev(inp), schedule=schedule)
     heads = [(0, 0), (0, H - 1), (0, H // 2)]
     check(inp, o, S, TOL["bfloat16"], heads=heads)
 
 
-def test_config2_reduced_all_elements():
-    print("prefill c2 reduced B=2 H=4 T=1000", flush=True)
+@pytest.mark.parametrize("schedule", ["fused", "two_kernel"])
+def test_config2_reduced_all_elements(schedule):
+    print(f"prefill c2 reduced B=2 H=4 T=1000 schedule={schedule}", flush=True)
     inp = inputs.prefill_config("c2_bf16_B8_H16_T4096", B=2, H=4, T=1000)
-    o, S = run(to_dev(inp))
+    o, S = run(to_dev(inp), schedule=schedule)
     check(inp, o, S, TOL["bfloat16"])
 
 
-def test_config2_full_size_sampled_heads():
+@pytest.mark.parametrize("schedule", ["auto", "two_kernel"])
+def test_config2_full_size_sampled_heads(schedule):
     """B = 8, H = 16, T = 4096 bf16: every token and state entry of 6 heads."""
-    print("prefill c2 full", flush=True)
+    print(f"prefill c2 full schedule={schedule}", flush=True)
     inp = inputs.prefill_config("c2_bf16_B8_H16_T4096")
-    o, S = run(to_dev(inp))
+    o, S = run(to_dev(inp), schedule=schedule)
     heads = [(0, 0), (7, 15), (3, 9), (5, 2), (1, 14), (6, 7)]
     check(inp, o, S, TOL["bfloat16"], heads=heads)
 
 
-def test_config3_full_size_sampled_heads():
+@pytest.mark.parametrize("schedule", ["auto", "fused"])
+def test_config3_full_size_sampled_heads(schedule):
     """B = 1, H = 32, T = 65536 bf16, S0 ~ N(0, 0.02^2): 2 heads end to end."""
-    print("prefill c3 full", flush=True)
+    print(f"prefill c3 full schedule={schedule}", flush=True)
     inp = inputs.prefill_config("c3_bf16_B1_H32_T65536")
-    o, S = run(to_dev(inp))
+    o, S = run(to_dev(inp), schedule=schedule)
     check(inp, o, S, TOL["bfloat16"], heads=[(0, 0), (0, 31)])
 
 
@@ -94,38 +107,50 @@ def test_strong_decay_near_range_limit():
     """Per-channel log-decay of about -0.8 per token: chunk sums down to about -65."""
     print("prefill strong decay", flush=True)
     inp = inputs.prefill_inputs(1, 200, 2, dtype="bfloat16", g_scale=1.0, s0_std=0.05, seed=8)
-    o, S = run(to_dev(inp))
-    check(inp, o, S, TOL["bfloat16"])
+    for schedule in ("fused", "two_kernel"):
+        o, S = run(to_dev(inp), schedule=schedule)
+        check(inp, o, S, TOL["bfloat16"])
     inp32 = inputs.prefill_inputs(1, 200, 2, dtype="float32", g_scale=1.0, s0_std=0.05, seed=8)
     o, S = run(to_dev(inp32))
     check(inp32, o, S, TOL["float32"])
 
 
-def test_state_options_and_edge_cases():
+def test_schedules_agree_closely():
+    """Fused and two-kernel schedules compute the same products in the same
+    precision; they agree far more tightly than either does with the oracle."""
+    inp = inputs.prefill_inputs(2, 300, 3, dtype="bfloat16", g_scale=0.05, s0_std=0.02, seed=31)
+    d = to_dev(inp)
+    o1, S1 = run(d, schedule="fused")
+    o2, S2 = run(d, schedule="two_kernel")
+    assert max_rel_err(o2, o1.float().cpu().numpy()) <= 1e-2
+    assert max_rel_err(S2, S1.cpu().numpy()) <= 1e-2
+
+
+@pytest.mark.parametrize("schedule", ["fused", "two_kernel"])
+def test_state_options_and_edge_cases(schedule):
     inp = inputs.prefill_inputs(2, 77, 2, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=5)
     d = to_dev(inp)
-    o_ref, S_ref = run(d)
+    go = lambda S0="inp", **kw: run(d, S0=S0, schedule=schedule, **kw)  # noqa: E731
+    o_ref, S_ref = go()
     # S_T not requested
-    o2, S2 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], return_state=False)
-    torch.cuda.synchronize()
+    o2, S2 = go(return_state=False)
     assert S2 is None and torch.equal(o2, o_ref)
     # in place: S_T == S0
     S_io = d["S0"].clone()
-    o3, S3 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S_io, S_T=S_io)
-    torch.cuda.synchronize()
+    o3, _ = go(S0=S_io, S_T=S_io)
     assert torch.equal(o3, o_ref) and torch.equal(S_io, S_ref)
     # S0 = None equals an explicit zero state
-    oz, Sz = run(d, S0=None)
-    oz2, Sz2 = run(d, S0=torch.zeros_like(d["S0"]))
+    oz, Sz = go(S0=None)
+    oz2, Sz2 = go(S0=torch.zeros_like(d["S0"]))
     assert torch.equal(oz, oz2) and torch.equal(Sz, Sz2)
     # T = 0 copies the initial state (or zeros)
-    e = lambda x: x[:, :0].contiguous()
+    e = lambda x: x[:, :0].contiguous()  # noqa: E731
     _, S0c = kda.chunk_fwd(e(d["q"]), e(d["k"]), e(d["v"]), e(d["g"]), e(d["beta"]), d["S0"])
     _, Sze = kda.chunk_fwd(e(d["q"]), e(d["k"]), e(d["v"]), e(d["g"]), e(d["beta"]), None)
     torch.cuda.synchronize()
     assert torch.equal(S0c, d["S0"]) and torch.count_nonzero(Sze) == 0
     # deterministic: bitwise equal reruns
-    o4, S4 = run(d)
+    o4, S4 = go()
     assert torch.equal(o4, o_ref) and torch.equal(S4, S_ref)
 
 
