@@ -11,10 +11,12 @@ head-tokens per second (B*T*H / time).  The JSON line also carries:
   * mfma: the pages' cost-model FLOPs as a fraction of the bf16 MFMA peak;
   * decode: the recurrent decode step over 256 x 32 heads, state GB/s and %
     of HBM peak;
+  * layer: the full token-mixing layer (d_model 2048, 16 heads, 32768
+    tokens), its time, the KDA operator's share and the achieved TFLOP/s;
   * cpu_baseline: the fp64 oracle timed on the host cores on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload c3|c1|decode  (single-workload lines, for profiling)
+       python bench.py --workload c3|c1|decode|layer  (single-workload lines, for profiling)
        python bench.py --copy-calibration       (plain copy kernel for counter scaling)
 """
 from __future__ import annotations
@@ -181,6 +183,43 @@ def decode_line(steps, warmup):
             "traffic": measured_traffic("recurrent_step_decode", DECODE_KERNEL_SRC)}
 
 
+def layer_line(steps, warmup):
+    """The full token-mixing layer (projections, conv/activations, gates, KDA,
+    gated RMSNorm, output projection) on the 32768-token, d_model 2048, 16-head
+    workload; also times the KDA operator alone on the layer's own inputs."""
+    import torch
+    import gated_delta_rule_32_amd as kda
+    from gated_delta_rule_32_amd import inputs
+
+    cfg = inputs.LAYER_CONFIG
+    B, T, dm, H = cfg["B"], cfg["T"], cfg["d_model"], cfg["H"]
+    rank = D
+    log(f"[bench] layer: generating B={B} T={T} d_model={dm} H={H}")
+    inp = inputs.layer_inputs(B=B, T=T, d_model=dm, H=H, seed=cfg["seed"], gate_rank=rank)
+    dev = torch.device("cuda", 0)
+    x = inp["x"].to(dev)
+    W = {n: inp[n].to(dev) for n in kda.LAYER_WEIGHTS}
+    total, _ = kda.layer_workspace_layout(B, T, dm, H, rank)
+    ws = torch.empty(total, dtype=torch.uint8, device=dev)
+    y = torch.empty((B, T, dm), dtype=torch.bfloat16, device=dev)
+    _, iv = kda.layer_fwd(x, W, H, out=y, workspace=ws, intermediates=True)
+    t_layer, _ = time_launches(lambda: kda.layer_fwd(x, W, H, out=y, workspace=ws), steps, warmup)
+    o = torch.empty_like(iv["v"])
+    t_kda, _ = time_launches(lambda: kda.chunk_fwd(iv["q"], iv["k"], iv["v"], iv["g"], iv["beta"],
+                                                   None, out=o, return_state=False), steps, warmup)
+    hd = H * D
+    gemm_flops = 2 * B * T * (dm * (4 * hd + rank + H) + rank * hd + hd * dm)
+    kda_flops = B * T * H * FLOP_PER_HEAD_TOKEN
+    return {"workload": f"kda_layer_fwd B={B} T={T} d_model={dm} H={H}x{D} gate rank {rank}, bf16",
+            "ms_per_layer": round(t_layer * 1e3, 4),
+            "tokens_per_s": round(B * T / t_layer, 1),
+            "kda_operator_ms": round(t_kda * 1e3, 4),
+            "rest_ms": round((t_layer - t_kda) * 1e3, 4),
+            "model_flops": gemm_flops + kda_flops,
+            "achieved_tflops": round((gemm_flops + kda_flops) / t_layer / 1e12, 1),
+            "frac_of_bf16_peak": round((gemm_flops + kda_flops) / t_layer / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def cpu_baseline(inp):
     """The fp64 oracle as it stands, on the host cores, on the whole workload."""
     import numpy as np
@@ -207,7 +246,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode"], default=None,
+    ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer"], default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--schedule", choices=["auto", "fused", "two_kernel"], default="auto",
                     help="prefill schedule (auto: the library's preferred one)")
@@ -239,6 +279,11 @@ def main():
         print(json.dumps({"metric": "KDA decode state GB/s", **dec}))
         return
 
+    if args.workload == "layer":
+        lay = layer_line(args.steps, args.warmup)
+        print(json.dumps({"metric": "KDA layer tokens/s", **lay}))
+        return
+
     name = WORKLOADS[args.workload or "c2"]
     pre = prefill_line(name, args.steps, args.warmup, args.schedule)
     line = {
@@ -256,6 +301,8 @@ def main():
     }
     if args.workload is None and not args.no_decode:
         line["decode"] = decode_line(max(args.steps, 20), args.warmup)
+    if args.workload is None and not args.no_layer:
+        line["layer"] = layer_line(min(args.steps, 20), args.warmup)
     if not args.no_cpu and args.workload is None:
         line["cpu_baseline"] = cpu_baseline(pre["inp"])
     print(json.dumps(line))

@@ -6,10 +6,13 @@ torch is used for device memory and streams only.
 """
 from __future__ import annotations
 
-from ._binding import (KDA_BF16, KDA_F32, KDAError, lib, status_string,  # noqa: F401
-                       version, _check)
+import ctypes
+
+from ._binding import (KDA_BF16, KDA_F32, LAYER_REGIONS, KDAError, lib,  # noqa: F401
+                       status_string, version, _check)
 
 __all__ = ["chunk_fwd", "recurrent_step", "workspace_size", "scan_workspace_bytes",
+           "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS",
            "status_string", "version", "KDAError",
            "KDA_F32", "KDA_BF16", "lib"]
 
@@ -130,3 +133,73 @@ def recurrent_step(q, k, v, log_alpha, beta, S, *, out=None):
                                   _ptr(S), _ptr(out), N, H, dk, dv, code, _stream(dev))
     _check("kda_recurrent_step", st)
     return out
+
+
+# weight arguments of kda_layer_fwd, in call order
+LAYER_WEIGHTS = ("W_q", "W_k", "W_v", "W_g", "conv_q", "conv_k", "conv_v",
+                 "W_down", "W_up", "W_beta", "W_o")
+
+
+def layer_workspace_layout(B, T, d_model, H, rank):
+    """(total bytes, {region: byte offset}) of kda_layer_fwd's workspace."""
+    offs = (ctypes.c_size_t * len(LAYER_REGIONS))()
+    total = int(lib().kda_layer_workspace_layout(B, T, d_model, H, rank, offs))
+    if total == 0:
+        raise ValueError(f"unsupported layer shape B={B} T={T} d_model={d_model} H={H} rank={rank}")
+    return total, dict(zip(LAYER_REGIONS, (int(o) for o in offs)))
+
+
+def _region(ws, off, dtype, shape):
+    import math
+    import torch
+    n = math.prod(shape) * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + n].view(dtype).view(shape)
+
+
+def layer_fwd(x, weights, H, *, out=None, workspace=None, intermediates=False):
+    """One KDA token-mixing layer.  x: [B, T, d_model] bf16; ``weights``: dict
+    with the bf16 tensors named in LAYER_WEIGHTS ([out, in]; conv taps
+    [H*128, 4]).  Returns y [B, T, d_model], or (y, dict of intermediate views
+    into the workspace: q, k, v, g, beta, o, zg, pre, low) with
+    ``intermediates=True``."""
+    import torch
+    B, T, d_model = x.shape
+    dev = x.device
+    rank = weights["W_down"].shape[0]
+    hd = H * 128
+    shapes = {"W_q": (hd, d_model), "W_k": (hd, d_model), "W_v": (hd, d_model),
+              "W_g": (hd, d_model), "conv_q": (hd, 4), "conv_k": (hd, 4), "conv_v": (hd, 4),
+              "W_down": (rank, d_model), "W_up": (hd, rank), "W_beta": (H, d_model),
+              "W_o": (d_model, hd)}
+    _need(x, "x", torch.bfloat16, (B, T, d_model), dev)
+    for n in LAYER_WEIGHTS:
+        _need(weights[n], n, torch.bfloat16, shapes[n], dev)
+    total, offs = layer_workspace_layout(B, T, d_model, H, rank)
+    if out is None:
+        out = torch.empty((B, T, d_model), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, (B, T, d_model), dev)
+    if workspace is None:
+        workspace = torch.empty(total, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < total:
+        raise ValueError(f"workspace must be a uint8 tensor of >= {total} bytes on {dev}")
+    st = lib().kda_layer_fwd(_ptr(x), *(_ptr(weights[n]) for n in LAYER_WEIGHTS), _ptr(out),
+                             B, T, d_model, H, rank, workspace.data_ptr(), workspace.numel(),
+                             _stream(dev))
+    _check("kda_layer_fwd", st)
+    if not intermediates:
+        return out
+    ldz = (rank + H + 3) // 4 * 4
+    bf, f32 = torch.bfloat16, torch.float32
+    views = {
+        "pre": _region(workspace, offs["pre"], bf, (B, T, 4 * hd)),
+        "low": _region(workspace, offs["low"], f32, (B, T, ldz)),
+        "q": _region(workspace, offs["q"], bf, (B, T, H, 128)),
+        "k": _region(workspace, offs["k"], bf, (B, T, H, 128)),
+        "v": _region(workspace, offs["v"], bf, (B, T, H, 128)),
+        "g": _region(workspace, offs["g"], f32, (B, T, H, 128)),
+        "beta": _region(workspace, offs["beta"], bf, (B, T, H)),
+        "o": _region(workspace, offs["o"], bf, (B, T, H, 128)),
+        "zg": _region(workspace, offs["zg"], bf, (B, T, hd)),
+    }
+    return out, views

@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(PKG, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_OK = 0
+# workspace regions of kda_layer_fwd, in the order of the KDA_LAYER_WS_* enum
+LAYER_REGIONS = ("pre", "low", "q", "k", "v", "g", "beta", "o", "zg", "chunk")
 STATUS_NAMES = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
                 -3: "KDA_ERR_ALIGNMENT", -4: "KDA_ERR_HIP"}
 
@@ -26,6 +28,8 @@ SIGNATURES = {
     "kda_chunk_fwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "kda_recurrent_step": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                 _I, _I, _I, _I, _I, _VP]),
+    "kda_layer_fwd": (_I, [_VP] * 13 + [_I] * 5 + [_VP, _SZ, _VP]),
+    "kda_layer_workspace_layout": (_SZ, [_I] * 5 + [ctypes.POINTER(_SZ)]),
     "kda_status_string": (ctypes.c_char_p, [_I]),
     "kda_version": (ctypes.c_char_p, []),
 }

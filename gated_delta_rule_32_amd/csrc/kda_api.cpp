@@ -166,4 +166,51 @@ int kda_recurrent_step(const void* q, const void* k, const void* v,
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+size_t kda_layer_workspace_layout(int B, int T, int d_model, int H, int rank, size_t* offsets)
+{
+    if (B < 0 || T < 0 || H <= 0 || d_model <= 0 || rank <= 0) return 0;
+    if (d_model % 64 || rank % 64) return 0;
+    const long long elems = (long long)B * T * 4 * H * kHeadDim;
+    if (elems >= ((long long)1 << 31)) return 0;
+    return kda::layer_ws_layout(B, T, H, rank, offsets);
+}
+
+int kda_layer_fwd(const void* x, const void* W_q, const void* W_k, const void* W_v,
+                  const void* W_g, const void* conv_q, const void* conv_k, const void* conv_v,
+                  const void* W_down, const void* W_up, const void* W_beta, const void* W_o,
+                  void* y, int B, int T, int d_model, int H, int rank,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || T < 0 || H <= 0 || d_model <= 0 || rank <= 0) return KDA_ERR_INVALID_ARG;
+    if (d_model % 64 || rank % 64) return KDA_ERR_UNSUPPORTED;
+    const long long R = (long long)B * T, HDm = (long long)H * kHeadDim;
+    if (R * 4 * HDm >= ((long long)1 << 31)) return KDA_ERR_UNSUPPORTED;
+    if (R == 0) return KDA_OK;
+
+    const size_t need = kda::layer_ws_layout(B, T, H, rank, nullptr);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    int rc;
+    const void* ptrs[] = {x, W_q, W_k, W_v, W_g, conv_q, conv_k, conv_v, W_down, W_up, W_beta, W_o, y};
+    for (const void* p : ptrs)
+        if ((rc = check_ptr(p, 16)) != KDA_OK) return rc;
+    if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
+    const size_t dm = (size_t)d_model, hd = (size_t)HDm, r = (size_t)rank;
+    const Range in[] = {{x, (size_t)R * dm * 2},   {W_q, hd * dm * 2},    {W_k, hd * dm * 2},
+                        {W_v, hd * dm * 2},        {W_g, hd * dm * 2},    {conv_q, hd * 8},
+                        {conv_k, hd * 8},          {conv_v, hd * 8},      {W_down, r * dm * 2},
+                        {W_up, hd * r * 2},        {W_beta, (size_t)H * dm * 2},
+                        {W_o, dm * hd * 2}};
+    const Range ry{y, (size_t)R * dm * 2}, rw{workspace, need};
+    for (const Range& a : in)
+        if (overlap(ry, a) || overlap(rw, a)) return KDA_ERR_INVALID_ARG;
+    if (overlap(ry, rw)) return KDA_ERR_INVALID_ARG;
+
+    typedef const kda::bf16_t* P;
+    const kda::LayerWeights Wt{(P)W_q, (P)W_k, (P)W_v, (P)W_g, (P)conv_q, (P)conv_k,
+                               (P)conv_v, (P)W_down, (P)W_up, (P)W_beta, (P)W_o};
+    hipError_t e = kda::launch_layer_fwd(Wt, (P)x, (kda::bf16_t*)y, B, T, d_model, H, rank,
+                                         (char*)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -1,0 +1,210 @@
+// kda_gemm.hip -- dense projections of the KDA token-mixing layer on gfx950.
+//
+// C[M, N] = A[M, K] * B[N, K]^T with both operands stored K-contiguous
+// (activations [tokens, features], weights [out_features, in_features]),
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation.  These are the
+// projections W_q, W_k, W_v, W_g, W_down, W_beta, W_up and W_o of the layer
+// on page "Kimi K3论文：Kimi Linear", section 3.
+//
+// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C, each of its
+// 4 waves a 64 x 64 sub-tile (4 x 4 MFMA tiles), over K in steps of 64.
+// Operand tiles are staged through double-buffered LDS (rows padded by 16 B
+// against bank conflicts); the next K-step's global loads are in flight while
+// the current step's MFMAs run, with one barrier per step.  The MFMA computes
+// C^T tiles (weights as the first operand) so that each lane ends up holding
+// 4 consecutive columns of one row of C, which it stores as one vector.
+//
+// Variants: A may be fp32 (AF32): each element is split into bf16 hi + lo
+// parts (x = hi + lo to about 16 bits) and two MFMAs are issued, which keeps
+// the low-rank gate path of the layer close to fp32 accuracy.  The epilogue
+// may apply g = -softplus(c) (the decay gate log alpha = -softplus(.)).
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int GT = 256;                  // threads
+constexpr int LDT = BK + 8;              // LDS row pitch (bf16 elements)
+
+__device__ __forceinline__ void block_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+template <typename T> __device__ __forceinline__ void store_out4(T* p, f32x4 v, int nvalid);
+template <> __device__ __forceinline__ void store_out4<float>(float* p, f32x4 v, int nvalid) {
+    if (nvalid >= 4) { *reinterpret_cast<f32x4*>(p) = v; return; }
+    for (int e = 0; e < nvalid; ++e) p[e] = v[e];
+}
+template <> __device__ __forceinline__ void store_out4<bf16_t>(bf16_t* p, f32x4 v, int nvalid) {
+    if (nvalid >= 4) {
+        bf16x4 b; b[0] = (bf16_t)v[0]; b[1] = (bf16_t)v[1]; b[2] = (bf16_t)v[2]; b[3] = (bf16_t)v[3];
+        *reinterpret_cast<bf16x4*>(p) = b;
+        return;
+    }
+    for (int e = 0; e < nvalid; ++e) p[e] = (bf16_t)v[e];
+}
+
+// -softplus(x) = -(max(x, 0) + log(1 + e^-|x|)), with hardware exp2/log2.
+__device__ __forceinline__ float neg_softplus(float x) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+    return -(fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * 0.6931471805599453f);
+}
+
+template <bool AF32, typename OutT, int EPI>
+__global__ void __launch_bounds__(GT)
+gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
+               int lda, int ldb, int ldc)
+{
+    constexpr int NA = AF32 ? 2 : 1;     // A planes in LDS (hi, lo)
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2][NA][BM * LDT];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDT];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int ln = lane & 15, lg = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;      // 64 x 64 sub-tile of the wave
+
+    // tile order: consecutive workgroups walk down M for a fixed N strip
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // global -> register staging: 16-byte units, rows clamped into range (rows
+    // past M or N compute values that are never stored)
+    constexpr int UA = AF32 ? 8 : 4;             // 16-byte units of A per thread
+    i32x4 ra[UA], rb[4];
+    auto gload = [&](int k0) {
+        if constexpr (AF32) {
+            const float* A = static_cast<const float*>(A_);
+#pragma unroll
+            for (int i = 0; i < UA; ++i) {       // 128 rows x 16 units of 4 floats
+                const int u = t + GT * i, row = u >> 4, cu = u & 15;
+                const int gr = min(m0 + row, M - 1);
+                ra[i] = *reinterpret_cast<const i32x4*>(A + (size_t)gr * lda + k0 + 4 * cu);
+            }
+        } else {
+            const bf16_t* A = static_cast<const bf16_t*>(A_);
+#pragma unroll
+            for (int i = 0; i < UA; ++i) {       // 128 rows x 8 units of 8 bf16
+                const int u = t + GT * i, row = u >> 3, cu = u & 7;
+                const int gr = min(m0 + row, M - 1);
+                ra[i] = *reinterpret_cast<const i32x4*>(A + (size_t)gr * lda + k0 + 8 * cu);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int u = t + GT * i, row = u >> 3, cu = u & 7;
+            const int gr = min(n0 + row, N - 1);
+            rb[i] = *reinterpret_cast<const i32x4*>(B + (size_t)gr * ldb + k0 + 8 * cu);
+        }
+    };
+    auto lstore = [&](int buf) {
+        if constexpr (AF32) {
+#pragma unroll
+            for (int i = 0; i < UA; ++i) {
+                const int u = t + GT * i, row = u >> 4, cu = u & 15;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&ra[i]);
+                bf16x4 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = (bf16_t)x[e];
+                    lo[e] = (bf16_t)(x[e] - (float)hi[e]);
+                }
+                *reinterpret_cast<bf16x4*>(&sA[buf][0][row * LDT + 4 * cu]) = hi;
+                *reinterpret_cast<bf16x4*>(&sA[buf][1][row * LDT + 4 * cu]) = lo;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < UA; ++i) {
+                const int u = t + GT * i, row = u >> 3, cu = u & 7;
+                *reinterpret_cast<i32x4*>(&sA[buf][0][row * LDT + 8 * cu]) = ra[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int u = t + GT * i, row = u >> 3, cu = u & 7;
+            *reinterpret_cast<i32x4*>(&sB[buf][row * LDT + 8 * cu]) = rb[i];
+        }
+    };
+
+    // acc[nb][mb]: C^T tile rows n = 64 wn + 16 nb + .., columns m = 64 wm + 16 mb + ..
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = K / BK;
+    gload(0);
+    lstore(0);
+    block_sync();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) gload((kt + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 32) {
+            bf16x8 fb[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                fb[nb] = *reinterpret_cast<const bf16x8*>(&sB[buf][(64 * wn + 16 * nb + ln) * LDT + kk + 8 * lg]);
+#pragma unroll
+            for (int p = 0; p < NA; ++p) {
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    const bf16x8 fa = *reinterpret_cast<const bf16x8*>(&sA[buf][p][(64 * wm + 16 * mb + ln) * LDT + kk + 8 * lg]);
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+                        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[nb], fa, acc[nb][mb], 0, 0, 0);
+                }
+            }
+        }
+        if (kt + 1 < KT) lstore(buf ^ 1);
+        block_sync();
+    }
+
+    // epilogue: lane holds C[m][n .. n+3] for m = .. + ln, n = .. + 4 lg
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int m = m0 + 64 * wm + 16 * mb + ln;
+            const int n = n0 + 64 * wn + 16 * nb + 4 * lg;
+            if (m < M && n < N) {
+                f32x4 v = acc[nb][mb];
+                if constexpr (EPI == 1) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = neg_softplus(v[e]);
+                }
+                store_out4<OutT>(C + (size_t)m * ldc + n, v, N - n);
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, bool c_f32,
+                          int epilogue, int M, int N, int K, int lda, int ldb, int ldc,
+                          hipStream_t stream)
+{
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const dim3 grid((unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN))), block(GT);
+#define KDA_GEMM(AF, OT, EP) \
+    hipLaunchKernelGGL((gemm_nt_kernel<AF, OT, EP>), grid, block, 0, stream, A, B, (OT*)C, M, N, K, lda, ldb, ldc)
+    if (a_f32) {
+        if (c_f32 && epilogue == 1) KDA_GEMM(true, float, 1);
+        else if (c_f32) KDA_GEMM(true, float, 0);
+        else KDA_GEMM(true, bf16_t, 0);
+    } else {
+        if (c_f32 && epilogue == 1) KDA_GEMM(false, float, 1);
+        else if (c_f32) KDA_GEMM(false, float, 0);
+        else KDA_GEMM(false, bf16_t, 0);
+    }
+#undef KDA_GEMM
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -3,6 +3,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include "../../include/kda.h"
+
 namespace kda {
 
 // Decode step over `heads` = N*H independent heads; dtype 0 = fp32, 1 = bf16.
@@ -28,5 +30,27 @@ bool chunk_prefers_two_kernel(long long B, long long T, long long H, int dtype);
 // S_T = S0 (or zeros when S0 is NULL) for `heads` states; used when T = 0.
 hipError_t launch_state_copy(const float* S0, float* S_T, long long heads,
                              hipStream_t stream);
+
+// C[M, N] = A[M, K] B[N, K]^T (both K-contiguous, K % 64 == 0, leading
+// dimensions in elements, multiples of 8).  A is bf16 or, with a_f32, fp32
+// (split into bf16 hi + lo parts); B is bf16; C is fp32 (c_f32) or bf16.
+// epilogue 0: none, 1: c -> -softplus(c).
+typedef __bf16 bf16_t;
+hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, bool c_f32,
+                          int epilogue, int M, int N, int K, int lda, int ldb, int ldc,
+                          hipStream_t stream);
+
+// Weights of one KDA token-mixing layer, all bf16, [out_features, in_features]
+// (conv taps [H*128, 4]).
+struct LayerWeights {
+    const bf16_t *W_q, *W_k, *W_v, *W_g, *conv_q, *conv_k, *conv_v, *W_down, *W_up, *W_beta, *W_o;
+};
+
+// Byte offsets of the layer's workspace regions (indexed by KDA_LAYER_WS_*,
+// written to `off` when non-null); returns the total size.
+size_t layer_ws_layout(long long B, long long T, long long H, long long rank, size_t* off);
+
+hipError_t launch_layer_fwd(const LayerWeights& W, const bf16_t* x, bf16_t* y, int B, int T,
+                            int d_model, int H, int rank, char* ws, hipStream_t stream);
 
 }  // namespace kda

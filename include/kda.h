@@ -123,6 +123,68 @@ int kda_recurrent_step(const void* q, const void* k, const void* v,
                        void* o, int N, int H, int dk, int dv, int dtype,
                        void* stream);
 
+/*
+ * One KDA token-mixing layer (page "Kimi K3论文：Kimi Linear", section 3:
+ * input parameterisation of q, k, v, alpha, beta, the KDA recurrence and the
+ * gated output path), for B sequences of T tokens, all bf16 except where noted:
+ *
+ *   q = L2Norm(Swish(ShortConv(W_q x)))    k likewise with W_k, conv_k
+ *   v = Swish(ShortConv(W_v x))
+ *   log alpha = -softplus(W_up (W_down x))  (fp32, rank = rows of W_down)
+ *   beta = Sigmoid(W_beta x)
+ *   o = KDA(q, k, v, log alpha, beta), zero initial state, per head
+ *   y = W_o (RMSNorm(o, per head) * Sigmoid(W_g x))
+ *
+ * ShortConv is causal and depthwise with 4 taps: for channel c,
+ * conv(x)_t = sum_{j=0..3} w[c][j] x_{t-3+j}, with x_s = 0 before the start of
+ * the sequence.  Swish(x) = x Sigmoid(x); L2Norm divides a head's 128 channels
+ * by sqrt(sum of squares + 1e-6); RMSNorm divides them by sqrt(mean of squares
+ * + 1e-6) (no gain).  No biases.
+ *
+ *   x       [B, T, d_model]            layer input
+ *   W_q, W_k, W_v, W_g  [H*128, d_model]
+ *   conv_q, conv_k, conv_v  [H*128, 4] taps, tap 3 multiplies the current token
+ *   W_down  [rank, d_model]   W_up [H*128, rank]   W_beta [H, d_model]
+ *   W_o     [d_model, H*128]
+ *   y       [B, T, d_model]   out
+ *   workspace  device scratch of at least kda_layer_workspace_layout(...)
+ *              bytes, 256-byte aligned, owned by the caller.  After the call
+ *              it holds the layer's intermediate tensors at the offsets that
+ *              kda_layer_workspace_layout reports (regions below).
+ * Requires d_model and rank to be multiples of 64, H >= 1 and B * T * 4 * H *
+ * 128 < 2^31.  T = 0 or B = 0 is a no-op.  Errors as for kda_chunk_fwd; y
+ * must not overlap any input or the workspace.  The intermediate activations
+ * are rounded to bf16 between steps (log alpha and the low-rank gate input
+ * stay fp32); the KDA step runs the same kernels as kda_chunk_fwd.
+ */
+enum {
+    KDA_LAYER_WS_PRE = 0,  /* [B*T, 4*H*128] bf16: W_q x | W_k x | W_v x | W_g x   */
+    KDA_LAYER_WS_LOW,      /* [B*T, ldz] fp32, ldz = rank + H rounded up to 4:
+                              W_down x (rank columns) then W_beta x (H columns)  */
+    KDA_LAYER_WS_Q,        /* [B, T, H, 128] bf16                                */
+    KDA_LAYER_WS_K,        /* [B, T, H, 128] bf16                                */
+    KDA_LAYER_WS_V,        /* [B, T, H, 128] bf16                                */
+    KDA_LAYER_WS_G,        /* [B, T, H, 128] fp32 log alpha                      */
+    KDA_LAYER_WS_BETA,     /* [B, T, H] bf16                                     */
+    KDA_LAYER_WS_O,        /* [B, T, H, 128] bf16 KDA output                     */
+    KDA_LAYER_WS_ZG,       /* [B*T, H*128] bf16 RMSNorm(o) * Sigmoid(W_g x)      */
+    KDA_LAYER_WS_CHUNK,    /* scratch of the chunked KDA schedule                */
+    KDA_LAYER_WS_REGIONS
+};
+
+int kda_layer_fwd(const void* x, const void* W_q, const void* W_k, const void* W_v,
+                  const void* W_g, const void* conv_q, const void* conv_k, const void* conv_v,
+                  const void* W_down, const void* W_up, const void* W_beta, const void* W_o,
+                  void* y, int B, int T, int d_model, int H, int rank,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes kda_layer_fwd needs for this shape; when `offsets` is not
+ * NULL it receives the byte offset of each of the KDA_LAYER_WS_REGIONS
+ * regions.  Invalid arguments return 0.
+ */
+size_t kda_layer_workspace_layout(int B, int T, int d_model, int H, int rank, size_t* offsets);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* kda_status_string(int status);
 

@@ -34,6 +34,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_recurrent_step",
+                          "kda_layer_fwd", "kda_layer_workspace_layout",
                           "kda_status_string", "kda_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -122,3 +123,53 @@ def test_binding_raises_without_gpu_tensors():
     x = torch.zeros(1, 4, 1, 128)
     with pytest.raises(ValueError):
         kda.chunk_fwd(x, x, x[..., :64], x, torch.zeros(1, 4, 1))
+
+
+# ----------------------------------------------------------------- layer
+LAYER_W = 11                                   # weight pointers of kda_layer_fwd
+
+
+def layer(lib, x=P, ws=P + 2**32, wsb=2**31, y=P + 2**33, B=1, T=64, dm=256, H=2, rank=64,
+          w=None):
+    w = list(w) if w is not None else [P + 2**34 + i * 2**26 for i in range(LAYER_W)]
+    return lib.kda_layer_fwd(x, *w, y, B, T, dm, H, rank, ws, wsb, None)
+
+
+def test_layer_workspace_layout(lib):
+    offs = (ctypes.c_size_t * 10)()
+    B, T, dm, H, r = 1, 32768, 2048, 16, 128
+    total = lib.kda_layer_workspace_layout(B, T, dm, H, r, offs)
+    R, hd = B * T, H * 128
+    sizes = [R * 4 * hd * 2, R * 144 * 4, R * hd * 2, R * hd * 2, R * hd * 2, R * hd * 4,
+             R * H * 2, R * hd * 2, R * hd * 2, H * 512 * 66048]
+    assert list(offs)[0] == 0
+    for i in range(9):
+        assert offs[i + 1] - offs[i] == (sizes[i] + 255) // 256 * 256
+        assert offs[i] % 256 == 0
+    assert total == offs[9] + sizes[9]
+    # many heads: the fused chunk kernel runs and needs no chunk scratch
+    total8 = lib.kda_layer_workspace_layout(8, 4096, 2048, 16, 128, offs)
+    assert total8 == offs[9]
+    assert lib.kda_layer_workspace_layout(1, 64, 100, 2, 64, None) == 0     # d_model % 64
+    assert lib.kda_layer_workspace_layout(1, 64, 256, 2, 96, None) == 0     # rank % 64
+    assert lib.kda_layer_workspace_layout(1, 2**20, 2048, 16, 128, None) == 0  # too large
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(ws=None), INVALID),
+    (dict(wsb=1000), INVALID),                  # workspace too small
+    (dict(B=-1), INVALID), (dict(H=0), INVALID), (dict(rank=0), INVALID),
+    (dict(dm=100), UNSUP), (dict(rank=96), UNSUP), (dict(T=2**20, dm=2048, H=16), UNSUP),
+    (dict(x=P + 8), ALIGN), (dict(ws=P + 2**32 + 128), ALIGN),
+    (dict(w=[None] + [P + 2**34 + i * 2**26 for i in range(1, LAYER_W)]), INVALID),
+    (dict(w=[P + 2**34 + i * 2**26 + (4 if i == 5 else 0) for i in range(LAYER_W)]), ALIGN),
+    (dict(y=P), INVALID),                       # y overlaps x
+    (dict(y=P + 2**32 + 4096), INVALID),        # y inside the workspace
+    (dict(ws=P + 2**34), INVALID),              # workspace overlaps W_q
+])
+def test_layer_fwd_rejects(lib, kw, code):
+    assert layer(lib, **kw) == code
+
+
+def test_layer_fwd_empty_is_noop(lib):
+    assert layer(lib, T=0, x=None, y=None, ws=None, wsb=0) == OK

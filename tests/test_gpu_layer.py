@@ -1,0 +1,90 @@
+"""GPU parity of the KDA token-mixing layer (kda_layer_fwd) against the fp64
+layer oracle: the output y and every intermediate the layer exposes in its
+workspace (projections, conv/activation outputs, gates, KDA output, gated
+norm), on small shapes, on the full-width shape with a short sequence, and on
+the full 32768-token workload."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+kda = pytest.importorskip("gated_delta_rule_32_amd")
+from gated_delta_rule_32_amd import inputs  # noqa: E402
+from oracle import kda_layer_ref  # noqa: E402
+from kda_testutil import max_rel_err  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2     # bf16 inputs and outputs
+TOL_G = 1e-3        # log alpha stays fp32 through the low-rank path
+
+
+def run_layer(B, T, d_model, H, rank, seed):
+    inp = inputs.layer_inputs(B=B, T=T, d_model=d_model, H=H, seed=seed, gate_rank=rank)
+    dev = torch.device("cuda", 0)
+    W = {n: inp[n].to(dev) for n in kda.LAYER_WEIGHTS}
+    print(f"layer B={B} T={T} d_model={d_model} H={H} rank={rank} seed={seed}", flush=True)
+    y, iv = kda.layer_fwd(inp["x"].to(dev), W, H, intermediates=True)
+    torch.cuda.synchronize()
+    return inp, y.cpu(), {n: t.cpu() for n, t in iv.items()}
+
+
+def oracle(inp, H):
+    W = {n: inp[n] for n in kda.LAYER_WEIGHTS}
+    return kda_layer_ref.layer_forward(inp["x"], W, H)
+
+
+def check(inp, y, iv, H, full_intermediates=True):
+    y_ref, o_ref, parts = oracle(inp, H)
+    errs = {"y": max_rel_err(y, y_ref), "o": max_rel_err(iv["o"], o_ref)}
+    if full_intermediates:
+        B, T = y.shape[:2]
+        for n in ("q", "k", "v", "g", "beta"):
+            ref = np.stack([p[n] for p in parts])
+            errs[n] = max_rel_err(iv[n], ref)
+        gate = np.stack([p["gate"] for p in parts])
+        errs["gate_pre"] = max_rel_err(iv["pre"][..., 3 * H * 128:], gate)
+        zg = kda_layer_ref.rmsnorm_heads(o_ref.reshape(B * T, H * 128), H, 128).reshape(B, T, -1)
+        errs["zg"] = max_rel_err(iv["zg"], zg * kda_layer_ref.sigmoid(gate))
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= (TOL_G if n == "g" else TOL_BF16), (n, e)
+    assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("B,T,d_model,H,rank", [
+    (2, 200, 256, 2, 64),      # two-kernel KDA schedule, ragged last chunk
+    (1, 64, 256, 2, 64),       # one chunk: fused KDA kernel
+    (3, 77, 192, 1, 64),       # d_model not a multiple of the 128-wide GEMM tile
+    (1, 1, 256, 2, 64),        # single token
+    (8, 130, 256, 16, 128),    # 128 heads: fused KDA kernel, H * 128 = 2048 channels
+])
+def test_layer_small_shapes(B, T, d_model, H, rank):
+    inp, y, iv = run_layer(B, T, d_model, H, rank, seed=11)
+    check(inp, y, iv, H)
+
+
+def test_layer_full_width_short_sequence():
+    inp, y, iv = run_layer(1, 1000, 2048, 16, 128, seed=12)
+    check(inp, y, iv, 16)
+
+
+@pytest.mark.timeout(900)
+def test_layer_full_workload():
+    """The 32768-token, d_model 2048, 16-head layer in full, against the
+    complete fp64 oracle (about half a minute of host time)."""
+    cfg = {k: v for k, v in inputs.LAYER_CONFIG.items() if k != "dtype"}
+    inp, y, iv = run_layer(cfg["B"], cfg["T"], cfg["d_model"], cfg["H"], 128, cfg["seed"])
+    check(inp, y, iv, cfg["H"], full_intermediates=False)
+
+
+def test_layer_validates_tensors():
+    dev = torch.device("cuda", 0)
+    inp = inputs.layer_inputs(B=1, T=8, d_model=256, H=2, seed=1, gate_rank=64)
+    W = {n: inp[n].to(dev) for n in kda.LAYER_WEIGHTS}
+    x = inp["x"].to(dev)
+    with pytest.raises(ValueError):
+        kda.layer_fwd(x, {**W, "W_o": W["W_o"][:, :128].contiguous()}, 2)
+    with pytest.raises(TypeError):
+        kda.layer_fwd(x.float(), W, 2)
+    with pytest.raises(ValueError):
+        kda.layer_fwd(x, W, 2, workspace=torch.empty(16, dtype=torch.uint8, device=dev))
