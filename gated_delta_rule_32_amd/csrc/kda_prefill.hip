@@ -109,6 +109,22 @@ __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NB], const E* A, int lda, 
     }
 }
 
+// ---- lane exchange between 16-lane rows -----------------------------------
+// Value held by lane l ^ 16 (rows 0<->1, 2<->3) and by lane l ^ 32 (rows
+// 0,1 <-> 2,3), with the gfx950 row-swap instructions (plain VALU, unlike a
+// general shuffle, which goes through the LDS crossbar).  Inactive source
+// lanes are read too (fetch-inactive set), so a call under a partial exec
+// mask still sees the partner's value; callers nevertheless call these with
+// the whole wave active.
+__device__ __forceinline__ float lane_xor16(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), true, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), true, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
+
 // ---- element pairs and runs ------------------------------------------------
 template <typename E> struct Pair;
 template <> struct Pair<bf16_t> { typedef bf16x2 type; };
@@ -401,8 +417,9 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 
         // ===== E: cumulative log2-decay and the decay-scaled operands =====
         // G is kept in log2 units so that 2^G = e^{sum g}.  Each lane owns
-        // 8 channels x 4 consecutive rows; the prefix over rows is local, then
-        // across the 4 row quads of a wave (shuffles), then across waves (LDS).
+        // 8 channels x 2 consecutive rows; the prefix over rows is local, then
+        // across the 4 row pairs of a wave (row-swap exchanges), then across
+        // waves (LDS).
         // Full chunks take a path without per-row masking.
         auto ephase = [&](auto masked_t) {
             constexpr bool MASKED = decltype(masked_t)::value;
@@ -418,11 +435,11 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     run += row_ok(r0 + i) ? gi : 0.f;
                     G[i][c] = run;
                 }
-                float inc = run;                       // inclusive scan over rq
-                float up = __shfl_up(inc, 16);
-                inc += rq >= 1 ? up : 0.f;
-                up = __shfl_up(inc, 32);
-                inc += rq >= 2 ? up : 0.f;
+                // inclusive scan over rq: pairs (0,1), (2,3), then the lower
+                // pair's total into the upper pair
+                const float p16 = lane_xor16(run, lane);
+                const float p32 = lane_xor32(run + p16, lane);   // other pair's total
+                const float inc = run + ((rq & 1) ? p16 : 0.f) + ((rq & 2) ? p32 : 0.f);
                 const float excl = inc - run;
 #pragma unroll
                 for (int i = 0; i < RPL; ++i) G[i][c] += excl;
@@ -551,7 +568,9 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
                     const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
                     const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
-                    *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = z4;
+                    // (bf16: only the lower blocks of Akk are ever read; fp32
+                    // turns Akk into Tm in place, whose upper blocks are read)
+                    if constexpr (L::kF32) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = z4;
                     store_vec4<E>(sQK + r * L::P64 + i0, z4);
                 }
             }
@@ -630,7 +649,10 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         // Prefetch the next chunk while the rest of this one is computed.  It is
         // issued here, not earlier, so that its registers are free during the
         // register-heavy Akk/Aqk products and diagonal-block substitution.
-        if (!PREP && n + 1 < nchunks) load_chunk(n + 1, in);
+        // Waves 3-7, which have little work in the off-diagonal step, issue
+        // first; waves 0-2 issue after their substitution chains, so that the
+        // chains do not queue behind the address unit.
+        if (!PREP && wave >= 3 && n + 1 < nchunks) load_chunk(n + 1, in);
 
         // ===== UT off-diagonal blocks; Tm Diag(beta) in E =====
         if constexpr (!L::kF32) {
@@ -654,8 +676,10 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     store_vec4<E>(RT + (16 * R + ln) * L::P64 + 16 * I + 4 * lg, z4);
                 }
             }
+            if (!PREP && wave < 3 && n + 1 < nchunks) load_chunk(n + 1, in);
             lds_barrier();
         } else {
+            if (!PREP && wave < 3 && n + 1 < nchunks) load_chunk(n + 1, in);
             // fp32: block rows R = 1..3 by plain dot products, in place in RA,
             // then scale the columns by beta.
             float* s_z = reinterpret_cast<float*>(sVN);   // Vn^T is not in use yet
@@ -732,11 +756,12 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         }
         lds_barrier();
 
-        // ===== O += Aqk Vn (to HBM, waves 1-3) | S <- Diag(gamma) (S + Kb^T Vn) =====
-        if (wave > 0) {
+        // ===== O += Aqk Vn (to HBM; the parked Qt S tiles, spread over all
+        // waves) | S <- Diag(gamma) (S + Kb^T Vn) =====
+        {
 #pragma unroll
-            for (int m = 0; m < MO; ++m) {
-                const int tt = (wave - 1) + (NW - 1) * m;
+            for (int m = 0; m < (NO + NW - 1) / NW; ++m) {
+                const int tt = wave + NW * m;
                 if (tt < NO) {
                     const int jb = tt / 4, R = tt % 4;
                     f32x4 one[1] = {*reinterpret_cast<const f32x4*>(sOI + (tt * 64 + lane) * 4)};
