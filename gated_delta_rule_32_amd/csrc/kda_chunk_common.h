@@ -1,0 +1,197 @@
+// kda_chunk_common.h -- device helpers shared by the chunked KDA kernels
+// (the fused and two-kernel schedules in kda_prefill.hip and the
+// wave-specialised schedule in kda_prefill_ws.hip).  Internal to libkda.
+#pragma once
+#include "kda_device.h"
+
+namespace kda {
+namespace {
+
+constexpr int C = 64;     // chunk length
+constexpr int DK = 128;   // key / value head dimension
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Barrier that orders LDS traffic only: global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---- MFMA wrappers -------------------------------------------------------
+// A 16 x 16 output tile D = A B.  `frag_kc` fetches an operand from a row-major
+// LDS matrix whose rows are the tile's M (or N) index and whose columns are the
+// contraction index (pitch `ld`); `frag_mc` (fp32 only) fetches it from the
+// transposed layout.  Both operands of one product use the same per-lane
+// contraction slots, so the product is a plain sum over k.
+// Output: acc[e] holds D[4 * (lane / 16) + e][lane % 16].
+template <typename E> struct Mma;
+
+template <> struct Mma<bf16_t> {
+    static constexpr int KS = 32;
+    typedef bf16x8 frag_t;
+    __device__ static frag_t frag_kc(const bf16_t* p, int ld, int row0, int k0, int lane) {
+        return *reinterpret_cast<const bf16x8*>(p + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+    }
+    __device__ static f32x4 mma(frag_t a, frag_t b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int KS = 4;
+    typedef float frag_t;
+    __device__ static frag_t frag_kc(const float* p, int ld, int row0, int k0, int lane) {
+        return p[(row0 + (lane & 15)) * ld + k0 + (lane >> 4)];
+    }
+    __device__ static frag_t frag_mc(const float* p, int ld, int row0, int k0, int lane) {
+        return p[(k0 + (lane >> 4)) * ld + row0 + (lane & 15)];
+    }
+    __device__ static f32x4 mma(frag_t a, frag_t b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// acc[t] += A[arow0.., K] * B[brow[t].., K]^T over k in [0, K); A fragments are
+// loaded once and reused for the NB output tiles.
+template <typename E, int K, int NB>
+__device__ __forceinline__ void mma_rows(f32x4 (&acc)[NB], const E* A, int lda, int arow0,
+                                         const E* B, int ldb, const int (&brow)[NB], int lane) {
+    constexpr int UNR = (K / Mma<E>::KS) < 2 ? (K / Mma<E>::KS) : 2;
+#pragma unroll UNR
+    for (int k = 0; k < K; k += Mma<E>::KS) {
+        const auto a = Mma<E>::frag_kc(A, lda, arow0, k, lane);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) acc[t] = Mma<E>::mma(a, Mma<E>::frag_kc(B, ldb, brow[t], k, lane), acc[t]);
+    }
+}
+
+// ---- lane exchange between 16-lane rows -----------------------------------
+// Value held by lane l ^ 16 (rows 0<->1, 2<->3) and by lane l ^ 32 (rows
+// 0,1 <-> 2,3), with the gfx950 row-swap instructions (plain VALU, unlike a
+// general shuffle, which goes through the LDS crossbar).  Inactive source
+// lanes are read too (fetch-inactive set), so a call under a partial exec
+// mask still sees the partner's value; callers nevertheless call these with
+// the whole wave active.
+__device__ __forceinline__ float lane_xor16(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), true, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), true, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
+
+// ---- element pairs and runs ------------------------------------------------
+template <typename E> struct Pair;
+template <> struct Pair<bf16_t> { typedef bf16x2 type; };
+template <> struct Pair<float> { typedef float2 type; };
+
+__device__ __forceinline__ float2 unpack(bf16x2 x) { return make_float2((float)x[0], (float)x[1]); }
+__device__ __forceinline__ float2 unpack(float2 x) { return x; }
+template <typename E> __device__ __forceinline__ typename Pair<E>::type pack(float a, float b);
+template <> __device__ __forceinline__ bf16x2 pack<bf16_t>(float a, float b) {
+    bf16x2 r; r[0] = (bf16_t)a; r[1] = (bf16_t)b; return r;
+}
+template <> __device__ __forceinline__ float2 pack<float>(float a, float b) { return make_float2(a, b); }
+
+template <typename E> __device__ __forceinline__ void store_vec4(E* p, f32x4 x);
+template <> __device__ __forceinline__ void store_vec4<bf16_t>(bf16_t* p, f32x4 x) {
+    bf16x4 v; v[0] = (bf16_t)x[0]; v[1] = (bf16_t)x[1]; v[2] = (bf16_t)x[2]; v[3] = (bf16_t)x[3];
+    *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void store_vec4<float>(float* p, f32x4 x) {
+    *reinterpret_cast<f32x4*>(p) = x;
+}
+template <typename E> __device__ __forceinline__ f32x4 load_vec4(const E* p);
+template <> __device__ __forceinline__ f32x4 load_vec4<bf16_t>(const bf16_t* p) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <> __device__ __forceinline__ f32x4 load_vec4<float>(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+
+// Store N contiguous values (N = 1, 2, 4, 8, ...).
+template <typename E, int N>
+__device__ __forceinline__ void store_run(E* p, const float* x) {
+    if constexpr (N == 1) {
+        *p = (E)x[0];
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<typename Pair<E>::type*>(p) = pack<E>(x[0], x[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) store_vec4<E>(p + i, f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]});
+    }
+}
+
+// ---- UT transform, off-diagonal blocks of one block column -------------------
+// Column I of X = (I + A)^{-1} (A strictly lower, 4x4 blocks of 16, diagonal
+// blocks X_RR already inverted in place in RA):  X_RI = -X_RR sum_{J=I}^{R-1}
+// A_RJ X_JI.  The products are 16x16x16 bf16 MFMAs chained through registers:
+// the D layout of one product (lane holds rows 4*(lane/16)+e of column
+// lane%16) is exactly the B-operand layout of the next.  Each X_RI is written
+// to RT scaled by beta of its column.
+__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
+    bf16x4 r; r[0] = (bf16_t)x[0]; r[1] = (bf16_t)x[1]; r[2] = (bf16_t)x[2]; r[3] = (bf16_t)x[3];
+    return r;
+}
+
+template <int I, int PA, int PT>
+__device__ __forceinline__ void ut_offdiag_column(const float* RA, bf16_t* RT, const float* s_beta, int lane) {
+    const int ln = lane & 15, lg = lane >> 4;
+    auto a_op = [&](int R, int J) {   // A operand: block (R, J) of RA, row-major
+        return to_bf16x4(*reinterpret_cast<const f32x4*>(RA + (16 * R + ln) * PA + 16 * J + 4 * lg));
+    };
+    f32x4 X[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[I][e] = RA[(16 * I + 4 * lg + e) * PA + 16 * I + ln];
+    const float bcol = s_beta[16 * I + ln];
+#pragma unroll
+    for (int R = I + 1; R < 4; ++R) {
+        f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = I; J < R; ++J)
+            Y = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_op(R, J), to_bf16x4(X[J]), Y, 0, 0, 0);
+        X[R] = -__builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_op(R, R), to_bf16x4(Y),
+                                                          f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) RT[(16 * R + 4 * lg + e) * PT + 16 * I + ln] = (bf16_t)(bcol * X[R][e]);
+    }
+}
+
+// Eight consecutive elements (one 16-byte load for bf16, two for fp32).
+template <typename E> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    bf16x8 x;
+    __device__ __forceinline__ void load(const bf16_t* p) { x = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ float operator[](int i) const { return (float)x[i]; }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const f32x4*>(p)[0];
+        b = reinterpret_cast<const f32x4*>(p)[1];
+    }
+    __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+struct Raw8f {   // eight fp32 values (the log-decay)
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const f32x4*>(p)[0];
+        b = reinterpret_cast<const f32x4*>(p)[1];
+    }
+    __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+template <typename E> __device__ __forceinline__ void store8(E* p, const float* x);
+template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* x) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16_t)x[i];
+    *reinterpret_cast<bf16x8*>(p) = v;
+}
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* x) {
+    reinterpret_cast<f32x4*>(p)[0] = f32x4{x[0], x[1], x[2], x[3]};
+    reinterpret_cast<f32x4*>(p)[1] = f32x4{x[4], x[5], x[6], x[7]};
+}
+
+}  // namespace
+}  // namespace kda
