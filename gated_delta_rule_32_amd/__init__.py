@@ -56,7 +56,7 @@ def workspace_size(B, T, H, dtype_code, d=128):
 
 def scan_workspace_bytes(B, T, H):
     """Workspace that selects the two-kernel schedule for any bf16 shape."""
-    return B * H * ((T + 63) // 64) * 66048
+    return B * H * ((T + 63) // 64) * 72704
 
 
 def _workspace(device, nbytes):

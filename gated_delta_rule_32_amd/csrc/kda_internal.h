@@ -20,7 +20,7 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             void* o, float* S_T, int B, int T, int H, int dtype,
                             void* ws, hipStream_t stream);
 
-// Bytes of workspace the two-kernel schedule needs: one 66,048-byte block of
+// Bytes of workspace the two-kernel schedule needs: one 72,704-byte block of
 // key-side operands per (batch, head, 64-token chunk).
 size_t chunk_ws_bytes(long long B, long long T, long long H);
 

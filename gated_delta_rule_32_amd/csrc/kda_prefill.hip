@@ -109,14 +109,19 @@ struct ChunkIn {
 };
 
 // Workspace block of one chunk, written by the prep instantiation of the
-// kernel below and read by chunk_scan_kernel (bf16 only).  Byte offsets:
-constexpr int WS_QT = 0;                       // Qt   [64][128] bf16, token-major
-constexpr int WS_KH = WS_QT + C * DK * 2;      // Kh   [64][128] bf16, token-major
-constexpr int WS_KBT = WS_KH + C * DK * 2;     // Kb^T [128][64] bf16, channel-major
-constexpr int WS_TM = WS_KBT + DK * C * 2;     // Tm Diag(beta) [64][64] bf16
-constexpr int WS_QK = WS_TM + C * C * 2;       // Aqk  [64][64] bf16
-constexpr int WS_GAM = WS_QK + C * C * 2;      // e^{G_64} [128] fp32
-constexpr int WS_CHUNK = WS_GAM + DK * 4;      // 66,048 bytes
+// kernel below and read by chunk_scan_kernel (bf16 only).  It is the image of
+// the scan's LDS stage: rows keep their 16-byte padding and Kb^T its swizzle,
+// so the scan copies it linearly.  Byte offsets:
+constexpr int WS_P128 = DK + 8, WS_P64 = C + 8;    // padded row pitches (elements)
+constexpr int WS_QT = 0;                            // Qt   [64][136] bf16, token-major
+constexpr int WS_KH = WS_QT + C * WS_P128 * 2;      // Kh   [64][136] bf16, token-major
+constexpr int WS_KBT = WS_KH + C * WS_P128 * 2;     // Kb^T [128][72] bf16, channel-major, swizzled
+constexpr int WS_TM = WS_KBT + DK * WS_P64 * 2;     // Tm Diag(beta) [64][72] bf16
+constexpr int WS_QK = WS_TM + C * WS_P64 * 2;       // Aqk  [64][72] bf16
+constexpr int WS_GAM = WS_QK + C * WS_P64 * 2;      // e^{G_64} [128] fp32
+constexpr int WS_USED = WS_GAM + DK * 4;            // 72,192 bytes written
+constexpr int WS_CHUNK = (WS_USED + 1023) / 1024 * 1024;   // 72,704: whole KiB per block
+constexpr int PREP_CHUNKS = 4;                      // chunks per prep workgroup
 
 // The fused kernel (PREP = false): one workgroup per (head, value slice)
 // walks all chunks of its head.  The prep instantiation (PREP = true): one
@@ -172,12 +177,13 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     // (workgroups are dealt to the 8 XCDs round-robin); prep: (head, chunk).
     const int nwg = gridDim.x, w = blockIdx.x;
     const int lid = (!PREP && nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
-    const int head = PREP ? lid / nchunks : lid / nsplit;
+    const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;   // prep: chunk groups per head
+    const int head = PREP ? lid / nblk : lid / nsplit;
     const int slice = PREP ? 0 : lid % nsplit;
     const int b = head / H, h = head % H;
     const int j0 = slice * DV;
-    const int n_first = PREP ? lid % nchunks : 0;
-    const int n_end = PREP ? n_first + 1 : nchunks;
+    const int n_first = PREP ? (lid % nblk) * PREP_CHUNKS : 0;
+    const int n_end = PREP ? min(n_first + PREP_CHUNKS, nchunks) : nchunks;
 
     const size_t tokstride = (size_t)H * DK;                       // one token, all heads
     const size_t hbase = ((size_t)b * T * H + h) * DK;             // (b, t=0, h, 0)
@@ -468,7 +474,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         // Waves 3-7, which have little work in the off-diagonal step, issue
         // first; waves 0-2 issue after their substitution chains, so that the
         // chains do not queue behind the address unit.
-        if (!PREP && wave >= 3 && n + 1 < nchunks) load_chunk(n + 1, in);
+        if (wave >= 3 && n + 1 < n_end) load_chunk(n + 1, in);
 
         // ===== UT off-diagonal blocks; Tm Diag(beta) in E =====
         if constexpr (!L::kF32) {
@@ -492,10 +498,10 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     store_vec4<E>(RT + (16 * R + ln) * L::P64 + 16 * I + 4 * lg, z4);
                 }
             }
-            if (!PREP && wave < 3 && n + 1 < nchunks) load_chunk(n + 1, in);
+            if (wave < 3 && n + 1 < n_end) load_chunk(n + 1, in);
             lds_barrier();
         } else {
-            if (!PREP && wave < 3 && n + 1 < nchunks) load_chunk(n + 1, in);
+            if (wave < 3 && n + 1 < n_end) load_chunk(n + 1, in);
             // fp32: block rows R = 1..3 by plain dot products, in place in RA,
             // then scale the columns by beta.
             float* s_z = reinterpret_cast<float*>(sVN);   // Vn^T is not in use yet
@@ -528,24 +534,20 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 
         if constexpr (PREP) {
             // ===== export the key-side operands of this chunk =====
+            // (byte copies of the LDS regions: the layouts already match)
             char* blk = ws + ((size_t)head * nchunks + n) * WS_CHUNK;
             typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-            for (int u = t; u < C * DK / 8; u += NT) {            // Qt, Kh: [64][128]
-                const int r = u >> 4, cb = u & 15;
-                reinterpret_cast<i32x4*>(blk + WS_QT)[u] = *reinterpret_cast<const i32x4*>(sQt + r * L::P128 + 8 * cb);
-                reinterpret_cast<i32x4*>(blk + WS_KH)[u] = *reinterpret_cast<const i32x4*>(sKh + r * L::P128 + 8 * cb);
-            }
-            for (int u = t; u < DK * C / 8; u += NT) {            // Kb^T: [128][64], unswizzled
-                const int c = u >> 3, b8 = u & 7;
-                reinterpret_cast<i32x4*>(blk + WS_KBT)[u] = *reinterpret_cast<const i32x4*>(sKbT + L::kbt(c, 8 * b8));
-            }
-            for (int u = t; u < C * C / 8; u += NT) {             // Tm Diag(beta), Aqk: [64][64]
-                const int r = u >> 3, b8 = u & 7;
-                reinterpret_cast<i32x4*>(blk + WS_TM)[u] = *reinterpret_cast<const i32x4*>(RT + r * L::P64 + 8 * b8);
-                reinterpret_cast<i32x4*>(blk + WS_QK)[u] = *reinterpret_cast<const i32x4*>(sQK + r * L::P64 + 8 * b8);
-            }
-            if (t < DK / 4)
-                reinterpret_cast<f32x4*>(blk + WS_GAM)[t] = reinterpret_cast<const f32x4*>(s_gam)[t];
+            static_assert(L::P128 == WS_P128 && L::P64 == WS_P64, "workspace rows match the LDS rows");
+            static_assert(L::OFF_KH == L::OFF_QT + C * WS_P128 * 2, "Qt and Kh are adjacent");
+            auto copy = [&](int dst, int src, int bytes) {
+                for (int u = t; u < bytes / 16; u += NT)
+                    reinterpret_cast<i32x4*>(blk + dst)[u] = reinterpret_cast<const i32x4*>(smem + src)[u];
+            };
+            copy(WS_QT, L::OFF_QT, WS_KBT - WS_QT);       // Qt and Kh
+            copy(WS_KBT, L::OFF_KBT, WS_TM - WS_KBT);
+            copy(WS_TM, L::OFF_RT, WS_QK - WS_TM);
+            copy(WS_QK, L::OFF_QK, WS_GAM - WS_QK);
+            copy(WS_GAM, L::OFF_GAM, WS_USED - WS_GAM);
             continue;
         }
 
@@ -637,225 +639,246 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 
 
 // ---- serial scan over chunks from the workspace (bf16) --------------------
-// One workgroup per (head, value slice), 8 waves.  For every chunk it loads
-// the key-side operands that chunk_fwd_kernel<.., PREP = true> exported (the
-// slices of one head read the same bytes, shared through L2) and the V slice,
-// and runs only the state-dependent products:
-//   Z = V - Kh S;  Vn = Tm Diag(beta) Z;  O = Qt S + Aqk Vn;
-//   S <- Diag(gamma) (S + Kb^T Vn).
-// The next chunk's operands are fetched into registers while the current one
-// is computed.
-template <int DV>
-struct ScanLayout {
-    typedef bf16_t E;
-    static constexpr int ES = 2, PAD = 8;
-    static constexpr int P128 = DK + PAD, P64 = C + PAD, PV = DV + PAD;
-    static constexpr int OFF_QT = 0;
-    static constexpr int OFF_KH = OFF_QT + C * P128 * ES;
-    static constexpr int OFF_KBT = OFF_KH + C * P128 * ES;
-    static constexpr int OFF_TM = OFF_KBT + DK * P64 * ES;
-    static constexpr int OFF_QK = OFF_TM + C * P64 * ES;
-    static constexpr int OFF_V = OFF_QK + C * P64 * ES;
-    static constexpr int OFF_ST = OFF_V + C * PV * ES;
-    static constexpr int OFF_ZT = OFF_ST + DV * P128 * ES;
-    static constexpr int OFF_VN = OFF_ZT + DV * P64 * ES;
-    static constexpr int OFF_GAM = OFF_VN + DV * P64 * ES;
-    static constexpr int TOTAL = OFF_GAM + DK * 4;
+// One workgroup per (head, 16 NCW value columns), NCW + 4 waves:
+//   waves 0-3 (loaders) move data: the next chunk's workspace block -- the
+//     key-side operands Qt, Kh, Kb^T, Tm Diag(beta), Aqk, e^{G_64} of that
+//     chunk, laid out as this kernel's LDS image -- is copied global -> LDS
+//     directly (16-byte LDS-destination loads) into the other of two stages,
+//     the V slice is written transposed next to it, and the previous chunk's
+//     output is stored from an LDS staging tile to HBM with 16-byte stores;
+//   waves 4.. (consumers) each own 16 value columns and keep their 128 x 16
+//     slice of the state in MFMA accumulators.  For chunk n they form
+//       P = Kh S,  Qt S,  Z = V - P,  Vn = Tm Z,  O = Qt S + Aqk Vn (to LDS),
+//       S <- Diag(e^{G_64}) (S + Kb^T Vn)
+//     chaining every product through registers: the accumulator layout of one
+//     product (lane holds rows 4*(lane/16)+e of column lane%16) is the
+//     B-operand layout of the next.  Only A-operands are read from LDS, and
+//     consumers issue no global memory operations inside the loop.
+// One barrier per chunk.  The 16x16x32 MFMA takes eight contraction values per
+// lane; the consumers feed it two 16-row blocks at once (four values from
+// each), reading the A-operand with the same split, so each product is a
+// plain sum over k.
+constexpr int SC_NLW = 4;                                 // loader waves
+constexpr int SC_KIB = WS_CHUNK / 1024;                   // 1 KiB pieces per block
+template <int NCW> struct ScanCfg {                       // NCW consumer waves
+    static constexpr int DV = 16 * NCW;                   // value columns per workgroup
+    static constexpr int NT = 64 * (SC_NLW + NCW);
+    static constexpr int OFF_VT = 0;                      // V^T [DV cols][72] bf16
+    static constexpr int OFF_BLK = DV * WS_P64 * 2;       // workspace image
+    static constexpr int STAGE = OFF_BLK + WS_CHUNK;
+    static constexpr int OFF_O = 2 * STAGE;               // output staging [2][64][DV] bf16
+    static constexpr int TOTAL = OFF_O + 2 * C * DV * 2;
+    static constexpr int VG = DV / 8;                     // 16-byte units per token row
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
-    __device__ static constexpr int kbt(int c, int i) {
-        return c * P64 + ((((i >> 3) ^ ((c >> 3) & 7)) << 3) | (i & 7));
-    }
+    static_assert(C * VG <= 64 * SC_NLW, "one V / output unit per loader lane");
 };
 
-template <int DV>
-__global__ void __launch_bounds__(NT)
-chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
-                  int T, int H, int nsplit)
-{
-    typedef bf16_t E;
-    using L = ScanLayout<DV>;
-    using M = Mma<E>;
-    typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-    constexpr int NJ = DV / 16;
-    constexpr int VL = DV / 8;              // lanes per value row (16 bytes each)
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[i + 4] = b[i]; }
+    return r;
+}
+__device__ __forceinline__ bf16x4 ld4(const bf16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
-    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-    E* sQt = reinterpret_cast<E*>(smem + L::OFF_QT);
-    E* sKh = reinterpret_cast<E*>(smem + L::OFF_KH);
-    E* sKbT = reinterpret_cast<E*>(smem + L::OFF_KBT);
-    E* sTM = reinterpret_cast<E*>(smem + L::OFF_TM);
-    E* sQK = reinterpret_cast<E*>(smem + L::OFF_QK);
-    E* sV = reinterpret_cast<E*>(smem + L::OFF_V);
-    E* sST = reinterpret_cast<E*>(smem + L::OFF_ST);
-    E* sZT = reinterpret_cast<E*>(smem + L::OFF_ZT);
-    E* sVN = reinterpret_cast<E*>(smem + L::OFF_VN);
-    float* s_gam = reinterpret_cast<float*>(smem + L::OFF_GAM);
+// Two adjacent 16-column blocks (2p, 2p+1) of one row as an A-operand: lane
+// (row ln, group lg) takes columns 32p + 4lg .. +3 and 32p + 16 + 4lg .. +3;
+// with `hi` false the second half is zero.
+__device__ __forceinline__ bf16x8 a_pair(const bf16_t* row, int p, int lg, bool hi) {
+    const bf16x4 a = ld4(row + 32 * p + 4 * lg);
+    const bf16x4 b = hi ? ld4(row + 32 * p + 16 + 4 * lg) : bf16x4{};
+    return cat8(a, b);
+}
+
+template <int NCW>
+__global__ void __launch_bounds__(ScanCfg<NCW>::NT)
+chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
+                  int T, int H)
+{
+    typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+    using SC = ScanCfg<NCW>;
+    __shared__ __attribute__((aligned(1024))) char smem[SC::TOTAL];
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const bool loader = wave < SC_NLW;
     const int ln = lane & 15, lg = lane >> 4;
+    const int cw = wave - SC_NLW;
+    constexpr int nsplit = DK / SC::DV;
     const int nchunks = (T + C - 1) / C;
     const int nwg = gridDim.x, w = blockIdx.x;
-    const int lid = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
+    const int lid = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;   // slices of a head on one XCD
     const int head = lid / nsplit, slice = lid % nsplit;
     const int b = head / H, h = head % H;
-    const int j0 = slice * DV;
+    const int j0 = slice * SC::DV;
     const size_t tokstride = (size_t)H * DK;
     const size_t hbase = ((size_t)b * T * H + h) * DK;
     const size_t sbase = (size_t)head * DK * DK;
     const char* wsh = ws + (size_t)head * nchunks * WS_CHUNK;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
-    // registers of one chunk: 8 x 16 bytes of the workspace block per thread
-    // (the first 64 KiB), e^{G_64} (threads 0-31) and one value row segment
-    struct Pre { i32x4 blk[8]; f32x4 gam; Raw8<E> v; };
-    const int vg = t % VL, vr = t / VL;
-    auto load = [&](int n, Pre& pr) {
+    // ---- loader side: lane pt moves V / output unit (token ut, columns 8 ug ..)
+    const int pt = t & 255, ug = pt % SC::VG, ut = pt / SC::VG;
+    const bool ulane = ut < C;
+    bf16x8 vrow = bf16x8{};
+    auto load_block = [&](int n) {            // workspace block n -> stage n % 2
         const char* src = wsh + (size_t)n * WS_CHUNK;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) pr.blk[m] = reinterpret_cast<const i32x4*>(src)[t + NT * m];
-        if (t < DK / 4) pr.gam = reinterpret_cast<const f32x4*>(src + WS_GAM)[t];
-        if (vr < C) pr.v.load(v + hbase + (size_t)min(n * C + vr, T - 1) * tokstride + j0 + 8 * vg);
+        char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
+        for (int u = wave; u < SC_KIB; u += SC_NLW)
+            __builtin_amdgcn_global_load_lds(src + (size_t)u * 1024 + lane * 16,
+                                             (__attribute__((address_space(3))) void*)(dst + u * 1024), 16, 0, 0);
     };
-    auto store = [&](int n, const Pre& pr) {
+    auto load_v = [&](int n) {
+        const int tok = min(n * C + min(ut, C - 1), T - 1);
+        vrow = *reinterpret_cast<const bf16x8*>(v + hbase + (size_t)tok * tokstride + j0 + 8 * ug);
+    };
+    auto write_vt = [&](int n) {              // V^T of chunk n into stage n % 2
+        bf16_t* vt = reinterpret_cast<bf16_t*>(smem + (n & 1) * SC::STAGE + SC::OFF_VT);
+        if (ulane) {
+            const bool ok = n * C + ut < T;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int u = t + NT * m;                       // 16-byte unit in the block
-            i32x4* dst;
-            if (m < 2) dst = reinterpret_cast<i32x4*>(sQt + (u >> 4) * L::P128 + 8 * (u & 15));
-            else if (m < 4) { const int x = u - 1024; dst = reinterpret_cast<i32x4*>(sKh + (x >> 4) * L::P128 + 8 * (x & 15)); }
-            else if (m < 6) { const int x = u - 2048; dst = reinterpret_cast<i32x4*>(sKbT + L::kbt(x >> 3, 8 * (x & 7))); }
-            else if (m < 7) { const int x = u - 3072; dst = reinterpret_cast<i32x4*>(sTM + (x >> 3) * L::P64 + 8 * (x & 7)); }
-            else { const int x = u - 3584; dst = reinterpret_cast<i32x4*>(sQK + (x >> 3) * L::P64 + 8 * (x & 7)); }
-            *dst = pr.blk[m];
+            for (int c = 0; c < 8; ++c) vt[(8 * ug + c) * WS_P64 + ut] = ok ? vrow[c] : bf16_t{};
         }
-        if (t < DK / 4) reinterpret_cast<f32x4*>(s_gam)[t] = pr.gam;
-        if (vr < C) {
-            const bool ok = n * C + vr < T;
-            float row[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) row[c] = ok ? pr.v[c] : 0.f;
-            store8<E>(sV + vr * L::PV + 8 * vg, row);
-        }
+    };
+    auto store_out = [&](int n) {             // output tile of chunk n: LDS -> HBM
+        const bf16_t* ot = reinterpret_cast<const bf16_t*>(smem + SC::OFF_O + (n & 1) * C * SC::DV * 2);
+        if (ulane && n * C + ut < T)
+            *reinterpret_cast<bf16x8*>(o + hbase + (size_t)(n * C + ut) * tokstride + j0 + 8 * ug) =
+                *reinterpret_cast<const bf16x8*>(ot + ut * SC::DV + 8 * ug);
     };
 
-    // state rows 16w .. 16w+15 of the slice in accumulators
-    f32x4 acc_s[NJ];
+    // ---- consumer side: S[16cb + 4lg + e][j0 + jc] in acc_s[cb][e] ----
+    const int jc = 16 * cw + ln;
+    f32x4 acc_s[8];
+    if (!loader) {
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb) {
-        const int c = 16 * wave + 4 * lg, j = j0 + 16 * jb + ln;
+        for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc_s[jb][e] = S0 ? S0[sbase + (size_t)(c + e) * DK + j] : 0.f;
+            for (int e = 0; e < 4; ++e)
+                acc_s[cb][e] = S0 ? S0[sbase + (size_t)(16 * cb + 4 * lg + e) * DK + j0 + jc] : 0.f;
+    } else {
+        load_block(0);
+        load_v(0);
+        __builtin_amdgcn_s_waitcnt(0);        // vmcnt, lgkmcnt and expcnt all zero
+        write_vt(0);
     }
-    auto write_state_lds = [&]() {
-#pragma unroll
-        for (int jb = 0; jb < NJ; ++jb)
-            store_vec4<E>(sST + (16 * jb + ln) * L::P128 + 16 * wave + 4 * lg, acc_s[jb]);
-    };
-    write_state_lds();
+    lds_barrier();
 
-    Pre pre;
-    load(0, pre);
     for (int n = 0; n < nchunks; ++n) {
-        store(n, pre);
-        if (n + 1 < nchunks) load(n + 1, pre);
-        lds_barrier();
-
-        // ---- waves 0-3: Z = V - Kh S for token block R = wave | waves 4-7: Qt S
-        f32x4 oacc[NJ];
-        if (wave < 4) {
-            const int R = wave;
-            f32x4 pacc[NJ];
-            int br[NJ];
-#pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) { pacc[jb] = z4; br[jb] = 16 * jb; }
-            mma_rows<E, DK, NJ>(pacc, sKh, L::P128, 16 * R, sST, L::P128, br, lane);
-#pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) {
-                const int j = 16 * jb + ln, r = 16 * R + 4 * lg;
-                f32x4 vv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vv[e] = (float)sV[(r + e) * L::PV + j];
-                store_vec4<E>(sZT + j * L::P64 + r, vv - pacc[jb]);
-            }
+        if (loader) {
+            if (n + 1 < nchunks) { load_block(n + 1); load_v(n + 1); }
+            if (n > 0) store_out(n - 1);
+            __builtin_amdgcn_s_waitcnt(0);    // the stage must be complete at the barrier
+            if (n + 1 < nchunks) write_vt(n + 1);
         } else {
-            // output tiles (jb, R = wave - 4): A = S^T rows jb, B = Qt rows R
-            const int R = wave - 4;
+            const char* st = smem + (n & 1) * SC::STAGE;
+            const bf16_t* sQt = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_QT);
+            const bf16_t* sKh = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_KH);
+            const bf16_t* sKbT = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_KBT);
+            const bf16_t* sTm = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_TM);
+            const bf16_t* sQK = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_QK);
+            const float* sGam = reinterpret_cast<const float*>(st + SC::OFF_BLK + WS_GAM);
+            const bf16_t* sVT = reinterpret_cast<const bf16_t*>(st + SC::OFF_VT);
+            bf16_t* sO = reinterpret_cast<bf16_t*>(smem + SC::OFF_O + (n & 1) * C * SC::DV * 2);
+
+            // P = Kh S and Qt S; a block's eight operand loads go out before its
+            // products, the next block's while they run
+            bf16x8 sb[4];
 #pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) {
-                f32x4 one[1] = {z4};
-                const int br[1] = {16 * R};
-                mma_rows<E, DK, 1>(one, sST, L::P128, 16 * jb, sQt, L::P128, br, lane);
-                oacc[jb] = one[0];
+            for (int p = 0; p < 4; ++p) sb[p] = cat8(to_bf16x4(acc_s[2 * p]), to_bf16x4(acc_s[2 * p + 1]));
+            bf16x8 fa[2][8];
+            auto frags = [&](int Rb, bf16x8 (&f)[8]) {
+                const bf16_t* kr = sKh + (16 * Rb + ln) * WS_P128;
+                const bf16_t* qr = sQt + (16 * Rb + ln) * WS_P128;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) { f[p] = a_pair(kr, p, lg, true); f[4 + p] = a_pair(qr, p, lg, true); }
+            };
+            f32x4 pk[4], qs[4];
+            frags(0, fa[0]);
+#pragma unroll
+            for (int Rb = 0; Rb < 4; ++Rb) {
+                if (Rb + 1 < 4) frags(Rb + 1, fa[(Rb + 1) & 1]);
+                f32x4 a = z4, c2 = z4;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[Rb & 1][p], sb[p], a, 0, 0, 0);
+                    c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[Rb & 1][4 + p], sb[p], c2, 0, 0, 0);
+                }
+                pk[Rb] = a;
+                qs[Rb] = c2;
+                if (Rb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
+
+            // Z = V - P (V^T read in the B layout), Vn = Tm Z (lower blocks only)
+            f32x4 zt[4], vn[4];
+#pragma unroll
+            for (int Rb = 0; Rb < 4; ++Rb) {
+                const bf16x4 vv = ld4(sVT + jc * WS_P64 + 16 * Rb + 4 * lg);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) zt[Rb][e] = (float)vv[e] - pk[Rb][e];
+            }
+#pragma unroll
+            for (int Rb = 0; Rb < 4; ++Rb) {
+                f32x4 a = z4;
+                const bf16_t* row = sTm + (16 * Rb + ln) * WS_P64;
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    if (2 * p <= Rb)
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a_pair(row, p, lg, 2 * p + 1 <= Rb),
+                            cat8(to_bf16x4(zt[2 * p]), to_bf16x4(zt[2 * p + 1])), a, 0, 0, 0);
+                vn[Rb] = a;
+            }
+
+            // O = Qt S + Aqk Vn -> LDS staging (stored to HBM by the loaders)
+#pragma unroll
+            for (int Rb = 0; Rb < 4; ++Rb) {
+                f32x4 a = qs[Rb];
+                const bf16_t* row = sQK + (16 * Rb + ln) * WS_P64;
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    if (2 * p <= Rb)
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a_pair(row, p, lg, 2 * p + 1 <= Rb),
+                            cat8(to_bf16x4(vn[2 * p]), to_bf16x4(vn[2 * p + 1])), a, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sO[(16 * Rb + 4 * lg + e) * SC::DV + jc] = (bf16_t)a[e];
+            }
+
+            // S <- Diag(gamma) (S + Kb^T Vn).  kbt(16cb + ln, 32p + 16hh + 4lg)
+            // splits into a lane part and a compile-time part: the swizzle bits
+            // 1-2 depend on (cb, p, hh) only.
+            bf16x8 vb[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) vb[p] = cat8(to_bf16x4(vn[2 * p]), to_bf16x4(vn[2 * p + 1]));
+            const bf16_t* kl = sKbT + ln * WS_P64 + ((((lg >> 1) ^ (ln >> 3)) & 1) << 3) + 4 * (lg & 1);
+            auto kbt_at = [&](int cb, int p, int hh) {
+                return kl + 16 * cb * WS_P64 + ((p ^ ((cb >> 1) & 1)) << 5) + ((hh ^ (cb & 1)) << 4);
+            };
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const bf16x8 a = cat8(ld4(kbt_at(cb, p, 0)), ld4(kbt_at(cb, p, 1)));
+                    acc_s[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vb[p], acc_s[cb], 0, 0, 0);
+                }
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(sGam + 16 * cb + 4 * lg);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc_s[cb][e] *= gv[e];
             }
         }
         lds_barrier();
-
-        // ---- Vn = Tm Diag(beta) Z: wave -> token block R = wave % 4, column blocks wave / 4 + 2u
-        {
-            constexpr int PER = (NJ + 1) / 2;
-            const int R = wave % 4;
-            if (wave / 4 < NJ) {
-                f32x4 acc[PER];
-                int br[PER];
-#pragma unroll
-                for (int u = 0; u < PER; ++u) {
-                    acc[u] = z4;
-                    const int jb = wave / 4 + 2 * u;
-                    br[u] = 16 * (jb < NJ ? jb : 0);
-                }
-                mma_rows<E, C, PER>(acc, sTM, L::P64, 16 * R, sZT, L::P64, br, lane);
-#pragma unroll
-                for (int u = 0; u < PER; ++u) {
-                    const int jb = wave / 4 + 2 * u;
-                    if (jb < NJ) store_vec4<E>(sVN + (16 * jb + ln) * L::P64 + 16 * R + 4 * lg, acc[u]);
-                }
-            }
-        }
-        lds_barrier();
-
-        // ---- O = Qt S + Aqk Vn (waves 4-7) | S <- Diag(gamma) (S + Kb^T Vn) (all)
-        if (wave >= 4) {
-            const int R = wave - 4;
-            const int tok = n * C + 16 * R + ln;
-#pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) {
-                f32x4 one[1] = {oacc[jb]};
-                const int br[1] = {16 * R};
-                mma_rows<E, C, 1>(one, sVN, L::P64, 16 * jb, sQK, L::P64, br, lane);
-                if (tok < T) store_vec4<E>(o + hbase + (size_t)tok * tokstride + j0 + 16 * jb + 4 * lg, one[0]);
-            }
-        }
-        {
-            int br[NJ];
-#pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) br[jb] = 16 * jb;
-            const int row = 16 * wave + ln;
-#pragma unroll
-            for (int kk = 0; kk < C; kk += M::KS) {
-                const int blk = ((kk >> 3) + lg) ^ ((row >> 3) & 7);
-                const auto a = *reinterpret_cast<const bf16x8*>(sKbT + row * L::P64 + (blk << 3));
-#pragma unroll
-                for (int jb = 0; jb < NJ; ++jb)
-                    acc_s[jb] = M::mma(a, M::frag_kc(sVN, L::P64, br[jb], kk, lane), acc_s[jb]);
-            }
-            const int c = 16 * wave + 4 * lg;
-#pragma unroll
-            for (int jb = 0; jb < NJ; ++jb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc_s[jb][e] *= s_gam[c + e];
-        }
-        lds_barrier();      // everyone is done with this chunk's operands and S^T
-        write_state_lds();
     }
 
-    if (S_T) {
+    if (loader) {
+        store_out(nchunks - 1);
+    } else if (S_T) {
 #pragma unroll
-        for (int jb = 0; jb < NJ; ++jb) {
-            const int c = 16 * wave + 4 * lg, j = j0 + 16 * jb + ln;
+        for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S_T[sbase + (size_t)(c + e) * DK + j] = acc_s[jb][e];
-        }
+            for (int e = 0; e < 4; ++e)
+                S_T[sbase + (size_t)(16 * cb + 4 * lg + e) * DK + j0 + jc] = acc_s[cb][e];
     }
 }
 
@@ -895,22 +918,18 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const f
         launch_one<float, 16>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
     } else if (ws) {
         const int nchunks = (T + C - 1) / C;
-        hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true>), dim3((unsigned)(heads * nchunks)), dim3(NT),
+        const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
+        hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true>), dim3((unsigned)(heads * nblk)), dim3(NT),
                            0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
                            (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws);
-        // value slices: enough workgroups to cover the machine
-        const int dv = heads * 2 >= 256 ? 64 : (heads * 4 >= 256 ? 32 : 16);
-        const int nsplit = DK / dv;
-        const dim3 grid((unsigned)(heads * nsplit));
-        if (dv == 64)
-            hipLaunchKernelGGL(chunk_scan_kernel<64>, grid, dim3(NT), 0, stream, (const char*)ws,
-                               (const bf16_t*)v, S0, (bf16_t*)o, S_T, T, H, nsplit);
-        else if (dv == 32)
-            hipLaunchKernelGGL(chunk_scan_kernel<32>, grid, dim3(NT), 0, stream, (const char*)ws,
-                               (const bf16_t*)v, S0, (bf16_t*)o, S_T, T, H, nsplit);
-        else
-            hipLaunchKernelGGL(chunk_scan_kernel<16>, grid, dim3(NT), 0, stream, (const char*)ws,
-                               (const bf16_t*)v, S0, (bf16_t*)o, S_T, T, H, nsplit);
+        // value columns per scan workgroup: enough workgroups to cover the machine
+        const int ncw = heads * 4 >= 256 ? 2 : 1;
+#define KDA_SCAN(NCW) hipLaunchKernelGGL(chunk_scan_kernel<NCW>, dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
+                                         dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws, (const bf16_t*)v, S0, \
+                                         (bf16_t*)o, S_T, T, H)
+        if (ncw == 2) KDA_SCAN(2);
+        else KDA_SCAN(1);
+#undef KDA_SCAN
     } else if (heads * 2 >= 256) {
         launch_one<bf16_t, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
     } else if (heads * 4 >= 256) {

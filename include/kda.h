@@ -78,7 +78,7 @@ enum {
  *                                           any other overlap is rejected.
  *   workspace                 device scratch, owned by the caller, or NULL.
  *                             With dtype == KDA_BF16 and workspace_bytes >=
- *                             B * H * ceil(T / 64) * 66048, the call runs two
+ *                             B * H * ceil(T / 64) * 72704, the call runs two
  *                             kernels: the key-side operands of every chunk
  *                             are computed in parallel into the workspace,
  *                             then a serial scan applies them to the state.
@@ -98,7 +98,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Workspace bytes that kda_chunk_fwd should be given for the fastest schedule
- * on this shape: B * H * ceil(T / 64) * 66048 when the two-kernel schedule is
+ * on this shape: B * H * ceil(T / 64) * 72704 when the two-kernel schedule is
  * expected to win (bf16 with fewer than 128 heads in total), else 0 (the fused
  * kernel is used and no workspace is needed).  Invalid arguments return 0.
  */

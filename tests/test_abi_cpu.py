@@ -68,8 +68,8 @@ def step(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S=P + 
     (dict(ST=P + 2**26 + 64), INVALID),         # S_T overlaps g
     (dict(S0=P + 2**30, ST=P + 2**30 + 16), INVALID),  # partial S0/S_T overlap
     (dict(B=2**30, H=2**30), UNSUP),            # size overflow
-    (dict(ws=P + 2**31 + 16, wsb=66048), ALIGN),           # workspace needs 256-byte alignment
-    (dict(ws=P + 2**24, wsb=66048), INVALID),               # workspace overlaps k
+    (dict(ws=P + 2**31 + 16, wsb=72704), ALIGN),           # workspace needs 256-byte alignment
+    (dict(ws=P + 2**24, wsb=72704), INVALID),               # workspace overlaps k
 ])
 def test_chunk_fwd_rejects(lib, kw, code):
     assert chunk(lib, **kw) == code
@@ -99,10 +99,10 @@ def test_recurrent_step_rejects(lib, kw, code):
 
 def test_workspace_size_query(lib):
     f = lib.kda_chunk_fwd_workspace_size
-    # few heads, bf16: two-kernel schedule, one 66,048-byte block per chunk
-    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 66048
-    assert f(1, 32768, 16, 128, 128, BF16) == 16 * 512 * 66048
-    assert f(1, 100, 3, 128, 128, BF16) == 3 * 2 * 66048
+    # few heads, bf16: two-kernel schedule, one 72,704-byte block per chunk
+    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 72704
+    assert f(1, 32768, 16, 128, 128, BF16) == 16 * 512 * 72704
+    assert f(1, 100, 3, 128, 128, BF16) == 3 * 2 * 72704
     # many heads, fp32, tiny T or bad arguments: fused kernel, no workspace
     assert f(8, 4096, 16, 128, 128, BF16) == 0
     assert f(1, 256, 1, 128, 128, F32) == 0
@@ -141,7 +141,7 @@ def test_layer_workspace_layout(lib):
     total = lib.kda_layer_workspace_layout(B, T, dm, H, r, offs)
     R, hd = B * T, H * 128
     sizes = [R * 4 * hd * 2, R * 144 * 4, R * hd * 2, R * hd * 2, R * hd * 2, R * hd * 4,
-             R * H * 2, R * hd * 2, R * hd * 2, H * 512 * 66048]
+             R * H * 2, R * hd * 2, R * hd * 2, H * 512 * 72704]
     assert list(offs)[0] == 0
     for i in range(9):
         assert offs[i + 1] - offs[i] == (sizes[i] + 255) // 256 * 256
