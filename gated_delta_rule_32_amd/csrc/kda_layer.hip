@@ -47,21 +47,28 @@ __device__ __forceinline__ float head_sum(float s) {
     return s;
 }
 
-// grid (rows = B*T, 3): blockIdx.y selects q (0), k (1) or v (2).  Each thread
-// covers 8 consecutive channels; a 16-lane group covers one head.
+// grid (token tiles of CONV_TT tokens per sequence, B, 3): blockIdx.z selects
+// q (0), k (1) or v (2).  Each thread covers 8 consecutive channels (a 16-lane
+// group covers one head) and walks the tile's tokens in order, keeping the
+// last three inputs in registers, so every pre-activation row is read once
+// (plus a three-row halo per tile) and the taps are loaded once per tile.
+constexpr int CONV_TT = 64;      // tokens per tile
+constexpr int CONV_G = 8;        // tokens whose loads are issued together
+
 __global__ void __launch_bounds__(256)
 conv_act_kernel(const bf16_t* pre, int ld_pre, const bf16_t* conv_q, const bf16_t* conv_k,
                 const bf16_t* conv_v, bf16_t* q, bf16_t* k, bf16_t* v, const float* beta_pre,
                 int ld_bp, bf16_t* beta, int T, int H)
 {
-    const int row = blockIdx.x;                 // b * T + t
-    const int which = blockIdx.y;
-    const int t = row % T;
+    const int which = blockIdx.z;
+    const int t0 = blockIdx.x * CONV_TT;
+    const size_t row0 = (size_t)blockIdx.y * T;          // first row of the sequence
     const int C = H * HD;
+    const int t1 = min(t0 + CONV_TT, T);
     bf16_t* out = which == 0 ? q : (which == 1 ? k : v);
     const bf16_t* cw = which == 0 ? conv_q : (which == 1 ? conv_k : conv_v);
     for (int c0 = 8 * threadIdx.x; c0 < C; c0 += 8 * blockDim.x) {
-        const int col = which * C + c0;         // column in the pre-activations
+        const int col = which * C + c0;                  // column in the pre-activations
         float w[8][TAPS];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -69,33 +76,51 @@ conv_act_kernel(const bf16_t* pre, int ld_pre, const bf16_t* conv_q, const bf16_
 #pragma unroll
             for (int j = 0; j < TAPS; ++j) w[i][j] = (float)wt[j];
         }
-        float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // window: x[t-3], x[t-2], x[t-1] (zero before the sequence starts)
+        float x3[8], x2[8], x1[8];
 #pragma unroll
-        for (int j = 0; j < TAPS; ++j) {
-            const int shift = TAPS - 1 - j;     // tap j multiplies x_{t - shift}
-            if (t - shift >= 0) {
-                float x[8];
-                load8(pre + (size_t)(row - shift) * ld_pre + col, x);
+        for (int i = 0; i < 8; ++i) { x3[i] = 0.f; x2[i] = 0.f; x1[i] = 0.f; }
+        if (t0 >= 3) load8(pre + (row0 + t0 - 3) * ld_pre + col, x3);
+        if (t0 >= 2) load8(pre + (row0 + t0 - 2) * ld_pre + col, x2);
+        if (t0 >= 1) load8(pre + (row0 + t0 - 1) * ld_pre + col, x1);
+        for (int tg = t0; tg < t1; tg += CONV_G) {
+            bf16x8 raw[CONV_G];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) y[i] += w[i][j] * x[i];
+            for (int u = 0; u < CONV_G; ++u)                 // clamped: rows past t1 are not used
+                raw[u] = *reinterpret_cast<const bf16x8*>(pre + (row0 + min(tg + u, t1 - 1)) * ld_pre + col);
+#pragma unroll
+            for (int u = 0; u < CONV_G; ++u) {
+                if (tg + u < t1) {
+                    float x0[8], y[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        x0[i] = (float)raw[u][i];
+                        y[i] = w[i][0] * x3[i] + w[i][1] * x2[i] + w[i][2] * x1[i] + w[i][3] * x0[i];
+                        y[i] = y[i] * sigmoid_f(y[i]);            // Swish
+                    }
+                    if (which < 2) {                             // L2Norm over the head
+                        float ss = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ss += y[i] * y[i];
+                        ss = head_sum(ss);
+                        const float inv = __builtin_amdgcn_rsqf(ss + 1e-6f);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) y[i] *= inv;
+                    }
+                    store8b(out + (row0 + tg + u) * C + c0, y);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) { x3[i] = x2[i]; x2[i] = x1[i]; x1[i] = x0[i]; }
+                }
             }
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = y[i] * sigmoid_f(y[i]);   // Swish
-        if (which < 2) {                         // L2Norm over the head
-            float ss = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss += y[i] * y[i];
-            ss = head_sum(ss);
-            const float inv = __builtin_amdgcn_rsqf(ss + 1e-6f);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] *= inv;
-        }
-        store8b(out + (size_t)row * C + c0, y);
     }
-    if (which == 2)
-        for (int h = threadIdx.x; h < H; h += blockDim.x)
-            beta[(size_t)row * H + h] = (bf16_t)sigmoid_f(beta_pre[(size_t)row * ld_bp + h]);
+    if (which == 2) {
+        for (int e = threadIdx.x; e < (t1 - t0) * H; e += blockDim.x) {
+            const size_t row = row0 + t0 + e / H;
+            const int hh = e % H;
+            beta[row * H + hh] = (bf16_t)sigmoid_f(beta_pre[row * ld_bp + hh]);
+        }
+    }
 }
 
 // grid rows = B*T; o [rows, H*128] bf16, gate [rows, ld_gate] bf16 (pre-sigmoid)
@@ -132,9 +157,9 @@ hipError_t launch_conv_act(const bf16_t* pre, int ld_pre, const bf16_t* conv_q,
                            bf16_t* v, const float* beta_pre, int ld_bp, bf16_t* beta, int B, int T,
                            int H, hipStream_t stream)
 {
-    const long long rows = (long long)B * T;
-    if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(conv_act_kernel, dim3((unsigned)rows, 3), dim3(row_threads(H)), 0, stream,
+    if ((long long)B * T <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((T + CONV_TT - 1) / CONV_TT), (unsigned)B, 3);
+    hipLaunchKernelGGL(conv_act_kernel, grid, dim3(row_threads(H)), 0, stream,
                        pre, ld_pre, conv_q, conv_k, conv_v, q, k, v, beta_pre, ld_bp, beta, T, H);
     return hipGetLastError();
 }
