@@ -6,8 +6,9 @@
 // projections W_q, W_k, W_v, W_g, W_down, W_beta, W_up and W_o of the layer
 // on page "Kimi K3论文：Kimi Linear", section 3.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C, each of its
-// 4 waves a 64 x 64 sub-tile (4 x 4 MFMA tiles), over K in steps of 64.
+// Tiling (general kernel): a 256-thread workgroup computes a 128 x 128 tile
+// of C, each of its 4 waves a 64 x 64 sub-tile (4 x 4 MFMA tiles), over K in
+// steps of 64.  Large bf16 products use the 256 x 256-tile kernel below.
 // Operand tiles are staged through double-buffered LDS (rows padded by 16 B
 // against bank conflicts); the next K-step's global loads are in flight while
 // the current step's MFMAs run, with one barrier per step.  The MFMA computes
@@ -184,6 +185,99 @@ gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
         }
 }
 
+// ---- large tiles: bf16 A, bf16 C -------------------------------------------
+// A 512-thread workgroup computes a 256 x 256 tile of C; wave w owns rows
+// 128 (w / 4) .. +127 and columns 64 (w % 4) .. +63 (8 x 4 MFMA tiles).  Each
+// K-step of 64 stages the A and B tiles (256 rows x 128 bytes each) in LDS
+// with 16-byte global-to-LDS loads: one load instruction fills 1 KiB = 8
+// rows, and lane l fetches the 16-byte chunk (l % 8) ^ (row % 8) of its row,
+// so LDS rows hold their chunks XOR-swizzled and the MFMA fetches (16 rows,
+// one chunk column) touch distinct banks.  Two stages: the next K-step's
+// loads are in flight while the current one is multiplied; one barrier per
+// K-step.
+constexpr int LBM = 256, LBN = 256, LBK = 64;
+constexpr int LGT = 512;
+constexpr int LSTAGE = (LBM + LBN) * LBK * 2;      // 64 KiB
+
+__global__ void __launch_bounds__(LGT)
+gemm_nt_large_kernel(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, int K,
+                     int lda, int ldb, int ldc)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[2 * LSTAGE];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int ln = lane & 15, lg = lane >> 4;
+    const int wm = wave >> 2, wn = wave & 3;
+
+    // N strips fastest: workgroup i goes to XCD i % 8, which then keeps one
+    // strip of B in its L2
+    const int tiles_n = (N + LBN - 1) / LBN;
+    const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+    const int m0 = tm * LBM, n0 = tn * LBN;
+
+    // loads of one K-step: 32 segments of A, 32 of B, 8 per wave
+    const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;    // row within segment, chunk fetched
+    auto issue = [&](int k0, int stage) {
+        char* st = smem + stage * LSTAGE;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int seg = wave + 8 * i;                  // 0..63, uniform per wave
+            const bool isA = seg < 32;
+            const int row = 8 * (seg & 31) + lrow;
+            const bf16_t* src = isA ? A + (size_t)min(m0 + row, M - 1) * lda
+                                    : B + (size_t)min(n0 + row, N - 1) * ldb;
+            __builtin_amdgcn_global_load_lds(src + k0 + 8 * lchunk,
+                                             (__attribute__((address_space(3))) void*)(st + seg * 1024), 16, 0, 0);
+        }
+    };
+    // 16-byte fragment of row r, logical chunk lc, from a swizzled tile
+    auto frag = [&](const char* tile, int r, int lc) {
+        return *reinterpret_cast<const bf16x8*>(tile + r * 128 + ((lc ^ (r & 7)) << 4));
+    };
+
+    f32x4 acc[4][8];      // [nb][mb]: C^T tile rows n = 64 wn + 16 nb, columns m = 128 wm + 16 mb
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = K / LBK;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    block_sync();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int stage = kt & 1;
+        if (kt + 1 < KT) issue((kt + 1) * LBK, stage ^ 1);
+        const char* sA = smem + stage * LSTAGE;
+        const char* sB = sA + LBM * LBK * 2;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {               // two 32-wide K slices
+            bf16x8 fb[4], fa[8];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) fb[nb] = frag(sB, 64 * wn + 16 * nb + ln, 4 * kk + lg);
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) fa[mb] = frag(sA, 128 * wm + 16 * mb + ln, 4 * kk + lg);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb)
+                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);                 // next stage loaded (and this one's reads done)
+        block_sync();
+    }
+
+    // epilogue: lane holds C[m][n .. n+3] for m = .. + ln, n = .. + 4 lg
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            const int m = m0 + 128 * wm + 16 * mb + ln;
+            const int n = n0 + 64 * wn + 16 * nb + 4 * lg;
+            if (m < M && n < N) store_out4<bf16_t>(C + (size_t)m * ldc + n, acc[nb][mb], N - n);
+        }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, bool c_f32,
@@ -191,6 +285,12 @@ hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, b
                           hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
+    if (!a_f32 && !c_f32 && epilogue == 0 && M >= LBM && N >= LBN) {
+        const unsigned tiles = (unsigned)(((M + LBM - 1) / LBM) * ((N + LBN - 1) / LBN));
+        hipLaunchKernelGGL(gemm_nt_large_kernel, dim3(tiles), dim3(LGT), 0, stream,
+                           (const bf16_t*)A, B, (bf16_t*)C, M, N, K, lda, ldb, ldc);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN))), block(GT);
 #define KDA_GEMM(AF, OT, EP) \
     hipLaunchKernelGGL((gemm_nt_kernel<AF, OT, EP>), grid, block, 0, stream, A, B, (OT*)C, M, N, K, lda, ldb, ldc)
