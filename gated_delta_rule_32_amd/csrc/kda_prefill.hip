@@ -639,14 +639,14 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 
 
 // ---- serial scan over chunks from the workspace (bf16) --------------------
-// One workgroup per (head, 16 NCW value columns), NCW + 4 waves:
-//   waves 0-3 (loaders) move data: the next chunk's workspace block -- the
+// One workgroup per (head, 16 NCW value columns), eight waves:
+//   waves 0 .. 7-NCW (loaders) move data: the next chunk's workspace block -- the
 //     key-side operands Qt, Kh, Kb^T, Tm Diag(beta), Aqk, e^{G_64} of that
 //     chunk, laid out as this kernel's LDS image -- is copied global -> LDS
 //     directly (16-byte LDS-destination loads) into the other of two stages,
 //     the V slice is written transposed next to it, and the previous chunk's
 //     output is stored from an LDS staging tile to HBM with 16-byte stores;
-//   waves 4.. (consumers) each own 16 value columns and keep their 128 x 16
+//   the last NCW waves (consumers) each own 16 value columns and keep their 128 x 16
 //     slice of the state in MFMA accumulators.  For chunk n they form
 //       P = Kh S,  Qt S,  Z = V - P,  Vn = Tm Z,  O = Qt S + Aqk Vn (to LDS),
 //       S <- Diag(e^{G_64}) (S + Kb^T Vn)
@@ -658,11 +658,11 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 // lane; the consumers feed it two 16-row blocks at once (four values from
 // each), reading the A-operand with the same split, so each product is a
 // plain sum over k.
-constexpr int SC_NLW = 4;                                 // loader waves
 constexpr int SC_KIB = WS_CHUNK / 1024;                   // 1 KiB pieces per block
 template <int NCW> struct ScanCfg {                       // NCW consumer waves
     static constexpr int DV = 16 * NCW;                   // value columns per workgroup
-    static constexpr int NT = 64 * (SC_NLW + NCW);
+    static constexpr int NLW = 8 - NCW;                   // loader waves (two waves per SIMD)
+    static constexpr int NT = 64 * (NLW + NCW);
     static constexpr int OFF_VT = 0;                      // V^T [DV cols][72] bf16
     static constexpr int OFF_BLK = DV * WS_P64 * 2;       // workspace image
     static constexpr int STAGE = OFF_BLK + WS_CHUNK;
@@ -670,7 +670,7 @@ template <int NCW> struct ScanCfg {                       // NCW consumer waves
     static constexpr int TOTAL = OFF_O + 2 * C * DV * 2;
     static constexpr int VG = DV / 8;                     // 16-byte units per token row
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
-    static_assert(C * VG <= 64 * SC_NLW, "one V / output unit per loader lane");
+    static_assert(C * VG <= 256, "one V / output unit per lane of the first four loader waves");
 };
 
 __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
@@ -701,9 +701,9 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const bool loader = wave < SC_NLW;
+    const bool loader = wave < SC::NLW;
     const int ln = lane & 15, lg = lane >> 4;
-    const int cw = wave - SC_NLW;
+    const int cw = wave - SC::NLW;
     constexpr int nsplit = DK / SC::DV;
     const int nchunks = (T + C - 1) / C;
     const int nwg = gridDim.x, w = blockIdx.x;
@@ -719,17 +719,18 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
 
     // ---- loader side: lane pt moves V / output unit (token ut, columns 8 ug ..)
     const int pt = t & 255, ug = pt % SC::VG, ut = pt / SC::VG;
-    const bool ulane = ut < C;
+    const bool ulane = t < 256 && ut < C;     // lanes of the first four loader waves
     bf16x8 vrow = bf16x8{};
     auto load_block = [&](int n) {            // workspace block n -> stage n % 2
         const char* src = wsh + (size_t)n * WS_CHUNK;
         char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
-        for (int u = wave; u < SC_KIB; u += SC_NLW)
+        for (int u = wave; u < SC_KIB; u += SC::NLW)
             __builtin_amdgcn_global_load_lds(src + (size_t)u * 1024 + lane * 16,
                                              (__attribute__((address_space(3))) void*)(dst + u * 1024), 16, 0, 0);
     };
     auto load_v = [&](int n) {
-        const int tok = min(n * C + min(ut, C - 1), T - 1);
+        if (!ulane) return;
+        const int tok = min(n * C + ut, T - 1);
         vrow = *reinterpret_cast<const bf16x8*>(v + hbase + (size_t)tok * tokstride + j0 + 8 * ug);
     };
     auto write_vt = [&](int n) {              // V^T of chunk n into stage n % 2
