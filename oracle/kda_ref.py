@@ -9,6 +9,9 @@ Contents (all fp64):
 * :func:`recurrent` -- the oracle proper: the sequential recurrence of eq. (1) on
   page "Kimi K3论文：Kimi Linear" (section 3), in plain C (``kda_ref.c``),
   loaded through ctypes.
+* :func:`recurrent_grad` -- the gradient oracle: reverse mode through the same
+  recurrence, in plain C, for the backward pass of the chunked form (dq, dk,
+  dv, d log(alpha), d beta, dS0 from dL/do and dL/dS_T).
 * Independent cross-forms that the tests use to pin the oracle.  Each follows a
   different passage, so a dropped term, a wrong sign or a swapped gate order in
   one of them shows up as a mismatch:
@@ -26,6 +29,9 @@ Contents (all fp64):
   - :func:`product_form` -- the transition-product form used to argue that
     KDA acts as a learnable position encoding (page "Kimi K3论文：Kimi Linear",
     section 6), with the write strength beta_i and the gate order of eq. (1).
+  - :func:`autograd_grad` -- torch autograd (CPU, fp64) through a torch
+    transcription of the recurrence, against which :func:`recurrent_grad` is
+    checked (besides central finite differences of :func:`recurrent`).
   - :func:`deltanet`, :func:`gated_deltanet` -- the two predecessors of KDA
     (page "Kimi K3论文：Kimi Linear", section 2), which KDA must reduce to.
 
@@ -69,6 +75,8 @@ def _load():
                                           ctypes.c_long, ctypes.c_long, ctypes.c_long,
                                           ctypes.c_long, ctypes.c_long, ctypes.c_int]
         lib.kda_ref_recurrent.restype = ctypes.c_int
+        lib.kda_ref_recurrent_grad.argtypes = [dp] * 14 + [ctypes.c_long] * 5 + [ctypes.c_int]
+        lib.kda_ref_recurrent_grad.restype = ctypes.c_int
         lib.kda_ref_max_threads.argtypes = []
         lib.kda_ref_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -117,6 +125,64 @@ def recurrent(q, k, v, g, beta, S0=None, nthreads: int = 0):
     if rc != 0:
         raise RuntimeError("kda_ref_recurrent failed")
     return o, S_T
+
+
+def recurrent_grad(q, k, v, g, beta, S0, dO, dS_T=None, nthreads: int = 0):
+    """Gradient oracle: reverse mode through the recurrence of :func:`recurrent`.
+
+    For the scalar loss L = sum(dO * o) + sum(dS_T * S_T) (dS_T None => 0),
+    returns ``(dq, dk, dv, dg, dbeta, dS0)`` in fp64 with the shapes of
+    q, k, v, g, beta and S0 (dS0 is returned even when S0 is None: it is the
+    gradient at the zero state).  The chain rule is taken step by step back
+    through eq. (1) of page "Kimi K3论文：Kimi Linear", section 3, in plain C
+    (``kda_ref.c``); ``g`` is log(alpha), so dg is the gradient in log space.
+    """
+    q, k, v, g, beta, S0, dO, dS_T = (_f64(x) for x in (q, k, v, g, beta, S0, dO, dS_T))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and g.shape == q.shape
+    assert v.shape == (B, T, H, dv) and beta.shape == (B, T, H) and dO.shape == v.shape
+    for x in (S0, dS_T):
+        if x is not None:
+            assert x.shape == (B, H, dk, dv)
+    out = [np.zeros(x.shape) for x in (q, k, v, g, beta)] + [np.zeros((B, H, dk, dv))]
+    rc = _load().kda_ref_recurrent_grad(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+        *(_ptr(x) for x in out), B, T, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kda_ref_recurrent_grad failed")
+    return tuple(out)
+
+
+def autograd_grad(q, k, v, g, beta, S0, dO, dS_T=None):
+    """Cross-form of :func:`recurrent_grad`: torch autograd (CPU, fp64) through
+    the same recurrence written with torch tensor operations, single head:
+    q, k, g [T, dk]; v, dO [T, dv]; beta [T]; S0, dS_T [dk, dv] or None."""
+    import torch
+
+    def t64(x, req):
+        x = torch.zeros(0) if x is None else torch.as_tensor(np.asarray(x, np.float64))
+        return x.clone().requires_grad_(req)
+
+    q_, k_, v_, g_, b_ = (t64(x, True) for x in (q, k, v, g, beta))
+    dk, dv = q_.shape[1], v_.shape[1]
+    S0_ = (torch.zeros(dk, dv, dtype=torch.float64) if S0 is None else t64(S0, False)).clone()
+    S0_.requires_grad_(True)
+    S = S0_
+    outs = []
+    for t in range(q_.shape[0]):
+        Sp = torch.exp(g_[t])[:, None] * S
+        u = b_[t] * (v_[t] - Sp.T @ k_[t])
+        S = Sp + torch.outer(k_[t], u)
+        outs.append(S.T @ q_[t])
+    o = torch.stack(outs) if outs else torch.zeros(0, dv, dtype=torch.float64)
+    loss = (o * torch.as_tensor(np.asarray(dO, np.float64))).sum()
+    if dS_T is not None:
+        loss = loss + (S * torch.as_tensor(np.asarray(dS_T, np.float64))).sum()
+    grads = torch.autograd.grad(loss, [q_, k_, v_, g_, b_, S0_], allow_unused=True)
+    ref = (q_, k_, v_, g_, b_, S0_)
+    return tuple((torch.zeros_like(x) if gr is None else gr).detach().numpy()
+                 for gr, x in zip(grads, ref))
 
 
 # ---------------------------------------------------------------------------
