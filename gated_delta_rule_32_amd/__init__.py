@@ -1,7 +1,9 @@
 """libkda Python binding: Kimi Delta Attention kernels for MI355X (gfx950).
 
-``chunk_fwd`` (chunkwise prefill) and ``recurrent_step`` (decode) take torch
-tensors on the GPU and call the C ABI of ``libkda.so`` on the current stream.
+``chunk_fwd`` (chunkwise prefill), ``chunk_bwd`` (its backward pass),
+``recurrent_step`` (decode) and ``layer_fwd`` (one token-mixing layer) take
+torch tensors on the GPU and call the C ABI of ``libkda.so`` on the current
+stream.
 torch is used for device memory and streams only.
 """
 from __future__ import annotations
@@ -11,7 +13,7 @@ import ctypes
 from ._binding import (KDA_BF16, KDA_F32, LAYER_REGIONS, KDAError, lib,  # noqa: F401
                        status_string, version, _check)
 
-__all__ = ["chunk_fwd", "recurrent_step", "workspace_size", "scan_workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_bwd", "bwd_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
            "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS",
            "status_string", "version", "KDAError",
            "KDA_F32", "KDA_BF16", "lib"]
@@ -110,6 +112,49 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out=None, S_T=None,
                              ws_ptr, ws_bytes, _stream(dev))
     _check("kda_chunk_fwd", st)
     return out, S_T
+
+
+def bwd_workspace_size(B, T, H, d=128):
+    """Workspace bytes kda_chunk_bwd needs (bf16)."""
+    return int(lib().kda_chunk_bwd_workspace_size(B, T, H, d, d, KDA_BF16))
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T=None, *, workspace="auto",
+              grad_S0: bool = True):
+    """Backward pass of :func:`chunk_fwd` (bf16 only).  Inputs as for chunk_fwd
+    plus grad_o [B, T, H, 128] bf16 and grad_S_T [B, H, 128, 128] fp32 (None:
+    zero).  ``workspace``: "auto" (cached per device) or a uint8 device tensor
+    of at least :func:`bwd_workspace_size` bytes.  Returns ``(dq, dk, dv,
+    dlog_alpha, dbeta, dS0)``; dS0 is None when ``grad_S0`` is false."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for t, n, shp in ((k, "k", q.shape), (v, "v", (B, T, H, dv)), (beta, "beta", (B, T, H)),
+                      (grad_o, "grad_o", (B, T, H, dv))):
+        _need(t, n, dt, shp, dev)
+    _need(log_alpha, "log_alpha", torch.float32, q.shape, dev)
+    for t, n in ((S0, "S0"), (grad_S_T, "grad_S_T")):
+        if t is not None:
+            _need(t, n, torch.float32, (B, H, dk, dv), dev)
+    out = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+           torch.empty_like(log_alpha), torch.empty_like(beta)]
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if grad_S0 else None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto' or a tensor")
+        workspace = _workspace(dev, bwd_workspace_size(B, T, H, dk))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device != dev or workspace.dtype != torch.uint8:
+            raise ValueError("workspace must be a uint8 tensor on the same device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                             _ptr(grad_o), _ptr(grad_S_T), *(_ptr(x) for x in out), _ptr(dS0),
+                             B, T, H, dk, dv, code, ws_ptr, ws_bytes, _stream(dev))
+    _check("kda_chunk_bwd", st)
+    return (*out, dS0)
 
 
 def recurrent_step(q, k, v, log_alpha, beta, S, *, out=None):

@@ -26,6 +26,8 @@ SIGNATURES = {
     "kda_chunk_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                            _I, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
     "kda_chunk_fwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "kda_chunk_bwd": (_I, [_VP] * 14 + [_I] * 6 + [_VP, _SZ, _VP]),
+    "kda_chunk_bwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "kda_recurrent_step": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                 _I, _I, _I, _I, _I, _VP]),
     "kda_layer_fwd": (_I, [_VP] * 13 + [_I] * 5 + [_VP, _SZ, _VP]),

@@ -132,6 +132,77 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype)
+{
+    if (B < 0 || T < 0 || H < 0 || dk != kHeadDim || dv != kHeadDim || dtype != KDA_BF16) return 0;
+    return kda::chunk_bwd_ws_layout(B, T, H, nullptr);
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v,
+                  const float* log_alpha, const void* beta, const float* S0,
+                  const void* grad_o, const float* grad_S_T,
+                  void* grad_q, void* grad_k, void* grad_v, float* grad_log_alpha,
+                  void* grad_beta, float* grad_S0,
+                  int B, int T, int H, int dk, int dv, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;   // bf16 only
+    if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return KDA_OK;
+
+    bool ok = true;
+    const size_t es = 2;
+    const size_t tok = mul3(B, T, H, &ok);
+    const size_t heads = mul3(B, H, 1, &ok);
+    const size_t n_qk = mul3((long long)tok, kHeadDim, 1, &ok);
+    const size_t n_state = mul3((long long)heads, kHeadDim, kHeadDim, &ok);
+    const size_t units = mul3((long long)heads, (T + 63) / 64, 1, &ok);
+    if (!ok) return KDA_ERR_UNSUPPORTED;
+    if (heads * 8 > (size_t)INT_MAX || units > (size_t)INT_MAX) return KDA_ERR_UNSUPPORTED;   // grids
+
+    int rc;
+    const Range rS0{S0, S0 ? n_state * 4 : 0}, rdST{grad_S_T, grad_S_T ? n_state * 4 : 0};
+    const Range rdS0{grad_S0, grad_S0 ? n_state * 4 : 0};
+    if (S0 && (rc = check_ptr(S0, 16)) != KDA_OK) return rc;
+    if (grad_S_T && (rc = check_ptr(grad_S_T, 16)) != KDA_OK) return rc;
+    if (grad_S0 && (rc = check_ptr(grad_S0, 16)) != KDA_OK) return rc;
+    if (overlap(rdS0, rS0) || overlap(rdS0, rdST)) return KDA_ERR_INVALID_ARG;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (!grad_S0) return KDA_OK;
+        return kda::launch_state_copy(grad_S_T, grad_S0, (long long)heads, s) == hipSuccess ? KDA_OK
+                                                                                          : KDA_ERR_HIP;
+    }
+
+    const void* ins[] = {q, k, v, log_alpha, grad_o, grad_q, grad_k, grad_v, grad_log_alpha};
+    for (const void* p : ins)
+        if ((rc = check_ptr(p, 16)) != KDA_OK) return rc;
+    if ((rc = check_ptr(beta, es)) != KDA_OK || (rc = check_ptr(grad_beta, es)) != KDA_OK) return rc;
+    const size_t need = kda::chunk_bwd_ws_layout(B, T, H, nullptr);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
+
+    const Range in[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, n_qk * 4},
+                        {beta, tok * es}, rS0, {grad_o, n_qk * es}, rdST};
+    const Range out[] = {{grad_q, n_qk * es}, {grad_k, n_qk * es}, {grad_v, n_qk * es},
+                         {grad_log_alpha, n_qk * 4}, {grad_beta, tok * es}, rdS0,
+                         {workspace, need}};
+    constexpr int n_out = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < n_out; ++i) {
+        for (const Range& r : in)
+            if (overlap(out[i], r)) return KDA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(out[i], out[j])) return KDA_ERR_INVALID_ARG;
+    }
+
+    hipError_t e = kda::launch_chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T,
+                                         grad_q, grad_k, grad_v, grad_log_alpha, grad_beta, grad_S0,
+                                         B, T, H, (char*)workspace, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_recurrent_step(const void* q, const void* k, const void* v,
                        const float* log_alpha, const void* beta, float* S,
                        void* o, int N, int H, int dk, int dv, int dtype,

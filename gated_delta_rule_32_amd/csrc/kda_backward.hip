@@ -1,0 +1,557 @@
+// kda_backward.hip -- backward pass of the chunked KDA prefill for gfx950.
+//
+// The forward pass is the chunkwise algorithm of page "Kimi Linear：高效注意力
+// 机制在长序列处理中的创新应用" (sections 2.1-2.3) and page "Kimi K3论文：Kimi
+// Linear" (section 4).  Per chunk of 64 tokens, with S the state entering it,
+// G the in-chunk cumulative log-decay and gamma = e^{G_64}:
+//
+//   Qt = e^G q,  Kh = e^G k,  Kb = e^-G k,  Kt = e^{G_64 - G} k
+//   Aqk = tril(Qt Kb^T),  Akk = Diag(beta) stril(Kh Kb^T),  Tm = (I + Akk)^-1
+//   Y = V - Kh S,  Vn = Tm Diag(beta) Y
+//   O = Qt S + Aqk Vn,   S' = Diag(gamma) S + Kt^T Vn
+//
+// Reverse mode through these lines, given dO and dS' (the gradient of the
+// state leaving the chunk), is
+//
+//   dVn = Aqk^T dO + Kt dS'          dZ = Tm^T dVn        dV = Diag(beta) dZ
+//   dS  = Diag(gamma) dS' + Qt^T dO - Kh^T dV                    (to chunk n-1)
+//   dAqk = tril(dO Vn^T)             dAkk = -stril(dZ Vn^T),  dA' = Diag(beta) dAkk
+//   dQt = dO S^T + dAqk Kb           dKh = -dV S^T + dA' Kb
+//   dKb = dAqk^T Qt + dA'^T Kh       dKt = Vn dS'^T
+//   dbeta_r = sum_j Y[r,j] dZ[r,j] + sum_i dAkk[r,i] (Kh Kb^T)[r,i]
+//   dq = e^G dQt,  dk = e^G dKh + e^-G dKb + e^{G_64-G} dKt
+//   dG = Qt.dQt + Kh.dKh - Kb.dKb - Kt.dKt (elementwise)
+//   dG_64 += e^{G_64} sum_j S[c,j] dS'[c,j] + sum_r Kt[r,c] dKt[r,c]
+//   dg = reverse cumulative sum of dG over the chunk's tokens.
+//
+// The pass runs four kernels:
+//   1. the forward prep kernel, which also writes the operands of the reverse
+//      scan (Aqk^T, Tm^T, Qt^T, Kh^T, Kt, gamma, beta) per chunk;
+//   2. the forward scan in save mode: S, Y and Vn of every chunk (bf16);
+//   3. chunk_bwd_scan_kernel: the serial reverse pass over chunks carrying dS
+//      in MFMA accumulators; writes dV (final), dZ and dS' per chunk;
+//   4. chunk_bwd_grad_kernel: one workgroup per chunk, all chunks in
+//      parallel: dq, dk, dg, dbeta.
+#include "kda_chunk_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+// ---- reverse state scan -----------------------------------------------------
+// One workgroup per (head, 16 NCW value columns), eight waves: 8 - NCW loader
+// waves copy the next (lower) chunk's operand block global -> LDS with 16-byte
+// LDS-destination loads and write dO^T of the value slice next to it; NCW
+// consumer waves each hold a 128 x 16 slice of dS in accumulators.  The
+// contraction operands that are products of the previous step stay in
+// registers (accumulator tiles packed in pairs as B operands, a_pair A reads).
+template <int NCW> struct BScanCfg {
+    static constexpr int DV = 16 * NCW;
+    static constexpr int NLW = 8 - NCW;
+    static constexpr int NT = 512;
+    static constexpr int OFF_DOT = 0;                       // dO^T [DV][72]
+    static constexpr int OFF_BLK = DV * WSB_P64 * 2;
+    static constexpr int STAGE = OFF_BLK + WSB_CHUNK;
+    static constexpr int TOTAL = 2 * STAGE;
+    static constexpr int VG = DV / 8;                       // 16-byte units per token row
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(C * VG <= 256, "one dO unit per lane of the first four loader waves");
+};
+constexpr int BS_KIB = WSB_CHUNK / 1024;
+
+template <int NCW>
+__global__ void __launch_bounds__(512)
+chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_t* dv, float* dS0,
+                      bf16_t* svdS, bf16_t* svdZ, int T, int H)
+{
+    using SC = BScanCfg<NCW>;
+    __shared__ __attribute__((aligned(1024))) char smem[SC::TOTAL];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const bool loader = wave < SC::NLW;
+    const int ln = lane & 15, lg = lane >> 4;
+    const int cw = wave - SC::NLW;
+    constexpr int nsplit = DK / SC::DV;
+    const int nchunks = (T + C - 1) / C;
+    const int nwg = gridDim.x, w = blockIdx.x;
+    const int lid = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;   // slices of a head on one XCD
+    const int head = lid / nsplit, slice = lid % nsplit;
+    const int b = head / H, h = head % H;
+    const int j0 = slice * SC::DV;
+    const size_t tokstride = (size_t)H * DK;
+    const size_t hbase = ((size_t)b * T * H + h) * DK;
+    const size_t sbase = (size_t)head * DK * DK;
+    const char* wsh = wsb + (size_t)head * nchunks * WSB_CHUNK;
+
+    // ---- loader side: lane pt moves dO unit (token ut, columns 8 ug ..)
+    const int pt = t & 255, ug = pt % SC::VG, ut = pt / SC::VG;
+    const bool ulane = t < 256 && ut < C;
+    bf16x8 drow = bf16x8{};
+    auto load_block = [&](int n) {
+        const char* src = wsh + (size_t)n * WSB_CHUNK;
+        char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
+        for (int u = wave; u < BS_KIB; u += SC::NLW)
+            __builtin_amdgcn_global_load_lds(src + (size_t)u * 1024 + lane * 16,
+                                             (__attribute__((address_space(3))) void*)(dst + u * 1024), 16, 0, 0);
+    };
+    auto load_do = [&](int n) {
+        if (!ulane) return;
+        const int tok = min(n * C + ut, T - 1);
+        drow = *reinterpret_cast<const bf16x8*>(dO + hbase + (size_t)tok * tokstride + j0 + 8 * ug);
+    };
+    auto write_dot = [&](int n) {             // dO^T of chunk n into stage n % 2 (zero past T)
+        bf16_t* dt = reinterpret_cast<bf16_t*>(smem + (n & 1) * SC::STAGE + SC::OFF_DOT);
+        if (ulane) {
+            const bool ok = n * C + ut < T;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) dt[(8 * ug + c) * WSB_P64 + ut] = ok ? drow[c] : bf16_t{};
+        }
+    };
+
+    // ---- consumer side: dS[16cb + 4lg + e][j0 + jc] in acc_s[cb][e]
+    const int jc = 16 * cw + ln;
+    f32x4 acc_s[8];
+    if (!loader) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc_s[cb][e] = dST ? dST[sbase + (size_t)(16 * cb + 4 * lg + e) * DK + j0 + jc] : 0.f;
+    } else {
+        load_block(nchunks - 1);
+        load_do(nchunks - 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        write_dot(nchunks - 1);
+    }
+    lds_barrier();
+
+    for (int n = nchunks - 1; n >= 0; --n) {
+        if (loader) {
+            if (n > 0) { load_block(n - 1); load_do(n - 1); }
+            __builtin_amdgcn_s_waitcnt(0);    // the stage must be complete at the barrier
+            if (n > 0) write_dot(n - 1);
+        } else {
+            const char* st = smem + (n & 1) * SC::STAGE;
+            const char* blk = st + SC::OFF_BLK;
+            const bf16_t* sdOT = reinterpret_cast<const bf16_t*>(st + SC::OFF_DOT);
+            const bf16_t* sAqkT = reinterpret_cast<const bf16_t*>(blk + WSB_AQKT);
+            const bf16_t* sTmT = reinterpret_cast<const bf16_t*>(blk + WSB_TMT);
+            const bf16_t* sQtT = reinterpret_cast<const bf16_t*>(blk + WSB_QTT);
+            const bf16_t* sKhT = reinterpret_cast<const bf16_t*>(blk + WSB_KHT);
+            const bf16_t* sKt = reinterpret_cast<const bf16_t*>(blk + WSB_KT);
+            const float* sGam = reinterpret_cast<const float*>(blk + WSB_GAM);
+            const float* sBeta = reinterpret_cast<const float*>(blk + WSB_BETA);
+            const size_t cidx = (size_t)head * nchunks + n;
+
+            // dS' of this chunk (gradient of the state it hands on), for the
+            // gradient kernel
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    svdS[(cidx * DK + 16 * cb + 4 * lg + e) * DK + j0 + jc] = (bf16_t)acc_s[cb][e];
+
+            bf16x8 sb[4], dob[2];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) sb[p] = cat8(to_bf16x4(acc_s[2 * p]), to_bf16x4(acc_s[2 * p + 1]));
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                dob[p] = cat8(ld4(sdOT + jc * WSB_P64 + 32 * p + 4 * lg),
+                              ld4(sdOT + jc * WSB_P64 + 32 * p + 16 + 4 * lg));
+
+            // dVn = Aqk^T dO + Kt dS'
+            f32x4 dvn[4];
+#pragma unroll
+            for (int Rb = 0; Rb < 4; ++Rb) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                const bf16_t* ra = sAqkT + (16 * Rb + ln) * WSB_P64;
+                const bf16_t* rk = sKt + (16 * Rb + ln) * WSB_P128;
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(ra, p, lg, true), dob[p], a, 0, 0, 0);
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rk, p, lg, true), sb[p], a, 0, 0, 0);
+                dvn[Rb] = a;
+            }
+
+            // dZ = Tm^T dVn, dV = Diag(beta) dZ
+            bf16x8 vb[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) vb[p] = cat8(to_bf16x4(dvn[2 * p]), to_bf16x4(dvn[2 * p + 1]));
+            f32x4 dvv[4];
+#pragma unroll
+            for (int Rb = 0; Rb < 4; ++Rb) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                const bf16_t* rt = sTmT + (16 * Rb + ln) * WSB_P64;
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rt, p, lg, true), vb[p], a, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * Rb + 4 * lg + e, tok = n * C + r;
+                    dvv[Rb][e] = sBeta[r] * a[e];
+                    svdZ[(cidx * C + r) * DK + j0 + jc] = (bf16_t)a[e];
+                    if (tok < T) dv[hbase + (size_t)tok * tokstride + j0 + jc] = (bf16_t)dvv[Rb][e];
+                }
+            }
+
+            // dS <- Diag(gamma) dS' + Qt^T dO - Kh^T dV
+            bf16x8 nb[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) nb[p] = cat8(to_bf16x4(-dvv[2 * p]), to_bf16x4(-dvv[2 * p + 1]));
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(sGam + 16 * cb + 4 * lg);
+                f32x4 a = acc_s[cb] * gv;
+                const bf16_t* rq = sQtT + (16 * cb + ln) * WSB_P64;
+                const bf16_t* rh = sKhT + (16 * cb + ln) * WSB_P64;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rq, p, lg, true), dob[p], a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rh, p, lg, true), nb[p], a, 0, 0, 0);
+                }
+                acc_s[cb] = a;
+            }
+        }
+        lds_barrier();
+    }
+
+    if (!loader && dS0) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dS0[sbase + (size_t)(16 * cb + 4 * lg + e) * DK + j0 + jc] = acc_s[cb][e];
+    }
+}
+
+// ---- per-chunk gradients -------------------------------------------------------
+// One workgroup (eight waves) per (head, chunk).  Wave w owns key channels
+// 16w .. 16w+15 for all 64 tokens, lane (lg, ln) the channel 16w + ln and rows
+// 16m + 4lg + e (m, e = 0..3): the layout of a 16 x 16 MFMA output tile, so the
+// decay computed first and the gradient tiles accumulated last line up in
+// registers.  Operands indexed by (token, channel) are staged in LDS; the
+// value-side ones (dO, dV, Vn, dZ, S, dS') are read straight from memory as
+// 16-byte MFMA fragments.
+struct GradLds {
+    static constexpr int P64 = C + 8, P128 = DK + 8;
+    static constexpr int OFF_KH = 0;                          // Kh [64][136]
+    static constexpr int OFF_KB = OFF_KH + C * P128 * 2;      // Kb [64][136]
+    static constexpr int OFF_QTT = OFF_KB + C * P128 * 2;     // Qt^T [128][72]
+    static constexpr int OFF_KHT = OFF_QTT + DK * P64 * 2;    // Kh^T
+    static constexpr int OFF_KBT = OFF_KHT + DK * P64 * 2;    // Kb^T
+    static constexpr int OFF_DAQK = OFF_KBT + DK * P64 * 2;   // dAqk [64][72]
+    static constexpr int OFF_DAQKT = OFF_DAQK + C * P64 * 2;  // dAqk^T
+    static constexpr int OFF_DAP = OFF_DAQKT + C * P64 * 2;   // dA' = Diag(beta) dAkk
+    static constexpr int OFF_DAPT = OFF_DAP + C * P64 * 2;    // dA'^T
+    static constexpr int OFF_BETA = OFF_DAPT + C * P64 * 2;   // beta [64] fp32
+    static constexpr int OFF_DB = OFF_BETA + C * 4;           // dbeta [64] fp32
+    static constexpr int TOTAL = OFF_DB + C * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ bf16x8 ld8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x8 neg8(bf16x8 x) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = -x[i];
+    return x;
+}
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(512)
+chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf16_t* beta,
+                      const bf16_t* dO, const bf16_t* dV, const bf16_t* svS, const bf16_t* svdS,
+                      const bf16_t* svY, const bf16_t* svVn, const bf16_t* svdZ,
+                      bf16_t* dq, bf16_t* dk, float* dg, bf16_t* dbeta, int T, int H)
+{
+    using L = GradLds;
+    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    bf16_t* sKh = reinterpret_cast<bf16_t*>(smem + L::OFF_KH);
+    bf16_t* sKb = reinterpret_cast<bf16_t*>(smem + L::OFF_KB);
+    bf16_t* sQtT = reinterpret_cast<bf16_t*>(smem + L::OFF_QTT);
+    bf16_t* sKhT = reinterpret_cast<bf16_t*>(smem + L::OFF_KHT);
+    bf16_t* sKbT = reinterpret_cast<bf16_t*>(smem + L::OFF_KBT);
+    bf16_t* sdAqk = reinterpret_cast<bf16_t*>(smem + L::OFF_DAQK);
+    bf16_t* sdAqkT = reinterpret_cast<bf16_t*>(smem + L::OFF_DAQKT);
+    bf16_t* sdAp = reinterpret_cast<bf16_t*>(smem + L::OFF_DAP);
+    bf16_t* sdApT = reinterpret_cast<bf16_t*>(smem + L::OFF_DAPT);
+    float* sbeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
+    float* sdb = reinterpret_cast<float*>(smem + L::OFF_DB);
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int ln = lane & 15, lg = lane >> 4;
+    const int nchunks = (T + C - 1) / C;
+    const int head = blockIdx.x / nchunks, n = blockIdx.x % nchunks;
+    const int b = head / H, h = head % H;
+    const size_t tokstride = (size_t)H * DK;
+    const size_t hbase = ((size_t)b * T * H + h) * DK;
+    const size_t cidx = (size_t)head * nchunks + n;
+    const int tok0 = n * C;
+    const int c = 16 * wave + ln;                 // this lane's key channel
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+    // ===== decay and the decay-scaled keys / queries =====
+    float G[4][4], qv[4][4], kv[4][4];
+    float carry = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        float s4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = tok0 + 16 * m + 4 * lg + e;
+            const bool ok = tok < T;
+            const size_t off = hbase + (size_t)min(tok, T - 1) * tokstride + c;
+            const float gl = ok ? g[off] * LOG2E : 0.f;
+            qv[m][e] = ok ? (float)q[off] : 0.f;
+            kv[m][e] = ok ? (float)k[off] : 0.f;
+            s4[e] = (e ? s4[e - 1] : 0.f) + gl;
+        }
+        float bs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bs[j] = __shfl(s4[3], ln + 16 * j);
+        const float excl = (lg > 0 ? bs[0] : 0.f) + (lg > 1 ? bs[1] : 0.f) + (lg > 2 ? bs[2] : 0.f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) G[m][e] = carry + excl + s4[e];   // log2 units
+        carry += bs[0] + bs[1] + bs[2] + bs[3];
+    }
+    const float Gc = carry;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f32x4 qt, kh, kb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float eg = __builtin_amdgcn_exp2f(G[m][e]), egi = __builtin_amdgcn_exp2f(-G[m][e]);
+            qt[e] = eg * qv[m][e]; kh[e] = eg * kv[m][e]; kb[e] = egi * kv[m][e];
+            const int r = 16 * m + 4 * lg + e;
+            sKh[r * L::P128 + c] = (bf16_t)kh[e];
+            sKb[r * L::P128 + c] = (bf16_t)kb[e];
+        }
+        store_vec4<bf16_t>(sQtT + c * L::P64 + 16 * m + 4 * lg, qt);
+        store_vec4<bf16_t>(sKhT + c * L::P64 + 16 * m + 4 * lg, kh);
+        store_vec4<bf16_t>(sKbT + c * L::P64 + 16 * m + 4 * lg, kb);
+    }
+    if (t < C) {
+        const int tok = tok0 + t;
+        sbeta[t] = tok < T ? (float)beta[((size_t)b * T + tok) * H + h] : 0.f;
+        sdb[t] = 0.f;
+    }
+    lds_barrier();
+
+    // ===== C x C products: KK = Kh Kb^T, M1 = dZ Vn^T, M2 = dO Vn^T =====
+    // tile (mb, nb): rows 16mb.., columns 16nb..; tiles above the diagonal are zero
+    for (int tt = wave; tt < 16; tt += 8) {
+        const int mb = tt >> 2, nb = tt & 3;
+        if (nb > mb) {
+            const int r = 16 * mb + 4 * lg, i = 16 * nb + ln;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { sdAqk[(r + e) * L::P64 + i] = bf16_t{}; sdAp[(r + e) * L::P64 + i] = bf16_t{}; }
+            store_vec4<bf16_t>(sdAqkT + i * L::P64 + r, z4);
+            store_vec4<bf16_t>(sdApT + i * L::P64 + r, z4);
+            continue;
+        }
+        const int ra = 16 * mb + ln, rb = 16 * nb + ln;
+        const int toka = tok0 + ra;
+        const bool oka = toka < T;
+        const bf16_t* pdO = dO + hbase + (size_t)min(toka, T - 1) * tokstride;
+        const bf16_t* pdZ = svdZ + (cidx * C + ra) * DK;
+        const bf16_t* pVn = svVn + (cidx * C + rb) * DK;
+        f32x4 kk = z4, m1 = z4, m2 = z4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int ko = 32 * s + 8 * lg;
+            const bf16x8 vnf = ld8(pVn + ko);
+            const bf16x8 dof = oka ? ld8(pdO + ko) : bf16x8{};
+            kk = mma(ld8(sKh + ra * L::P128 + ko), ld8(sKb + rb * L::P128 + ko), kk);
+            m1 = mma(ld8(pdZ + ko), vnf, m1);
+            m2 = mma(dof, vnf, m2);
+        }
+        const int r0 = 16 * mb + 4 * lg, i = 16 * nb + ln;
+        f32x4 aq, ap;
+        float part[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = r0 + e;
+            aq[e] = (i <= r) ? m2[e] : 0.f;
+            const float dakk = (i < r) ? -m1[e] : 0.f;
+            ap[e] = sbeta[r] * dakk;
+            part[e] = dakk * kk[e];
+            sdAqk[r * L::P64 + i] = (bf16_t)aq[e];
+            sdAp[r * L::P64 + i] = (bf16_t)ap[e];
+        }
+        store_vec4<bf16_t>(sdAqkT + i * L::P64 + r0, aq);
+        store_vec4<bf16_t>(sdApT + i * L::P64 + r0, ap);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) part[e] += __shfl_xor(part[e], off);
+        }
+        if (ln == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&sdb[r0 + e], part[e]);
+        }
+    }
+    {   // dbeta, first term: row r = t / 8, columns 16 (t % 8) ..
+        const int r = t >> 3, p8 = t & 7;
+        const bf16_t* py = svY + (cidx * C + r) * DK + 16 * p8;
+        const bf16_t* pz = svdZ + (cidx * C + r) * DK + 16 * p8;
+        const bf16x8 y0 = ld8(py), y1 = ld8(py + 8), z0 = ld8(pz), z1 = ld8(pz + 8);
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d += (float)y0[i] * (float)z0[i] + (float)y1[i] * (float)z1[i];
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        d += __shfl_xor(d, 4);
+        if (p8 == 0) atomicAdd(&sdb[r], d);
+    }
+    lds_barrier();
+    if (t < C && tok0 + t < T) dbeta[((size_t)b * T + tok0 + t) * H + h] = (bf16_t)sdb[t];
+
+    // ===== C x d_k products: wave w -> channel block w, token blocks m = 0..3 =====
+    f32x4 aQ[4], aH[4], aB[4], aT[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) { aQ[m] = z4; aH[m] = z4; aB[m] = z4; aT[m] = z4; }
+    float sds = 0.f;
+    {
+        const bf16_t* pS = svS + (cidx * DK + c) * DK;
+        const bf16_t* pdS = svdS + (cidx * DK + c) * DK;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {             // contraction over value columns
+            const int ko = 32 * s + 8 * lg;
+            const bf16x8 sf = ld8(pS + ko), dsf = ld8(pdS + ko);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sds += (float)sf[i] * (float)dsf[i];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * m + ln, tok = tok0 + r;
+                const bool ok = tok < T;
+                const size_t at = hbase + (size_t)min(tok, T - 1) * tokstride + ko;
+                const bf16x8 dof = ok ? ld8(dO + at) : bf16x8{};
+                const bf16x8 dvf = ok ? neg8(ld8(dV + at)) : bf16x8{};
+                const bf16x8 vnf = ld8(svVn + (cidx * C + r) * DK + ko);
+                aQ[m] = mma(dof, sf, aQ[m]);
+                aH[m] = mma(dvf, sf, aH[m]);
+                aT[m] = mma(vnf, dsf, aT[m]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {             // contraction over tokens
+            const int ko = 32 * s + 8 * lg;
+            const bf16x8 kbt = ld8(sKbT + c * L::P64 + ko);
+            const bf16x8 qtt = ld8(sQtT + c * L::P64 + ko);
+            const bf16x8 kht = ld8(sKhT + c * L::P64 + ko);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int ar = (16 * m + ln) * L::P64 + ko;
+                aQ[m] = mma(ld8(sdAqk + ar), kbt, aQ[m]);
+                aH[m] = mma(ld8(sdAp + ar), kbt, aH[m]);
+                aB[m] = mma(ld8(sdAqkT + ar), qtt, aB[m]);
+                aB[m] = mma(ld8(sdApT + ar), kht, aB[m]);
+            }
+        }
+    }
+
+    // ===== chain rule to q, k, g =====
+    sds += __shfl_xor(sds, 16);
+    sds += __shfl_xor(sds, 32);
+    float dG[4][4], ktp = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float eg = __builtin_amdgcn_exp2f(G[m][e]), egi = __builtin_amdgcn_exp2f(-G[m][e]);
+            const float et = __builtin_amdgcn_exp2f(Gc - G[m][e]);
+            const float dqt = aQ[m][e], dkh = aH[m][e], dkb = aB[m][e], dkt = aT[m][e];
+            dG[m][e] = qv[m][e] * eg * dqt + kv[m][e] * (eg * dkh - egi * dkb - et * dkt);
+            ktp += kv[m][e] * et * dkt;
+            const int tok = tok0 + 16 * m + 4 * lg + e;
+            if (tok < T) {
+                const size_t off = hbase + (size_t)tok * tokstride + c;
+                dq[off] = (bf16_t)(eg * dqt);
+                dk[off] = (bf16_t)(eg * dkh + egi * dkb + et * dkt);
+            }
+        }
+    }
+    ktp += __shfl_xor(ktp, 16);
+    ktp += __shfl_xor(ktp, 32);
+    // dg_r = sum over rows r' >= r of dG, plus the gradient of G_64 (which every
+    // row's g enters)
+    float acc = __builtin_amdgcn_exp2f(Gc) * sds + ktp;
+#pragma unroll
+    for (int m = 3; m >= 0; --m) {
+        float sf[4];
+        sf[3] = dG[m][3];
+#pragma unroll
+        for (int e = 2; e >= 0; --e) sf[e] = sf[e + 1] + dG[m][e];
+        float bs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bs[j] = __shfl(sf[0], ln + 16 * j);
+        const float excl = (lg < 3 ? bs[3] : 0.f) + (lg < 2 ? bs[2] : 0.f) + (lg < 1 ? bs[1] : 0.f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = tok0 + 16 * m + 4 * lg + e;
+            if (tok < T) dg[hbase + (size_t)tok * tokstride + c] = acc + excl + sf[e];
+        }
+        acc += bs[0] + bs[1] + bs[2] + bs[3];
+    }
+}
+
+}  // namespace
+
+size_t chunk_bwd_ws_layout(long long B, long long T, long long H, size_t* off)
+{
+    const size_t units = (size_t)B * (size_t)H * (size_t)((T + C - 1) / C);   // (head, chunk) pairs
+    size_t o[KDA_BWD_WS_REGIONS + 1];
+    o[KDA_BWD_WS_FWD] = 0;
+    o[KDA_BWD_WS_BWD] = chunk_ws_bytes(B, T, H);
+    o[KDA_BWD_WS_S] = o[KDA_BWD_WS_BWD] + units * WSB_CHUNK;
+    o[KDA_BWD_WS_DS] = o[KDA_BWD_WS_S] + units * DK * DK * 2;
+    o[KDA_BWD_WS_Y] = o[KDA_BWD_WS_DS] + units * DK * DK * 2;
+    o[KDA_BWD_WS_VN] = o[KDA_BWD_WS_Y] + units * C * DK * 2;
+    o[KDA_BWD_WS_DZ] = o[KDA_BWD_WS_VN] + units * C * DK * 2;
+    o[KDA_BWD_WS_REGIONS] = o[KDA_BWD_WS_DZ] + units * C * DK * 2;
+    if (off)
+        for (int i = 0; i < KDA_BWD_WS_REGIONS; ++i) off[i] = o[i];
+    return o[KDA_BWD_WS_REGIONS];
+}
+
+hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                            const void* beta, const float* S0, const void* dO, const float* dST,
+                            void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dS0,
+                            int B, int T, int H, char* ws, hipStream_t stream)
+{
+    const long long heads = (long long)B * H;
+    const int nchunks = (T + C - 1) / C;
+    size_t off[KDA_BWD_WS_REGIONS];
+    chunk_bwd_ws_layout(B, T, H, off);
+    bf16_t* svS = reinterpret_cast<bf16_t*>(ws + off[KDA_BWD_WS_S]);
+    bf16_t* svdS = reinterpret_cast<bf16_t*>(ws + off[KDA_BWD_WS_DS]);
+    bf16_t* svY = reinterpret_cast<bf16_t*>(ws + off[KDA_BWD_WS_Y]);
+    bf16_t* svVn = reinterpret_cast<bf16_t*>(ws + off[KDA_BWD_WS_VN]);
+    bf16_t* svdZ = reinterpret_cast<bf16_t*>(ws + off[KDA_BWD_WS_DZ]);
+    char* wsb = ws + off[KDA_BWD_WS_BWD];
+
+    hipError_t err = launch_bwd_forward_part(q, k, v, g, beta, S0, B, T, H, ws + off[KDA_BWD_WS_FWD],
+                                             wsb, svS, svY, svVn, stream);
+    if (err != hipSuccess) return err;
+
+    const int ncw = heads * 4 >= 256 ? 2 : 1;
+#define KDA_BSCAN(NCW) hipLaunchKernelGGL(chunk_bwd_scan_kernel<NCW>, dim3((unsigned)(heads * (DK / BScanCfg<NCW>::DV))), \
+                                          dim3(512), 0, stream, (const char*)wsb, (const bf16_t*)dO, dST, (bf16_t*)dv, \
+                                          dS0, svdS, svdZ, T, H)
+    if (ncw == 2) KDA_BSCAN(2);
+    else KDA_BSCAN(1);
+#undef KDA_BSCAN
+
+    hipLaunchKernelGGL(chunk_bwd_grad_kernel, dim3((unsigned)(heads * nchunks)), dim3(512), 0, stream,
+                       (const bf16_t*)q, (const bf16_t*)k, g, (const bf16_t*)beta, (const bf16_t*)dO,
+                       (const bf16_t*)dv, svS, svdS, svY, svVn, svdZ,
+                       (bf16_t*)dq, (bf16_t*)dk, dg, (bf16_t*)dbeta, T, H);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,6 +1,6 @@
-// kda_chunk_common.h -- device helpers shared by the chunked KDA kernels
-// (the fused and two-kernel schedules in kda_prefill.hip and the
-// wave-specialised schedule in kda_prefill_ws.hip).  Internal to libkda.
+// kda_chunk_common.h -- device helpers and workspace layouts shared by the
+// chunked KDA kernels (the forward schedules in kda_prefill.hip and the
+// backward pass in kda_backward.hip).  Internal to libkda.
 #pragma once
 #include "kda_device.h"
 
@@ -135,8 +135,11 @@ __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
     return r;
 }
 
+// When TmT is not null, X_RI is also written unscaled and transposed there
+// (TmT[i][r] = X[r][i], row pitch PT), for the backward pass.
 template <int I, int PA, int PT>
-__device__ __forceinline__ void ut_offdiag_column(const float* RA, bf16_t* RT, const float* s_beta, int lane) {
+__device__ __forceinline__ void ut_offdiag_column(const float* RA, bf16_t* RT, const float* s_beta, int lane,
+                                                  bf16_t* TmT = nullptr) {
     const int ln = lane & 15, lg = lane >> 4;
     auto a_op = [&](int R, int J) {   // A operand: block (R, J) of RA, row-major
         return to_bf16x4(*reinterpret_cast<const f32x4*>(RA + (16 * R + ln) * PA + 16 * J + 4 * lg));
@@ -155,8 +158,45 @@ __device__ __forceinline__ void ut_offdiag_column(const float* RA, bf16_t* RT, c
                                                           f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) RT[(16 * R + 4 * lg + e) * PT + 16 * I + ln] = (bf16_t)(bcol * X[R][e]);
+        if (TmT) *reinterpret_cast<bf16x4*>(TmT + (16 * I + ln) * PT + 16 * R + 4 * lg) = to_bf16x4(X[R]);
     }
 }
+
+// ---- MFMA operands split over two 16-column blocks ---------------------------
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[i + 4] = b[i]; }
+    return r;
+}
+__device__ __forceinline__ bf16x4 ld4(const bf16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
+
+// Two adjacent 16-column blocks (2p, 2p+1) of one row as an A-operand: lane
+// (row ln, group lg) takes columns 32p + 4lg .. +3 and 32p + 16 + 4lg .. +3;
+// with `hi` false the second half is zero.  The matching B operand is two
+// accumulator tiles (rows 32p + 4lg + e and 32p + 16 + 4lg + e of a product's
+// output) packed side by side, so a product's output feeds the next product
+// without leaving registers.
+__device__ __forceinline__ bf16x8 a_pair(const bf16_t* row, int p, int lg, bool hi) {
+    const bf16x4 a = ld4(row + 32 * p + 4 * lg);
+    const bf16x4 b = hi ? ld4(row + 32 * p + 16 + 4 * lg) : bf16x4{};
+    return cat8(a, b);
+}
+
+// ---- backward pass: per-chunk operand block of the reverse state scan --------
+// Written by the prep kernel next to the forward block, read by
+// chunk_bwd_scan_kernel.  All bf16 except the two vectors; rows padded to
+// 72 / 136 elements as in the forward block.
+constexpr int WSB_P64 = C + 8, WSB_P128 = DK + 8;
+constexpr int WSB_AQKT = 0;                              // Aqk^T [64][72]
+constexpr int WSB_TMT = WSB_AQKT + C * WSB_P64 * 2;      // Tm^T  [64][72] (no beta)
+constexpr int WSB_QTT = WSB_TMT + C * WSB_P64 * 2;       // Qt^T  [128][72]
+constexpr int WSB_KHT = WSB_QTT + DK * WSB_P64 * 2;      // Kh^T  [128][72]
+constexpr int WSB_KT = WSB_KHT + DK * WSB_P64 * 2;       // Kt = e^{G_64 - G} k [64][136]
+constexpr int WSB_GAM = WSB_KT + C * WSB_P128 * 2;       // e^{G_64} [128] fp32
+constexpr int WSB_BETA = WSB_GAM + DK * 4;               // beta [64] fp32 (0 past T)
+constexpr int WSB_USED = WSB_BETA + C * 4;               // 73,472 bytes
+constexpr int WSB_CHUNK = (WSB_USED + 1023) / 1024 * 1024;   // 73,728
 
 // Eight consecutive elements (one 16-byte load for bf16, two for fp32).
 template <typename E> struct Raw8;

@@ -27,6 +27,36 @@ size_t chunk_ws_bytes(long long B, long long T, long long H);
 // Whether the two-kernel schedule is expected to be faster for this shape.
 bool chunk_prefers_two_kernel(long long B, long long T, long long H, int dtype);
 
+// Backward pass of the chunked prefill (bf16, T >= 1): regions of its
+// workspace, in order.
+enum {
+    KDA_BWD_WS_FWD = 0,   // forward operand blocks, chunk_ws_bytes(B, T, H)
+    KDA_BWD_WS_BWD,       // reverse-scan operand blocks, WSB_CHUNK per chunk
+    KDA_BWD_WS_S,         // S entering each chunk, bf16 [128][128]
+    KDA_BWD_WS_DS,        // gradient of the state leaving each chunk, bf16 [128][128]
+    KDA_BWD_WS_Y,         // V - Kh S per chunk, bf16 [64][128]
+    KDA_BWD_WS_VN,        // Vn per chunk, bf16 [64][128]
+    KDA_BWD_WS_DZ,        // Tm^T dVn per chunk, bf16 [64][128]
+    KDA_BWD_WS_REGIONS
+};
+// Byte offsets of the regions (to `off` when non-null); returns the total.
+size_t chunk_bwd_ws_layout(long long B, long long T, long long H, size_t* off);
+
+// The prep kernel (writing both operand blocks) and the forward scan in save
+// mode, as the first half of the backward pass.
+typedef __bf16 bf16_t;
+hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, const float* g,
+                                   const void* beta, const float* S0, int B, int T, int H,
+                                   char* ws_fwd, char* ws_bwd, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
+                                   hipStream_t stream);
+
+// dq, dk, dv, dg, dbeta (and dS0 when non-null) from dO (and dS_T when
+// non-null); `ws` holds chunk_bwd_ws_layout(B, T, H) bytes.
+hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                            const void* beta, const float* S0, const void* dO, const float* dST,
+                            void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dS0,
+                            int B, int T, int H, char* ws, hipStream_t stream);
+
 // S_T = S0 (or zeros when S0 is NULL) for `heads` states; used when T = 0.
 hipError_t launch_state_copy(const float* S0, float* S_T, long long heads,
                              hipStream_t stream);
@@ -35,7 +65,6 @@ hipError_t launch_state_copy(const float* S0, float* S_T, long long heads,
 // dimensions in elements, multiples of 8).  A is bf16 or, with a_f32, fp32
 // (split into bf16 hi + lo parts); B is bf16; C is fp32 (c_f32) or bf16.
 // epilogue 0: none, 1: c -> -softplus(c).
-typedef __bf16 bf16_t;
 hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, bool c_f32,
                           int epilogue, int M, int N, int K, int lda, int ldb, int ldc,
                           hipStream_t stream);

@@ -126,11 +126,15 @@ constexpr int PREP_CHUNKS = 4;                      // chunks per prep workgroup
 // The fused kernel (PREP = false): one workgroup per (head, value slice)
 // walks all chunks of its head.  The prep instantiation (PREP = true): one
 // workgroup per (head, chunk) runs only the key-side work -- decay, Aqk, Akk,
-// Tm -- and exports it to the workspace for chunk_scan_kernel.
-template <typename E, int DV, bool PREP>
+// Tm -- and exports it to the workspace for chunk_scan_kernel; with BWD it
+// also exports to `wsb` the operands of the backward state scan (the
+// transposes Aqk^T, Tm^T, Qt^T, Kh^T and Kt = Diag(e^{G_64}) Kb, layout
+// WSB_* in kda_chunk_common.h).
+template <typename E, int DV, bool PREP, bool BWD = false>
 __global__ void __launch_bounds__(NT)
 chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* beta,
-                 const float* S0, E* o, float* S_T, int T, int H, int nsplit, char* ws)
+                 const float* S0, E* o, float* S_T, int T, int H, int nsplit, char* ws,
+                 char* wsb)
 {
     // (No __restrict__ on the inputs: the LDS barriers are asm statements with
     // a memory clobber, and without restrict the compiler keeps the prefetch
@@ -165,6 +169,10 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     float* s_gam = reinterpret_cast<float*>(smem + L::OFF_GAM);
     float* s_beta = reinterpret_cast<float*>(smem + L::OFF_BETA);
     float* s_tot = reinterpret_cast<float*>(smem + L::OFF_TOT);
+    // prep for the backward pass: Tm^T, unscaled, in the (unused) value-side
+    // buffers; null otherwise
+    static_assert(!BWD || (PREP && L::OFF_VN - L::OFF_V >= C * WSB_P64 * 2), "Tm^T fits in the value-side buffers");
+    bf16_t* sTmT = BWD ? reinterpret_cast<bf16_t*>(smem + L::OFF_V) : nullptr;
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform per wave
@@ -478,24 +486,29 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 
         // ===== UT off-diagonal blocks; Tm Diag(beta) in E =====
         if constexpr (!L::kF32) {
-            if (wave == 0) ut_offdiag_column<0, L::PA, L::P64>(RA, RT, s_beta, lane);
-            else if (wave == 1) ut_offdiag_column<1, L::PA, L::P64>(RA, RT, s_beta, lane);
-            else if (wave == 2) ut_offdiag_column<2, L::PA, L::P64>(RA, RT, s_beta, lane);
+            if (wave == 0) ut_offdiag_column<0, L::PA, L::P64>(RA, RT, s_beta, lane, sTmT);
+            else if (wave == 1) ut_offdiag_column<1, L::PA, L::P64>(RA, RT, s_beta, lane, sTmT);
+            else if (wave == 2) ut_offdiag_column<2, L::PA, L::P64>(RA, RT, s_beta, lane, sTmT);
             else if (wave == 3) {
                 // diagonal blocks, scaled by beta of their column
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
                     const int r = 16 * bb + 4 * lg;
                     const float bcol = s_beta[16 * bb + ln];
+                    f32x4 x;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        RT[(r + e) * L::P64 + 16 * bb + ln] = (E)(bcol * RA[(r + e) * L::PA + 16 * bb + ln]);
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = RA[(r + e) * L::PA + 16 * bb + ln];
+                        RT[(r + e) * L::P64 + 16 * bb + ln] = (E)(bcol * x[e]);
+                    }
+                    if (sTmT) store_vec4<bf16_t>(sTmT + (16 * bb + ln) * WSB_P64 + r, x);
                 }
             } else {
-                for (int u = wave - 4; u < 6; u += 4) {   // zero upper blocks of RT
+                for (int u = wave - 4; u < 6; u += 4) {   // zero upper blocks of RT (lower of Tm^T)
                     const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
                     const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
                     store_vec4<E>(RT + (16 * R + ln) * L::P64 + 16 * I + 4 * lg, z4);
+                    if (sTmT) store_vec4<bf16_t>(sTmT + (16 * I + ln) * WSB_P64 + 16 * R + 4 * lg, z4);
                 }
             }
             if (wave < 3 && n + 1 < n_end) load_chunk(n + 1, in);
@@ -548,6 +561,38 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
             copy(WS_TM, L::OFF_RT, WS_QK - WS_TM);
             copy(WS_QK, L::OFF_QK, WS_GAM - WS_QK);
             copy(WS_GAM, L::OFF_GAM, WS_USED - WS_GAM);
+            if constexpr (BWD) {
+                // operands of the backward state scan: transposes read from LDS
+                // eight strided elements at a time, written 16 bytes at a time
+                char* bb = wsb + ((size_t)head * nchunks + n) * WSB_CHUNK;
+                auto transpose = [&](bf16_t* dst, const E* src, int src_pitch, int rows) {
+                    for (int u = t; u < rows * (C / 8); u += NT) {     // dst row, 8-column group
+                        const int row = u >> 3, c8 = 8 * (u & 7);
+                        bf16x8 x;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) x[i] = src[(c8 + i) * src_pitch + row];
+                        *reinterpret_cast<bf16x8*>(dst + row * WSB_P64 + c8) = x;
+                    }
+                };
+                transpose(reinterpret_cast<bf16_t*>(bb + WSB_AQKT), sQK, L::P64, C);
+                transpose(reinterpret_cast<bf16_t*>(bb + WSB_QTT), sQt, L::P128, DK);
+                transpose(reinterpret_cast<bf16_t*>(bb + WSB_KHT), sKh, L::P128, DK);
+                for (int u = t; u < C * WSB_P64 * 2 / 16; u += NT)
+                    reinterpret_cast<i32x4*>(bb + WSB_TMT)[u] = reinterpret_cast<const i32x4*>(sTmT)[u];
+                for (int u = t; u < C * (DK / 8); u += NT) {           // Kt = Diag(e^{G_64}) Kb
+                    const int r = u >> 4, c8 = 8 * (u & 15);
+                    const bf16x8 kb = *reinterpret_cast<const bf16x8*>(sKb + r * L::P128 + c8);
+                    bf16x8 x;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x[i] = (bf16_t)(s_gam[c8 + i] * (float)kb[i]);
+                    *reinterpret_cast<bf16x8*>(bb + WSB_KT + (r * WSB_P128 + c8) * 2) = x;
+                }
+                if (t < DK) reinterpret_cast<float*>(bb + WSB_GAM)[t] = s_gam[t];
+                if (t < C) reinterpret_cast<float*>(bb + WSB_BETA)[t] = s_beta[t];
+                // the next chunk's first LDS writes (beta, column totals) come
+                // before its first barrier
+                lds_barrier();
+            }
             continue;
         }
 
@@ -673,27 +718,13 @@ template <int NCW> struct ScanCfg {                       // NCW consumer waves
     static_assert(C * VG <= 256, "one V / output unit per lane of the first four loader waves");
 };
 
-__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[i + 4] = b[i]; }
-    return r;
-}
-__device__ __forceinline__ bf16x4 ld4(const bf16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
-
-// Two adjacent 16-column blocks (2p, 2p+1) of one row as an A-operand: lane
-// (row ln, group lg) takes columns 32p + 4lg .. +3 and 32p + 16 + 4lg .. +3;
-// with `hi` false the second half is zero.
-__device__ __forceinline__ bf16x8 a_pair(const bf16_t* row, int p, int lg, bool hi) {
-    const bf16x4 a = ld4(row + 32 * p + 4 * lg);
-    const bf16x4 b = hi ? ld4(row + 32 * p + 16 + 4 * lg) : bf16x4{};
-    return cat8(a, b);
-}
-
-template <int NCW>
+// SAVE (the forward part of the backward pass): no output; instead each
+// chunk's entry state S_n [128][128], Y = V - Kh S_n [64][128] and Vn
+// [64][128] are written in bf16 to svS / svY / svVn, indexed (head, chunk).
+template <int NCW, bool SAVE>
 __global__ void __launch_bounds__(ScanCfg<NCW>::NT)
 chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
-                  int T, int H)
+                  int T, int H, bf16_t* svS, bf16_t* svY, bf16_t* svVn)
 {
     typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
     using SC = ScanCfg<NCW>;
@@ -768,7 +799,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     for (int n = 0; n < nchunks; ++n) {
         if (loader) {
             if (n + 1 < nchunks) { load_block(n + 1); load_v(n + 1); }
-            if (n > 0) store_out(n - 1);
+            if (!SAVE && n > 0) store_out(n - 1);
             __builtin_amdgcn_s_waitcnt(0);    // the stage must be complete at the barrier
             if (n + 1 < nchunks) write_vt(n + 1);
         } else {
@@ -781,6 +812,14 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             const float* sGam = reinterpret_cast<const float*>(st + SC::OFF_BLK + WS_GAM);
             const bf16_t* sVT = reinterpret_cast<const bf16_t*>(st + SC::OFF_VT);
             bf16_t* sO = reinterpret_cast<bf16_t*>(smem + SC::OFF_O + (n & 1) * C * SC::DV * 2);
+            const size_t cidx = (size_t)head * nchunks + n;
+            if constexpr (SAVE) {
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        svS[(cidx * DK + 16 * cb + 4 * lg + e) * DK + j0 + jc] = (bf16_t)acc_s[cb][e];
+            }
 
             // P = Kh S and Qt S; a block's eight operand loads go out before its
             // products, the next block's while they run
@@ -831,6 +870,16 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
                             cat8(to_bf16x4(zt[2 * p]), to_bf16x4(zt[2 * p + 1])), a, 0, 0, 0);
                 vn[Rb] = a;
             }
+            if constexpr (SAVE) {
+#pragma unroll
+                for (int Rb = 0; Rb < 4; ++Rb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const size_t at = (cidx * C + 16 * Rb + 4 * lg + e) * DK + j0 + jc;
+                        svY[at] = (bf16_t)zt[Rb][e];
+                        svVn[at] = (bf16_t)vn[Rb][e];
+                    }
+            }
 
             // O = Qt S + Aqk Vn -> LDS staging (stored to HBM by the loaders)
 #pragma unroll
@@ -873,7 +922,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     }
 
     if (loader) {
-        store_out(nchunks - 1);
+        if (!SAVE) store_out(nchunks - 1);
     } else if (S_T) {
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
@@ -891,7 +940,7 @@ void launch_one(const void* q, const void* k, const void* v, const float* g, con
     const unsigned nwg = (unsigned)((long long)B * H * nsplit);
     hipLaunchKernelGGL((chunk_fwd_kernel<E, DV, false>), dim3(nwg), dim3(NT), 0, stream,
                        (const E*)q, (const E*)k, (const E*)v, g, (const E*)beta, S0, (E*)o, S_T,
-                       T, H, nsplit, (char*)nullptr);
+                       T, H, nsplit, (char*)nullptr, (char*)nullptr);
 }
 
 }  // namespace
@@ -909,6 +958,27 @@ bool chunk_prefers_two_kernel(long long B, long long T, long long H, int dtype)
     return dtype == 1 && B * H < 128 && T > C;
 }
 
+hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, const float* g,
+                                  const void* beta, const float* S0, int B, int T, int H,
+                                  char* ws_fwd, char* ws_bwd, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
+                                  hipStream_t stream)
+{
+    const long long heads = (long long)B * H;
+    const int nchunks = (T + C - 1) / C;
+    const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
+    hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true, true>), dim3((unsigned)(heads * nblk)), dim3(NT), 0,
+                       stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g, (const bf16_t*)beta, S0,
+                       (bf16_t*)nullptr, (float*)nullptr, T, H, 1, ws_fwd, ws_bwd);
+    const int ncw = heads * 4 >= 256 ? 2 : 1;
+#define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, true>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
+                                         dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws_fwd, (const bf16_t*)v, S0, \
+                                         (bf16_t*)nullptr, (float*)nullptr, T, H, svS, svY, svVn)
+    if (ncw == 2) KDA_SCAN(2);
+    else KDA_SCAN(1);
+#undef KDA_SCAN
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                             const void* beta, const float* S0, void* o, float* S_T,
                             int B, int T, int H, int dtype, void* ws, hipStream_t stream)
@@ -922,12 +992,12 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const f
         const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
         hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true>), dim3((unsigned)(heads * nblk)), dim3(NT),
                            0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
-                           (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws);
+                           (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws, (char*)nullptr);
         // value columns per scan workgroup: enough workgroups to cover the machine
         const int ncw = heads * 4 >= 256 ? 2 : 1;
-#define KDA_SCAN(NCW) hipLaunchKernelGGL(chunk_scan_kernel<NCW>, dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
+#define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, false>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
                                          dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws, (const bf16_t*)v, S0, \
-                                         (bf16_t*)o, S_T, T, H)
+                                         (bf16_t*)o, S_T, T, H, (bf16_t*)nullptr, (bf16_t*)nullptr, (bf16_t*)nullptr)
         if (ncw == 2) KDA_SCAN(2);
         else KDA_SCAN(1);
 #undef KDA_SCAN

@@ -69,6 +69,19 @@ def prefill_inputs(B, T, H, dtype="bfloat16", g_scale=0.05, s0_std=0.0, seed=0, 
                 beta=cast(beta), S0=S0)
 
 
+def grad_inputs(B, T, H, dtype="bfloat16", ds_std=0.0, seed=0, d=D):
+    """Incoming gradients for the backward pass: dO ~ N(0, 1) in `dtype`
+    [B, T, H, d] and dS_T ~ N(0, ds_std^2) fp32 [B, H, d, d] (None when
+    ds_std is 0), from a generator of their own (seed, 1)."""
+    import torch
+    rng = np.random.default_rng([seed, 1])
+    dO = torch.from_numpy(rng.standard_normal((B, T, H, d), dtype=np.float32)).to(_torch_dtype(dtype))
+    dST = None
+    if ds_std > 0:
+        dST = torch.from_numpy(np.float32(ds_std) * rng.standard_normal((B, H, d, d), dtype=np.float32))
+    return dict(dO=dO, dS_T=dST)
+
+
 def prefill_config(name, **override):
     """Inputs of a named prefill workload; keyword overrides (e.g. T=...)."""
     cfg = dict(PREFILL_CONFIGS[name])

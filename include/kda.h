@@ -105,6 +105,51 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
 
 /*
+ * Backward pass of kda_chunk_fwd: for a scalar loss L, given dL/do (grad_o)
+ * and dL/dS_T (grad_S_T), the gradient of L with respect to every input of the
+ * forward call.  The chunkwise algorithm (same pages and sections as
+ * kda_chunk_fwd) computes eq. (1) exactly, so these are the gradients of the
+ * recurrence itself; they are formed by reverse mode through the chunked form:
+ * the forward pass is recomputed chunk by chunk, a serial reverse pass carries
+ * dL/dS from the last chunk to the first, and the per-token gradients of all
+ * chunks are then formed in parallel.
+ *
+ *   q, k, v, log_alpha, beta, S0   as for kda_chunk_fwd (S0 NULL means zeros)
+ *   grad_o         [B, T, H, dv]  bf16          dL/do
+ *   grad_S_T       [B, H, dk, dv] fp32          dL/dS_T; NULL means zero
+ *   grad_q, grad_k [B, T, H, dk]  bf16   out
+ *   grad_v         [B, T, H, dv]  bf16   out
+ *   grad_log_alpha [B, T, H, dk]  fp32   out    with respect to g = log alpha
+ *   grad_beta      [B, T, H]      bf16   out
+ *   grad_S0        [B, H, dk, dv] fp32   out    dL/dS0; NULL means not written
+ *   workspace  device scratch of at least kda_chunk_bwd_workspace_size(...)
+ *              bytes, 256-byte aligned, owned by the caller; contents on entry
+ *              and exit unspecified.  It holds the recomputed forward pass:
+ *              per (batch, head, 64-token chunk) 261,120 bytes -- the key-side
+ *              operand blocks of both scans and, in bf16, the state entering
+ *              the chunk, its gradient on leaving it, V - Kh S, Vn and
+ *              Tm^T dVn.
+ * dtype must be KDA_BF16 (KDA_F32 returns KDA_ERR_UNSUPPORTED).  T = 0 writes
+ * grad_S0 = grad_S_T (or zeros); B*H = 0 is a no-op.  Outputs must not
+ * overlap any input, each other or the workspace.  Returns KDA_OK or a
+ * negative status.
+ */
+int kda_chunk_bwd(const void* q, const void* k, const void* v,
+                  const float* log_alpha, const void* beta, const float* S0,
+                  const void* grad_o, const float* grad_S_T,
+                  void* grad_q, void* grad_k, void* grad_v, float* grad_log_alpha,
+                  void* grad_beta, float* grad_S0,
+                  int B, int T, int H, int dk, int dv, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes kda_chunk_bwd needs: B * H * ceil(T / 64) * 261120 for
+ * dtype == KDA_BF16 and d_k = d_v = 128; 0 for invalid or unsupported
+ * arguments.
+ */
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
+
+/*
  * Recurrent decode step: applies eq. (1) once (one token) to each of N x H
  * independent heads, updating the state in place, and returns o = S^T q
  * (page "Kimi K3论文：Kimi Linear", section 3 eq. (1) and section 4, the

@@ -33,7 +33,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_recurrent_step",
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_bwd",
+                          "kda_chunk_bwd_workspace_size", "kda_recurrent_step",
                           "kda_layer_fwd", "kda_layer_workspace_layout",
                           "kda_status_string", "kda_version"}
     for n in names:
@@ -173,3 +174,49 @@ def test_layer_fwd_rejects(lib, kw, code):
 
 def test_layer_fwd_empty_is_noop(lib):
     assert layer(lib, T=0, x=None, y=None, ws=None, wsb=0) == OK
+
+
+# ------------------------------------------------------------ backward pass
+BWD_UNIT = 261120   # workspace bytes per (batch, head, 64-token chunk)
+
+
+def bwd(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S0=None,
+        do=P + 2**28, dST=None, dq=P + 2**29, dk=P + 2**30, dv=P + 2**31, dg=P + 2**32,
+        dbeta=P + 2**33, dS0=None, B=1, T=64, H=1, kd=128, vd=128, dt=BF16,
+        ws=P + 2**34, wsb=BWD_UNIT):
+    return lib.kda_chunk_bwd(q, k, v, g, beta, S0, do, dST, dq, dk, dv, dg, dbeta, dS0,
+                             B, T, H, kd, vd, dt, ws, wsb, None)
+
+
+def test_bwd_workspace_size(lib):
+    f = lib.kda_chunk_bwd_workspace_size
+    assert f(8, 4096, 16, 128, 128, BF16) == 8 * 16 * 64 * BWD_UNIT
+    assert f(1, 65, 3, 128, 128, BF16) == 3 * 2 * BWD_UNIT
+    assert f(1, 0, 3, 128, 128, BF16) == 0
+    assert f(1, 64, 1, 128, 128, F32) == 0 and f(1, 64, 1, 64, 128, BF16) == 0
+    assert f(-1, 64, 1, 128, 128, BF16) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(dq=None), INVALID),
+    (dict(dg=None), INVALID), (dict(dbeta=None), INVALID), (dict(ws=None), INVALID),
+    (dict(B=-1), INVALID), (dict(T=-3), INVALID),
+    (dict(dt=F32), UNSUP), (dict(dt=5), UNSUP), (dict(kd=64), UNSUP), (dict(vd=32), UNSUP),
+    (dict(q=P + 2), ALIGN), (dict(dk=P + 2**30 + 8), ALIGN), (dict(dbeta=P + 2**33 + 1), ALIGN),
+    (dict(ws=P + 2**34 + 16), ALIGN), (dict(dS0=P + 2**35 + 4), ALIGN),
+    (dict(wsb=BWD_UNIT - 1), INVALID),           # workspace too small
+    (dict(dq=P + 2**24), INVALID),               # dq overlaps k
+    (dict(dv=P + 2**29 + 64), INVALID),          # dv overlaps dq
+    (dict(ws=P + 2**26), INVALID),               # workspace overlaps g
+    (dict(dS0=P + 2**35, dST=P + 2**35 + 16), INVALID),   # dS0 overlaps dS_T
+    (dict(B=2**30, H=2**30), UNSUP),             # size overflow
+])
+def test_chunk_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_chunk_bwd_noop(lib):
+    # B*H == 0 returns before any launch, even with NULL pointers
+    assert lib.kda_chunk_bwd(*([None] * 14), 0, 64, 4, 128, 128, BF16, None, 0, None) == OK
+    # T == 0 without dS0: nothing to write
+    assert lib.kda_chunk_bwd(*([None] * 14), 2, 0, 4, 128, 128, BF16, None, 0, None) == OK

@@ -1,0 +1,120 @@
+"""GPU parity of the backward pass (kda_chunk_bwd through the C ABI) against
+the fp64 gradient oracle (reverse mode through the recurrence), element by
+element on every gradient at sizes the oracle finishes in seconds (several
+chunks, ragged tails, with and without S0 and dS_T), and on sampled heads at
+the full B = 8, H = 16, T = 4096 workload in the launch configuration the
+benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_32_amd as kda
+from gated_delta_rule_32_amd import inputs
+from oracle import kda_ref
+from tests.kda_testutil import TOL_GRAD, max_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+
+
+def run_bwd(inp, gr, with_ds0=True):
+    d = {n: (x.to(DEV) if x is not None else None) for n, x in {**inp, **gr}.items()}
+    out = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["dO"], d["dS_T"],
+                        grad_S0=with_ds0)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_grads(inp, gr, heads=None):
+    args = [inp[n] for n in ("q", "k", "v", "g", "beta", "S0")] + [gr["dO"], gr["dS_T"]]
+    if heads is None:
+        return kda_ref.recurrent_grad(*args)
+    outs = []
+    for b, h in heads:
+        one = [x[b:b + 1, :, h:h + 1] for x in args[:5]]
+        s0 = None if args[5] is None else args[5][b:b + 1, h:h + 1]
+        dO = args[6][b:b + 1, :, h:h + 1]
+        dST = None if args[7] is None else args[7][b:b + 1, h:h + 1]
+        outs.append(kda_ref.recurrent_grad(*one, s0, dO, dST))
+    return outs
+
+
+def check(got, ref, names=NAMES):
+    errs = {}
+    for n, x, r in zip(names, got, ref):
+        if x is None:
+            continue
+        errs[n] = max_rel_err(x, r)
+    print("  " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= TOL_GRAD[n], (n, e)
+    return errs
+
+
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 200])
+def test_ragged_lengths_with_state_and_final_gradient(T):
+    print(f"backward ragged T={T}", flush=True)
+    inp = inputs.prefill_inputs(2, T, 3, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=T)
+    gr = inputs.grad_inputs(2, T, 3, ds_std=0.05, seed=T)
+    check(run_bwd(inp, gr), oracle_grads(inp, gr))
+
+
+@pytest.mark.parametrize("T", [64, 150])
+def test_no_initial_state_no_final_gradient(T):
+    print(f"backward S0=None dS_T=None T={T}", flush=True)
+    inp = inputs.prefill_inputs(1, T, 2, dtype="bfloat16", g_scale=0.05, seed=100 + T)
+    gr = inputs.grad_inputs(1, T, 2, seed=100 + T)
+    got = run_bwd(inp, gr)
+    check(got, oracle_grads(inp, gr))
+
+
+def test_without_ds0_output():
+    print("backward without dS0", flush=True)
+    inp = inputs.prefill_inputs(1, 100, 2, dtype="bfloat16", g_scale=0.05, s0_std=0.02, seed=5)
+    gr = inputs.grad_inputs(1, 100, 2, ds_std=0.02, seed=5)
+    got = run_bwd(inp, gr, with_ds0=False)
+    assert got[5] is None
+    check(got[:5], oracle_grads(inp, gr)[:5], NAMES[:5])
+
+
+@pytest.mark.parametrize("H", [1, 64])
+def test_scan_slice_widths(H):
+    """H = 1 and H = 64 select 16- and 32-column slices in both state scans."""
+    print(f"backward slice widths H={H}", flush=True)
+    inp = inputs.prefill_inputs(1, 150, H, dtype="bfloat16", g_scale=0.05, s0_std=0.02, seed=H)
+    gr = inputs.grad_inputs(1, 150, H, ds_std=0.02, seed=H)
+    got = run_bwd(inp, gr)
+    heads = [(0, 0), (0, H - 1), (0, H // 2)]
+    refs = oracle_grads(inp, gr, heads)
+    for (b, h), ref in zip(heads, refs):
+        one = [x[b:b + 1, :, h:h + 1] for x in got[:5]] + [got[5][b:b + 1, h:h + 1]]
+        check(one, ref)
+
+
+def test_beta_zero_and_gate_one():
+    """beta = 0 (no writes: dk = dv = 0 exactly) and g = 0 (no decay)."""
+    print("backward beta=0, g=0", flush=True)
+    inp = inputs.prefill_inputs(1, 130, 2, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=9)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    gr = inputs.grad_inputs(1, 130, 2, ds_std=0.05, seed=9)
+    got = run_bwd(inp, gr)
+    assert torch.count_nonzero(got[1]) == 0 and torch.count_nonzero(got[2]) == 0
+    check(got, oracle_grads(inp, gr))
+    inp = inputs.prefill_inputs(1, 130, 2, dtype="bfloat16", g_scale=0.0, s0_std=0.05, seed=10)
+    gr = inputs.grad_inputs(1, 130, 2, ds_std=0.05, seed=10)
+    check(run_bwd(inp, gr), oracle_grads(inp, gr))
+
+
+def test_config2_full_size_sampled_heads():
+    """B = 8, H = 16, T = 4096 (the benchmarked backward workload): all
+    gradients of three sampled heads against the oracle."""
+    print("backward c2 full size, sampled heads", flush=True)
+    inp = inputs.prefill_config("c2_bf16_B8_H16_T4096")
+    gr = inputs.grad_inputs(8, 4096, 16, seed=2)
+    got = run_bwd(inp, gr)
+    heads = [(0, 0), (3, 7), (7, 15)]
+    refs = oracle_grads(inp, gr, heads)
+    for (b, h), ref in zip(heads, refs):
+        one = [x[b:b + 1, :, h:h + 1] for x in got[:5]] + [got[5][b:b + 1, h:h + 1]]
+        check(one, ref)
