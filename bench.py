@@ -13,10 +13,13 @@ head-tokens per second (B*T*H / time).  The JSON line also carries:
     of HBM peak;
   * layer: the full token-mixing layer (d_model 2048, 16 heads, 32768
     tokens), its time, the KDA operator's share and the achieved TFLOP/s;
+  * backward: kda_chunk_bwd on the prefill workload (incoming gradients dL/do
+    ~ N(0,1), dL/dS_T = 0), head-tokens/s, compulsory-HBM-bytes rate, and the
+    gradient oracle timed on the host cores on the same workload;
   * cpu_baseline: the fp64 oracle timed on the host cores on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload c3|c1|decode|layer  (single-workload lines, for profiling)
+       python bench.py --workload c3|c1|decode|layer|bwd  (single-workload lines, for profiling)
        python bench.py --copy-calibration       (plain copy kernel for counter scaling)
 """
 from __future__ import annotations
@@ -42,6 +45,10 @@ FLOP_PER_HEAD_TOKEN = 6 * D * D + 3 * C * D + C * C          # 126,976
 BYTES_PER_HEAD_TOKEN_BF16 = 3 * 2 * D + 4 * D + 2 + 2 * D     # 1,538
 BYTES_PER_HEAD_TOKEN_F32 = 3 * 4 * D + 4 * D + 4 + 4 * D      # 2,564
 STATE_BYTES = 4 * D * D                                        # 65,536 per head
+# Backward pass, compulsory HBM bytes per head-token (bf16): reads q, k, v, dO
+# (4 x 256), log-decay fp32 (512), beta (2); writes dq, dk, dv (3 x 256),
+# dlog-decay fp32 (512), dbeta (2).  Plus dS0 (fp32 state) per head.
+BWD_BYTES_PER_HEAD_TOKEN = 4 * 2 * D + 4 * D + 2 + 3 * 2 * D + 4 * D + 2   # 2,820
 # Decode: per head and step the state is read and written once, plus q, k, v
 # (bf16), log-decay (fp32), beta (bf16) and o (bf16).
 DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + 3 * 2 * D + 4 * D + 2 + 2 * D   # 132,610
@@ -220,6 +227,50 @@ def layer_line(steps, warmup):
             "frac_of_bf16_peak": round((gemm_flops + kda_flops) / t_layer / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
 
+def backward_line(steps, warmup, with_cpu=False):
+    """kda_chunk_bwd on the B = 8, H = 16, T = 4096 prefill workload."""
+    import torch
+    import gated_delta_rule_32_amd as kda
+    from gated_delta_rule_32_amd import inputs
+
+    name = WORKLOADS["c2"]
+    cfg = inputs.PREFILL_CONFIGS[name]
+    B, T, H = cfg["B"], cfg["T"], cfg["H"]
+    log(f"[bench] backward: generating inputs for {name}")
+    inp = inputs.prefill_config(name)
+    gr = inputs.grad_inputs(B, T, H, seed=cfg["seed"])
+    d = {n: (x.to("cuda:0") if x is not None else None) for n, x in {**inp, **gr}.items()}
+    ws = torch.empty(kda.bwd_workspace_size(B, T, H), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["dO"], d["dS_T"],
+                      workspace=ws)
+
+    log(f"[bench] backward: timing {steps} steps after {warmup} warmup")
+    t, _ = time_launches(step, steps, warmup)
+    ht = B * T * H
+    alg = ht * BWD_BYTES_PER_HEAD_TOKEN + STATE_BYTES * B * H
+    gbs = alg / t / 1e9
+    out = {"workload": f"kda_chunk_bwd {name} (dL/do ~ N(0,1), dL/dS_T = 0)",
+           "ms_per_step": round(t * 1e3, 4), "head_tokens_per_s": round(ht / t, 1),
+           "alg_bytes_per_step": alg, "compulsory_gb_s": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "workspace_bytes": ws.numel()}
+    if with_cpu:
+        from oracle import kda_ref
+        threads = kda_ref.max_threads()
+        args = [kda_ref._f64(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+        log(f"[bench] backward cpu baseline: gradient oracle, {threads} threads")
+        t0 = time.perf_counter()
+        kda_ref.recurrent_grad(*args, None, kda_ref._f64(gr["dO"]), None, nthreads=threads)
+        dt = time.perf_counter() - t0
+        out["cpu_oracle"] = {"value": round(ht / dt, 1), "unit": "head-tokens/s", "cores": threads,
+                             "kind": "oracle",
+                             "sample": f"whole workload: {B}x{H} heads x {T} tokens, fp64 reverse-mode "
+                                       f"recurrence (C, -O2, OpenMP over heads), {dt:.2f} s wall"}
+    return out
+
+
 def cpu_baseline(inp):
     """The fp64 oracle as it stands, on the host cores, on the whole workload."""
     import numpy as np
@@ -247,7 +298,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
-    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer"], default=None,
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer", "bwd"], default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--schedule", choices=["auto", "fused", "two_kernel"], default="auto",
                     help="prefill schedule (auto: the library's preferred one)")
@@ -279,6 +331,11 @@ def main():
         print(json.dumps({"metric": "KDA decode state GB/s", **dec}))
         return
 
+    if args.workload == "bwd":
+        bwd = backward_line(args.steps, args.warmup)
+        print(json.dumps({"metric": "KDA backward head-tokens/s", **bwd}))
+        return
+
     if args.workload == "layer":
         lay = layer_line(args.steps, args.warmup)
         print(json.dumps({"metric": "KDA layer tokens/s", **lay}))
@@ -303,6 +360,8 @@ def main():
         line["decode"] = decode_line(max(args.steps, 20), args.warmup)
     if args.workload is None and not args.no_layer:
         line["layer"] = layer_line(min(args.steps, 20), args.warmup)
+    if args.workload is None and not args.no_bwd:
+        line["backward"] = backward_line(min(args.steps, 20), args.warmup, with_cpu=not args.no_cpu)
     if not args.no_cpu and args.workload is None:
         line["cpu_baseline"] = cpu_baseline(pre["inp"])
     print(json.dumps(line))

@@ -232,24 +232,39 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
 // 16w .. 16w+15 for all 64 tokens, lane (lg, ln) the channel 16w + ln and rows
 // 16m + 4lg + e (m, e = 0..3): the layout of a 16 x 16 MFMA output tile, so the
 // decay computed first and the gradient tiles accumulated last line up in
-// registers.  Operands indexed by (token, channel) are staged in LDS; the
-// value-side ones (dO, dV, Vn, dZ, S, dS') are read straight from memory as
-// 16-byte MFMA fragments.
+// registers.
+//
+// Every global read is issued at the start: q, k and g go global -> LDS with
+// 16-byte LDS-destination loads, the rest into registers (the S and dS' rows
+// of the wave's channel block as B fragments, the dZ rows of its C x C tiles
+// as A fragments, and the dO, Vn, dV tiles that are then parked in LDS).  LDS
+// regions are reused phase by phase:
+//   A  : g staging (fp32) -> Kh, Kb -> dV -> dq, dk staging
+//   B  : Qt^T, Kh^T, Kb^T -> dg staging (fp32)
+//   CR : q, k staging -> dAqk, dAqk^T, dA', dA'^T
+//   DO, VN: dO and Vn tiles for both product phases.
 struct GradLds {
     static constexpr int P64 = C + 8, P128 = DK + 8;
-    static constexpr int OFF_KH = 0;                          // Kh [64][136]
-    static constexpr int OFF_KB = OFF_KH + C * P128 * 2;      // Kb [64][136]
-    static constexpr int OFF_QTT = OFF_KB + C * P128 * 2;     // Qt^T [128][72]
-    static constexpr int OFF_KHT = OFF_QTT + DK * P64 * 2;    // Kh^T
-    static constexpr int OFF_KBT = OFF_KHT + DK * P64 * 2;    // Kb^T
-    static constexpr int OFF_DAQK = OFF_KBT + DK * P64 * 2;   // dAqk [64][72]
-    static constexpr int OFF_DAQKT = OFF_DAQK + C * P64 * 2;  // dAqk^T
-    static constexpr int OFF_DAP = OFF_DAQKT + C * P64 * 2;   // dA' = Diag(beta) dAkk
-    static constexpr int OFF_DAPT = OFF_DAP + C * P64 * 2;    // dA'^T
-    static constexpr int OFF_BETA = OFF_DAPT + C * P64 * 2;   // beta [64] fp32
+    static constexpr int T128 = C * P128 * 2;                 // one [64][136] bf16 tile
+    static constexpr int T64 = C * P64 * 2;                   // one [64][72] bf16 tile
+    static constexpr int OFF_A = 0;
+    static constexpr int OFF_KB = OFF_A + T128;
+    static constexpr int OFF_B = OFF_A + 2 * T128;
+    static constexpr int OFF_KHT = OFF_B + DK * P64 * 2;
+    static constexpr int OFF_KBT = OFF_KHT + DK * P64 * 2;
+    static constexpr int OFF_CR = OFF_KBT + DK * P64 * 2;
+    static constexpr int OFF_DAQKT = OFF_CR + T64;
+    static constexpr int OFF_DAP = OFF_DAQKT + T64;
+    static constexpr int OFF_DAPT = OFF_DAP + T64;
+    static constexpr int OFF_DO = OFF_DAPT + T64;
+    static constexpr int OFF_VN = OFF_DO + T128;
+    static constexpr int OFF_BETA = OFF_VN + T128;            // beta [64] fp32
     static constexpr int OFF_DB = OFF_BETA + C * 4;           // dbeta [64] fp32
     static constexpr int TOTAL = OFF_DB + C * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(2 * T128 >= C * DK * 4, "g staging fits in region A");
+    static_assert(4 * T64 >= 2 * C * DK * 2, "q, k staging fits in region CR");
+    static_assert(OFF_CR - OFF_B >= C * DK * 4, "dg staging fits in region B");
 };
 
 __device__ __forceinline__ bf16x8 ld8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -261,6 +276,9 @@ __device__ __forceinline__ bf16x8 neg8(bf16x8 x) {
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
 
 __global__ void __launch_bounds__(512)
 chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf16_t* beta,
@@ -269,18 +287,25 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
                       bf16_t* dq, bf16_t* dk, float* dg, bf16_t* dbeta, int T, int H)
 {
     using L = GradLds;
-    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-    bf16_t* sKh = reinterpret_cast<bf16_t*>(smem + L::OFF_KH);
+    __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
+    bf16_t* sKh = reinterpret_cast<bf16_t*>(smem + L::OFF_A);
     bf16_t* sKb = reinterpret_cast<bf16_t*>(smem + L::OFF_KB);
-    bf16_t* sQtT = reinterpret_cast<bf16_t*>(smem + L::OFF_QTT);
+    bf16_t* sDV = reinterpret_cast<bf16_t*>(smem + L::OFF_A);
+    bf16_t* sQtT = reinterpret_cast<bf16_t*>(smem + L::OFF_B);
     bf16_t* sKhT = reinterpret_cast<bf16_t*>(smem + L::OFF_KHT);
     bf16_t* sKbT = reinterpret_cast<bf16_t*>(smem + L::OFF_KBT);
-    bf16_t* sdAqk = reinterpret_cast<bf16_t*>(smem + L::OFF_DAQK);
+    bf16_t* sdAqk = reinterpret_cast<bf16_t*>(smem + L::OFF_CR);
     bf16_t* sdAqkT = reinterpret_cast<bf16_t*>(smem + L::OFF_DAQKT);
     bf16_t* sdAp = reinterpret_cast<bf16_t*>(smem + L::OFF_DAP);
     bf16_t* sdApT = reinterpret_cast<bf16_t*>(smem + L::OFF_DAPT);
+    bf16_t* sDO = reinterpret_cast<bf16_t*>(smem + L::OFF_DO);
+    bf16_t* sVN = reinterpret_cast<bf16_t*>(smem + L::OFF_VN);
     float* sbeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
     float* sdb = reinterpret_cast<float*>(smem + L::OFF_DB);
+    // staging, unpadded row-major [64][128]
+    const float* stG = reinterpret_cast<const float*>(smem + L::OFF_A);
+    const bf16_t* stQ = reinterpret_cast<const bf16_t*>(smem + L::OFF_CR);
+    const bf16_t* stK = stQ + C * DK;
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -295,6 +320,51 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     const int c = 16 * wave + ln;                 // this lane's key channel
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
+    // ===== issue every global read =====
+    for (int u = wave; u < 32; u += 8) {          // q, k: 16 rows of 1 KiB each = 4 tokens
+        const bf16_t* src = u < 16 ? q : k;
+        const int row = 4 * (u & 15) + (lane >> 4);
+        dma16(src + hbase + (size_t)min(tok0 + row, T - 1) * tokstride + 8 * (lane & 15),
+              smem + L::OFF_CR + u * 1024);
+    }
+    for (int u = wave; u < 32; u += 8) {          // g: 1 KiB = 2 tokens
+        const int row = 2 * u + (lane >> 5);
+        dma16(g + hbase + (size_t)min(tok0 + row, T - 1) * tokstride + 4 * (lane & 31),
+              smem + L::OFF_A + u * 1024);
+    }
+    bf16x8 sf[4], dsf[4];                          // S, dS' rows c as B fragments
+    {
+        const bf16_t* pS = svS + (cidx * DK + c) * DK + 8 * lg;
+        const bf16_t* pdS = svdS + (cidx * DK + c) * DK + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) { sf[s] = ld8(pS + 32 * s); dsf[s] = ld8(pdS + 32 * s); }
+    }
+    // C x C tiles tt = wave, wave + 8 as (mb, nb); those above the diagonal are zero
+    bf16x8 dzf[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int tt = wave + 8 * j, mb = tt >> 2;
+        const bf16_t* p = svdZ + (cidx * C + 16 * mb + ln) * DK + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) dzf[j][s] = ((tt & 3) <= mb) ? ld8(p + 32 * s) : bf16x8{};
+    }
+    // row r = t / 8, columns 16 (t % 8) .. +15 of the 64 x 128 value-side tiles
+    const int vr = t >> 3, vc = 16 * (t & 7);
+    const bool vok = tok0 + vr < T;
+    const size_t vat = hbase + (size_t)min(tok0 + vr, T - 1) * tokstride + vc;
+    const size_t wat = (cidx * C + vr) * DK + vc;
+    bf16x8 yv[2], zv[2], dov[2], vnv[2], dvv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        yv[i] = ld8(svY + wat + 8 * i);
+        zv[i] = ld8(svdZ + wat + 8 * i);
+        vnv[i] = ld8(svVn + wat + 8 * i);
+        dov[i] = vok ? ld8(dO + vat + 8 * i) : bf16x8{};
+        dvv[i] = vok ? ld8(dV + vat + 8 * i) : bf16x8{};
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+
     // ===== decay and the decay-scaled keys / queries =====
     float G[4][4], qv[4][4], kv[4][4];
     float carry = 0.f;
@@ -303,12 +373,11 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         float s4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int tok = tok0 + 16 * m + 4 * lg + e;
-            const bool ok = tok < T;
-            const size_t off = hbase + (size_t)min(tok, T - 1) * tokstride + c;
-            const float gl = ok ? g[off] * LOG2E : 0.f;
-            qv[m][e] = ok ? (float)q[off] : 0.f;
-            kv[m][e] = ok ? (float)k[off] : 0.f;
+            const int r = 16 * m + 4 * lg + e;
+            const bool ok = tok0 + r < T;
+            const float gl = ok ? stG[r * DK + c] * LOG2E : 0.f;
+            qv[m][e] = ok ? (float)stQ[r * DK + c] : 0.f;
+            kv[m][e] = ok ? (float)stK[r * DK + c] : 0.f;
             s4[e] = (e ? s4[e - 1] : 0.f) + gl;
         }
         float bs[4];
@@ -320,6 +389,12 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         carry += bs[0] + bs[1] + bs[2] + bs[3];
     }
     const float Gc = carry;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        *reinterpret_cast<bf16x8*>(sDO + vr * L::P128 + vc + 8 * i) = dov[i];
+        *reinterpret_cast<bf16x8*>(sVN + vr * L::P128 + vc + 8 * i) = vnv[i];
+    }
+    lds_barrier();                                 // staging reads done before A and CR are reused
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         f32x4 qt, kh, kb;
@@ -343,34 +418,27 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     lds_barrier();
 
     // ===== C x C products: KK = Kh Kb^T, M1 = dZ Vn^T, M2 = dO Vn^T =====
-    // tile (mb, nb): rows 16mb.., columns 16nb..; tiles above the diagonal are zero
-    for (int tt = wave; tt < 16; tt += 8) {
-        const int mb = tt >> 2, nb = tt & 3;
-        if (nb > mb) {
-            const int r = 16 * mb + 4 * lg, i = 16 * nb + ln;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { sdAqk[(r + e) * L::P64 + i] = bf16_t{}; sdAp[(r + e) * L::P64 + i] = bf16_t{}; }
-            store_vec4<bf16_t>(sdAqkT + i * L::P64 + r, z4);
-            store_vec4<bf16_t>(sdApT + i * L::P64 + r, z4);
+    for (int j = 0; j < 2; ++j) {
+        const int tt = wave + 8 * j, mb = tt >> 2, nb = tt & 3;
+        const int r0 = 16 * mb + 4 * lg, i = 16 * nb + ln;
+        if (nb > mb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { sdAqk[(r0 + e) * L::P64 + i] = bf16_t{}; sdAp[(r0 + e) * L::P64 + i] = bf16_t{}; }
+            store_vec4<bf16_t>(sdAqkT + i * L::P64 + r0, z4);
+            store_vec4<bf16_t>(sdApT + i * L::P64 + r0, z4);
             continue;
         }
         const int ra = 16 * mb + ln, rb = 16 * nb + ln;
-        const int toka = tok0 + ra;
-        const bool oka = toka < T;
-        const bf16_t* pdO = dO + hbase + (size_t)min(toka, T - 1) * tokstride;
-        const bf16_t* pdZ = svdZ + (cidx * C + ra) * DK;
-        const bf16_t* pVn = svVn + (cidx * C + rb) * DK;
         f32x4 kk = z4, m1 = z4, m2 = z4;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int ko = 32 * s + 8 * lg;
-            const bf16x8 vnf = ld8(pVn + ko);
-            const bf16x8 dof = oka ? ld8(pdO + ko) : bf16x8{};
+            const bf16x8 vnf = ld8(sVN + rb * L::P128 + ko);
             kk = mma(ld8(sKh + ra * L::P128 + ko), ld8(sKb + rb * L::P128 + ko), kk);
-            m1 = mma(ld8(pdZ + ko), vnf, m1);
-            m2 = mma(dof, vnf, m2);
+            m1 = mma(dzf[j][s], vnf, m1);
+            m2 = mma(ld8(sDO + ra * L::P128 + ko), vnf, m2);
         }
-        const int r0 = 16 * mb + 4 * lg, i = 16 * nb + ln;
         f32x4 aq, ap;
         float part[4];
 #pragma unroll
@@ -395,70 +463,62 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
             for (int e = 0; e < 4; ++e) atomicAdd(&sdb[r0 + e], part[e]);
         }
     }
-    {   // dbeta, first term: row r = t / 8, columns 16 (t % 8) ..
-        const int r = t >> 3, p8 = t & 7;
-        const bf16_t* py = svY + (cidx * C + r) * DK + 16 * p8;
-        const bf16_t* pz = svdZ + (cidx * C + r) * DK + 16 * p8;
-        const bf16x8 y0 = ld8(py), y1 = ld8(py + 8), z0 = ld8(pz), z1 = ld8(pz + 8);
+    {   // dbeta, first term: sum over value columns of (V - Kh S) * dZ
         float d = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d += (float)y0[i] * (float)z0[i] + (float)y1[i] * (float)z1[i];
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int x = 0; x < 8; ++x) d += (float)yv[i][x] * (float)zv[i][x];
         d += __shfl_xor(d, 1);
         d += __shfl_xor(d, 2);
         d += __shfl_xor(d, 4);
-        if (p8 == 0) atomicAdd(&sdb[r], d);
+        if ((t & 7) == 0) atomicAdd(&sdb[vr], d);
     }
-    lds_barrier();
+    lds_barrier();                                 // Kh, Kb dead; dA tiles and dbeta complete
     if (t < C && tok0 + t < T) dbeta[((size_t)b * T + tok0 + t) * H + h] = (bf16_t)sdb[t];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<bf16x8*>(sDV + vr * L::P128 + vc + 8 * i) = neg8(dvv[i]);
+    lds_barrier();
 
     // ===== C x d_k products: wave w -> channel block w, token blocks m = 0..3 =====
     f32x4 aQ[4], aH[4], aB[4], aT[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) { aQ[m] = z4; aH[m] = z4; aB[m] = z4; aT[m] = z4; }
     float sds = 0.f;
-    {
-        const bf16_t* pS = svS + (cidx * DK + c) * DK;
-        const bf16_t* pdS = svdS + (cidx * DK + c) * DK;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {             // contraction over value columns
-            const int ko = 32 * s + 8 * lg;
-            const bf16x8 sf = ld8(pS + ko), dsf = ld8(pdS + ko);
+    for (int s = 0; s < 4; ++s) {                  // contraction over value columns
+        const int ko = 32 * s + 8 * lg;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sds += (float)sf[i] * (float)dsf[i];
+        for (int i = 0; i < 8; ++i) sds += (float)sf[s][i] * (float)dsf[s][i];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int r = 16 * m + ln, tok = tok0 + r;
-                const bool ok = tok < T;
-                const size_t at = hbase + (size_t)min(tok, T - 1) * tokstride + ko;
-                const bf16x8 dof = ok ? ld8(dO + at) : bf16x8{};
-                const bf16x8 dvf = ok ? neg8(ld8(dV + at)) : bf16x8{};
-                const bf16x8 vnf = ld8(svVn + (cidx * C + r) * DK + ko);
-                aQ[m] = mma(dof, sf, aQ[m]);
-                aH[m] = mma(dvf, sf, aH[m]);
-                aT[m] = mma(vnf, dsf, aT[m]);
-            }
+        for (int m = 0; m < 4; ++m) {
+            const int ar = (16 * m + ln) * L::P128 + ko;
+            aQ[m] = mma(ld8(sDO + ar), sf[s], aQ[m]);
+            aH[m] = mma(ld8(sDV + ar), sf[s], aH[m]);     // sDV holds -dV
+            aT[m] = mma(ld8(sVN + ar), dsf[s], aT[m]);
         }
+    }
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {             // contraction over tokens
-            const int ko = 32 * s + 8 * lg;
-            const bf16x8 kbt = ld8(sKbT + c * L::P64 + ko);
-            const bf16x8 qtt = ld8(sQtT + c * L::P64 + ko);
-            const bf16x8 kht = ld8(sKhT + c * L::P64 + ko);
+    for (int s = 0; s < 2; ++s) {                  // contraction over tokens
+        const int ko = 32 * s + 8 * lg;
+        const bf16x8 kbt = ld8(sKbT + c * L::P64 + ko);
+        const bf16x8 qtt = ld8(sQtT + c * L::P64 + ko);
+        const bf16x8 kht = ld8(sKhT + c * L::P64 + ko);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int ar = (16 * m + ln) * L::P64 + ko;
-                aQ[m] = mma(ld8(sdAqk + ar), kbt, aQ[m]);
-                aH[m] = mma(ld8(sdAp + ar), kbt, aH[m]);
-                aB[m] = mma(ld8(sdAqkT + ar), qtt, aB[m]);
-                aB[m] = mma(ld8(sdApT + ar), kht, aB[m]);
-            }
+        for (int m = 0; m < 4; ++m) {
+            const int ar = (16 * m + ln) * L::P64 + ko;
+            aQ[m] = mma(ld8(sdAqk + ar), kbt, aQ[m]);
+            aH[m] = mma(ld8(sdAp + ar), kbt, aH[m]);
+            aB[m] = mma(ld8(sdAqkT + ar), qtt, aB[m]);
+            aB[m] = mma(ld8(sdApT + ar), kht, aB[m]);
         }
     }
 
-    // ===== chain rule to q, k, g =====
+    // ===== chain rule to q, k, g; results staged in LDS, stored 16 bytes at a time =====
     sds += __shfl_xor(sds, 16);
     sds += __shfl_xor(sds, 32);
     float dG[4][4], ktp = 0.f;
+    f32x4 oq[4], ok_[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -468,35 +528,54 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
             const float dqt = aQ[m][e], dkh = aH[m][e], dkb = aB[m][e], dkt = aT[m][e];
             dG[m][e] = qv[m][e] * eg * dqt + kv[m][e] * (eg * dkh - egi * dkb - et * dkt);
             ktp += kv[m][e] * et * dkt;
-            const int tok = tok0 + 16 * m + 4 * lg + e;
-            if (tok < T) {
-                const size_t off = hbase + (size_t)tok * tokstride + c;
-                dq[off] = (bf16_t)(eg * dqt);
-                dk[off] = (bf16_t)(eg * dkh + egi * dkb + et * dkt);
-            }
+            oq[m][e] = eg * dqt;
+            ok_[m][e] = eg * dkh + egi * dkb + et * dkt;
         }
     }
     ktp += __shfl_xor(ktp, 16);
     ktp += __shfl_xor(ktp, 32);
     // dg_r = sum over rows r' >= r of dG, plus the gradient of G_64 (which every
     // row's g enters)
+    float dgo[4][4];
     float acc = __builtin_amdgcn_exp2f(Gc) * sds + ktp;
 #pragma unroll
     for (int m = 3; m >= 0; --m) {
-        float sf[4];
-        sf[3] = dG[m][3];
+        float sfx[4];
+        sfx[3] = dG[m][3];
 #pragma unroll
-        for (int e = 2; e >= 0; --e) sf[e] = sf[e + 1] + dG[m][e];
+        for (int e = 2; e >= 0; --e) sfx[e] = sfx[e + 1] + dG[m][e];
         float bs[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bs[j] = __shfl(sf[0], ln + 16 * j);
+        for (int j = 0; j < 4; ++j) bs[j] = __shfl(sfx[0], ln + 16 * j);
         const float excl = (lg < 3 ? bs[3] : 0.f) + (lg < 2 ? bs[2] : 0.f) + (lg < 1 ? bs[1] : 0.f);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int tok = tok0 + 16 * m + 4 * lg + e;
-            if (tok < T) dg[hbase + (size_t)tok * tokstride + c] = acc + excl + sf[e];
-        }
+        for (int e = 0; e < 4; ++e) dgo[m][e] = acc + excl + sfx[e];
         acc += bs[0] + bs[1] + bs[2] + bs[3];
+    }
+    lds_barrier();                                 // regions A and B no longer read
+    bf16_t* stDQ = reinterpret_cast<bf16_t*>(smem + L::OFF_A);
+    bf16_t* stDK = stDQ + C * DK;
+    float* stDG = reinterpret_cast<float*>(smem + L::OFF_B);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * m + 4 * lg + e;
+            stDQ[r * DK + c] = (bf16_t)oq[m][e];
+            stDK[r * DK + c] = (bf16_t)ok_[m][e];
+            stDG[r * DK + c] = dgo[m][e];
+        }
+    lds_barrier();
+    if (vok) {
+        const size_t at = hbase + (size_t)(tok0 + vr) * tokstride + vc;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<bf16x8*>(dq + at + 8 * i) = ld8(stDQ + vr * DK + vc + 8 * i);
+            *reinterpret_cast<bf16x8*>(dk + at + 8 * i) = ld8(stDK + vr * DK + vc + 8 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4*>(dg + at + 4 * i) = *reinterpret_cast<const f32x4*>(stDG + vr * DK + vc + 4 * i);
     }
 }
 
