@@ -55,6 +55,7 @@ DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + 3 * 2 * D + 4 * D + 2 + 2 * D   # 132,
 
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_prefill.hip")
 DECODE_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_decode.hip")
+BACKWARD_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_backward.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {
@@ -251,10 +252,18 @@ def backward_line(steps, warmup, with_cpu=False):
     ht = B * T * H
     alg = ht * BWD_BYTES_PER_HEAD_TOKEN + STATE_BYTES * B * H
     gbs = alg / t / 1e9
+    # measured HBM traffic of the four kernels (rocprofv3 counters, committed
+    # under profiles/), when taken on the current sources
+    parts = [measured_traffic(key, src) for key, src in
+             (("chunk_bwd_prep", PREFILL_KERNEL_SRC), ("chunk_bwd_fwd_scan", PREFILL_KERNEL_SRC),
+              ("chunk_bwd_scan", BACKWARD_KERNEL_SRC), ("chunk_bwd_grad", BACKWARD_KERNEL_SRC))]
+    traffic = sum(parts) if all(p is not None for p in parts) else None
     out = {"workload": f"kda_chunk_bwd {name} (dL/do ~ N(0,1), dL/dS_T = 0)",
            "ms_per_step": round(t * 1e3, 4), "head_tokens_per_s": round(ht / t, 1),
            "alg_bytes_per_step": alg, "compulsory_gb_s": round(gbs, 1),
            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "traffic_bytes_per_step": traffic,
+           "traffic_gb_s": None if traffic is None else round(traffic / t / 1e9, 1),
            "workspace_bytes": ws.numel()}
     if with_cpu:
         from oracle import kda_ref
