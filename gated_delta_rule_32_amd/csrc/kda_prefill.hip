@@ -376,23 +376,27 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 #pragma unroll
                 for (int R = 1; R < 4; ++R) epilogue(acc[R - 1], 0, R, true);
                 epilogue(acc2[0], 1, 1, false); epilogue(acc2[1], 1, 2, false);
-            } else if (wave == 2) {   // I = 1: Aqk R = 3, Akk R = 1..3
+            } else if (wave == 2) {   // I = 1: Aqk R = 3, Akk R = 1..3;  I = 3: Akk R = 3
                 f32x4 acc[4] = {z4, z4, z4, z4};
                 const int br[4] = {48, 80, 96, 112};
                 mma_rows<E, DK, 4>(acc, sKb, L::P128, 16, sQt, L::P128, br, lane);
+                f32x4 acc3[1] = {z4};
+                const int br3[1] = {112};
+                mma_rows<E, DK, 1>(acc3, sKb, L::P128, 48, sQt, L::P128, br3, lane);
                 epilogue(acc[0], 1, 3, false);
 #pragma unroll
                 for (int R = 1; R < 4; ++R) epilogue(acc[R], 1, R, true);
-            } else if (wave == 3) {   // I = 2, 3 for both, and the zero upper tiles
+                epilogue(acc3[0], 3, 3, true);
+            } else if (wave == 3) {   // I = 2 for both, I = 3: Aqk R = 3, and the zero upper tiles
                 f32x4 acc[4] = {z4, z4, z4, z4};
                 const int br[4] = {32, 48, 96, 112};
                 mma_rows<E, DK, 4>(acc, sKb, L::P128, 32, sQt, L::P128, br, lane);
-                f32x4 acc3[2] = {z4, z4};
-                const int br3[2] = {48, 112};
-                mma_rows<E, DK, 2>(acc3, sKb, L::P128, 48, sQt, L::P128, br3, lane);
+                f32x4 acc3[1] = {z4};
+                const int br3[1] = {48};
+                mma_rows<E, DK, 1>(acc3, sKb, L::P128, 48, sQt, L::P128, br3, lane);
                 epilogue(acc[0], 2, 2, false); epilogue(acc[1], 2, 3, false);
                 epilogue(acc[2], 2, 2, true); epilogue(acc[3], 2, 3, true);
-                epilogue(acc3[0], 3, 3, false); epilogue(acc3[1], 3, 3, true);
+                epilogue(acc3[0], 3, 3, false);
 #pragma unroll
                 for (int u = 0; u < 6; ++u) {       // zero the upper tiles (I > R)
                     const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
