@@ -13,13 +13,15 @@ head-tokens per second (B*T*H / time).  The JSON line also carries:
     of HBM peak;
   * layer: the full token-mixing layer (d_model 2048, 16 heads, 32768
     tokens), its time, the KDA operator's share and the achieved TFLOP/s;
+  * gate_variants: the same prefill with one decay per head and token (Gated
+    DeltaNet) and with no decay (DeltaNet), through kda_chunk_fwd_gated;
   * backward: kda_chunk_bwd on the prefill workload (incoming gradients dL/do
     ~ N(0,1), dL/dS_T = 0), head-tokens/s, compulsory-HBM-bytes rate, and the
     gradient oracle timed on the host cores on the same workload;
   * cpu_baseline: the fp64 oracle timed on the host cores on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload c3|c1|decode|layer|bwd  (single-workload lines, for profiling)
+       python bench.py --workload c3|c1|decode|layer|bwd|gdn|deltanet  (single-workload lines, for profiling)
        python bench.py --copy-calibration       (plain copy kernel for counter scaling)
 """
 from __future__ import annotations
@@ -62,7 +64,10 @@ WORKLOADS = {
     "c2": "c2_bf16_B8_H16_T4096",
     "c3": "c3_bf16_B1_H32_T65536",
     "c1": "c1_fp32_T256",
+    "gdn": "c2_gdn_bf16_B8_H16_T4096",
+    "deltanet": "c2_deltanet_bf16_B8_H16_T4096",
 }
+GATE_BYTES = {"channel": 4 * D, "head": 4, "none": 0}   # log-decay bytes per head-token
 
 
 def log(*a):
@@ -133,6 +138,8 @@ def prefill_line(name, steps, warmup, schedule="auto"):
     t_kernel, wall = time_launches(step, steps, warmup)
     head_tokens = B * T * H
     per_ht = BYTES_PER_HEAD_TOKEN_BF16 if cfg["dtype"] == "bfloat16" else BYTES_PER_HEAD_TOKEN_F32
+    gate = cfg.get("gate", "channel")
+    per_ht += GATE_BYTES[gate] - GATE_BYTES["channel"]
     s0_bytes = STATE_BYTES * B * H if d["S0"] is not None else 0
     alg_bytes = head_tokens * per_ht + STATE_BYTES * B * H + s0_bytes
     flops = head_tokens * FLOP_PER_HEAD_TOKEN
@@ -154,10 +161,11 @@ def prefill_line(name, steps, warmup, schedule="auto"):
               "peak_tflops": BF16_PEAK_TFLOPS,
               "frac_of_bf16_peak": round(flops / t_kernel / 1e12 / BF16_PEAK_TFLOPS, 4),
               "frac_of_roofline": round(t_floor / t_kernel, 4)},
-        config={"workload": f"kda_chunk_fwd {name}", "schedule": sched,
+        config={"workload": f"kda_chunk_fwd {name}", "schedule": sched, "gate": gate,
                 "B": B, "T": T, "H": H, "d_k": D, "d_v": D,
                 "chunk": C, "dtype": cfg["dtype"], "S0": "N(0,%g)" % cfg["s0_std"] if d["S0"] is not None else "zero",
-                "log_decay": "-%g*softplus(N(0,1))" % cfg["g_scale"]},
+                "log_decay": ("none" if gate == "none" else
+                              "-%g*softplus(N(0,1))" % cfg["g_scale"] + (" per head" if gate == "head" else ""))},
     )
 
 
@@ -308,7 +316,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
-    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer", "bwd"], default=None,
+    ap.add_argument("--no-gates", action="store_true")
+    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer", "bwd", "gdn", "deltanet"],
+                    default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--schedule", choices=["auto", "fused", "two_kernel"], default="auto",
                     help="prefill schedule (auto: the library's preferred one)")
@@ -369,6 +379,16 @@ def main():
         line["decode"] = decode_line(max(args.steps, 20), args.warmup)
     if args.workload is None and not args.no_layer:
         line["layer"] = layer_line(min(args.steps, 20), args.warmup)
+    if args.workload is None and not args.no_gates:
+        line["gate_variants"] = {}
+        for wl in ("gdn", "deltanet"):
+            r = prefill_line(WORKLOADS[wl], args.steps, args.warmup)
+            line["gate_variants"][wl] = {"workload": r["config"]["workload"], "gate": r["config"]["gate"],
+                                         "ms_per_step": round(r["t"] * 1e3, 4),
+                                         "head_tokens_per_s": round(r["value"], 1),
+                                         "alg_bytes_per_launch": r["roofline"]["alg_bytes_per_launch"],
+                                         "hbm_frac": r["roofline"]["frac"],
+                                         "mfma_frac": r["mfma"]["frac_of_bf16_peak"]}
     if args.workload is None and not args.no_bwd:
         line["backward"] = backward_line(min(args.steps, 20), args.warmup, with_cpu=not args.no_cpu)
     if not args.no_cpu and args.workload is None:

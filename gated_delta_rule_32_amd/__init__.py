@@ -10,8 +10,8 @@ from __future__ import annotations
 
 import ctypes
 
-from ._binding import (KDA_BF16, KDA_F32, LAYER_REGIONS, KDAError, lib,  # noqa: F401
-                       status_string, version, _check)
+from ._binding import (KDA_BF16, KDA_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,  # noqa: F401
+                       KDA_GATE_NONE, LAYER_REGIONS, KDAError, lib, status_string, version, _check)
 
 __all__ = ["chunk_fwd", "chunk_bwd", "bwd_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
            "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS",
@@ -72,13 +72,23 @@ def _workspace(device, nbytes):
     return buf
 
 
+def _gate(log_alpha, per_channel_dim):
+    """Gate kind from the shape of log_alpha: None -> no decay (DeltaNet), one
+    value per head -> Gated DeltaNet, one per channel -> KDA."""
+    if log_alpha is None:
+        return KDA_GATE_NONE
+    return KDA_GATE_CHANNEL if log_alpha.dim() == per_channel_dim else KDA_GATE_HEAD
+
+
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out=None, S_T=None,
               return_state: bool = True, workspace="auto"):
     """Chunked KDA prefill.  q, k, v: [B, T, H, 128] (fp32 or bf16); log_alpha:
-    [B, T, H, 128] fp32; beta: [B, T, H] (same dtype as q); S0: [B, H, 128, 128]
-    fp32 or None.  ``workspace``: "auto" (the size the library asks for, cached
-    per device), None (fused single-kernel schedule) or a uint8 device tensor.
-    Returns ``(o, S_T)`` (``S_T`` is None if not requested)."""
+    [B, T, H, 128] fp32 (KDA), [B, T, H] fp32 (one decay per head: Gated
+    DeltaNet) or None (no decay: DeltaNet); beta: [B, T, H] (same dtype as q);
+    S0: [B, H, 128, 128] fp32 or None.  ``workspace``: "auto" (the size the
+    library asks for, cached per device), None (fused single-kernel schedule)
+    or a uint8 device tensor.  Returns ``(o, S_T)`` (``S_T`` is None if not
+    requested)."""
     import torch
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -86,7 +96,9 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out=None, S_T=None,
     code = _dtype_code(q)
     for t, n, shp in ((k, "k", q.shape), (v, "v", (B, T, H, dv)), (beta, "beta", (B, T, H))):
         _need(t, n, dt, shp, dev)
-    _need(log_alpha, "log_alpha", torch.float32, q.shape, dev)
+    gate = _gate(log_alpha, 4)
+    if gate != KDA_GATE_NONE:
+        _need(log_alpha, "log_alpha", torch.float32, q.shape if gate == KDA_GATE_CHANNEL else (B, T, H), dev)
     _need(q, "q", dt, q.shape, dev)
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
@@ -107,10 +119,10 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out=None, S_T=None,
         if workspace.device != dev or workspace.dtype != torch.uint8:
             raise ValueError("workspace must be a uint8 tensor on the same device")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                             _ptr(S0), _ptr(out), _ptr(S_T), B, T, H, dk, dv, code,
-                             ws_ptr, ws_bytes, _stream(dev))
-    _check("kda_chunk_fwd", st)
+    st = lib().kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), gate, _ptr(beta),
+                                   _ptr(S0), _ptr(out), _ptr(S_T), B, T, H, dk, dv, code,
+                                   ws_ptr, ws_bytes, _stream(dev))
+    _check("kda_chunk_fwd_gated", st)
     return out, S_T
 
 
@@ -159,8 +171,8 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T=None, *, workspace=
 
 def recurrent_step(q, k, v, log_alpha, beta, S, *, out=None):
     """One KDA decode step, state updated in place.  q, k, v: [N, H, 128];
-    log_alpha: [N, H, 128] fp32; beta: [N, H]; S: [N, H, 128, 128] fp32.
-    Returns o [N, H, 128]."""
+    log_alpha: [N, H, 128] fp32 (KDA), [N, H] fp32 (Gated DeltaNet) or None
+    (DeltaNet); beta: [N, H]; S: [N, H, 128, 128] fp32.  Returns o [N, H, 128]."""
     import torch
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -168,15 +180,17 @@ def recurrent_step(q, k, v, log_alpha, beta, S, *, out=None):
     code = _dtype_code(q)
     for t, n, shp in ((k, "k", q.shape), (v, "v", (N, H, dv)), (beta, "beta", (N, H))):
         _need(t, n, dt, shp, dev)
-    _need(log_alpha, "log_alpha", torch.float32, q.shape, dev)
+    gate = _gate(log_alpha, 3)
+    if gate != KDA_GATE_NONE:
+        _need(log_alpha, "log_alpha", torch.float32, q.shape if gate == KDA_GATE_CHANNEL else (N, H), dev)
     _need(S, "S", torch.float32, (N, H, dk, dv), dev)
     if out is None:
         out = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _need(out, "out", dt, (N, H, dv), dev)
-    st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                  _ptr(S), _ptr(out), N, H, dk, dv, code, _stream(dev))
-    _check("kda_recurrent_step", st)
+    st = lib().kda_recurrent_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), gate, _ptr(beta),
+                                        _ptr(S), _ptr(out), N, H, dk, dv, code, _stream(dev))
+    _check("kda_recurrent_step_gated", st)
     return out
 
 

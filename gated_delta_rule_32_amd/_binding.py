@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
 KDA_OK = 0
 # workspace regions of kda_layer_fwd, in the order of the KDA_LAYER_WS_* enum
 LAYER_REGIONS = ("pre", "low", "q", "k", "v", "g", "beta", "o", "zg", "chunk")
@@ -26,6 +27,10 @@ SIGNATURES = {
     "kda_chunk_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                            _I, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
     "kda_chunk_fwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "kda_chunk_fwd_gated": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP,
+                                 _I, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
+    "kda_recurrent_step_gated": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP,
+                                      _I, _I, _I, _I, _I, _VP]),
     "kda_chunk_bwd": (_I, [_VP] * 14 + [_I] * 6 + [_VP, _SZ, _VP]),
     "kda_chunk_bwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "kda_recurrent_step": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,

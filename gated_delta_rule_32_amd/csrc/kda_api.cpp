@@ -72,8 +72,19 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   int B, int T, int H, int dk, int dv, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream)
 {
+    return kda_chunk_fwd_gated(q, k, v, log_alpha, KDA_GATE_CHANNEL, beta, S0, o, S_T, B, T, H, dk, dv,
+                               dtype, workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
+                        const float* log_alpha, int gate, const void* beta, const float* S0,
+                        void* o, float* S_T,
+                        int B, int T, int H, int dk, int dv, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED;
     if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return KDA_OK;
 
@@ -90,13 +101,16 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
     if (S0 && (rc = check_ptr(S0, 16)) != KDA_OK) return rc;
     if (S_T && (rc = check_ptr(S_T, 16)) != KDA_OK) return rc;
     const Range rS0{S0, S0 ? n_state * 4 : 0}, rST{S_T, S_T ? n_state * 4 : 0};
+    // gate input: per channel, per head, or none (must be NULL)
+    const size_t g_bytes = gate == KDA_GATE_CHANNEL ? n_qk * 4 : gate == KDA_GATE_HEAD ? tok * 4 : 0;
+    if (gate == KDA_GATE_NONE && log_alpha) return KDA_ERR_INVALID_ARG;
     if (T > 0) {
         if ((rc = check_ptr(q, 16)) || (rc = check_ptr(k, 16)) || (rc = check_ptr(v, 16)) ||
-            (rc = check_ptr(log_alpha, 16)) || (rc = check_ptr(beta, es)) ||
-            (rc = check_ptr(o, 16)))
+            (gate != KDA_GATE_NONE && (rc = check_ptr(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4))) ||
+            (rc = check_ptr(beta, es)) || (rc = check_ptr(o, 16)))
             return rc;
         const Range in[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es},
-                            {log_alpha, n_qk * 4}, {beta, tok * es}, rS0};
+                            {log_alpha, g_bytes}, {beta, tok * es}, rS0};
         const Range ro{o, n_qk * es};
         for (const Range& r : in)
             if (overlap(ro, r)) return KDA_ERR_INVALID_ARG;
@@ -114,7 +128,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
         workspace_bytes >= kda::chunk_ws_bytes(B, T, H)) {
         if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
         const Range rw{workspace, kda::chunk_ws_bytes(B, T, H)};
-        const Range all[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, n_qk * 4},
+        const Range all[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, g_bytes},
                              {beta, tok * es}, rS0, rST, {o, n_qk * es}};
         for (const Range& r : all)
             if (overlap(rw, r)) return KDA_ERR_INVALID_ARG;
@@ -127,7 +141,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
         if (!S_T || (const void*)S0 == (const void*)S_T) return KDA_OK;
         e = kda::launch_state_copy(S0, S_T, (long long)heads, s);
     } else {
-        e = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dtype, ws, s);
+        e = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dtype, ws, s, gate);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -208,8 +222,18 @@ int kda_recurrent_step(const void* q, const void* k, const void* v,
                        void* o, int N, int H, int dk, int dv, int dtype,
                        void* stream)
 {
+    return kda_recurrent_step_gated(q, k, v, log_alpha, KDA_GATE_CHANNEL, beta, S, o, N, H, dk, dv,
+                                    dtype, stream);
+}
+
+int kda_recurrent_step_gated(const void* q, const void* k, const void* v,
+                             const float* log_alpha, int gate, const void* beta, float* S,
+                             void* o, int N, int H, int dk, int dv, int dtype,
+                             void* stream)
+{
     if (N < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED;
     if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
     if ((long long)N * H == 0) return KDA_OK;
 
@@ -221,19 +245,21 @@ int kda_recurrent_step(const void* q, const void* k, const void* v,
     if (!ok || heads > (size_t)INT_MAX) return KDA_ERR_UNSUPPORTED;
 
     int rc;
+    if (gate == KDA_GATE_NONE && log_alpha) return KDA_ERR_INVALID_ARG;
     if ((rc = check_ptr(q, 16)) || (rc = check_ptr(k, 16)) || (rc = check_ptr(v, 16)) ||
-        (rc = check_ptr(log_alpha, 16)) || (rc = check_ptr(beta, es)) ||
-        (rc = check_ptr(S, 16)) || (rc = check_ptr(o, 16)))
+        (gate != KDA_GATE_NONE && (rc = check_ptr(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4))) ||
+        (rc = check_ptr(beta, es)) || (rc = check_ptr(S, 16)) || (rc = check_ptr(o, 16)))
         return rc;
+    const size_t g_bytes = gate == KDA_GATE_CHANNEL ? n_vec * 4 : gate == KDA_GATE_HEAD ? heads * 4 : 0;
     const Range in[] = {{q, n_vec * es}, {k, n_vec * es}, {v, n_vec * es},
-                        {log_alpha, n_vec * 4}, {beta, heads * es}};
+                        {log_alpha, g_bytes}, {beta, heads * es}};
     const Range rS{S, n_state * 4}, ro{o, n_vec * es};
     for (const Range& r : in)
         if (overlap(rS, r) || overlap(ro, r)) return KDA_ERR_INVALID_ARG;
     if (overlap(rS, ro)) return KDA_ERR_INVALID_ARG;
 
     hipError_t e = kda::launch_decode_step(q, k, v, log_alpha, beta, S, o,
-                                           (long long)heads, dtype, (hipStream_t)stream);
+                                           (long long)heads, dtype, (hipStream_t)stream, gate);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

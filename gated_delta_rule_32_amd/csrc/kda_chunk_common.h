@@ -11,6 +11,9 @@ constexpr int C = 64;     // chunk length
 constexpr int DK = 128;   // key / value head dimension
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Forget-gate layouts (the kda_gate_t values of the C ABI).
+constexpr int GATE_CHANNEL = 0, GATE_HEAD = 1, GATE_NONE = 2;
+
 // Barrier that orders LDS traffic only: global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");

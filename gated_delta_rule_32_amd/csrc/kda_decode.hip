@@ -24,6 +24,9 @@
 // the same address), and each wave forms k . q with shuffles, so the only
 // barrier is the one that combines the 16 waves' partial sums of S'^T k and
 // S'^T q.  The small token loads are issued before the state loads.
+//
+// GATE: per-channel decay (KDA, g [heads, 128]), one decay per head (Gated
+// DeltaNet, g [heads]) or none (DeltaNet, alpha = 1, g unused).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -31,7 +34,9 @@ namespace kda {
 
 constexpr int DEC_THREADS = 1024;
 
-template <typename TI>
+constexpr int GATE_CHANNEL = 0, GATE_HEAD = 1, GATE_NONE = 2;
+
+template <typename TI, int GATE>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_step_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                    const TI* __restrict__ v, const float* __restrict__ g,
@@ -53,7 +58,12 @@ decode_step_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
         const int row = rg + RG * i;
         rk[i] = to_f32(k[vbase + row]);
         rq[i] = to_f32(q[vbase + row]);
-        rg_[i] = g[vbase + row];
+        if constexpr (GATE == GATE_CHANNEL) rg_[i] = g[vbase + row];
+    }
+    if constexpr (GATE == GATE_HEAD) {
+        const float gh = g[head];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) rg_[i] = gh;
     }
     float kq = to_f32(k[vbase + lane]) * to_f32(q[vbase + lane]) +
                to_f32(k[vbase + lane + 64]) * to_f32(q[vbase + lane + 64]);
@@ -71,7 +81,7 @@ decode_step_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
     f32x4 r = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        st[i] *= exp_fast(rg_[i]);
+        if constexpr (GATE != GATE_NONE) st[i] *= exp_fast(rg_[i]);
         r += st[i] * rk[i];
         s += st[i] * rq[i];
     }
@@ -100,21 +110,30 @@ decode_step_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
         __builtin_nontemporal_store(st[i] + rk[i] * u, &Sout[(rg + RG * i) * 32 + cg]);
 }
 
-hipError_t launch_decode_step(const void* q, const void* k, const void* v,
-                              const float* g, const void* beta, float* S, void* o,
-                              long long heads, int dtype, hipStream_t stream)
+template <int GATE>
+void launch_decode_gate(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                        float* S, void* o, long long heads, int dtype, hipStream_t stream)
 {
-    if (heads <= 0) return hipSuccess;
     const dim3 grid((unsigned)heads), block(DEC_THREADS);
     if (dtype == 1) {
-        hipLaunchKernelGGL(decode_step_kernel<bf16_t>, grid, block, 0, stream,
+        hipLaunchKernelGGL((decode_step_kernel<bf16_t, GATE>), grid, block, 0, stream,
                            (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
                            (const bf16_t*)beta, S, (bf16_t*)o);
     } else {
-        hipLaunchKernelGGL(decode_step_kernel<float>, grid, block, 0, stream,
+        hipLaunchKernelGGL((decode_step_kernel<float, GATE>), grid, block, 0, stream,
                            (const float*)q, (const float*)k, (const float*)v, g,
                            (const float*)beta, S, (float*)o);
     }
+}
+
+hipError_t launch_decode_step(const void* q, const void* k, const void* v,
+                              const float* g, const void* beta, float* S, void* o,
+                              long long heads, int dtype, hipStream_t stream, int gate)
+{
+    if (heads <= 0) return hipSuccess;
+    if (gate == GATE_HEAD) launch_decode_gate<GATE_HEAD>(q, k, v, g, beta, S, o, heads, dtype, stream);
+    else if (gate == GATE_NONE) launch_decode_gate<GATE_NONE>(q, k, v, g, beta, S, o, heads, dtype, stream);
+    else launch_decode_gate<GATE_CHANNEL>(q, k, v, g, beta, S, o, heads, dtype, stream);
     return hipGetLastError();
 }
 

@@ -7,18 +7,22 @@
 
 namespace kda {
 
-// Decode step over `heads` = N*H independent heads; dtype 0 = fp32, 1 = bf16.
+// Decode step over `heads` = N*H independent heads; dtype 0 = fp32, 1 = bf16;
+// `gate` as for launch_chunk_fwd (g [heads, 128], [heads] or unused).
 hipError_t launch_decode_step(const void* q, const void* k, const void* v,
                               const float* g, const void* beta, float* S, void* o,
-                              long long heads, int dtype, hipStream_t stream);
+                              long long heads, int dtype, hipStream_t stream,
+                              int gate = KDA_GATE_CHANNEL);
 
 // Chunked prefill over B*H heads of T >= 1 tokens (d_k = d_v = 128).  With
 // `ws` non-null (bf16 only, at least chunk_ws_bytes(B, T, H) bytes) the
-// two-kernel schedule runs; otherwise the fused single kernel.
+// two-kernel schedule runs; otherwise the fused single kernel.  `gate` is a
+// kda_gate_t: g is [B, T, H, 128] (per channel), [B, T, H] (per head) or
+// unused (no decay).
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             const float* g, const void* beta, const float* S0,
                             void* o, float* S_T, int B, int T, int H, int dtype,
-                            void* ws, hipStream_t stream);
+                            void* ws, hipStream_t stream, int gate = KDA_GATE_CHANNEL);
 
 // Bytes of workspace the two-kernel schedule needs: one 72,704-byte block of
 // key-side operands per (batch, head, 64-token chunk).

@@ -102,7 +102,8 @@ template <typename E, int DV>
 struct ChunkIn {
     static constexpr int VL = DV / 8;                   // lanes per value row
     static constexpr int RVR = (64 * VL + NT - 1) / NT; // value rows per thread
-    Raw8f g[RPL];
+    Raw8f g[RPL];                                       // per-channel gate
+    float gh[RPL];                                      // per-head gate
     Raw8<E> q[RPL], k[RPL];
     Raw8<E> v[RVR];
     E beta;
@@ -130,7 +131,12 @@ constexpr int PREP_CHUNKS = 4;                      // chunks per prep workgroup
 // also exports to `wsb` the operands of the backward state scan (the
 // transposes Aqk^T, Tm^T, Qt^T, Kh^T and Kt = Diag(e^{G_64}) Kb, layout
 // WSB_* in kda_chunk_common.h).
-template <typename E, int DV, bool PREP, bool BWD = false>
+//
+// GATE selects the forget gate: GATE_CHANNEL (KDA, g [B, T, H, 128]),
+// GATE_HEAD (one decay per head and token, g [B, T, H]: Gated DeltaNet) or
+// GATE_NONE (alpha = 1: DeltaNet, g unused).  With one decay per row the
+// decay factors are computed once per row instead of once per channel.
+template <typename E, int DV, bool PREP, bool BWD = false, int GATE = GATE_CHANNEL>
 __global__ void __launch_bounds__(NT)
 chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* beta,
                  const float* S0, E* o, float* S_T, int T, int H, int nsplit, char* ws,
@@ -207,7 +213,8 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         for (int i = 0; i < RPL; ++i) {
             const int tok = min(tok0 + RPT * wave + RPL * rq + i, T - 1);
             const size_t off = hbase + (size_t)tok * tokstride + 8 * cg;
-            in.g[i].load(g + off);
+            if constexpr (GATE == GATE_CHANNEL) in.g[i].load(g + off);
+            else if constexpr (GATE == GATE_HEAD) in.gh[i] = g[((size_t)b * T + tok) * H + h];
             in.q[i].load(q + off);
             in.k[i].load(k + off);
         }
@@ -255,13 +262,23 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
             constexpr bool MASKED = decltype(masked_t)::value;
             auto row_ok = [&](int r) { return !MASKED || n * C + r < T; };
             const int r0 = RPT * wave + RPL * rq;
-            float G[RPL][8];
+            constexpr int NG = GATE == GATE_CHANNEL ? 8 : 1;   // distinct decays per lane row
+            float G[RPL][NG];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
+            for (int c = 0; c < NG; ++c) {
+                if constexpr (GATE == GATE_NONE) {
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) G[i][c] = 0.f;
+                    if (rq == 3) {
+#pragma unroll
+                        for (int c2 = 0; c2 < 8; ++c2) s_tot[wave * DK + 8 * cg + c2] = 0.f;
+                    }
+                    continue;
+                }
                 float run = 0.f;
 #pragma unroll
                 for (int i = 0; i < RPL; ++i) {
-                    const float gi = in.g[i][c] * LOG2E;
+                    const float gi = (GATE == GATE_CHANNEL ? in.g[i][c] : in.gh[i]) * LOG2E;
                     run += row_ok(r0 + i) ? gi : 0.f;
                     G[i][c] = run;
                 }
@@ -273,7 +290,13 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                 const float excl = inc - run;
 #pragma unroll
                 for (int i = 0; i < RPL; ++i) G[i][c] += excl;
-                if (rq == 3) s_tot[wave * DK + 8 * cg + c] = inc;
+                if (rq == 3) {
+                    if constexpr (NG == 8) s_tot[wave * DK + 8 * cg + c] = inc;
+                    else {
+#pragma unroll
+                        for (int c2 = 0; c2 < 8; ++c2) s_tot[wave * DK + 8 * cg + c2] = inc;
+                    }
+                }
             }
             if (wave == 0) s_beta[lane] = row_ok(lane) ? to_f32(in.beta) : 0.f;
             lds_barrier();
@@ -290,22 +313,33 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
             }
             lds_barrier();
             {
-                const f32x4 o0 = *reinterpret_cast<const f32x4*>(s_tot + wave * DK + 8 * cg);
-                const f32x4 o1 = *reinterpret_cast<const f32x4*>(s_tot + wave * DK + 8 * cg + 4);
+                if constexpr (NG == 8) {
+                    const f32x4 o0 = *reinterpret_cast<const f32x4*>(s_tot + wave * DK + 8 * cg);
+                    const f32x4 o1 = *reinterpret_cast<const f32x4*>(s_tot + wave * DK + 8 * cg + 4);
 #pragma unroll
-                for (int i = 0; i < RPL; ++i)
+                    for (int i = 0; i < RPL; ++i)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) { G[i][c] += o0[c]; G[i][c + 4] += o1[c]; }
+                        for (int c = 0; c < 4; ++c) { G[i][c] += o0[c]; G[i][c + 4] += o1[c]; }
+                } else if constexpr (GATE == GATE_HEAD) {
+                    const float o = s_tot[wave * DK + 8 * cg];
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) G[i][0] += o;
+                }
             }
             float kb[RPL][8];
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 const int r = r0 + i;
                 const bool ok = row_ok(r);
-                float qe[8], ke[8];
+                float qe[8], ke[8], eg[NG], neg[NG];
+#pragma unroll
+                for (int c = 0; c < NG; ++c) {
+                    eg[c] = GATE == GATE_NONE ? 1.f : __builtin_amdgcn_exp2f(G[i][c]);
+                    neg[c] = GATE == GATE_NONE ? 1.f : __builtin_amdgcn_exp2f(-G[i][c]);
+                }
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const float e = __builtin_amdgcn_exp2f(G[i][c]), ne = __builtin_amdgcn_exp2f(-G[i][c]);
+                    const float e = eg[NG == 8 ? c : 0], ne = neg[NG == 8 ? c : 0];
                     const float qv = ok ? in.q[i][c] : 0.f, kv = ok ? in.k[i][c] : 0.f;
                     qe[c] = qv * e; ke[c] = kv * e; kb[i][c] = kv * ne;
                 }
@@ -936,15 +970,47 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     }
 }
 
-template <typename E, int DV>
+template <typename E, int DV, int GATE>
 void launch_one(const void* q, const void* k, const void* v, const float* g, const void* beta,
                 const float* S0, void* o, float* S_T, int B, int T, int H, hipStream_t stream)
 {
     const int nsplit = DK / DV;
     const unsigned nwg = (unsigned)((long long)B * H * nsplit);
-    hipLaunchKernelGGL((chunk_fwd_kernel<E, DV, false>), dim3(nwg), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((chunk_fwd_kernel<E, DV, false, false, GATE>), dim3(nwg), dim3(NT), 0, stream,
                        (const E*)q, (const E*)k, (const E*)v, g, (const E*)beta, S0, (E*)o, S_T,
                        T, H, nsplit, (char*)nullptr, (char*)nullptr);
+}
+
+template <int GATE>
+void launch_gate(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                 const float* S0, void* o, float* S_T, int B, int T, int H, int dtype, void* ws,
+                 hipStream_t stream)
+{
+    const long long heads = (long long)B * H;
+    if (dtype == 0) {
+        // fp32 operands need the narrowest slice to fit the LDS budget
+        launch_one<float, 16, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+    } else if (ws) {
+        const int nchunks = (T + C - 1) / C;
+        const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
+        hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true, false, GATE>), dim3((unsigned)(heads * nblk)),
+                           dim3(NT), 0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
+                           (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws, (char*)nullptr);
+        // value columns per scan workgroup: enough workgroups to cover the machine
+        const int ncw = heads * 4 >= 256 ? 2 : 1;
+#define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, false>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
+                                         dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws, (const bf16_t*)v, S0, \
+                                         (bf16_t*)o, S_T, T, H, (bf16_t*)nullptr, (bf16_t*)nullptr, (bf16_t*)nullptr)
+        if (ncw == 2) KDA_SCAN(2);
+        else KDA_SCAN(1);
+#undef KDA_SCAN
+    } else if (heads * 2 >= 256) {
+        launch_one<bf16_t, 64, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+    } else if (heads * 4 >= 256) {
+        launch_one<bf16_t, 32, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+    } else {
+        launch_one<bf16_t, 16, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+    }
 }
 
 }  // namespace
@@ -985,33 +1051,11 @@ hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, 
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                             const void* beta, const float* S0, void* o, float* S_T,
-                            int B, int T, int H, int dtype, void* ws, hipStream_t stream)
+                            int B, int T, int H, int dtype, void* ws, hipStream_t stream, int gate)
 {
-    const long long heads = (long long)B * H;
-    if (dtype == 0) {
-        // fp32 operands need the narrowest slice to fit the LDS budget
-        launch_one<float, 16>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
-    } else if (ws) {
-        const int nchunks = (T + C - 1) / C;
-        const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
-        hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true>), dim3((unsigned)(heads * nblk)), dim3(NT),
-                           0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
-                           (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws, (char*)nullptr);
-        // value columns per scan workgroup: enough workgroups to cover the machine
-        const int ncw = heads * 4 >= 256 ? 2 : 1;
-#define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, false>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
-                                         dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws, (const bf16_t*)v, S0, \
-                                         (bf16_t*)o, S_T, T, H, (bf16_t*)nullptr, (bf16_t*)nullptr, (bf16_t*)nullptr)
-        if (ncw == 2) KDA_SCAN(2);
-        else KDA_SCAN(1);
-#undef KDA_SCAN
-    } else if (heads * 2 >= 256) {
-        launch_one<bf16_t, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
-    } else if (heads * 4 >= 256) {
-        launch_one<bf16_t, 32>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
-    } else {
-        launch_one<bf16_t, 16>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
-    }
+    if (gate == GATE_HEAD) launch_gate<GATE_HEAD>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream);
+    else if (gate == GATE_NONE) launch_gate<GATE_NONE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream);
+    else launch_gate<GATE_CHANNEL>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream);
     return hipGetLastError();
 }
 

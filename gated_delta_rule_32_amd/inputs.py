@@ -9,7 +9,9 @@ Prefill draws: ``numpy.random.default_rng(seed)``, in the order q, k, v, g,
 beta, S0, each ``[B, T, H, .]`` in C order, as fp32:
   q, k ~ N(0, 1), then divided by their L2 norm per (token, head);
   v ~ N(0, 1);
-  g = -g_scale * softplus(N(0, 1))  (log of the per-channel forget gate);
+  g = -g_scale * softplus(N(0, 1))  (log of the per-channel forget gate; with
+      gate="head" one draw per (token, head), shape [B, T, H]: the Gated
+      DeltaNet gate; with gate="none" no draw and g = None: DeltaNet);
   beta = sigmoid(N(0, 1));
   S0 ~ N(0, s0_std^2) if s0_std > 0 else None.
 Decode draws (per step, one token per (sequence, head)) use a torch generator
@@ -28,6 +30,11 @@ PREFILL_CONFIGS = {
     "c1_fp32_T256": dict(B=1, T=256, H=1, dtype="float32", g_scale=0.1, s0_std=0.0, seed=1),
     "c2_bf16_B8_H16_T4096": dict(B=8, T=4096, H=16, dtype="bfloat16", g_scale=0.05, s0_std=0.0, seed=2),
     "c3_bf16_B1_H32_T65536": dict(B=1, T=65536, H=32, dtype="bfloat16", g_scale=0.05, s0_std=0.02, seed=3),
+    # the B = 8, H = 16, T = 4096 prefill with the other two gates of the family
+    "c2_gdn_bf16_B8_H16_T4096": dict(B=8, T=4096, H=16, dtype="bfloat16", g_scale=0.05, s0_std=0.0, seed=2,
+                                     gate="head"),
+    "c2_deltanet_bf16_B8_H16_T4096": dict(B=8, T=4096, H=16, dtype="bfloat16", g_scale=0.05, s0_std=0.0,
+                                          seed=2, gate="none"),
 }
 DECODE_CONFIG = dict(N=256, H=32, steps=1000, dtype="bfloat16", s_std=0.02, seed=4)
 LAYER_CONFIG = dict(B=1, T=32768, d_model=2048, H=16, dtype="bfloat16", w_std=0.02, seed=5)
@@ -50,22 +57,25 @@ def _sigmoid(x):
     return (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
 
 
-def prefill_inputs(B, T, H, dtype="bfloat16", g_scale=0.05, s0_std=0.0, seed=0, d=D):
-    """Returns a dict of CPU torch tensors q, k, v, g, beta (and S0 or None)."""
+def prefill_inputs(B, T, H, dtype="bfloat16", g_scale=0.05, s0_std=0.0, seed=0, d=D, gate="channel"):
+    """Returns a dict of CPU torch tensors q, k, v, g, beta (and S0 or None).
+    gate: "channel" (g [B, T, H, d]), "head" (g [B, T, H]) or "none" (g None)."""
     import torch
     rng = np.random.default_rng(seed)
     shp = (B, T, H, d)
     q = _l2n(rng.standard_normal(shp, dtype=np.float32))
     k = _l2n(rng.standard_normal(shp, dtype=np.float32))
     v = rng.standard_normal(shp, dtype=np.float32)
-    g = (-np.float32(g_scale)) * _softplus(rng.standard_normal(shp, dtype=np.float32))
+    gshp = {"channel": shp, "head": (B, T, H), "none": None}[gate]
+    g = None if gshp is None else (-np.float32(g_scale)) * _softplus(rng.standard_normal(gshp, dtype=np.float32))
     beta = _sigmoid(rng.standard_normal((B, T, H), dtype=np.float32))
     S0 = None
     if s0_std > 0:
         S0 = torch.from_numpy(np.float32(s0_std) * rng.standard_normal((B, H, d, d), dtype=np.float32))
     td = _torch_dtype(dtype)
     cast = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(td)
-    return dict(q=cast(q), k=cast(k), v=cast(v), g=torch.from_numpy(np.ascontiguousarray(g)),
+    return dict(q=cast(q), k=cast(k), v=cast(v),
+                g=None if g is None else torch.from_numpy(np.ascontiguousarray(g)),
                 beta=cast(beta), S0=S0)
 
 
@@ -95,9 +105,10 @@ def decode_state(N, H, s_std=0.02, seed=0, device="cpu", d=D):
     return s_std * torch.randn((N, H, d, d), generator=gen, device=device, dtype=torch.float32)
 
 
-def decode_tokens(N, H, steps, dtype="bfloat16", seed=0, device="cpu", d=D):
+def decode_tokens(N, H, steps, dtype="bfloat16", seed=0, device="cpu", d=D, gate="channel"):
     """Tokens for ``steps`` decode steps: dict of tensors with a leading step
-    axis, q/k/v [steps, N, H, d], g [steps, N, H, d] fp32, beta [steps, N, H]."""
+    axis, q/k/v [steps, N, H, d], g [steps, N, H, d] fp32 (gate="head": [steps,
+    N, H]; gate="none": None), beta [steps, N, H]."""
     import torch
     gen = torch.Generator(device=device).manual_seed(seed + 1)
     td = _torch_dtype(dtype)
@@ -110,8 +121,11 @@ def decode_tokens(N, H, steps, dtype="bfloat16", seed=0, device="cpu", d=D):
     k = l2n(torch.randn((steps, N, H, d), generator=gen, device=device, dtype=f32)).to(td)
     v = torch.randn((steps, N, H, d), generator=gen, device=device, dtype=f32).to(td)
     beta = torch.sigmoid(torch.randn((steps, N, H), generator=gen, device=device, dtype=f32)).to(td)
-    alpha = 0.9 + 0.1 * torch.rand((steps, N, H, d), generator=gen, device=device, dtype=f32)
-    g = torch.log(alpha)
+    gshp = {"channel": (steps, N, H, d), "head": (steps, N, H), "none": None}[gate]
+    g = None
+    if gshp is not None:
+        alpha = 0.9 + 0.1 * torch.rand(gshp, generator=gen, device=device, dtype=f32)
+        g = torch.log(alpha)
     return dict(q=q, k=k, v=v, g=g, beta=beta)
 
 

@@ -50,6 +50,19 @@ typedef enum {
     KDA_BF16 = 1  /* bfloat16 (upper half of an fp32) */
 } kda_dtype_t;
 
+/*
+ * Kind of forget gate, for the *_gated entry points.  KDA's gate is one decay
+ * per key channel (eq. (1) of page "Kimi K3论文：Kimi Linear", section 3); the
+ * same page (section 2) places KDA after Gated DeltaNet, whose gate is one
+ * decay per head and token, and DeltaNet, which has no decay (alpha = 1).
+ * The three share the recurrence and these kernels.
+ */
+typedef enum {
+    KDA_GATE_CHANNEL = 0,  /* log_alpha [.., H, dk] fp32: KDA                  */
+    KDA_GATE_HEAD = 1,     /* log_alpha [.., H] fp32: Gated DeltaNet           */
+    KDA_GATE_NONE = 2      /* no decay, log_alpha must be NULL: DeltaNet       */
+} kda_gate_t;
+
 /* Status codes. */
 enum {
     KDA_OK = 0,
@@ -95,6 +108,21 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   void* o, float* S_T,
                   int B, int T, int H, int dk, int dv, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd with a choice of forget gate (kda_gate_t): `log_alpha` is
+ * [B, T, H, dk] fp32 for KDA_GATE_CHANNEL (identical to kda_chunk_fwd),
+ * [B, T, H] fp32 (4-byte aligned) for KDA_GATE_HEAD, and NULL for
+ * KDA_GATE_NONE.  With one decay per head the decay factors are computed once
+ * per token and the gate input shrinks from 512 to 4 bytes per head-token.
+ * The workspace rules (and kda_chunk_fwd_workspace_size) are those of
+ * kda_chunk_fwd.  An unknown gate returns KDA_ERR_UNSUPPORTED.
+ */
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
+                        const float* log_alpha, int gate, const void* beta, const float* S0,
+                        void* o, float* S_T,
+                        int B, int T, int H, int dk, int dv, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes that kda_chunk_fwd should be given for the fastest schedule
@@ -167,6 +195,16 @@ int kda_recurrent_step(const void* q, const void* k, const void* v,
                        const float* log_alpha, const void* beta, float* S,
                        void* o, int N, int H, int dk, int dv, int dtype,
                        void* stream);
+
+/*
+ * kda_recurrent_step with a choice of forget gate: `log_alpha` is [N, H, dk]
+ * for KDA_GATE_CHANNEL (identical to kda_recurrent_step), [N, H] (4-byte
+ * aligned) for KDA_GATE_HEAD, NULL for KDA_GATE_NONE.
+ */
+int kda_recurrent_step_gated(const void* q, const void* k, const void* v,
+                             const float* log_alpha, int gate, const void* beta, float* S,
+                             void* o, int N, int H, int dk, int dv, int dtype,
+                             void* stream);
 
 /*
  * One KDA token-mixing layer (page "Kimi K3论文：Kimi Linear", section 3:

@@ -34,7 +34,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_bwd",
-                          "kda_chunk_bwd_workspace_size", "kda_recurrent_step",
+                          "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated",
+                          "kda_recurrent_step_gated", "kda_recurrent_step",
                           "kda_layer_fwd", "kda_layer_workspace_layout",
                           "kda_status_string", "kda_version"}
     for n in names:
@@ -220,3 +221,38 @@ def test_chunk_bwd_noop(lib):
     assert lib.kda_chunk_bwd(*([None] * 14), 0, 64, 4, 128, 128, BF16, None, 0, None) == OK
     # T == 0 without dS0: nothing to write
     assert lib.kda_chunk_bwd(*([None] * 14), 2, 0, 4, 128, 128, BF16, None, 0, None) == OK
+
+
+# ------------------------------------------------------------- gate variants
+GATE_CHANNEL, GATE_HEAD, GATE_NONE = 0, 1, 2
+
+
+def chunk_g(lib, gate, g=P + 2**26, T=64, **kw):
+    a = dict(q=P, k=P + 2**24, v=P + 2**25, beta=P + 2**27, S0=None, o=P + 2**28, ST=P + 2**29,
+             B=1, H=1, dk=128, dv=128, dt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], g, gate, a["beta"], a["S0"], a["o"], a["ST"],
+                                   a["B"], T, a["H"], a["dk"], a["dv"], a["dt"], a["ws"], a["wsb"], None)
+
+
+def step_g(lib, gate, g=P + 2**26, **kw):
+    a = dict(q=P, k=P + 2**24, v=P + 2**25, beta=P + 2**27, S=P + 2**28, o=P + 2**29, N=1, H=1, dt=BF16)
+    a.update(kw)
+    return lib.kda_recurrent_step_gated(a["q"], a["k"], a["v"], g, gate, a["beta"], a["S"], a["o"],
+                                        a["N"], a["H"], 128, 128, a["dt"], None)
+
+
+def test_gated_entry_points_reject(lib):
+    assert chunk_g(lib, 3) == UNSUP and chunk_g(lib, -1) == UNSUP
+    assert step_g(lib, 7) == UNSUP
+    assert chunk_g(lib, GATE_NONE) == INVALID          # no decay: log_alpha must be NULL
+    assert step_g(lib, GATE_NONE) == INVALID
+    assert chunk_g(lib, GATE_HEAD, g=P + 2**26 + 2) == ALIGN   # per-head gate: 4-byte aligned
+    assert chunk_g(lib, GATE_CHANNEL, g=P + 2**26 + 4) == ALIGN
+    assert chunk_g(lib, GATE_HEAD, g=None) == INVALID
+    assert chunk_g(lib, GATE_HEAD, g=P + 2**28 + 4) == INVALID        # gate overlaps o
+    # zero heads: no-op for every gate
+    assert chunk_g(lib, GATE_HEAD, H=0) == OK and chunk_g(lib, GATE_NONE, g=None, H=0) == OK
+    assert step_g(lib, GATE_HEAD, N=0) == OK
+    # T = 0 without S_T touches nothing, whatever the gate
+    assert chunk_g(lib, GATE_NONE, g=None, T=0, q=None, k=None, v=None, beta=None, o=None, ST=None) == OK
