@@ -199,6 +199,35 @@ def decode_line(steps, warmup):
             "traffic": measured_traffic("recurrent_step_decode", DECODE_KERNEL_SRC)}
 
 
+def decode_latency_line(steps, warmup, N=1, H=32, per_graph=32):
+    """Small-batch decode (N sequences x H heads): per-step time of eager calls
+    through the Python binding against replays of a HIP graph holding
+    `per_graph` captured steps (serving loops capture the step so that launch
+    and binding overhead leave the per-token path)."""
+    import torch
+    import gated_delta_rule_32_amd as kda
+    from gated_delta_rule_32_amd import inputs
+
+    S = inputs.decode_state(N, H, s_std=0.02, seed=4, device="cuda:0")
+    toks = inputs.decode_tokens(N, H, 1, seed=4, device="cuda:0")
+    tk = {n: toks[n][0].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda:0")
+
+    def step():
+        kda.recurrent_step(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S, out=o)
+
+    t_eager, _ = time_launches(step, steps * per_graph // 4, warmup)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            step()
+    t_graph, _ = time_launches(graph.replay, max(steps // 4, 5), 2)
+    return {"workload": f"kda_recurrent_step {N}x{H} heads (one decode step of a single sequence)",
+            "eager_us_per_step": round(t_eager * 1e6, 2),
+            "graph_us_per_step": round(t_graph / per_graph * 1e6, 2),
+            "steps_per_graph": per_graph}
+
+
 def layer_line(steps, warmup):
     """The full token-mixing layer (projections, conv/activations, gates, KDA,
     gated RMSNorm, output projection) on the 32768-token, d_model 2048, 16-head
@@ -347,6 +376,7 @@ def main():
 
     if args.workload == "decode":
         dec = decode_line(args.steps, args.warmup)
+        dec["small_batch"] = decode_latency_line(args.steps, args.warmup)
         print(json.dumps({"metric": "KDA decode state GB/s", **dec}))
         return
 
@@ -377,6 +407,7 @@ def main():
     }
     if args.workload is None and not args.no_decode:
         line["decode"] = decode_line(max(args.steps, 20), args.warmup)
+        line["decode"]["small_batch"] = decode_latency_line(max(args.steps, 20), args.warmup)
     if args.workload is None and not args.no_layer:
         line["layer"] = layer_line(min(args.steps, 20), args.warmup)
     if args.workload is None and not args.no_gates:

@@ -13,7 +13,7 @@ import ctypes
 from ._binding import (KDA_BF16, KDA_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,  # noqa: F401
                        KDA_GATE_NONE, LAYER_REGIONS, KDAError, lib, status_string, version, _check)
 
-__all__ = ["chunk_fwd", "chunk_bwd", "bwd_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "bwd_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
            "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS",
            "status_string", "version", "KDAError",
            "KDA_F32", "KDA_BF16", "lib"]
@@ -123,6 +123,42 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out=None, S_T=None,
                                    _ptr(S0), _ptr(out), _ptr(S_T), B, T, H, dk, dv, code,
                                    ws_ptr, ws_bytes, _stream(dev))
     _check("kda_chunk_fwd_gated", st)
+    return out, S_T
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, out=None, S_T=None,
+                     return_state: bool = True):
+    """Chunked prefill over sequences packed along one token axis.  q, k, v:
+    [total, H, 128]; log_alpha: [total, H, 128] / [total, H] fp32 or None (gate
+    as for chunk_fwd); beta: [total, H]; cu_seqlens: int32 device tensor
+    [num_seqs + 1] of sequence offsets; S0: [num_seqs, H, 128, 128] fp32 or
+    None.  Returns ``(o, S_T)``; S_T is [num_seqs, H, 128, 128]."""
+    import torch
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    ns = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (ns + 1,), dev)
+    for t, n, shp in ((k, "k", q.shape), (v, "v", (total, H, dv)), (beta, "beta", (total, H))):
+        _need(t, n, dt, shp, dev)
+    gate = _gate(log_alpha, 3)
+    if gate != KDA_GATE_NONE:
+        _need(log_alpha, "log_alpha", torch.float32, q.shape if gate == KDA_GATE_CHANNEL else (total, H), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (ns, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((total, H, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (total, H, dv), dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((ns, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _need(S_T, "S_T", torch.float32, (ns, H, dk, dv), dev)
+    st = lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), gate, _ptr(beta),
+                                    _ptr(cu_seqlens), ns, _ptr(S0), _ptr(out), _ptr(S_T),
+                                    total, H, dk, dv, code, _stream(dev))
+    _check("kda_chunk_fwd_varlen", st)
     return out, S_T
 
 

@@ -29,6 +29,8 @@ SIGNATURES = {
     "kda_chunk_fwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "kda_chunk_fwd_gated": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP,
                                  _I, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
+    "kda_chunk_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _I, _VP, _VP, _VP,
+                                  _I, _I, _I, _I, _I, _VP]),
     "kda_recurrent_step_gated": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP,
                                       _I, _I, _I, _I, _I, _VP]),
     "kda_chunk_bwd": (_I, [_VP] * 14 + [_I] * 6 + [_VP, _SZ, _VP]),

@@ -217,6 +217,57 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v,
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                         const float* log_alpha, int gate, const void* beta,
+                         const int32_t* cu_seqlens, int num_seqs, const float* S0,
+                         void* o, float* S_T, int total_tokens, int H, int dk, int dv,
+                         int dtype, void* stream)
+{
+    if (num_seqs < 0 || total_tokens < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED;
+    if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if ((long long)num_seqs * H == 0) return KDA_OK;
+
+    bool ok = true;
+    const size_t es = elem_size(dtype);
+    const size_t tok = mul3(total_tokens, H, 1, &ok);
+    const size_t heads = mul3(num_seqs, H, 1, &ok);
+    const size_t n_qk = mul3((long long)tok, kHeadDim, 1, &ok);
+    const size_t n_state = mul3((long long)heads, kHeadDim, kHeadDim, &ok);
+    if (!ok) return KDA_ERR_UNSUPPORTED;
+    if (heads * 8 > (size_t)INT_MAX) return KDA_ERR_UNSUPPORTED;   // grid size
+
+    int rc;
+    if ((rc = check_ptr(cu_seqlens, 4)) != KDA_OK) return rc;
+    if (gate == KDA_GATE_NONE && log_alpha) return KDA_ERR_INVALID_ARG;
+    if (S0 && (rc = check_ptr(S0, 16)) != KDA_OK) return rc;
+    if (S_T && (rc = check_ptr(S_T, 16)) != KDA_OK) return rc;
+    const size_t g_bytes = gate == KDA_GATE_CHANNEL ? n_qk * 4 : gate == KDA_GATE_HEAD ? tok * 4 : 0;
+    const Range rS0{S0, S0 ? n_state * 4 : 0}, rST{S_T, S_T ? n_state * 4 : 0};
+    const Range rcu{cu_seqlens, ((size_t)num_seqs + 1) * 4};
+    if (total_tokens > 0) {
+        if ((rc = check_ptr(q, 16)) || (rc = check_ptr(k, 16)) || (rc = check_ptr(v, 16)) ||
+            (gate != KDA_GATE_NONE && (rc = check_ptr(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4))) ||
+            (rc = check_ptr(beta, es)) || (rc = check_ptr(o, 16)))
+            return rc;
+    }
+    const Range in[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, g_bytes},
+                        {beta, tok * es}, rS0, rcu};
+    const Range ro{total_tokens > 0 ? o : nullptr, n_qk * es};
+    for (const Range& r : in)
+        if (overlap(ro, r)) return KDA_ERR_INVALID_ARG;
+    if (overlap(ro, rST)) return KDA_ERR_INVALID_ARG;
+    for (int i = 0; i < 5; ++i)
+        if (overlap(rST, in[i])) return KDA_ERR_INVALID_ARG;
+    if (overlap(rST, rcu)) return KDA_ERR_INVALID_ARG;
+    if (overlap(rS0, rST) && (const void*)S0 != (const void*)S_T) return KDA_ERR_INVALID_ARG;
+
+    hipError_t e = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, S0, o, S_T, num_seqs, total_tokens, H,
+                                         dtype, nullptr, (hipStream_t)stream, gate, cu_seqlens);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_recurrent_step(const void* q, const void* k, const void* v,
                        const float* log_alpha, const void* beta, float* S,
                        void* o, int N, int H, int dk, int dv, int dtype,

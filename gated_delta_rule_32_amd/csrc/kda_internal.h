@@ -18,11 +18,14 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v,
 // `ws` non-null (bf16 only, at least chunk_ws_bytes(B, T, H) bytes) the
 // two-kernel schedule runs; otherwise the fused single kernel.  `gate` is a
 // kda_gate_t: g is [B, T, H, 128] (per channel), [B, T, H] (per head) or
-// unused (no decay).
+// unused (no decay).  With cu_seqlens (device, B + 1 entries) the B
+// "batches" are sequences packed along one token axis of T tokens (fused
+// kernel, `ws` ignored).
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             const float* g, const void* beta, const float* S0,
                             void* o, float* S_T, int B, int T, int H, int dtype,
-                            void* ws, hipStream_t stream, int gate = KDA_GATE_CHANNEL);
+                            void* ws, hipStream_t stream, int gate = KDA_GATE_CHANNEL,
+                            const int* cu_seqlens = nullptr);
 
 // Bytes of workspace the two-kernel schedule needs: one 72,704-byte block of
 // key-side operands per (batch, head, 64-token chunk).

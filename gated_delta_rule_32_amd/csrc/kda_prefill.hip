@@ -132,6 +132,10 @@ constexpr int PREP_CHUNKS = 4;                      // chunks per prep workgroup
 // transposes Aqk^T, Tm^T, Qt^T, Kh^T and Kt = Diag(e^{G_64}) Kb, layout
 // WSB_* in kda_chunk_common.h).
 //
+// With cu_seqlens (fused kernel only), batch index b is a sequence packed
+// along one token axis of T tokens: tokens cu_seqlens[b] .. cu_seqlens[b+1]
+// (clamped to [0, T]), chunked from its own first token.
+//
 // GATE selects the forget gate: GATE_CHANNEL (KDA, g [B, T, H, 128]),
 // GATE_HEAD (one decay per head and token, g [B, T, H]: Gated DeltaNet) or
 // GATE_NONE (alpha = 1: DeltaNet, g unused).  With one decay per row the
@@ -139,8 +143,8 @@ constexpr int PREP_CHUNKS = 4;                      // chunks per prep workgroup
 template <typename E, int DV, bool PREP, bool BWD = false, int GATE = GATE_CHANNEL>
 __global__ void __launch_bounds__(NT)
 chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* beta,
-                 const float* S0, E* o, float* S_T, int T, int H, int nsplit, char* ws,
-                 char* wsb)
+                 const float* S0, E* o, float* S_T, int T_axis, int H, int nsplit, char* ws,
+                 char* wsb, const int* cu_seqlens)
 {
     // (No __restrict__ on the inputs: the LDS barriers are asm statements with
     // a memory clobber, and without restrict the compiler keeps the prefetch
@@ -186,27 +190,36 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     const int vg = t % In::VL, vr = t / In::VL; // 8-channel group and row group for v
     const int ln = lane & 15, lg = lane >> 4;
 
-    const int nchunks = (T + C - 1) / C;
     // Workgroup -> (head, slice), keeping the slices of a head on one XCD
     // (workgroups are dealt to the 8 XCDs round-robin); prep: (head, chunk).
     const int nwg = gridDim.x, w = blockIdx.x;
     const int lid = (!PREP && nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
-    const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;   // prep: chunk groups per head
+    const int nblk = ((T_axis + C - 1) / C + PREP_CHUNKS - 1) / PREP_CHUNKS;   // prep: chunk groups per head
     const int head = PREP ? lid / nblk : lid / nsplit;
     const int slice = PREP ? 0 : lid % nsplit;
     const int b = head / H, h = head % H;
     const int j0 = slice * DV;
+    // this head's tokens: T of them from token index seq0 of the token axis
+    size_t seq0 = (size_t)b * T_axis;
+    int T = T_axis;
+    if (!PREP && cu_seqlens) {
+        const int s0 = min(max(cu_seqlens[b], 0), T_axis);
+        const int s1 = min(max(cu_seqlens[b + 1], s0), T_axis);
+        seq0 = (size_t)s0;
+        T = s1 - s0;
+    }
+    const int nchunks = (T + C - 1) / C;
     const int n_first = PREP ? (lid % nblk) * PREP_CHUNKS : 0;
     const int n_end = PREP ? min(n_first + PREP_CHUNKS, nchunks) : nchunks;
 
     const size_t tokstride = (size_t)H * DK;                       // one token, all heads
-    const size_t hbase = ((size_t)b * T * H + h) * DK;             // (b, t=0, h, 0)
+    const size_t hbase = (seq0 * H + h) * DK;                      // (b, t=0, h, 0)
     const size_t sbase = (size_t)head * DK * DK;                   // state of this head
 
     // Prefetch of one chunk into registers.  Branch-free: rows past T read the
     // last valid token (always in bounds) and are zeroed when consumed, so no
     // load result is needed before the next chunk starts.
-    const E* betap = beta + (size_t)b * T * H + h;
+    const E* betap = beta + seq0 * H + h;
     auto load_chunk = [&](int n, In& in) {
         const int tok0 = n * C;
 #pragma unroll
@@ -214,7 +227,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
             const int tok = min(tok0 + RPT * wave + RPL * rq + i, T - 1);
             const size_t off = hbase + (size_t)tok * tokstride + 8 * cg;
             if constexpr (GATE == GATE_CHANNEL) in.g[i].load(g + off);
-            else if constexpr (GATE == GATE_HEAD) in.gh[i] = g[((size_t)b * T + tok) * H + h];
+            else if constexpr (GATE == GATE_HEAD) in.gh[i] = g[(seq0 + tok) * H + h];
             in.q[i].load(q + off);
             in.k[i].load(k + off);
         }
@@ -246,7 +259,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     if constexpr (!PREP) write_state_lds();
 
     In in;
-    load_chunk(n_first, in);
+    if (n_first < n_end) load_chunk(n_first, in);   // (an empty sequence has no tokens to read)
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
     for (int n = n_first; n < n_end; ++n) {
@@ -972,30 +985,32 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
 
 template <typename E, int DV, int GATE>
 void launch_one(const void* q, const void* k, const void* v, const float* g, const void* beta,
-                const float* S0, void* o, float* S_T, int B, int T, int H, hipStream_t stream)
+                const float* S0, void* o, float* S_T, int B, int T, int H, hipStream_t stream,
+                const int* cu_seqlens = nullptr)
 {
     const int nsplit = DK / DV;
     const unsigned nwg = (unsigned)((long long)B * H * nsplit);
     hipLaunchKernelGGL((chunk_fwd_kernel<E, DV, false, false, GATE>), dim3(nwg), dim3(NT), 0, stream,
                        (const E*)q, (const E*)k, (const E*)v, g, (const E*)beta, S0, (E*)o, S_T,
-                       T, H, nsplit, (char*)nullptr, (char*)nullptr);
+                       T, H, nsplit, (char*)nullptr, (char*)nullptr, cu_seqlens);
 }
 
 template <int GATE>
 void launch_gate(const void* q, const void* k, const void* v, const float* g, const void* beta,
                  const float* S0, void* o, float* S_T, int B, int T, int H, int dtype, void* ws,
-                 hipStream_t stream)
+                 hipStream_t stream, const int* cu)
 {
     const long long heads = (long long)B * H;
     if (dtype == 0) {
         // fp32 operands need the narrowest slice to fit the LDS budget
-        launch_one<float, 16, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+        launch_one<float, 16, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream, cu);
     } else if (ws) {
         const int nchunks = (T + C - 1) / C;
         const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
         hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true, false, GATE>), dim3((unsigned)(heads * nblk)),
                            dim3(NT), 0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
-                           (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws, (char*)nullptr);
+                           (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws, (char*)nullptr,
+                           (const int*)nullptr);
         // value columns per scan workgroup: enough workgroups to cover the machine
         const int ncw = heads * 4 >= 256 ? 2 : 1;
 #define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, false>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
@@ -1005,11 +1020,11 @@ void launch_gate(const void* q, const void* k, const void* v, const float* g, co
         else KDA_SCAN(1);
 #undef KDA_SCAN
     } else if (heads * 2 >= 256) {
-        launch_one<bf16_t, 64, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+        launch_one<bf16_t, 64, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream, cu);
     } else if (heads * 4 >= 256) {
-        launch_one<bf16_t, 32, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+        launch_one<bf16_t, 32, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream, cu);
     } else {
-        launch_one<bf16_t, 16, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream);
+        launch_one<bf16_t, 16, GATE>(q, k, v, g, beta, S0, o, S_T, B, T, H, stream, cu);
     }
 }
 
@@ -1038,7 +1053,7 @@ hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, 
     const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
     hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true, true>), dim3((unsigned)(heads * nblk)), dim3(NT), 0,
                        stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g, (const bf16_t*)beta, S0,
-                       (bf16_t*)nullptr, (float*)nullptr, T, H, 1, ws_fwd, ws_bwd);
+                       (bf16_t*)nullptr, (float*)nullptr, T, H, 1, ws_fwd, ws_bwd, (const int*)nullptr);
     const int ncw = heads * 4 >= 256 ? 2 : 1;
 #define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, true>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
                                          dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws_fwd, (const bf16_t*)v, S0, \
@@ -1051,11 +1066,16 @@ hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, 
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                             const void* beta, const float* S0, void* o, float* S_T,
-                            int B, int T, int H, int dtype, void* ws, hipStream_t stream, int gate)
+                            int B, int T, int H, int dtype, void* ws, hipStream_t stream, int gate,
+                            const int* cu_seqlens)
 {
-    if (gate == GATE_HEAD) launch_gate<GATE_HEAD>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream);
-    else if (gate == GATE_NONE) launch_gate<GATE_NONE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream);
-    else launch_gate<GATE_CHANNEL>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream);
+    if (cu_seqlens) ws = nullptr;   // packed sequences: fused kernel
+    if (gate == GATE_HEAD)
+        launch_gate<GATE_HEAD>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens);
+    else if (gate == GATE_NONE)
+        launch_gate<GATE_NONE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens);
+    else
+        launch_gate<GATE_CHANNEL>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens);
     return hipGetLastError();
 }
 

@@ -125,6 +125,34 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill over variable-length sequences packed along one token axis
+ * (serving batches).  Sequence s is tokens cu_seqlens[s] .. cu_seqlens[s+1]-1
+ * of total_tokens; it is chunked from its own first token and has its own
+ * initial and final state, exactly as one kda_chunk_fwd_gated call per
+ * sequence would compute it.
+ *
+ *   q, k         [total_tokens, H, dk]  dtype
+ *   v, o         [total_tokens, H, dv]  dtype   (o: out)
+ *   log_alpha    [total_tokens, H, dk] / [total_tokens, H] fp32 / NULL, by gate
+ *   beta         [total_tokens, H]      dtype
+ *   cu_seqlens   [num_seqs + 1]         int32, DEVICE memory, non-decreasing
+ *                from 0 to total_tokens.  Not read by the host; the kernel
+ *                clamps each entry to [0, total_tokens] (and each end to at
+ *                least its start), so no offset can address outside the
+ *                buffers; tokens outside every sequence get no output.
+ *   S0, S_T      [num_seqs, H, dk, dv]  fp32   (S0 NULL = zeros; S_T NULL =
+ *                not written; S_T == S0 updates in place)
+ * Runs the fused kernel (no workspace).  num_seqs * H = 0 is a no-op.
+ * Errors as for kda_chunk_fwd_gated; cu_seqlens must be 4-byte aligned and
+ * must not overlap an output.
+ */
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                         const float* log_alpha, int gate, const void* beta,
+                         const int32_t* cu_seqlens, int num_seqs, const float* S0,
+                         void* o, float* S_T, int total_tokens, int H, int dk, int dv,
+                         int dtype, void* stream);
+
+/*
  * Workspace bytes that kda_chunk_fwd should be given for the fastest schedule
  * on this shape: B * H * ceil(T / 64) * 72704 when the two-kernel schedule is
  * expected to win (bf16 with fewer than 128 heads in total), else 0 (the fused

@@ -34,7 +34,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_bwd",
-                          "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated",
+                          "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated", "kda_chunk_fwd_varlen",
                           "kda_recurrent_step_gated", "kda_recurrent_step",
                           "kda_layer_fwd", "kda_layer_workspace_layout",
                           "kda_status_string", "kda_version"}
@@ -256,3 +256,25 @@ def test_gated_entry_points_reject(lib):
     assert step_g(lib, GATE_HEAD, N=0) == OK
     # T = 0 without S_T touches nothing, whatever the gate
     assert chunk_g(lib, GATE_NONE, g=None, T=0, q=None, k=None, v=None, beta=None, o=None, ST=None) == OK
+
+
+# ------------------------------------------------------ packed sequences
+def varlen(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, gate=0, beta=P + 2**27, cu=P + 2**30,
+           ns=2, S0=None, o=P + 2**28, ST=P + 2**29, total=100, H=1, dt=BF16):
+    return lib.kda_chunk_fwd_varlen(q, k, v, g, gate, beta, cu, ns, S0, o, ST, total, H, 128, 128, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), INVALID), (dict(cu=P + 2**30 + 2), ALIGN), (dict(ns=-1), INVALID),
+    (dict(total=-5), INVALID), (dict(gate=5), UNSUP), (dict(dt=9), UNSUP),
+    (dict(gate=2), INVALID),                     # no decay: log_alpha must be NULL
+    (dict(o=P + 2**30), INVALID),                # o overlaps cu_seqlens
+    (dict(ST=P + 2**30 - 64), INVALID),          # S_T overlaps cu_seqlens
+    (dict(q=P + 8), ALIGN), (dict(o=None), INVALID),
+])
+def test_varlen_rejects(lib, kw, code):
+    assert varlen(lib, **kw) == code
+
+
+def test_varlen_noop(lib):
+    assert varlen(lib, ns=0) == OK and varlen(lib, H=0) == OK
