@@ -15,13 +15,15 @@ head-tokens per second (B*T*H / time).  The JSON line also carries:
     tokens), its time, the KDA operator's share and the achieved TFLOP/s;
   * gate_variants: the same prefill with one decay per head and token (Gated
     DeltaNet) and with no decay (DeltaNet), through kda_chunk_fwd_gated;
+  * full_attention_decode: the decode step of a NoPE MLA layer (MQA over a
+    512-wide latent) at 1M tokens, and per sequence and layer against KDA's;
   * backward: kda_chunk_bwd on the prefill workload (incoming gradients dL/do
     ~ N(0,1), dL/dS_T = 0), head-tokens/s, compulsory-HBM-bytes rate, and the
     gradient oracle timed on the host cores on the same workload;
   * cpu_baseline: the fp64 oracle timed on the host cores on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload c3|c1|decode|layer|bwd|gdn|deltanet  (single-workload lines, for profiling)
+       python bench.py --workload c3|c1|decode|layer|bwd|gdn|deltanet|mqa  (single-workload lines, for profiling)
        python bench.py --copy-calibration       (plain copy kernel for counter scaling)
 """
 from __future__ import annotations
@@ -228,6 +230,42 @@ def decode_latency_line(steps, warmup, N=1, H=32, per_graph=32):
             "steps_per_graph": per_graph}
 
 
+def mqa_line(steps, warmup, kda_decode=None):
+    """Full-attention decode step at 1M context (MQA over a 512-wide bf16
+    latent, the inference form of a NoPE MLA layer), and the comparison with
+    KDA's decode step that the pages make at the model level."""
+    import math
+    import torch
+    import gated_delta_rule_32_amd as kda
+    from gated_delta_rule_32_amd import inputs
+
+    cfg = inputs.MQA_CONFIG
+    B, T, H, Dc = cfg["B"], cfg["T"], cfg["H"], cfg["D"]
+    log(f"[bench] mqa decode: B={B} T={T} H={H} D={Dc}")
+    q, c = inputs.mqa_inputs(B, T, H, D=Dc, seed=cfg["seed"], device="cuda:0")
+    o = torch.empty((B, H, Dc), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(int(kda.lib().kda_mqa_decode_workspace_size(B, T, H, Dc)), dtype=torch.uint8,
+                     device="cuda:0")
+    scale = 1.0 / math.sqrt(Dc)
+    t, _ = time_launches(lambda: kda.mqa_decode(q, c, scale, out=o, workspace=ws), steps, warmup)
+    alg = B * T * Dc * 2 + 2 * B * H * Dc * 2
+    out = {"workload": f"kda_mqa_decode B={B} T={T} H={H} latent {Dc} bf16 (NoPE MLA as MQA)",
+           "us_per_step": round(t * 1e6, 2), "alg_bytes_per_step": alg,
+           "gb_s": round(alg / t / 1e9, 1), "frac_of_hbm_peak": round(alg / t / 1e9 / HBM_PEAK_GBS, 4)}
+    if kda_decode is not None:
+        # per sequence and layer: KDA's step amortised over the 256-sequence
+        # batch, against this step for one sequence at 1M tokens
+        t_kda = kda_decode["us_per_step"] / inputs.DECODE_CONFIG["N"]
+        t_mla = out["us_per_step"] / B
+        out["per_sequence_layer_us"] = {"kda": round(t_kda, 3), "full_attention_1m": round(t_mla, 2)}
+        # a 3:1 hybrid group (3 KDA + 1 full-attention layer) against 4
+        # full-attention layers: token-mixing time and cache per sequence
+        out["hybrid_3to1_vs_full_attention"] = {
+            "token_mixing_time_ratio": round(4 * t_mla / (t_mla + 3 * t_kda), 2),
+            "cache_saving": round(1 - (T * Dc * 2 + 3 * 32 * STATE_BYTES) / (4 * T * Dc * 2), 4)}
+    return out
+
+
 def layer_line(steps, warmup):
     """The full token-mixing layer (projections, conv/activations, gates, KDA,
     gated RMSNorm, output projection) on the 32768-token, d_model 2048, 16-head
@@ -346,7 +384,8 @@ def main():
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-gates", action="store_true")
-    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer", "bwd", "gdn", "deltanet"],
+    ap.add_argument("--no-mqa", action="store_true")
+    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer", "bwd", "gdn", "deltanet", "mqa"],
                     default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--schedule", choices=["auto", "fused", "two_kernel"], default="auto",
@@ -385,6 +424,10 @@ def main():
         print(json.dumps({"metric": "KDA backward head-tokens/s", **bwd}))
         return
 
+    if args.workload == "mqa":
+        print(json.dumps({"metric": "full-attention decode step", **mqa_line(args.steps, args.warmup)}))
+        return
+
     if args.workload == "layer":
         lay = layer_line(args.steps, args.warmup)
         print(json.dumps({"metric": "KDA layer tokens/s", **lay}))
@@ -408,6 +451,8 @@ def main():
     if args.workload is None and not args.no_decode:
         line["decode"] = decode_line(max(args.steps, 20), args.warmup)
         line["decode"]["small_batch"] = decode_latency_line(max(args.steps, 20), args.warmup)
+    if args.workload is None and not args.no_mqa:
+        line["full_attention_decode"] = mqa_line(max(args.steps, 20), args.warmup, line.get("decode"))
     if args.workload is None and not args.no_layer:
         line["layer"] = layer_line(min(args.steps, 20), args.warmup)
     if args.workload is None and not args.no_gates:

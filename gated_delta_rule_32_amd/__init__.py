@@ -14,7 +14,7 @@ from ._binding import (KDA_BF16, KDA_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,  # no
                        KDA_GATE_NONE, LAYER_REGIONS, KDAError, lib, status_string, version, _check)
 
 __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "bwd_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
-           "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS",
+           "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS", "mqa_decode",
            "status_string", "version", "KDAError",
            "KDA_F32", "KDA_BF16", "lib"]
 
@@ -160,6 +160,30 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, out=None,
                                     total, H, dk, dv, code, _stream(dev))
     _check("kda_chunk_fwd_varlen", st)
     return out, S_T
+
+
+def mqa_decode(q, cache, scale, *, out=None, workspace=None):
+    """Full-attention decode step (MQA over a shared latent: the inference form
+    of a NoPE MLA layer).  q [B, H, 512] bf16, cache [B, T, 512] bf16; returns
+    o [B, H, 512] bf16 = softmax(scale q c^T) c per head."""
+    import torch
+    B, H, D = q.shape
+    T = cache.shape[1]
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, H, D), dev)
+    _need(cache, "cache", torch.bfloat16, (B, T, D), dev)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, (B, H, D), dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib().kda_mqa_decode_workspace_size(B, T, H, D)))
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().kda_mqa_decode(_ptr(q), _ptr(cache), _ptr(out), B, T, H, D, float(scale),
+                              ws_ptr, ws_bytes, _stream(dev))
+    _check("kda_mqa_decode", st)
+    return out
 
 
 def bwd_workspace_size(B, T, H, d=128):

@@ -39,6 +39,8 @@ SIGNATURES = {
                                 _I, _I, _I, _I, _I, _VP]),
     "kda_layer_fwd": (_I, [_VP] * 13 + [_I] * 5 + [_VP, _SZ, _VP]),
     "kda_layer_workspace_layout": (_SZ, [_I] * 5 + [ctypes.POINTER(_SZ)]),
+    "kda_mqa_decode": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _VP, _SZ, _VP]),
+    "kda_mqa_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "kda_status_string": (ctypes.c_char_p, [_I]),
     "kda_version": (ctypes.c_char_p, []),
 }

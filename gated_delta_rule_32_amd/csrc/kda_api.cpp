@@ -314,6 +314,35 @@ int kda_recurrent_step_gated(const void* q, const void* k, const void* v,
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+size_t kda_mqa_decode_workspace_size(int B, int T, int H, int D)
+{
+    if (B < 0 || T < 1 || T > (1 << 22) || (H != 16 && H != 32) || D != 512) return 0;
+    return kda::mqa_ws_bytes(B, T, H);
+}
+
+int kda_mqa_decode(const void* q, const void* cache, void* o, int B, int T, int H, int D,
+                   float scale, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+    if (D != 512 || (H != 16 && H != 32)) return KDA_ERR_UNSUPPORTED;
+    if (B == 0) return KDA_OK;
+    if (T < 1) return KDA_ERR_INVALID_ARG;
+    bool ok = true;
+    const size_t nq = mul3(B, H, D, &ok) * 2;
+    const size_t nc = mul3(B, T, D, &ok) * 2;
+    if (!ok || B > 65535 || T > (1 << 22)) return KDA_ERR_UNSUPPORTED;   // at most 1024 splits of 4096
+    int rc;
+    if ((rc = check_ptr(q, 16)) || (rc = check_ptr(cache, 16)) || (rc = check_ptr(o, 16))) return rc;
+    const size_t need = kda::mqa_ws_bytes(B, T, H);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
+    const Range rq{q, nq}, rc_{cache, nc}, ro{o, nq}, rw{workspace, need};
+    if (overlap(ro, rq) || overlap(ro, rc_) || overlap(ro, rw) || overlap(rw, rq) || overlap(rw, rc_))
+        return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda::launch_mqa_decode(q, cache, o, B, T, H, scale, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 size_t kda_layer_workspace_layout(int B, int T, int d_model, int H, int rank, size_t* offsets)
 {
     if (B < 0 || T < 0 || H <= 0 || d_model <= 0 || rank <= 0) return 0;

@@ -64,6 +64,12 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const f
                             void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dS0,
                             int B, int T, int H, char* ws, hipStream_t stream);
 
+// Full-attention (MQA over a 512-wide latent) decode step, split over the
+// cache: mqa_ws_bytes of scratch for the per-split partial results.
+size_t mqa_ws_bytes(long long B, long long T, long long H);
+hipError_t launch_mqa_decode(const void* q, const void* cache, void* o, int B, int T, int H, float scale,
+                             void* ws, hipStream_t stream);
+
 // S_T = S0 (or zeros when S0 is NULL) for `heads` states; used when T = 0.
 hipError_t launch_state_copy(const float* S0, float* S_T, long long heads,
                              hipStream_t stream);

@@ -92,6 +92,20 @@ def grad_inputs(B, T, H, dtype="bfloat16", ds_std=0.0, seed=0, d=D):
     return dict(dO=dO, dS_T=dST)
 
 
+MQA_CONFIG = dict(B=1, T=1 << 20, H=32, D=512, seed=6)
+
+
+def mqa_inputs(B, T, H, D=512, seed=0, device="cpu"):
+    """Query heads and latent cache of a full-attention decode step: q [B, H, D]
+    and cache [B, T, D], both N(0, 1) rounded to bf16 (torch generator on
+    `device`, so a 1M-token cache is drawn where it is used)."""
+    import torch
+    gen = torch.Generator(device=device).manual_seed(seed)
+    q = torch.randn((B, H, D), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    cache = torch.randn((B, T, D), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return q, cache
+
+
 def prefill_config(name, **override):
     """Inputs of a named prefill workload; keyword overrides (e.g. T=...)."""
     cfg = dict(PREFILL_CONFIGS[name])

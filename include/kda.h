@@ -296,6 +296,29 @@ int kda_layer_fwd(const void* x, const void* W_q, const void* W_k, const void* W
  */
 size_t kda_layer_workspace_layout(int B, int T, int d_model, int H, int rank, size_t* offsets);
 
+/*
+ * Decode step of a full-attention layer with no position encoding -- the
+ * reference KDA's decode is compared against.  Page "Kimi K3论文：Kimi
+ * Linear", section 5: the hybrid's full-attention layers are MLA without
+ * position encoding, which at inference runs as MQA over a per-token latent;
+ * section 7 compares decode time per output token at 1M context.  For every
+ * query head h of sequence b, with the latent c_t as key and value:
+ *
+ *     o[b,h,:] = sum_t softmax_t(scale * q[b,h,:] . c[b,t,:]) c[b,t,:]
+ *
+ *   q      [B, H, D]  bf16      cache  [B, T, D]  bf16      o  [B, H, D]  bf16 out
+ * D must be 512 and H 16 or 32, 1 <= T <= 2^22 (else KDA_ERR_UNSUPPORTED or
+ * KDA_ERR_INVALID_ARG for T < 1).
+ * workspace: at least kda_mqa_decode_workspace_size(B, T, H, D) bytes,
+ * 256-byte aligned (per-split partial results).  B = 0 is a no-op.  o must not
+ * overlap q, the cache or the workspace.
+ */
+int kda_mqa_decode(const void* q, const void* cache, void* o, int B, int T, int H, int D,
+                   float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kda_mqa_decode needs (0 for invalid or unsupported sizes). */
+size_t kda_mqa_decode_workspace_size(int B, int T, int H, int D);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* kda_status_string(int status);
 

@@ -35,6 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_bwd",
                           "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated", "kda_chunk_fwd_varlen",
+                          "kda_mqa_decode", "kda_mqa_decode_workspace_size",
                           "kda_recurrent_step_gated", "kda_recurrent_step",
                           "kda_layer_fwd", "kda_layer_workspace_layout",
                           "kda_status_string", "kda_version"}
@@ -278,3 +279,31 @@ def test_varlen_rejects(lib, kw, code):
 
 def test_varlen_noop(lib):
     assert varlen(lib, ns=0) == OK and varlen(lib, H=0) == OK
+
+
+# ------------------------------------------------- full-attention decode
+def mqa(lib, q=P, c=P + 2**24, o=P + 2**34, B=1, T=100, H=32, D=512, ws=P + 2**35, wsb=1 << 20):
+    return lib.kda_mqa_decode(q, c, o, B, T, H, D, 0.04, ws, wsb, None)
+
+
+def test_mqa_workspace_size(lib):
+    f = lib.kda_mqa_decode_workspace_size
+    assert f(1, 1 << 20, 32, 512) == 256 * 32 * 512 * 4 + 256 * 32 * 2 * 4
+    assert f(2, 100, 16, 512) == 2 * 16 * 512 * 4 + 256
+    assert f(1, 0, 32, 512) == 0 and f(1, 10, 24, 512) == 0 and f(1, 10, 32, 256) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(c=None), INVALID), (dict(o=None), INVALID), (dict(ws=None), INVALID),
+    (dict(B=-1), INVALID), (dict(T=0), INVALID), (dict(H=24), UNSUP), (dict(D=128), UNSUP),
+    (dict(T=(1 << 22) + 1), UNSUP),
+    (dict(q=P + 4), ALIGN), (dict(ws=P + 2**35 + 64), ALIGN), (dict(wsb=100), INVALID),
+    (dict(o=P + 2**24 + 64), INVALID),           # o inside the cache
+    (dict(ws=P), INVALID),                       # workspace overlaps q
+])
+def test_mqa_rejects(lib, kw, code):
+    assert mqa(lib, **kw) == code
+
+
+def test_mqa_noop(lib):
+    assert lib.kda_mqa_decode(None, None, None, 0, 100, 32, 512, 0.1, None, 0, None) == OK
