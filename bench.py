@@ -415,7 +415,6 @@ def main():
 
     if args.workload == "decode":
         dec = decode_line(args.steps, args.warmup)
-        dec["small_batch"] = decode_latency_line(args.steps, args.warmup)
         print(json.dumps({"metric": "KDA decode state GB/s", **dec}))
         return
 
