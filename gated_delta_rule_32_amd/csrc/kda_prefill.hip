@@ -769,9 +769,10 @@ template <int NCW> struct ScanCfg {                       // NCW consumer waves
     static_assert(C * VG <= 256, "one V / output unit per lane of the first four loader waves");
 };
 
-// SAVE (the forward part of the backward pass): no output; instead each
-// chunk's entry state S_n [128][128], Y = V - Kh S_n [64][128] and Vn
-// [64][128] are written in bf16 to svS / svY / svVn, indexed (head, chunk).
+// SAVE (the forward part of the backward pass): no output (Qt S and Aqk Vn
+// are skipped); instead each chunk's entry state S_n [128][128],
+// Y = V - Kh S_n [64][128] and Vn [64][128] are written in bf16 to svS / svY /
+// svVn, indexed (head, chunk).
 template <int NCW, bool SAVE>
 __global__ void __launch_bounds__(ScanCfg<NCW>::NT)
 chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
@@ -877,12 +878,16 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             bf16x8 sb[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) sb[p] = cat8(to_bf16x4(acc_s[2 * p]), to_bf16x4(acc_s[2 * p + 1]));
-            bf16x8 fa[2][8];
-            auto frags = [&](int Rb, bf16x8 (&f)[8]) {
+            constexpr int NF = SAVE ? 4 : 8;          // Kh (and Qt) fragments per block
+            bf16x8 fa[2][NF];
+            auto frags = [&](int Rb, bf16x8 (&f)[NF]) {
                 const bf16_t* kr = sKh + (16 * Rb + ln) * WS_P128;
                 const bf16_t* qr = sQt + (16 * Rb + ln) * WS_P128;
 #pragma unroll
-                for (int p = 0; p < 4; ++p) { f[p] = a_pair(kr, p, lg, true); f[4 + p] = a_pair(qr, p, lg, true); }
+                for (int p = 0; p < 4; ++p) {
+                    f[p] = a_pair(kr, p, lg, true);
+                    if constexpr (!SAVE) f[4 + p] = a_pair(qr, p, lg, true);
+                }
             };
             f32x4 pk[4], qs[4];
             frags(0, fa[0]);
@@ -893,12 +898,13 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[Rb & 1][p], sb[p], a, 0, 0, 0);
-                    c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[Rb & 1][4 + p], sb[p], c2, 0, 0, 0);
+                    if constexpr (!SAVE)
+                        c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[Rb & 1][4 + p], sb[p], c2, 0, 0, 0);
                 }
                 pk[Rb] = a;
                 qs[Rb] = c2;
-                if (Rb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                if (Rb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
             }
 
             // Z = V - P (V^T read in the B layout), Vn = Tm Z (lower blocks only)
@@ -933,6 +939,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             }
 
             // O = Qt S + Aqk Vn -> LDS staging (stored to HBM by the loaders)
+            if constexpr (!SAVE)
 #pragma unroll
             for (int Rb = 0; Rb < 4; ++Rb) {
                 f32x4 a = qs[Rb];
