@@ -303,14 +303,16 @@ def layer_line(steps, warmup):
             "frac_of_bf16_peak": round((gemm_flops + kda_flops) / t_layer / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
 
-def backward_line(steps, warmup, with_cpu=False):
-    """kda_chunk_bwd on the B = 8, H = 16, T = 4096 prefill workload."""
+def backward_line(steps, warmup, with_cpu=False, wl="c2"):
+    """kda_chunk_bwd on the B = 8, H = 16, T = 4096 prefill workload (or, with
+    wl = "gdn" / "deltanet", the same shape with the other two gates)."""
     import torch
     import gated_delta_rule_32_amd as kda
     from gated_delta_rule_32_amd import inputs
 
-    name = WORKLOADS["c2"]
+    name = WORKLOADS[wl]
     cfg = inputs.PREFILL_CONFIGS[name]
+    gate = cfg.get("gate", "channel")
     B, T, H = cfg["B"], cfg["T"], cfg["H"]
     log(f"[bench] backward: generating inputs for {name}")
     inp = inputs.prefill_config(name)
@@ -325,8 +327,13 @@ def backward_line(steps, warmup, with_cpu=False):
     log(f"[bench] backward: timing {steps} steps after {warmup} warmup")
     t, _ = time_launches(step, steps, warmup)
     ht = B * T * H
-    alg = ht * BWD_BYTES_PER_HEAD_TOKEN + STATE_BYTES * B * H
+    # the log-decay is read once and its gradient written once
+    alg = ht * (BWD_BYTES_PER_HEAD_TOKEN + 2 * (GATE_BYTES[gate] - GATE_BYTES["channel"])) + STATE_BYTES * B * H
     gbs = alg / t / 1e9
+    if wl != "c2":
+        return {"workload": f"kda_chunk_bwd {name} (dL/do ~ N(0,1), dL/dS_T = 0)", "gate": gate,
+                "ms_per_step": round(t * 1e3, 4), "head_tokens_per_s": round(ht / t, 1),
+                "alg_bytes_per_step": alg, "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
     # measured HBM traffic of the four kernels (rocprofv3 counters, committed
     # under profiles/), when taken on the current sources
     parts = [measured_traffic(key, src) for key, src in
@@ -464,6 +471,8 @@ def main():
                                          "alg_bytes_per_launch": r["roofline"]["alg_bytes_per_launch"],
                                          "hbm_frac": r["roofline"]["frac"],
                                          "mfma_frac": r["mfma"]["frac_of_bf16_peak"]}
+            if not args.no_bwd:
+                line["gate_variants"][wl]["backward"] = backward_line(min(args.steps, 20), args.warmup, wl=wl)
     if args.workload is None and not args.no_bwd:
         line["backward"] = backward_line(min(args.steps, 20), args.warmup, with_cpu=not args.no_cpu)
     if not args.no_cpu and args.workload is None:

@@ -197,7 +197,10 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T=None, *, workspace=
     plus grad_o [B, T, H, 128] bf16 and grad_S_T [B, H, 128, 128] fp32 (None:
     zero).  ``workspace``: "auto" (cached per device) or a uint8 device tensor
     of at least :func:`bwd_workspace_size` bytes.  Returns ``(dq, dk, dv,
-    dlog_alpha, dbeta, dS0)``; dS0 is None when ``grad_S0`` is false."""
+    dlog_alpha, dbeta, dS0)``; dS0 is None when ``grad_S0`` is false.  The
+    gate follows log_alpha's shape as in chunk_fwd: [B, T, H, 128] (KDA),
+    [B, T, H] (Gated DeltaNet: dlog_alpha [B, T, H]) or None (DeltaNet:
+    dlog_alpha None)."""
     import torch
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -206,12 +209,14 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T=None, *, workspace=
     for t, n, shp in ((k, "k", q.shape), (v, "v", (B, T, H, dv)), (beta, "beta", (B, T, H)),
                       (grad_o, "grad_o", (B, T, H, dv))):
         _need(t, n, dt, shp, dev)
-    _need(log_alpha, "log_alpha", torch.float32, q.shape, dev)
+    gate = _gate(log_alpha, 4)
+    if gate != KDA_GATE_NONE:
+        _need(log_alpha, "log_alpha", torch.float32, q.shape if gate == KDA_GATE_CHANNEL else (B, T, H), dev)
     for t, n in ((S0, "S0"), (grad_S_T, "grad_S_T")):
         if t is not None:
             _need(t, n, torch.float32, (B, H, dk, dv), dev)
     out = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-           torch.empty_like(log_alpha), torch.empty_like(beta)]
+           None if log_alpha is None else torch.empty_like(log_alpha), torch.empty_like(beta)]
     dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if grad_S0 else None
     if isinstance(workspace, str):
         if workspace != "auto":
@@ -222,10 +227,10 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T=None, *, workspace=
         if workspace.device != dev or workspace.dtype != torch.uint8:
             raise ValueError("workspace must be a uint8 tensor on the same device")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                             _ptr(grad_o), _ptr(grad_S_T), *(_ptr(x) for x in out), _ptr(dS0),
-                             B, T, H, dk, dv, code, ws_ptr, ws_bytes, _stream(dev))
-    _check("kda_chunk_bwd", st)
+    st = lib().kda_chunk_bwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), gate, _ptr(beta), _ptr(S0),
+                                   _ptr(grad_o), _ptr(grad_S_T), *(_ptr(x) for x in out), _ptr(dS0),
+                                   B, T, H, dk, dv, code, ws_ptr, ws_bytes, _stream(dev))
+    _check("kda_chunk_bwd_gated", st)
     return (*out, dS0)
 
 

@@ -34,6 +34,7 @@ SIGNATURES = {
     "kda_recurrent_step_gated": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP,
                                       _I, _I, _I, _I, _I, _VP]),
     "kda_chunk_bwd": (_I, [_VP] * 14 + [_I] * 6 + [_VP, _SZ, _VP]),
+    "kda_chunk_bwd_gated": (_I, [_VP] * 4 + [_I] + [_VP] * 10 + [_I] * 6 + [_VP, _SZ, _VP]),
     "kda_chunk_bwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "kda_recurrent_step": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                 _I, _I, _I, _I, _I, _VP]),

@@ -160,8 +160,23 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v,
                   int B, int T, int H, int dk, int dv, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream)
 {
+    return kda_chunk_bwd_gated(q, k, v, log_alpha, KDA_GATE_CHANNEL, beta, S0, grad_o, grad_S_T, grad_q,
+                               grad_k, grad_v, grad_log_alpha, grad_beta, grad_S0, B, T, H, dk, dv, dtype,
+                               workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_bwd_gated(const void* q, const void* k, const void* v,
+                        const float* log_alpha, int gate, const void* beta, const float* S0,
+                        const void* grad_o, const float* grad_S_T,
+                        void* grad_q, void* grad_k, void* grad_v, float* grad_log_alpha,
+                        void* grad_beta, float* grad_S0,
+                        int B, int T, int H, int dk, int dv, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;   // bf16 only
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED;
+    if (gate == KDA_GATE_NONE && (log_alpha || grad_log_alpha)) return KDA_ERR_INVALID_ARG;
     if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return KDA_OK;
 
@@ -190,18 +205,25 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v,
                                                                                           : KDA_ERR_HIP;
     }
 
-    const void* ins[] = {q, k, v, log_alpha, grad_o, grad_q, grad_k, grad_v, grad_log_alpha};
+    const void* ins[] = {q, k, v, grad_o, grad_q, grad_k, grad_v};
     for (const void* p : ins)
         if ((rc = check_ptr(p, 16)) != KDA_OK) return rc;
     if ((rc = check_ptr(beta, es)) != KDA_OK || (rc = check_ptr(grad_beta, es)) != KDA_OK) return rc;
+    // gate input and its gradient: per channel, per head, or none (both NULL)
+    const size_t g_bytes = gate == KDA_GATE_CHANNEL ? n_qk * 4 : gate == KDA_GATE_HEAD ? tok * 4 : 0;
+    if (gate != KDA_GATE_NONE) {
+        const size_t ga = gate == KDA_GATE_CHANNEL ? 16 : 4;
+        if ((rc = check_ptr(log_alpha, ga)) != KDA_OK || (rc = check_ptr(grad_log_alpha, ga)) != KDA_OK)
+            return rc;
+    }
     const size_t need = kda::chunk_bwd_ws_layout(B, T, H, nullptr);
     if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
     if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
 
-    const Range in[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, n_qk * 4},
+    const Range in[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, g_bytes},
                         {beta, tok * es}, rS0, {grad_o, n_qk * es}, rdST};
     const Range out[] = {{grad_q, n_qk * es}, {grad_k, n_qk * es}, {grad_v, n_qk * es},
-                         {grad_log_alpha, n_qk * 4}, {grad_beta, tok * es}, rdS0,
+                         {grad_log_alpha, g_bytes}, {grad_beta, tok * es}, rdS0,
                          {workspace, need}};
     constexpr int n_out = sizeof(out) / sizeof(out[0]);
     for (int i = 0; i < n_out; ++i) {
@@ -213,7 +235,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v,
 
     hipError_t e = kda::launch_chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T,
                                          grad_q, grad_k, grad_v, grad_log_alpha, grad_beta, grad_S0,
-                                         B, T, H, (char*)workspace, s);
+                                         B, T, H, (char*)workspace, s, gate);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

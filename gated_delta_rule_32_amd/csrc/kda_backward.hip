@@ -280,6 +280,10 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// GATE: GATE_CHANNEL (g and dg [B, T, H, 128]), GATE_HEAD (g and dg [B, T, H]:
+// the per-channel gradient summed over the head's channels, since the one decay
+// enters every channel) or GATE_NONE (g = 0, dg not written).
+template <int GATE>
 __global__ void __launch_bounds__(512)
 chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf16_t* beta,
                       const bf16_t* dO, const bf16_t* dV, const bf16_t* svS, const bf16_t* svdS,
@@ -327,10 +331,20 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         dma16(src + hbase + (size_t)min(tok0 + row, T - 1) * tokstride + 8 * (lane & 15),
               smem + L::OFF_CR + u * 1024);
     }
-    for (int u = wave; u < 32; u += 8) {          // g: 1 KiB = 2 tokens
-        const int row = 2 * u + (lane >> 5);
-        dma16(g + hbase + (size_t)min(tok0 + row, T - 1) * tokstride + 4 * (lane & 31),
-              smem + L::OFF_A + u * 1024);
+    if constexpr (GATE == GATE_CHANNEL) {
+        for (int u = wave; u < 32; u += 8) {      // g: 1 KiB = 2 tokens
+            const int row = 2 * u + (lane >> 5);
+            dma16(g + hbase + (size_t)min(tok0 + row, T - 1) * tokstride + 4 * (lane & 31),
+                  smem + L::OFF_A + u * 1024);
+        }
+    }
+    float gh[4][4];                                // GATE_HEAD: this lane's rows' decays
+    if constexpr (GATE == GATE_HEAD) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                gh[m][e] = g[((size_t)b * T + min(tok0 + 16 * m + 4 * lg + e, T - 1)) * H + h];
     }
     bf16x8 sf[4], dsf[4];                          // S, dS' rows c as B fragments
     {
@@ -375,7 +389,9 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * m + 4 * lg + e;
             const bool ok = tok0 + r < T;
-            const float gl = ok ? stG[r * DK + c] * LOG2E : 0.f;
+            float gl = 0.f;
+            if constexpr (GATE == GATE_CHANNEL) gl = ok ? stG[r * DK + c] * LOG2E : 0.f;
+            else if constexpr (GATE == GATE_HEAD) gl = ok ? gh[m][e] * LOG2E : 0.f;
             qv[m][e] = ok ? (float)stQ[r * DK + c] : 0.f;
             kv[m][e] = ok ? (float)stK[r * DK + c] : 0.f;
             s4[e] = (e ? s4[e - 1] : 0.f) + gl;
@@ -563,7 +579,7 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
             const int r = 16 * m + 4 * lg + e;
             stDQ[r * DK + c] = (bf16_t)oq[m][e];
             stDK[r * DK + c] = (bf16_t)ok_[m][e];
-            stDG[r * DK + c] = dgo[m][e];
+            if constexpr (GATE != GATE_NONE) stDG[r * DK + c] = dgo[m][e];
         }
     lds_barrier();
     if (vok) {
@@ -573,9 +589,22 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
             *reinterpret_cast<bf16x8*>(dq + at + 8 * i) = ld8(stDQ + vr * DK + vc + 8 * i);
             *reinterpret_cast<bf16x8*>(dk + at + 8 * i) = ld8(stDK + vr * DK + vc + 8 * i);
         }
+        if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<f32x4*>(dg + at + 4 * i) = *reinterpret_cast<const f32x4*>(stDG + vr * DK + vc + 4 * i);
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4*>(dg + at + 4 * i) = *reinterpret_cast<const f32x4*>(stDG + vr * DK + vc + 4 * i);
+        }
+    }
+    if constexpr (GATE == GATE_HEAD) {
+        // row vr's 128 channels: 16 per lane, then over the 8 lanes t % 8
+        // (every lane takes part in the shuffles, valid row or not)
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d += stDG[vr * DK + vc + i];
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        d += __shfl_xor(d, 4);
+        if (vok && (t & 7) == 0) dg[((size_t)b * T + tok0 + vr) * H + h] = d;
     }
 }
 
@@ -601,7 +630,7 @@ size_t chunk_bwd_ws_layout(long long B, long long T, long long H, size_t* off)
 hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                             const void* beta, const float* S0, const void* dO, const float* dST,
                             void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dS0,
-                            int B, int T, int H, char* ws, hipStream_t stream)
+                            int B, int T, int H, char* ws, hipStream_t stream, int gate)
 {
     const long long heads = (long long)B * H;
     const int nchunks = (T + C - 1) / C;
@@ -615,7 +644,7 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const f
     char* wsb = ws + off[KDA_BWD_WS_BWD];
 
     hipError_t err = launch_bwd_forward_part(q, k, v, g, beta, S0, B, T, H, ws + off[KDA_BWD_WS_FWD],
-                                             wsb, svS, svY, svVn, stream);
+                                             wsb, svS, svY, svVn, stream, gate);
     if (err != hipSuccess) return err;
 
     const int ncw = heads * 4 >= 256 ? 2 : 1;
@@ -626,10 +655,14 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const f
     else KDA_BSCAN(1);
 #undef KDA_BSCAN
 
-    hipLaunchKernelGGL(chunk_bwd_grad_kernel, dim3((unsigned)(heads * nchunks)), dim3(512), 0, stream,
-                       (const bf16_t*)q, (const bf16_t*)k, g, (const bf16_t*)beta, (const bf16_t*)dO,
-                       (const bf16_t*)dv, svS, svdS, svY, svVn, svdZ,
-                       (bf16_t*)dq, (bf16_t*)dk, dg, (bf16_t*)dbeta, T, H);
+#define KDA_GRAD(GT) hipLaunchKernelGGL(chunk_bwd_grad_kernel<GT>, dim3((unsigned)(heads * nchunks)), dim3(512), 0, \
+                                      stream, (const bf16_t*)q, (const bf16_t*)k, g, (const bf16_t*)beta,       \
+                                      (const bf16_t*)dO, (const bf16_t*)dv, svS, svdS, svY, svVn, svdZ,          \
+                                      (bf16_t*)dq, (bf16_t*)dk, dg, (bf16_t*)dbeta, T, H)
+    if (gate == GATE_HEAD) KDA_GRAD(GATE_HEAD);
+    else if (gate == GATE_NONE) KDA_GRAD(GATE_NONE);
+    else KDA_GRAD(GATE_CHANNEL);
+#undef KDA_GRAD
     return hipGetLastError();
 }
 

@@ -55,14 +55,15 @@ typedef __bf16 bf16_t;
 hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, const float* g,
                                    const void* beta, const float* S0, int B, int T, int H,
                                    char* ws_fwd, char* ws_bwd, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
-                                   hipStream_t stream);
+                                   hipStream_t stream, int gate = KDA_GATE_CHANNEL);
 
 // dq, dk, dv, dg, dbeta (and dS0 when non-null) from dO (and dS_T when
-// non-null); `ws` holds chunk_bwd_ws_layout(B, T, H) bytes.
+// non-null); `ws` holds chunk_bwd_ws_layout(B, T, H) bytes.  g and dg follow
+// `gate`: [B, T, H, 128], [B, T, H], or unused (GATE_NONE).
 hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                             const void* beta, const float* S0, const void* dO, const float* dST,
                             void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dS0,
-                            int B, int T, int H, char* ws, hipStream_t stream);
+                            int B, int T, int H, char* ws, hipStream_t stream, int gate = KDA_GATE_CHANNEL);
 
 // Full-attention (MQA over a 512-wide latent) decode step, split over the
 // cache: mqa_ws_bytes of scratch for the per-split partial results.

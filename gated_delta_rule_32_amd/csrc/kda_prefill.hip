@@ -1053,14 +1053,19 @@ bool chunk_prefers_two_kernel(long long B, long long T, long long H, int dtype)
 hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, const float* g,
                                   const void* beta, const float* S0, int B, int T, int H,
                                   char* ws_fwd, char* ws_bwd, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
-                                  hipStream_t stream)
+                                  hipStream_t stream, int gate)
 {
     const long long heads = (long long)B * H;
     const int nchunks = (T + C - 1) / C;
     const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
-    hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true, true>), dim3((unsigned)(heads * nblk)), dim3(NT), 0,
-                       stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g, (const bf16_t*)beta, S0,
-                       (bf16_t*)nullptr, (float*)nullptr, T, H, 1, ws_fwd, ws_bwd, (const int*)nullptr);
+#define KDA_PREP(GT) hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true, true, GT>), dim3((unsigned)(heads * nblk)),   \
+                                      dim3(NT), 0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,     \
+                                      (const bf16_t*)beta, S0, (bf16_t*)nullptr, (float*)nullptr, T, H, 1, ws_fwd,     \
+                                      ws_bwd, (const int*)nullptr)
+    if (gate == GATE_HEAD) KDA_PREP(GATE_HEAD);
+    else if (gate == GATE_NONE) KDA_PREP(GATE_NONE);
+    else KDA_PREP(GATE_CHANNEL);
+#undef KDA_PREP
     const int ncw = heads * 4 >= 256 ? 2 : 1;
 #define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, true>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
                                          dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws_fwd, (const bf16_t*)v, S0, \

@@ -199,6 +199,24 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_bwd with a choice of forget gate (see kda_chunk_fwd_gated):
+ * `log_alpha` and `grad_log_alpha` are [B, T, H, dk] fp32 (16-byte aligned)
+ * for KDA_GATE_CHANNEL (identical to kda_chunk_bwd), [B, T, H] fp32 (4-byte
+ * aligned) for KDA_GATE_HEAD -- there the gradient of a head's one decay is
+ * the sum over its channels of the per-channel gradient, since that decay
+ * enters every channel -- and both NULL for KDA_GATE_NONE (a non-NULL pointer
+ * returns KDA_ERR_INVALID_ARG).  Same workspace, other arguments and errors
+ * as kda_chunk_bwd; an unknown gate returns KDA_ERR_UNSUPPORTED.
+ */
+int kda_chunk_bwd_gated(const void* q, const void* k, const void* v,
+                        const float* log_alpha, int gate, const void* beta, const float* S0,
+                        const void* grad_o, const float* grad_S_T,
+                        void* grad_q, void* grad_k, void* grad_v, float* grad_log_alpha,
+                        void* grad_beta, float* grad_S0,
+                        int B, int T, int H, int dk, int dv, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Workspace bytes kda_chunk_bwd needs: B * H * ceil(T / 64) * 261120 for
  * dtype == KDA_BF16 and d_k = d_v = 128; 0 for invalid or unsupported
  * arguments.

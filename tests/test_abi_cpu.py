@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_bwd",
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_bwd", "kda_chunk_bwd_gated",
                           "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated", "kda_chunk_fwd_varlen",
                           "kda_mqa_decode", "kda_mqa_decode_workspace_size",
                           "kda_recurrent_step_gated", "kda_recurrent_step",
@@ -215,6 +215,32 @@ def test_bwd_workspace_size(lib):
 ])
 def test_chunk_bwd_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def bwd_g(lib, gate, g=P + 2**26, dg=P + 2**32, **kw):
+    a = dict(q=P, k=P + 2**24, v=P + 2**25, beta=P + 2**27, S0=None, do=P + 2**28, dST=None,
+             dq=P + 2**29, dk=P + 2**30, dv=P + 2**31, dbeta=P + 2**33, dS0=None, B=1, T=64, H=1,
+             kd=128, vd=128, dt=BF16, ws=P + 2**34, wsb=BWD_UNIT)
+    a.update(kw)
+    return lib.kda_chunk_bwd_gated(a["q"], a["k"], a["v"], g, gate, a["beta"], a["S0"], a["do"], a["dST"],
+                                   a["dq"], a["dk"], a["dv"], dg, a["dbeta"], a["dS0"], a["B"], a["T"],
+                                   a["H"], a["kd"], a["vd"], a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("gate,kw,code", [
+    (3, {}, UNSUP), (-1, {}, UNSUP),
+    (2, dict(g=P + 2**26, dg=None), INVALID),          # no gate: g must be NULL
+    (2, dict(g=None, dg=P + 2**32), INVALID),          # ... and so must dg
+    (2, dict(g=None, dg=None, ws=P + 2**34 + 16), ALIGN),   # NULL g, dg accepted: next check fails
+    (0, dict(g=None, dg=None, ws=P + 2**34 + 16), INVALID),  # per channel: g required
+    (1, dict(g=None), INVALID), (1, dict(dg=None), INVALID),
+    (1, dict(g=P + 2**26 + 2), ALIGN),                 # per head: 4-byte alignment
+    (0, dict(g=P + 2**26 + 4), ALIGN),                 # per channel: 16-byte alignment
+    (1, dict(dg=P + 2**26 + 128), INVALID),            # dg overlaps g ([1, 64, 1] fp32 = 256 B)
+    (1, dict(dg=P + 2**26 + 252), INVALID),            # dg overlaps g's last element
+])
+def test_chunk_bwd_gated_rejects(lib, gate, kw, code):
+    assert bwd_g(lib, gate, **kw) == code
 
 
 def test_chunk_bwd_noop(lib):

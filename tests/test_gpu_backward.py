@@ -118,3 +118,53 @@ def test_config2_full_size_sampled_heads():
     for (b, h), ref in zip(heads, refs):
         one = [x[b:b + 1, :, h:h + 1] for x in got[:5]] + [got[5][b:b + 1, h:h + 1]]
         check(one, ref)
+
+
+def gate_oracle_inputs(inp, gate, d=128):
+    """The per-channel g the oracle takes for a per-head gate (the decay copied
+    to every channel) or for no gate (g = 0)."""
+    B, T, H, _ = inp["q"].shape
+    o = dict(inp)
+    if gate == "head":
+        o["g"] = inp["g"][..., None].expand(B, T, H, d).contiguous()
+    else:
+        o["g"] = torch.zeros((B, T, H, d), dtype=torch.float32)
+    return o
+
+
+def reduce_gate(ref, gate):
+    """Oracle gradients in the gate's own shape: dg summed over channels for a
+    per-head gate (the one decay enters every channel), absent without one."""
+    ref = list(ref)
+    ref[3] = ref[3].sum(axis=-1) if gate == "head" else None
+    return ref
+
+
+@pytest.mark.parametrize("gate", ["head", "none"])
+@pytest.mark.parametrize("T", [1, 65, 200])
+def test_gate_variants(gate, T):
+    """Gated DeltaNet (one decay per head and token) and DeltaNet (no decay)."""
+    print(f"backward gate={gate} T={T}", flush=True)
+    inp = inputs.prefill_inputs(2, T, 3, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=40 + T, gate=gate)
+    gr = inputs.grad_inputs(2, T, 3, ds_std=0.05, seed=40 + T)
+    got = run_bwd(inp, gr)
+    if gate == "head":
+        assert got[3].shape == (2, T, 3)
+    else:
+        assert got[3] is None
+    check(got, reduce_gate(oracle_grads(gate_oracle_inputs(inp, gate), gr), gate))
+
+
+@pytest.mark.parametrize("name,gate", [("c2_gdn_bf16_B8_H16_T4096", "head"),
+                                       ("c2_deltanet_bf16_B8_H16_T4096", "none")])
+def test_gate_variants_full_size_sampled_heads(name, gate):
+    """B = 8, H = 16, T = 4096 with the other two gates: two sampled heads."""
+    print(f"backward {name}, sampled heads", flush=True)
+    inp = inputs.prefill_config(name)
+    gr = inputs.grad_inputs(8, 4096, 16, seed=2)
+    got = run_bwd(inp, gr)
+    heads = [(1, 2), (6, 13)]
+    refs = oracle_grads(gate_oracle_inputs(inp, gate), gr, heads)
+    for (b, h), ref in zip(heads, refs):
+        one = [x[b:b + 1, :, h:h + 1] if x is not None else None for x in got[:5]] + [got[5][b:b + 1, h:h + 1]]
+        check(one, reduce_gate(ref, gate))

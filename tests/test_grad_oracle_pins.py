@@ -60,6 +60,27 @@ def finite_difference(q, k, v, g, beta, S0, dO, dST, h=1e-6):
     return out
 
 
+def test_head_gate_gradient_is_the_channel_sum():
+    """One decay per head and token (Gated DeltaNet): the gradient of that
+    scalar, by central differences of the forward oracle with the decay copied
+    to every channel, equals the per-channel gradient summed over channels."""
+    rng = np.random.default_rng(21)
+    q, k, v, _, beta, S0, dO, dST = rand_case(rng, 1, 4, 2, 3, 2)
+    gh = -0.4 * np.log1p(np.exp(rng.standard_normal((1, 4, 2))))
+    g = np.repeat(gh[..., None], 3, axis=-1)
+    dg = kda_ref.recurrent_grad(q, k, v, g, beta, S0, dO, dST)[3]
+    h = 1e-6
+    fd = np.zeros(gh.shape)
+    for idx in np.ndindex(*gh.shape):
+        gp, gm = gh.copy(), gh.copy()
+        gp[idx] += h
+        gm[idx] -= h
+        lp = loss(q, k, v, np.repeat(gp[..., None], 3, axis=-1), beta, S0, dO, dST)
+        lm = loss(q, k, v, np.repeat(gm[..., None], 3, axis=-1), beta, S0, dO, dST)
+        fd[idx] = (lp - lm) / (2 * h)
+    assert relerr(dg.sum(axis=-1), fd) < 1e-7
+    assert relerr(dg[..., 0], fd) > 1e-3      # a single channel is not enough
+
 # ------------------------------------------------------- finite differences
 @pytest.mark.parametrize("T", [1, 3, 9])
 def test_matches_central_finite_differences(T):
