@@ -92,6 +92,38 @@ def grad_inputs(B, T, H, dtype="bfloat16", ds_std=0.0, seed=0, d=D):
     return dict(dO=dO, dS_T=dST)
 
 
+# General diagonal-plus-low-rank transition at the B = 8, H = 16, T = 4096 shape
+DPLR_CONFIG = dict(B=8, T=4096, H=16, dtype="bfloat16", g_scale=0.05, s0_std=0.0, seed=7)
+
+
+def dplr_inputs(B, T, H, dtype="bfloat16", g_scale=0.05, s0_std=0.0, seed=0, d=D):
+    """Inputs of the DPLR recurrence S_t = (Diag(e^{g_t}) - a_t b_t^T) S_{t-1} +
+    k_t v_t^T, o_t = S_t^T q_t.  ``numpy.random.default_rng(seed)``, drawn in
+    the order q, k, v, g, beta, ka, kb, S0: q, k, v, g, beta as for the prefill
+    (q, k L2-normalised, g = -g_scale softplus(N(0,1)) per channel, beta =
+    sigmoid(N(0,1))); ka, kb ~ N(0,1) L2-normalised, independent of k;
+    a = beta * ka and b = e^{g} * kb -- the shape of KDA's a and b (beta k and
+    alpha * k) with the two vectors no longer tied to each other or to k.
+    Returns a dict of CPU tensors q, k, v, a, b (dtype), g (fp32), S0 or None."""
+    import torch
+    rng = np.random.default_rng(seed)
+    shp = (B, T, H, d)
+    q = _l2n(rng.standard_normal(shp, dtype=np.float32))
+    k = _l2n(rng.standard_normal(shp, dtype=np.float32))
+    v = rng.standard_normal(shp, dtype=np.float32)
+    g = (-np.float32(g_scale)) * _softplus(rng.standard_normal(shp, dtype=np.float32))
+    beta = _sigmoid(rng.standard_normal((B, T, H), dtype=np.float32))
+    ka = _l2n(rng.standard_normal(shp, dtype=np.float32))
+    kb = _l2n(rng.standard_normal(shp, dtype=np.float32))
+    S0 = None
+    if s0_std > 0:
+        S0 = torch.from_numpy(np.float32(s0_std) * rng.standard_normal((B, H, d, d), dtype=np.float32))
+    td = _torch_dtype(dtype)
+    cast = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(td)
+    return dict(q=cast(q), k=cast(k), v=cast(v), a=cast(beta[..., None] * ka), b=cast(np.exp(g) * kb),
+                g=torch.from_numpy(np.ascontiguousarray(g)), S0=S0)
+
+
 MQA_CONFIG = dict(B=1, T=1 << 20, H=32, D=512, seed=6)
 
 
