@@ -23,7 +23,7 @@ head-tokens per second (B*T*H / time).  The JSON line also carries:
   * cpu_baseline: the fp64 oracle timed on the host cores on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload c3|c1|decode|layer|bwd|gdn|deltanet|mqa  (single-workload lines, for profiling)
+       python bench.py --workload c3|c1|decode|layer|bwd|gdn|deltanet|mqa|dplr  (single-workload lines, for profiling)
        python bench.py --copy-calibration       (plain copy kernel for counter scaling)
 """
 from __future__ import annotations
@@ -266,6 +266,46 @@ def mqa_line(steps, warmup, kda_decode=None):
     return out
 
 
+# DPLR comparison path, compulsory HBM bytes per head-token (bf16): reads q,
+# k, v, a, b (5 x 256), log-decay fp32 (512); writes o (256).
+DPLR_BYTES_PER_HEAD_TOKEN = 5 * 2 * D + 4 * D + 2 * D          # 2,048
+
+
+def dplr_line(steps, warmup, kda_ms=None):
+    """The general diagonal-plus-low-rank recurrence at the B = 8, H = 16,
+    T = 4096 shape (two kernels: prep + state scan), against KDA on the same
+    shape: the comparison of the Kimi Linear page, section 4 (KDA about twice
+    as fast as general DPLR)."""
+    import torch
+    import gated_delta_rule_32_amd as kda
+    from gated_delta_rule_32_amd import inputs
+
+    cfg = inputs.DPLR_CONFIG
+    B, T, H = cfg["B"], cfg["T"], cfg["H"]
+    log(f"[bench] dplr: generating B={B} T={T} H={H}")
+    inp = inputs.dplr_inputs(B, T, H, g_scale=cfg["g_scale"], s0_std=cfg["s0_std"], seed=cfg["seed"])
+    d = {n: (x.to("cuda:0") if x is not None else None) for n, x in inp.items()}
+    o = torch.empty_like(d["v"])
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(kda.dplr_workspace_size(B, T, H), dtype=torch.uint8, device="cuda:0")
+    t, _ = time_launches(lambda: kda.dplr_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["g"], None,
+                                                    out=o, S_T=S_T, workspace=ws), steps, warmup)
+    ht = B * T * H
+    alg = ht * DPLR_BYTES_PER_HEAD_TOKEN + STATE_BYTES * B * H
+    out = {"workload": f"kda_dplr_chunk_fwd B={B} T={T} H={H} bf16 (a = beta ka, b = alpha kb, ka, kb free)",
+           "ms_per_step": round(t * 1e3, 4), "head_tokens_per_s": round(ht / t, 1),
+           "alg_bytes_per_step": alg, "frac_of_hbm_peak": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+           "workspace_bytes": ws.numel()}
+    kda2 = prefill_line(WORKLOADS["c2"], steps, warmup, "two_kernel")
+    out["kda_same_shape_ms"] = {"two_kernel": round(kda2["t"] * 1e3, 4)}
+    if kda_ms is not None:
+        out["kda_same_shape_ms"]["library_schedule"] = round(kda_ms, 4)
+    best = min(out["kda_same_shape_ms"].values())
+    out["dplr_over_kda"] = {k: round(t * 1e3 / v, 2) for k, v in out["kda_same_shape_ms"].items()}
+    out["dplr_over_kda_best"] = round(t * 1e3 / best, 2)
+    return out
+
+
 def layer_line(steps, warmup):
     """The full token-mixing layer (projections, conv/activations, gates, KDA,
     gated RMSNorm, output projection) on the 32768-token, d_model 2048, 16-head
@@ -392,7 +432,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-gates", action="store_true")
     ap.add_argument("--no-mqa", action="store_true")
-    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer", "bwd", "gdn", "deltanet", "mqa"],
+    ap.add_argument("--no-dplr", action="store_true")
+    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer", "bwd", "gdn", "deltanet", "mqa", "dplr"],
                     default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--schedule", choices=["auto", "fused", "two_kernel"], default="auto",
@@ -428,6 +469,10 @@ def main():
     if args.workload == "bwd":
         bwd = backward_line(args.steps, args.warmup)
         print(json.dumps({"metric": "KDA backward head-tokens/s", **bwd}))
+        return
+
+    if args.workload == "dplr":
+        print(json.dumps({"metric": "DPLR chunked forward", **dplr_line(args.steps, args.warmup)}))
         return
 
     if args.workload == "mqa":
@@ -473,6 +518,8 @@ def main():
                                          "mfma_frac": r["mfma"]["frac_of_bf16_peak"]}
             if not args.no_bwd:
                 line["gate_variants"][wl]["backward"] = backward_line(min(args.steps, 20), args.warmup, wl=wl)
+    if args.workload is None and not args.no_dplr:
+        line["dplr_comparison"] = dplr_line(args.steps, args.warmup, pre["t"] * 1e3)
     if args.workload is None and not args.no_bwd:
         line["backward"] = backward_line(min(args.steps, 20), args.warmup, with_cpu=not args.no_cpu)
     if not args.no_cpu and args.workload is None:

@@ -13,7 +13,8 @@ import ctypes
 from ._binding import (KDA_BF16, KDA_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,  # noqa: F401
                        KDA_GATE_NONE, LAYER_REGIONS, KDAError, lib, status_string, version, _check)
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "bwd_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "bwd_workspace_size", "dplr_chunk_fwd",
+           "dplr_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
            "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS", "mqa_decode",
            "status_string", "version", "KDAError",
            "KDA_F32", "KDA_BF16", "lib"]
@@ -184,6 +185,52 @@ def mqa_decode(q, cache, scale, *, out=None, workspace=None):
                               ws_ptr, ws_bytes, _stream(dev))
     _check("kda_mqa_decode", st)
     return out
+
+
+def dplr_workspace_size(B, T, H, d=128):
+    """Workspace bytes kda_dplr_chunk_fwd needs (bf16)."""
+    return int(lib().kda_dplr_chunk_fwd_workspace_size(B, T, H, d, d, KDA_BF16))
+
+
+def dplr_chunk_fwd(q, k, v, a, b, log_alpha, S0=None, *, out=None, S_T=None, return_state: bool = True,
+                   workspace="auto"):
+    """General diagonal-plus-low-rank recurrence S_t = (Diag(e^{log_alpha_t}) -
+    a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t (bf16 only).  q, k, a, b, v:
+    [B, T, H, 128] bf16; log_alpha [B, T, H, 128] fp32; S0 [B, H, 128, 128] fp32
+    or None.  ``workspace``: "auto" (cached per device) or a uint8 device tensor
+    of at least :func:`dplr_workspace_size` bytes.  Returns (o, S_T)."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for t, n in ((k, "k"), (a, "a"), (b, "b")):
+        _need(t, n, dt, q.shape, dev)
+    _need(v, "v", dt, (B, T, H, dv), dev)
+    _need(log_alpha, "log_alpha", torch.float32, q.shape, dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, T, H, dv), dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _need(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto' or a tensor")
+        workspace = _workspace(dev, dplr_workspace_size(B, T, H, dk))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device != dev or workspace.dtype != torch.uint8:
+            raise ValueError("workspace must be a uint8 tensor on the same device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib().kda_dplr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha), _ptr(S0),
+                                  _ptr(out), _ptr(S_T), B, T, H, dk, dv, code, ws_ptr, ws_bytes, _stream(dev))
+    _check("kda_dplr_chunk_fwd", st)
+    return out, S_T
 
 
 def bwd_workspace_size(B, T, H, d=128):

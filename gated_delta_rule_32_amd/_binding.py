@@ -35,6 +35,8 @@ SIGNATURES = {
                                       _I, _I, _I, _I, _I, _VP]),
     "kda_chunk_bwd": (_I, [_VP] * 14 + [_I] * 6 + [_VP, _SZ, _VP]),
     "kda_chunk_bwd_gated": (_I, [_VP] * 4 + [_I] + [_VP] * 10 + [_I] * 6 + [_VP, _SZ, _VP]),
+    "kda_dplr_chunk_fwd": (_I, [_VP] * 9 + [_I] * 6 + [_VP, _SZ, _VP]),
+    "kda_dplr_chunk_fwd_workspace_size": (_SZ, [_I] * 6),
     "kda_chunk_bwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "kda_recurrent_step": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                 _I, _I, _I, _I, _I, _VP]),

@@ -365,6 +365,63 @@ int kda_mqa_decode(const void* q, const void* cache, void* o, int B, int T, int 
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+size_t kda_dplr_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype)
+{
+    if (B < 0 || T < 0 || H < 0 || dk != kHeadDim || dv != kHeadDim || dtype != KDA_BF16) return 0;
+    return kda::dplr_ws_layout(B, T, H, nullptr);
+}
+
+int kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
+                       const float* log_alpha, const float* S0, void* o, float* S_T,
+                       int B, int T, int H, int dk, int dv, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;   // bf16 only
+    if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return KDA_OK;
+
+    bool ok = true;
+    const size_t tok = mul3(B, T, H, &ok);
+    const size_t heads = mul3(B, H, 1, &ok);
+    const size_t n_qk = mul3((long long)tok, kHeadDim, 1, &ok);
+    const size_t n_state = mul3((long long)heads, kHeadDim, kHeadDim, &ok);
+    const size_t units = mul3((long long)heads, (T + 63) / 64, 1, &ok);
+    if (!ok) return KDA_ERR_UNSUPPORTED;
+    if (heads * 8 > (size_t)INT_MAX || units > (size_t)INT_MAX) return KDA_ERR_UNSUPPORTED;   // grids
+
+    int rc;
+    if (S0 && (rc = check_ptr(S0, 16)) != KDA_OK) return rc;
+    if (S_T && (rc = check_ptr(S_T, 16)) != KDA_OK) return rc;
+    const Range rS0{S0, S0 ? n_state * 4 : 0}, rST{S_T, S_T ? n_state * 4 : 0};
+    // S_T may coincide with S0 exactly (in-place update), never partially.
+    if (overlap(rS0, rST) && (const void*)S0 != (const void*)S_T) return KDA_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (!S_T || (const void*)S0 == (const void*)S_T) return KDA_OK;
+        return kda::launch_state_copy(S0, S_T, (long long)heads, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+
+    const void* ptrs[] = {q, k, v, a, b, log_alpha, o};
+    for (const void* p : ptrs)
+        if ((rc = check_ptr(p, 16)) != KDA_OK) return rc;
+    const size_t need = kda::dplr_ws_layout(B, T, H, nullptr);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
+    const Range in[] = {{q, n_qk * 2}, {k, n_qk * 2}, {v, n_qk * 2}, {a, n_qk * 2},
+                        {b, n_qk * 2}, {log_alpha, n_qk * 4}, rS0};
+    const Range out[] = {{o, n_qk * 2}, rST, {workspace, need}};
+    for (int i = 0; i < 3; ++i) {
+        for (const Range& r : in)
+            if (overlap(out[i], r) && !(i == 1 && r.p == (const void*)S0)) return KDA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(out[i], out[j])) return KDA_ERR_INVALID_ARG;
+    }
+    hipError_t e = kda::launch_dplr_chunk_fwd(q, k, v, a, b, log_alpha, S0, o, S_T, B, T, H,
+                                              (char*)workspace, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 size_t kda_layer_workspace_layout(int B, int T, int d_model, int H, int rank, size_t* offsets)
 {
     if (B < 0 || T < 0 || H <= 0 || d_model <= 0 || rank <= 0) return 0;

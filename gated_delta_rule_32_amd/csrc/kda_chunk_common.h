@@ -186,6 +186,27 @@ __device__ __forceinline__ bf16x8 a_pair(const bf16_t* row, int p, int lg, bool 
     return cat8(a, b);
 }
 
+// ---- forward state scan: per-chunk operand block -------------------------------
+// Workspace block of one chunk, written by a prep kernel and read by
+// chunk_scan_kernel (bf16 only).  It is the image of the scan's LDS stage:
+// rows keep their 16-byte padding and Kb^T its swizzle (kbt_swz), so the scan
+// copies it linearly in 1 KiB pieces.  Byte offsets:
+constexpr int WS_P128 = DK + 8, WS_P64 = C + 8;    // padded row pitches (elements)
+constexpr int WS_QT = 0;                            // Qt   [64][136] bf16, token-major
+constexpr int WS_KH = WS_QT + C * WS_P128 * 2;      // Kh   [64][136] bf16, token-major
+constexpr int WS_KBT = WS_KH + C * WS_P128 * 2;     // Kb^T [128][72] bf16, channel-major, swizzled
+constexpr int WS_TM = WS_KBT + DK * WS_P64 * 2;     // Tm Diag(beta) [64][72] bf16
+constexpr int WS_QK = WS_TM + C * WS_P64 * 2;       // Aqk  [64][72] bf16
+constexpr int WS_GAM = WS_QK + C * WS_P64 * 2;      // e^{G_64} [128] fp32
+constexpr int WS_USED = WS_GAM + DK * 4;            // 72,192 bytes written
+constexpr int WS_CHUNK = (WS_USED + 1023) / 1024 * 1024;   // 72,704: whole KiB per block
+
+// Element (channel c, token i) of the swizzled Kb^T: the 8-token blocks of a
+// row are XOR-permuted by bits 3..5 of the channel.
+__device__ __forceinline__ constexpr int kbt_swz(int c, int i) {
+    return c * WS_P64 + ((((i >> 3) ^ ((c >> 3) & 7)) << 3) | (i & 7));
+}
+
 // ---- backward pass: per-chunk operand block of the reverse state scan --------
 // Written by the prep kernel next to the forward block, read by
 // chunk_bwd_scan_kernel.  All bf16 except the two vectors; rows padded to

@@ -65,6 +65,19 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const f
                             void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dS0,
                             int B, int T, int H, char* ws, hipStream_t stream, int gate = KDA_GATE_CHANNEL);
 
+// State scan over the DPLR prep kernel's output: per-chunk operand blocks,
+// U0 and O0 [B, T, H, 128] bf16 and H0 [B*H*chunks][128][128] bf16.
+hipError_t launch_dplr_scan(const char* blocks, const bf16_t* u0, const bf16_t* h0, const bf16_t* o0,
+                            const float* S0, void* o, float* S_T, int B, int T, int H, hipStream_t stream);
+
+// General diagonal-plus-low-rank chunked forward (bf16): workspace regions
+// (blocks, H0, U0, O0) and the launch of both kernels.
+enum { KDA_DPLR_WS_BLK = 0, KDA_DPLR_WS_H0, KDA_DPLR_WS_U0, KDA_DPLR_WS_O0, KDA_DPLR_WS_REGIONS };
+size_t dplr_ws_layout(long long B, long long T, long long H, size_t* off);
+hipError_t launch_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
+                                 const float* g, const float* S0, void* o, float* S_T, int B, int T, int H,
+                                 char* ws, hipStream_t stream);
+
 // Full-attention (MQA over a 512-wide latent) decode step, split over the
 // cache: mqa_ws_bytes of scratch for the per-split partial results.
 size_t mqa_ws_bytes(long long B, long long T, long long H);

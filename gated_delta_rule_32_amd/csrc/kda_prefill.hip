@@ -109,19 +109,6 @@ struct ChunkIn {
     E beta;
 };
 
-// Workspace block of one chunk, written by the prep instantiation of the
-// kernel below and read by chunk_scan_kernel (bf16 only).  It is the image of
-// the scan's LDS stage: rows keep their 16-byte padding and Kb^T its swizzle,
-// so the scan copies it linearly.  Byte offsets:
-constexpr int WS_P128 = DK + 8, WS_P64 = C + 8;    // padded row pitches (elements)
-constexpr int WS_QT = 0;                            // Qt   [64][136] bf16, token-major
-constexpr int WS_KH = WS_QT + C * WS_P128 * 2;      // Kh   [64][136] bf16, token-major
-constexpr int WS_KBT = WS_KH + C * WS_P128 * 2;     // Kb^T [128][72] bf16, channel-major, swizzled
-constexpr int WS_TM = WS_KBT + DK * WS_P64 * 2;     // Tm Diag(beta) [64][72] bf16
-constexpr int WS_QK = WS_TM + C * WS_P64 * 2;       // Aqk  [64][72] bf16
-constexpr int WS_GAM = WS_QK + C * WS_P64 * 2;      // e^{G_64} [128] fp32
-constexpr int WS_USED = WS_GAM + DK * 4;            // 72,192 bytes written
-constexpr int WS_CHUNK = (WS_USED + 1023) / 1024 * 1024;   // 72,704: whole KiB per block
 constexpr int PREP_CHUNKS = 4;                      // chunks per prep workgroup
 
 // The fused kernel (PREP = false): one workgroup per (head, value slice)
@@ -773,11 +760,22 @@ template <int NCW> struct ScanCfg {                       // NCW consumer waves
 // are skipped); instead each chunk's entry state S_n [128][128],
 // Y = V - Kh S_n [64][128] and Vn [64][128] are written in bf16 to svS / svY /
 // svVn, indexed (head, chunk).
-template <int NCW, bool SAVE>
+//
+// DPLR (the general diagonal-plus-low-rank transition, see kda_dplr.hip): the
+// block holds Qt = e^G q, Kh = W, Kb^T = (e^{-G} a)^T and Aqk = A_qa, its Tm
+// slot is not used, and `v` points at U0.  Per chunk the scan computes
+// Vn = U0 - W S (no Tm product), O = Qt S + A_qa Vn + O0 and
+// S <- Diag(gamma) (S + Kb^T Vn) + H0, with O0 [token][128] and
+// H0 [head, chunk][128][128] (bf16) from the DPLR prep kernel: H0's slice of
+// this workgroup's value columns is loaded into the Tm slot, and O0 is added
+// by the loader lanes when they store the output.
+template <int NCW, bool SAVE, bool DPLR = false>
 __global__ void __launch_bounds__(ScanCfg<NCW>::NT)
 chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
-                  int T, int H, bf16_t* svS, bf16_t* svY, bf16_t* svVn)
+                  int T, int H, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
+                  const bf16_t* h0, const bf16_t* o0)
 {
+    static_assert(!(SAVE && DPLR), "the backward pass is KDA only");
     typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
     using SC = ScanCfg<NCW>;
     __shared__ __attribute__((aligned(1024))) char smem[SC::TOTAL];
@@ -803,13 +801,30 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     // ---- loader side: lane pt moves V / output unit (token ut, columns 8 ug ..)
     const int pt = t & 255, ug = pt % SC::VG, ut = pt / SC::VG;
     const bool ulane = t < 256 && ut < C;     // lanes of the first four loader waves
-    bf16x8 vrow = bf16x8{};
+    bf16x8 vrow = bf16x8{}, o0row = bf16x8{};
+    // DPLR: the H0 slice [128][DV] (unpadded) replaces the Tm pages
+    constexpr int TM_P0 = WS_TM / 1024, TM_P1 = WS_QK / 1024;
+    constexpr int HPR = SC::DV / 8;                       // 16-byte pieces per H0 row
+    constexpr int HRPP = 64 / HPR;                        // H0 rows per 1 KiB page
+    constexpr int HPAGES = DK / HRPP;
+    static_assert(WS_TM % 1024 == 0 && WS_QK % 1024 == 0 && HPAGES <= TM_P1 - TM_P0, "H0 slice fits the Tm slot");
     auto load_block = [&](int n) {            // workspace block n -> stage n % 2
         const char* src = wsh + (size_t)n * WS_CHUNK;
         char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
-        for (int u = wave; u < SC_KIB; u += SC::NLW)
-            __builtin_amdgcn_global_load_lds(src + (size_t)u * 1024 + lane * 16,
-                                             (__attribute__((address_space(3))) void*)(dst + u * 1024), 16, 0, 0);
+        for (int u = wave; u < SC_KIB; u += SC::NLW) {
+            const char* from = src + (size_t)u * 1024 + lane * 16;
+            if constexpr (DPLR) {
+                if (u >= TM_P0 && u < TM_P1) {
+                    const int hp = u - TM_P0;
+                    if (hp >= HPAGES) continue;
+                    const int row = HRPP * hp + lane / HPR;
+                    from = reinterpret_cast<const char*>(
+                        h0 + (((size_t)head * nchunks + n) * DK + row) * DK + j0 + 8 * (lane % HPR));
+                }
+            }
+            __builtin_amdgcn_global_load_lds(from, (__attribute__((address_space(3))) void*)(dst + u * 1024),
+                                             16, 0, 0);
+        }
     };
     auto load_v = [&](int n) {
         if (!ulane) return;
@@ -824,11 +839,21 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             for (int c = 0; c < 8; ++c) vt[(8 * ug + c) * WS_P64 + ut] = ok ? vrow[c] : bf16_t{};
         }
     };
+    auto load_o0 = [&](int n) {               // DPLR: O0 row of chunk n, stored with it next step
+        if (!ulane) return;
+        const int tok = min(n * C + ut, T - 1);
+        o0row = *reinterpret_cast<const bf16x8*>(o0 + hbase + (size_t)tok * tokstride + j0 + 8 * ug);
+    };
     auto store_out = [&](int n) {             // output tile of chunk n: LDS -> HBM
         const bf16_t* ot = reinterpret_cast<const bf16_t*>(smem + SC::OFF_O + (n & 1) * C * SC::DV * 2);
-        if (ulane && n * C + ut < T)
-            *reinterpret_cast<bf16x8*>(o + hbase + (size_t)(n * C + ut) * tokstride + j0 + 8 * ug) =
-                *reinterpret_cast<const bf16x8*>(ot + ut * SC::DV + 8 * ug);
+        if (ulane && n * C + ut < T) {
+            bf16x8 x = *reinterpret_cast<const bf16x8*>(ot + ut * SC::DV + 8 * ug);
+            if constexpr (DPLR) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[c] = (bf16_t)((float)x[c] + (float)o0row[c]);
+            }
+            *reinterpret_cast<bf16x8*>(o + hbase + (size_t)(n * C + ut) * tokstride + j0 + 8 * ug) = x;
+        }
     };
 
     // ---- consumer side: S[16cb + 4lg + e][j0 + jc] in acc_s[cb][e] ----
@@ -852,6 +877,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
         if (loader) {
             if (n + 1 < nchunks) { load_block(n + 1); load_v(n + 1); }
             if (!SAVE && n > 0) store_out(n - 1);
+            if constexpr (DPLR) load_o0(n);
             __builtin_amdgcn_s_waitcnt(0);    // the stage must be complete at the barrier
             if (n + 1 < nchunks) write_vt(n + 1);
         } else {
@@ -917,6 +943,10 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             }
 #pragma unroll
             for (int Rb = 0; Rb < 4; ++Rb) {
+                if constexpr (DPLR) {
+                    vn[Rb] = zt[Rb];
+                    continue;
+                }
                 f32x4 a = z4;
                 const bf16_t* row = sTm + (16 * Rb + ln) * WS_P64;
 #pragma unroll
@@ -974,6 +1004,11 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
                 const f32x4 gv = *reinterpret_cast<const f32x4*>(sGam + 16 * cb + 4 * lg);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc_s[cb][e] *= gv[e];
+                if constexpr (DPLR) {
+                    const bf16_t* sH0 = sTm;          // [128][DV] in the Tm slot
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc_s[cb][e] += (float)sH0[(16 * cb + 4 * lg + e) * SC::DV + jc];
+                }
             }
         }
         lds_barrier();
@@ -1022,7 +1057,8 @@ void launch_gate(const void* q, const void* k, const void* v, const float* g, co
         const int ncw = heads * 4 >= 256 ? 2 : 1;
 #define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, false>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
                                          dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws, (const bf16_t*)v, S0, \
-                                         (bf16_t*)o, S_T, T, H, (bf16_t*)nullptr, (bf16_t*)nullptr, (bf16_t*)nullptr)
+                                         (bf16_t*)o, S_T, T, H, (bf16_t*)nullptr, (bf16_t*)nullptr, (bf16_t*)nullptr, \
+                                         (const bf16_t*)nullptr, (const bf16_t*)nullptr)
         if (ncw == 2) KDA_SCAN(2);
         else KDA_SCAN(1);
 #undef KDA_SCAN
@@ -1069,7 +1105,23 @@ hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, 
     const int ncw = heads * 4 >= 256 ? 2 : 1;
 #define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, true>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
                                          dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws_fwd, (const bf16_t*)v, S0, \
-                                         (bf16_t*)nullptr, (float*)nullptr, T, H, svS, svY, svVn)
+                                         (bf16_t*)nullptr, (float*)nullptr, T, H, svS, svY, svVn, \
+                                         (const bf16_t*)nullptr, (const bf16_t*)nullptr)
+    if (ncw == 2) KDA_SCAN(2);
+    else KDA_SCAN(1);
+#undef KDA_SCAN
+    return hipGetLastError();
+}
+
+hipError_t launch_dplr_scan(const char* blocks, const bf16_t* u0, const bf16_t* h0, const bf16_t* o0,
+                            const float* S0, void* o, float* S_T, int B, int T, int H, hipStream_t stream)
+{
+    const long long heads = (long long)B * H;
+    const int ncw = heads * 4 >= 256 ? 2 : 1;
+#define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, false, true>),                                   \
+                                         dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), dim3(ScanCfg<NCW>::NT), \
+                                         0, stream, blocks, u0, S0, (bf16_t*)o, S_T, T, H, (bf16_t*)nullptr,       \
+                                         (bf16_t*)nullptr, (bf16_t*)nullptr, h0, o0)
     if (ncw == 2) KDA_SCAN(2);
     else KDA_SCAN(1);
 #undef KDA_SCAN

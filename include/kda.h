@@ -337,6 +337,36 @@ int kda_mqa_decode(const void* q, const void* cache, void* o, int B, int T, int 
 /* Workspace bytes kda_mqa_decode needs (0 for invalid or unsupported sizes). */
 size_t kda_mqa_decode_workspace_size(int B, int T, int H, int D);
 
+/*
+ * Chunked forward of the general diagonal-plus-low-rank (DPLR) recurrence,
+ * the comparison point for KDA (page "Kimi K3论文：Kimi Linear", section 4:
+ * the general gated delta rule with transition D_t - a_t b_t^T, of which KDA
+ * is the case a_t = beta_t k_t, b_t = alpha_t * k_t):
+ *
+ *   S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+ *
+ * independently for each (batch, head), with alpha_t = exp(log_alpha_t).
+ *   q, k, a, b [B, T, H, dk]  bf16        v [B, T, H, dv]  bf16
+ *   log_alpha  [B, T, H, dk]  fp32        S0, S_T [B, H, dk, dv] fp32
+ *   o          [B, T, H, dv]  bf16 out
+ * dk = dv = 128 and dtype = KDA_BF16 only (else KDA_ERR_UNSUPPORTED).  S0
+ * NULL means zeros; S_T NULL means not written; S_T == S0 updates in place.
+ * workspace: at least kda_dplr_chunk_fwd_workspace_size(...) bytes, 256-byte
+ * aligned, owned by the caller, contents unspecified on entry and exit (per
+ * 64-token chunk the scan's operand block and the state-independent terms of
+ * the chunk form, 137 KiB per (batch, head, chunk) plus 512 bytes per
+ * head-token).  T = 0 copies S0 (or zeros) to S_T; B*H = 0 is a no-op.  o,
+ * S_T and the workspace must not overlap any input or each other.  All
+ * pointers 16-byte aligned.  Returns KDA_OK or a negative status.
+ */
+int kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
+                       const float* log_alpha, const float* S0, void* o, float* S_T,
+                       int B, int T, int H, int dk, int dv, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kda_dplr_chunk_fwd needs (0 for invalid or unsupported arguments). */
+size_t kda_dplr_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* kda_status_string(int status);
 

@@ -36,6 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_bwd", "kda_chunk_bwd_gated",
                           "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated", "kda_chunk_fwd_varlen",
                           "kda_mqa_decode", "kda_mqa_decode_workspace_size",
+                          "kda_dplr_chunk_fwd", "kda_dplr_chunk_fwd_workspace_size",
                           "kda_recurrent_step_gated", "kda_recurrent_step",
                           "kda_layer_fwd", "kda_layer_workspace_layout",
                           "kda_status_string", "kda_version"}
@@ -333,3 +334,43 @@ def test_mqa_rejects(lib, kw, code):
 
 def test_mqa_noop(lib):
     assert lib.kda_mqa_decode(None, None, None, 0, 100, 32, 512, 0.1, None, 0, None) == OK
+
+
+# ------------------------------------------------------ DPLR comparison path
+DPLR_UNIT = 72704 + 32768   # workspace bytes per (batch, head, 64-token chunk), plus 512 per head-token
+
+
+def dplr(lib, q=P, k=P + 2**24, v=P + 2**25, a=P + 2**26, b=P + 2**27, g=P + 2**28, S0=None,
+         o=P + 2**29, ST=None, B=1, T=64, H=1, kd=128, vd=128, dt=BF16, ws=P + 2**34, wsb=None):
+    if wsb is None:
+        wsb = lib.kda_dplr_chunk_fwd_workspace_size(B, T, H, kd, vd, dt)
+    return lib.kda_dplr_chunk_fwd(q, k, v, a, b, g, S0, o, ST, B, T, H, kd, vd, dt, ws, wsb, None)
+
+
+def test_dplr_workspace_size(lib):
+    f = lib.kda_dplr_chunk_fwd_workspace_size
+    assert f(1, 64, 1, 128, 128, BF16) == DPLR_UNIT + 2 * 64 * 256
+    assert f(8, 4096, 16, 128, 128, BF16) == 8 * 16 * 64 * (DPLR_UNIT + 2 * 64 * 256)
+    assert f(1, 65, 1, 128, 128, BF16) == 2 * DPLR_UNIT + 2 * 65 * 256      # U0, O0: one row per token
+    assert f(1, 64, 1, 128, 128, F32) == 0 and f(1, 64, 1, 64, 128, BF16) == 0 and f(-1, 64, 1, 128, 128, BF16) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(a=None), INVALID), (dict(b=None), INVALID), (dict(g=None), INVALID),
+    (dict(o=None), INVALID), (dict(ws=None), INVALID), (dict(B=-1), INVALID), (dict(T=-1), INVALID),
+    (dict(dt=F32), UNSUP), (dict(kd=64), UNSUP), (dict(vd=256), UNSUP),
+    (dict(a=P + 2**26 + 8), ALIGN), (dict(g=P + 2**28 + 4), ALIGN), (dict(ws=P + 2**34 + 16), ALIGN),
+    (dict(wsb=1000), INVALID),                   # workspace too small
+    (dict(o=P + 2**27 + 64), INVALID),           # o overlaps b
+    (dict(ws=P + 2**28), INVALID),               # workspace overlaps the log-decay
+    (dict(S0=P + 2**35, ST=P + 2**35 + 16), INVALID),   # S_T overlaps S0 partially
+    (dict(ST=P + 2**29), INVALID),               # S_T overlaps o
+    (dict(B=2**30, H=2**30), UNSUP),             # size overflow
+])
+def test_dplr_rejects(lib, kw, code):
+    assert dplr(lib, **kw) == code
+
+
+def test_dplr_noop(lib):
+    assert lib.kda_dplr_chunk_fwd(*([None] * 9), 0, 64, 4, 128, 128, BF16, None, 0, None) == OK
+    assert lib.kda_dplr_chunk_fwd(*([None] * 9), 2, 0, 4, 128, 128, BF16, None, 0, None) == OK
