@@ -71,8 +71,9 @@ hipError_t launch_dplr_scan(const char* blocks, const bf16_t* u0, const bf16_t* 
                             const float* S0, void* o, float* S_T, int B, int T, int H, hipStream_t stream);
 
 // General diagonal-plus-low-rank chunked forward (bf16): workspace regions
-// (blocks, H0, U0, O0) and the launch of both kernels.
-enum { KDA_DPLR_WS_BLK = 0, KDA_DPLR_WS_H0, KDA_DPLR_WS_U0, KDA_DPLR_WS_O0, KDA_DPLR_WS_REGIONS };
+// (blocks, H0, U0, O0, a 256-byte sink for the rows past T) and the launch of
+// both kernels.
+enum { KDA_DPLR_WS_BLK = 0, KDA_DPLR_WS_H0, KDA_DPLR_WS_U0, KDA_DPLR_WS_O0, KDA_DPLR_WS_SINK, KDA_DPLR_WS_REGIONS };
 size_t dplr_ws_layout(long long B, long long T, long long H, size_t* off);
 hipError_t launch_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
                                  const float* g, const float* S0, void* o, float* S_T, int B, int T, int H,
