@@ -354,8 +354,8 @@ size_t kda_mqa_decode_workspace_size(int B, int T, int H, int D);
  * workspace: at least kda_dplr_chunk_fwd_workspace_size(...) bytes, 256-byte
  * aligned, owned by the caller, contents unspecified on entry and exit (per
  * 64-token chunk the scan's operand block and the state-independent terms of
- * the chunk form, 137 KiB per (batch, head, chunk) plus 512 bytes per
- * head-token).  T = 0 copies S0 (or zeros) to S_T; B*H = 0 is a no-op.  o,
+ * the chunk form, 103 KiB per (batch, head, chunk) plus 512 bytes per
+ * head-token and 256 bytes).  T = 0 copies S0 (or zeros) to S_T; B*H = 0 is a no-op.  o,
  * S_T and the workspace must not overlap any input or each other.  All
  * pointers 16-byte aligned.  Returns KDA_OK or a negative status.
  */

@@ -337,7 +337,7 @@ def test_mqa_noop(lib):
 
 
 # ------------------------------------------------------ DPLR comparison path
-DPLR_UNIT = 72704 + 32768   # workspace bytes per (batch, head, 64-token chunk), plus 512 per head-token
+DPLR_UNIT = 72704 + 32768   # workspace bytes per (batch, head, 64-token chunk), plus 512 per head-token and 256
 
 
 def dplr(lib, q=P, k=P + 2**24, v=P + 2**25, a=P + 2**26, b=P + 2**27, g=P + 2**28, S0=None,
@@ -349,9 +349,9 @@ def dplr(lib, q=P, k=P + 2**24, v=P + 2**25, a=P + 2**26, b=P + 2**27, g=P + 2**
 
 def test_dplr_workspace_size(lib):
     f = lib.kda_dplr_chunk_fwd_workspace_size
-    assert f(1, 64, 1, 128, 128, BF16) == DPLR_UNIT + 2 * 64 * 256
-    assert f(8, 4096, 16, 128, 128, BF16) == 8 * 16 * 64 * (DPLR_UNIT + 2 * 64 * 256)
-    assert f(1, 65, 1, 128, 128, BF16) == 2 * DPLR_UNIT + 2 * 65 * 256      # U0, O0: one row per token
+    assert f(1, 64, 1, 128, 128, BF16) == DPLR_UNIT + 2 * 64 * 256 + 256   # + one sink row
+    assert f(8, 4096, 16, 128, 128, BF16) == 8 * 16 * 64 * (DPLR_UNIT + 2 * 64 * 256) + 256
+    assert f(1, 65, 1, 128, 128, BF16) == 2 * DPLR_UNIT + 2 * 65 * 256 + 256    # U0, O0: one row per token
     assert f(1, 64, 1, 128, 128, F32) == 0 and f(1, 64, 1, 64, 128, BF16) == 0 and f(-1, 64, 1, 128, 128, BF16) == 0
 
 
