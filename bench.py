@@ -60,6 +60,7 @@ DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + 3 * 2 * D + 4 * D + 2 + 2 * D   # 132,
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_prefill.hip")
 DECODE_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_decode.hip")
 BACKWARD_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_backward.hip")
+DPLR_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_dplr.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {
@@ -292,9 +293,14 @@ def dplr_line(steps, warmup, kda_ms=None):
                                                     out=o, S_T=S_T, workspace=ws), steps, warmup)
     ht = B * T * H
     alg = ht * DPLR_BYTES_PER_HEAD_TOKEN + STATE_BYTES * B * H
+    parts = [measured_traffic(key, src) for key, src in
+             (("dplr_prep", DPLR_KERNEL_SRC), ("dplr_scan", PREFILL_KERNEL_SRC))]
+    traffic = sum(parts) if all(p is not None for p in parts) else None
     out = {"workload": f"kda_dplr_chunk_fwd B={B} T={T} H={H} bf16 (a = beta ka, b = alpha kb, ka, kb free)",
            "ms_per_step": round(t * 1e3, 4), "head_tokens_per_s": round(ht / t, 1),
            "alg_bytes_per_step": alg, "frac_of_hbm_peak": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+           "traffic_bytes_per_step": traffic,
+           "traffic_gb_s": None if traffic is None else round(traffic / t / 1e9, 1),
            "workspace_bytes": ws.numel()}
     kda2 = prefill_line(WORKLOADS["c2"], steps, warmup, "two_kernel")
     out["kda_same_shape_ms"] = {"two_kernel": round(kda2["t"] * 1e3, 4)}
