@@ -200,9 +200,10 @@ mqa_split_kernel(const bf16_t* q, const bf16_t* cache, float* part, float* ml, i
 }
 
 // Merge of the splits: workgroup (sequence, head, 64 latent columns); the
-// split weights e^{m_s - M} are formed once in LDS, then 4 lanes per column
-// each sum a quarter of the splits.
-constexpr int CMB_COLS = 64, CMB_LANES = 4, CMB_MAXSPLIT = 1024;
+// split weights e^{m_s - M} are formed once in LDS, then 16 lanes per column
+// each sum a sixteenth of the splits (many loads in flight: the merge is
+// latency-bound), and the 16 partial sums are added in LDS.
+constexpr int CMB_COLS = 64, CMB_LANES = 16, CMB_MAXSPLIT = 1024;
 __global__ void __launch_bounds__(CMB_COLS * CMB_LANES)
 mqa_combine_kernel(const float* part, const float* ml, bf16_t* o, int nsplit, int H)
 {
@@ -244,7 +245,9 @@ mqa_combine_kernel(const float* part, const float* ml, bf16_t* o, int nsplit, in
     red[t] = acc;
     __syncthreads();
     if (lane4 == 0) {
-        const float sum = (red[col] + red[col + CMB_COLS]) + (red[col + 2 * CMB_COLS] + red[col + 3 * CMB_COLS]);
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < CMB_LANES; ++i) sum += red[col + i * CMB_COLS];
         o[(size_t)bh * MD + d] = (bf16_t)(sum / Lsh);
     }
 }
