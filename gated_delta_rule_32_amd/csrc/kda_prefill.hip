@@ -742,18 +742,20 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 // each), reading the A-operand with the same split, so each product is a
 // plain sum over k.
 constexpr int SC_KIB = WS_CHUNK / 1024;                   // 1 KiB pieces per block
-template <int NCW> struct ScanCfg {                       // NCW consumer waves
+template <int NCW, bool SAVE = false> struct ScanCfg {   // NCW consumer waves
     static constexpr int DV = 16 * NCW;                   // value columns per workgroup
     static constexpr int NLW = 8 - NCW;                   // loader waves (two waves per SIMD)
     static constexpr int NT = 64 * (NLW + NCW);
     static constexpr int OFF_VT = 0;                      // V^T [DV cols][72] bf16
     static constexpr int OFF_BLK = DV * WS_P64 * 2;       // workspace image
     static constexpr int STAGE = OFF_BLK + WS_CHUNK;
-    static constexpr int OFF_O = 2 * STAGE;               // output staging [2][64][DV] bf16
-    static constexpr int TOTAL = OFF_O + 2 * C * DV * 2;
+    static constexpr int OFF_O = 2 * STAGE;               // output staging [2][64][DV] bf16 (not in SAVE mode)
+    static constexpr int TOTAL = OFF_O + (SAVE ? 0 : 2 * C * DV * 2);
     static constexpr int VG = DV / 8;                     // 16-byte units per token row
+    static constexpr int VPL = (C * VG + 255) / 256;      // V units per lane of the first four waves
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
-    static_assert(C * VG <= 256, "one V / output unit per lane of the first four loader waves");
+    static_assert(NLW >= 4, "the first four waves are loaders");
+    static_assert(SAVE || VPL == 1, "one output unit per lane of the first four loader waves");
 };
 
 // SAVE (the forward part of the backward pass): no output (Qt S and Aqk Vn
@@ -770,14 +772,15 @@ template <int NCW> struct ScanCfg {                       // NCW consumer waves
 // this workgroup's value columns is loaded into the Tm slot, and O0 is added
 // by the loader lanes when they store the output.
 template <int NCW, bool SAVE, bool DPLR = false>
-__global__ void __launch_bounds__(ScanCfg<NCW>::NT)
+__global__ void __launch_bounds__(512)
 chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
                   int T, int H, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
                   const bf16_t* h0, const bf16_t* o0)
 {
     static_assert(!(SAVE && DPLR), "the backward pass is KDA only");
     typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-    using SC = ScanCfg<NCW>;
+    using SC = ScanCfg<NCW, SAVE>;
+    static_assert(SC::NT == 512, "eight waves (the launch bounds)");
     __shared__ __attribute__((aligned(1024))) char smem[SC::TOTAL];
 
     const int t = threadIdx.x, lane = t & 63;
@@ -801,13 +804,14 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     // ---- loader side: lane pt moves V / output unit (token ut, columns 8 ug ..)
     const int pt = t & 255, ug = pt % SC::VG, ut = pt / SC::VG;
     const bool ulane = t < 256 && ut < C;     // lanes of the first four loader waves
-    bf16x8 vrow = bf16x8{}, o0row = bf16x8{};
+    bf16x8 vrow[SC::VPL], o0row = bf16x8{};   // unit i of a lane: pt + 256 i
     // DPLR: the H0 slice [128][DV] (unpadded) replaces the Tm pages
     constexpr int TM_P0 = WS_TM / 1024, TM_P1 = WS_QK / 1024;
     constexpr int HPR = SC::DV / 8;                       // 16-byte pieces per H0 row
     constexpr int HRPP = 64 / HPR;                        // H0 rows per 1 KiB page
     constexpr int HPAGES = DK / HRPP;
-    static_assert(WS_TM % 1024 == 0 && WS_QK % 1024 == 0 && HPAGES <= TM_P1 - TM_P0, "H0 slice fits the Tm slot");
+    static_assert(!DPLR || (WS_TM % 1024 == 0 && WS_QK % 1024 == 0 && HPAGES <= TM_P1 - TM_P0),
+                  "H0 slice fits the Tm slot");
     auto load_block = [&](int n) {            // workspace block n -> stage n % 2
         const char* src = wsh + (size_t)n * WS_CHUNK;
         char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
@@ -827,16 +831,25 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
         }
     };
     auto load_v = [&](int n) {
-        if (!ulane) return;
-        const int tok = min(n * C + ut, T - 1);
-        vrow = *reinterpret_cast<const bf16x8*>(v + hbase + (size_t)tok * tokstride + j0 + 8 * ug);
+        if (t >= 256) return;
+#pragma unroll
+        for (int i = 0; i < SC::VPL; ++i) {
+            const int u = pt + 256 * i, uu = u / SC::VG, ug2 = u % SC::VG;
+            if (uu >= C) continue;
+            const int tok = min(n * C + uu, T - 1);
+            vrow[i] = *reinterpret_cast<const bf16x8*>(v + hbase + (size_t)tok * tokstride + j0 + 8 * ug2);
+        }
     };
     auto write_vt = [&](int n) {              // V^T of chunk n into stage n % 2
         bf16_t* vt = reinterpret_cast<bf16_t*>(smem + (n & 1) * SC::STAGE + SC::OFF_VT);
-        if (ulane) {
-            const bool ok = n * C + ut < T;
+        if (t >= 256) return;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) vt[(8 * ug + c) * WS_P64 + ut] = ok ? vrow[c] : bf16_t{};
+        for (int i = 0; i < SC::VPL; ++i) {
+            const int u = pt + 256 * i, uu = u / SC::VG, ug2 = u % SC::VG;
+            if (uu >= C) continue;
+            const bool ok = n * C + uu < T;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) vt[(8 * ug2 + c) * WS_P64 + uu] = ok ? vrow[i][c] : bf16_t{};
         }
     };
     auto load_o0 = [&](int n) {               // DPLR: O0 row of chunk n, stored with it next step
@@ -1102,12 +1115,15 @@ hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, 
     else if (gate == GATE_NONE) KDA_PREP(GATE_NONE);
     else KDA_PREP(GATE_CHANNEL);
 #undef KDA_PREP
-    const int ncw = heads * 4 >= 256 ? 2 : 1;
-#define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, true>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
-                                         dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws_fwd, (const bf16_t*)v, S0, \
+    // (save mode has no output staging, so 64-column slices fit: one round of
+    // workgroups from 128 heads on)
+    const int ncw = heads * 2 >= 256 ? 4 : heads * 4 >= 256 ? 2 : 1;
+#define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, true>), dim3((unsigned)(heads * (DK / ScanCfg<NCW, true>::DV))), \
+                                         dim3(ScanCfg<NCW, true>::NT), 0, stream, (const char*)ws_fwd, (const bf16_t*)v, S0, \
                                          (bf16_t*)nullptr, (float*)nullptr, T, H, svS, svY, svVn, \
                                          (const bf16_t*)nullptr, (const bf16_t*)nullptr)
-    if (ncw == 2) KDA_SCAN(2);
+    if (ncw == 4) KDA_SCAN(4);
+    else if (ncw == 2) KDA_SCAN(2);
     else KDA_SCAN(1);
 #undef KDA_SCAN
     return hipGetLastError();
