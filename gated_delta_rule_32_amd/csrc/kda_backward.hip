@@ -49,14 +49,19 @@ template <int NCW> struct BScanCfg {
     static constexpr int DV = 16 * NCW;
     static constexpr int NLW = 8 - NCW;
     static constexpr int NT = 512;
-    static constexpr int OFF_DOT = 0;                       // dO^T [DV][72]
-    static constexpr int OFF_BLK = DV * WSB_P64 * 2;
+    static constexpr int OFF_DOT = 0;                       // dO^T [DV][64], swizzled (dot_at)
+    static constexpr int OFF_BLK = DV * C * 2;
     static constexpr int STAGE = OFF_BLK + WSB_CHUNK;
     static constexpr int TOTAL = 2 * STAGE;
     static constexpr int VG = DV / 8;                       // 16-byte units per token row
+    static constexpr int VPL = (C * VG + 255) / 256;        // dO units per lane of the first four waves
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
-    static_assert(C * VG <= 256, "one dO unit per lane of the first four loader waves");
+    static_assert(NLW >= 4, "the first four waves are loaders");
 };
+// Element (value column j, token r) of the dO^T tile: rows of 64 tokens with
+// no padding, their 8-token blocks XOR-permuted by the low bits of j, so that
+// the consumers' reads of 4 tokens from 16 consecutive rows hit distinct banks.
+__device__ __forceinline__ int dot_at(int j, int r) { return j * C + ((((r >> 3) ^ (j & 7))) << 3) + (r & 7); }
 constexpr int BS_KIB = WSB_CHUNK / 1024;
 
 template <int NCW>
@@ -85,9 +90,8 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
     const char* wsh = wsb + (size_t)head * nchunks * WSB_CHUNK;
 
     // ---- loader side: lane pt moves dO unit (token ut, columns 8 ug ..)
-    const int pt = t & 255, ug = pt % SC::VG, ut = pt / SC::VG;
-    const bool ulane = t < 256 && ut < C;
-    bf16x8 drow = bf16x8{};
+    const int pt = t & 255;
+    bf16x8 drow[SC::VPL];                     // unit i of a lane: pt + 256 i
     auto load_block = [&](int n) {
         const char* src = wsh + (size_t)n * WSB_CHUNK;
         char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
@@ -96,16 +100,25 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
                                              (__attribute__((address_space(3))) void*)(dst + u * 1024), 16, 0, 0);
     };
     auto load_do = [&](int n) {
-        if (!ulane) return;
-        const int tok = min(n * C + ut, T - 1);
-        drow = *reinterpret_cast<const bf16x8*>(dO + hbase + (size_t)tok * tokstride + j0 + 8 * ug);
+        if (t >= 256) return;
+#pragma unroll
+        for (int i = 0; i < SC::VPL; ++i) {
+            const int u = pt + 256 * i, ut = u / SC::VG, ug = u % SC::VG;
+            if (ut >= C) continue;
+            const int tok = min(n * C + ut, T - 1);
+            drow[i] = *reinterpret_cast<const bf16x8*>(dO + hbase + (size_t)tok * tokstride + j0 + 8 * ug);
+        }
     };
     auto write_dot = [&](int n) {             // dO^T of chunk n into stage n % 2 (zero past T)
         bf16_t* dt = reinterpret_cast<bf16_t*>(smem + (n & 1) * SC::STAGE + SC::OFF_DOT);
-        if (ulane) {
+        if (t >= 256) return;
+#pragma unroll
+        for (int i = 0; i < SC::VPL; ++i) {
+            const int u = pt + 256 * i, ut = u / SC::VG, ug = u % SC::VG;
+            if (ut >= C) continue;
             const bool ok = n * C + ut < T;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) dt[(8 * ug + c) * WSB_P64 + ut] = ok ? drow[c] : bf16_t{};
+            for (int c = 0; c < 8; ++c) dt[dot_at(8 * ug + c, ut)] = ok ? drow[i][c] : bf16_t{};
         }
     };
 
@@ -157,8 +170,8 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
             for (int p = 0; p < 4; ++p) sb[p] = cat8(to_bf16x4(acc_s[2 * p]), to_bf16x4(acc_s[2 * p + 1]));
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                dob[p] = cat8(ld4(sdOT + jc * WSB_P64 + 32 * p + 4 * lg),
-                              ld4(sdOT + jc * WSB_P64 + 32 * p + 16 + 4 * lg));
+                dob[p] = cat8(ld4(sdOT + dot_at(jc, 32 * p + 4 * lg)),
+                              ld4(sdOT + dot_at(jc, 32 * p + 16 + 4 * lg)));
 
             // dVn = Aqk^T dO + Kt dS'
             f32x4 dvn[4];
@@ -647,11 +660,12 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const f
                                              wsb, svS, svY, svVn, stream, gate);
     if (err != hipSuccess) return err;
 
-    const int ncw = heads * 4 >= 256 ? 2 : 1;
+    const int ncw = heads * 2 >= 256 ? 4 : heads * 4 >= 256 ? 2 : 1;   // one round of workgroups when possible
 #define KDA_BSCAN(NCW) hipLaunchKernelGGL(chunk_bwd_scan_kernel<NCW>, dim3((unsigned)(heads * (DK / BScanCfg<NCW>::DV))), \
                                           dim3(512), 0, stream, (const char*)wsb, (const bf16_t*)dO, dST, (bf16_t*)dv, \
                                           dS0, svdS, svdZ, T, H)
-    if (ncw == 2) KDA_BSCAN(2);
+    if (ncw == 4) KDA_BSCAN(4);
+    else if (ncw == 2) KDA_BSCAN(2);
     else KDA_BSCAN(1);
 #undef KDA_BSCAN
 
