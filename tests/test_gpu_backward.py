@@ -168,3 +168,13 @@ def test_gate_variants_full_size_sampled_heads(name, gate):
     for (b, h), ref in zip(heads, refs):
         one = [x[b:b + 1, :, h:h + 1] if x is not None else None for x in got[:5]] + [got[5][b:b + 1, h:h + 1]]
         check(one, reduce_gate(ref, gate))
+
+
+def test_one_round_slices_with_ragged_tail():
+    """128 heads select 64-column slices in both state scans (one round of
+    workgroups); T = 150 leaves a ragged last chunk.  Every gradient of every
+    head against the oracle."""
+    print("backward 128 heads (64-column scan slices), T=150", flush=True)
+    inp = inputs.prefill_inputs(2, 150, 64, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=77)
+    gr = inputs.grad_inputs(2, 150, 64, ds_std=0.05, seed=77)
+    check(run_bwd(inp, gr), oracle_grads(inp, gr))
