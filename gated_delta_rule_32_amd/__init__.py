@@ -63,13 +63,18 @@ def scan_workspace_bytes(B, T, H):
 
 
 def _workspace(device, nbytes):
+    """The "auto" workspace: one growing buffer per (device, stream), so calls
+    on different streams never share scratch memory.  It is allocated while
+    that stream is current, so torch's allocator orders its reuse after the
+    stream's pending work when it is replaced by a larger one."""
     import torch
     if nbytes <= 0:
         return None
-    buf = _ws_cache.get(device)
+    key = (torch.device(device), _stream(device))
+    buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _ws_cache[device] = buf
+        _ws_cache[key] = buf
     return buf
 
 

@@ -131,3 +131,23 @@ def test_graph_captured_decode_step_replays():
         print(f"  replay {st}: o equal {torch.equal(out_static, o_e)}  S equal {torch.equal(S_graph, S_eager)}",
               flush=True)
         assert torch.equal(out_static, o_e) and torch.equal(S_graph, S_eager)
+
+
+def test_auto_workspace_is_per_stream():
+    """Two streams, each running the two-kernel schedule with the "auto"
+    workspace at the same time, give exactly the results of running the two
+    calls one after the other (the cached workspace is per stream)."""
+    print("auto workspace on two streams", flush=True)
+    d = [{n: (x.to(DEV) if x is not None else None) for n, x in
+          inputs.prefill_inputs(1, 700, 4, dtype="bfloat16", seed=s).items()} for s in (31, 32)]
+    args = lambda x: (x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    ref = [kda.chunk_fwd(*args(x)) for x in d]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = []
+    for x, st in zip(d, streams):
+        with torch.cuda.stream(st):
+            got.append(kda.chunk_fwd(*args(x)))
+    torch.cuda.synchronize()
+    for (o, S), (ro, rS) in zip(got, ref):
+        assert torch.equal(o, ro) and torch.equal(S, rS)
