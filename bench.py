@@ -408,6 +408,75 @@ def backward_line(steps, warmup, with_cpu=False, wl="c2"):
     return out
 
 
+def _oracle_threads():
+    """Threads the numpy / BLAS parts of the oracle may use on this host."""
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def _oracle_timing(fn, units, unit, cores, sample):
+    """The oracle as it stands, timed on the host over one bounded sample."""
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    return {"value": round(units / dt, 1), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{sample}, {dt:.2f} s wall"}
+
+
+def oracle_timings():
+    """The oracles of the other measured paths, each on a sample of about a
+    second of CPU work (inputs drawn as for the GPU lines)."""
+    import numpy as np
+    import torch
+    from gated_delta_rule_32_amd import inputs
+    from oracle import dplr_ref, kda_layer_ref, kda_ref, mqa_ref
+    out = {}
+    threads = kda_ref.max_threads()
+    # decode: 32 sequences x 32 heads, 64 steps, through the recurrence from the decode state
+    N, H, steps = 32, 32, 64
+    S0 = inputs.decode_state(N, H, s_std=0.02, seed=4)
+    tk = inputs.decode_tokens(N, H, steps, seed=4)
+    args = [kda_ref._f64(tk[n]).transpose(1, 0, 2, 3) for n in ("q", "k", "v", "g")]
+    beta = kda_ref._f64(tk["beta"]).transpose(1, 0, 2)
+    s0 = kda_ref._f64(S0)
+    log(f"[bench] oracle timing: decode {N}x{H} heads x {steps} steps")
+    out["decode"] = _oracle_timing(lambda: kda_ref.recurrent(*args[:3], args[3], beta, s0, nthreads=threads),
+                                   N * H * steps * DECODE_BYTES_PER_HEAD / 1e9, "GB/s (state bytes)", threads,
+                                   f"{N}x{H} heads x {steps} steps of the fp64 recurrence (C, OpenMP)")
+    # gate variants: 4 x 16 heads x 4096 tokens each
+    for wl, gate in (("gdn", "head"), ("deltanet", "none")):
+        inp = inputs.prefill_inputs(4, 4096, 16, g_scale=0.05, seed=2, gate=gate)
+        g = (np.zeros(inp["q"].shape) if inp["g"] is None else
+             np.repeat(kda_ref._f64(inp["g"])[..., None], D, axis=-1))
+        a = [kda_ref._f64(inp[n]) for n in ("q", "k", "v")] + [g, kda_ref._f64(inp["beta"])]
+        log(f"[bench] oracle timing: {wl}")
+        out[wl] = _oracle_timing(lambda: kda_ref.recurrent(*a, None, nthreads=threads), 64 * 4096,
+                                 "head-tokens/s", threads, "4x16 heads x 4096 tokens of the fp64 recurrence "
+                                 "(decay copied to every channel or zero)")
+    # DPLR: 2 heads x 4096 tokens, numpy
+    dp = inputs.dplr_inputs(1, 4096, 2, seed=7)
+    log("[bench] oracle timing: dplr")
+    out["dplr"] = _oracle_timing(lambda: dplr_ref.recurrent(*(dp[n] for n in ("q", "k", "v", "a", "b", "g")), None),
+                                 2 * 4096, "head-tokens/s", 1, "2 heads x 4096 tokens of the fp64 DPLR "
+                                 "recurrence (numpy, one token at a time)")
+    # full-attention decode: 32 heads over 2^18 cached tokens
+    Tm = 1 << 18
+    q, c = inputs.mqa_inputs(1, Tm, 32, seed=6)
+    log("[bench] oracle timing: full-attention decode")
+    out["full_attention_decode"] = _oracle_timing(lambda: mqa_ref.decode(q, c, 1.0 / 512 ** 0.5), Tm * 1024 / 1e9,
+                                                  "GB/s (cache bytes)", _oracle_threads(),
+                                                  f"1 sequence, 32 heads over {Tm} cached tokens (fp64 numpy / BLAS)")
+    # layer: 1024 tokens with the full-size weights
+    Tl = 1024
+    li = inputs.layer_inputs(B=1, T=Tl, d_model=2048, H=16, seed=5, gate_rank=D)
+    W = {n: li[n] for n in li if n != "x"}
+    log("[bench] oracle timing: layer")
+    out["layer"] = _oracle_timing(lambda: kda_layer_ref.layer_forward(li["x"], W, 16), Tl, "tokens/s",
+                                  _oracle_threads(), f"{Tl} tokens, d_model 2048, 16 heads, full-size weights "
+                                  "(fp64 numpy / BLAS and the C recurrence)")
+    del torch
+    return out
+
+
 def cpu_baseline(inp):
     """The fp64 oracle as it stands, on the host cores, on the whole workload."""
     import numpy as np
@@ -530,6 +599,14 @@ def main():
         line["backward"] = backward_line(min(args.steps, 20), args.warmup, with_cpu=not args.no_cpu)
     if not args.no_cpu and args.workload is None:
         line["cpu_baseline"] = cpu_baseline(pre["inp"])
+        orc = oracle_timings()
+        for key, target in (("decode", line.get("decode")), ("full_attention_decode", line.get("full_attention_decode")),
+                            ("layer", line.get("layer")), ("dplr", line.get("dplr_comparison"))):
+            if target is not None:
+                target["cpu_oracle"] = orc[key]
+        for wl in ("gdn", "deltanet"):
+            if wl in line.get("gate_variants", {}):
+                line["gate_variants"][wl]["cpu_oracle"] = orc[wl]
     print(json.dumps(line))
 
 
