@@ -53,9 +53,22 @@ def test_prefill_gate_variants(gate, dtype, schedule, T):
 
 
 @pytest.mark.parametrize("gate", ["head", "none"])
-@pytest.mark.parametrize("H", [40, 100])
+@pytest.mark.parametrize("T", [1, 65, 200])
+def test_128_heads_gate_variants(gate, T):
+    """64-column slices (128 heads) with each gate layout: every output and state entry."""
+    print(f"gated prefill 128 heads gate={gate} T={T}", flush=True)
+    inp = inputs.prefill_inputs(2, T, 64, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=200 + T, gate=gate)
+    o, S = run(inp, "fused")
+    o_ref, S_ref = oracle(inp)
+    eo, es = max_rel_err(o, o_ref), max_rel_err(S, S_ref)
+    print(f"  o err {eo:.3e}  S err {es:.3e}", flush=True)
+    assert eo <= TOL["bfloat16"] and es <= TOL["bfloat16"]
+
+
+@pytest.mark.parametrize("gate", ["head", "none"])
+@pytest.mark.parametrize("H", [40, 100, 128])
 def test_prefill_gate_slice_widths(gate, H):
-    """Head counts that select the 32- and 64-column fused kernels."""
+    """Head counts that select the 16-, 32- and 64-column fused kernels."""
     print(f"gated prefill gate={gate} H={H}", flush=True)
     inp = inputs.prefill_inputs(1, 150, H, dtype="bfloat16", g_scale=0.05, s0_std=0.02, seed=H, gate=gate)
     o, S = run(inp, "fused")

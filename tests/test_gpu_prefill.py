@@ -65,8 +65,26 @@ def test_ragged_lengths_with_initial_state(dtype, schedule, T):
     check(inp, o, S, TOL[dtype])
 
 
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 200])
+def test_128_heads_ragged_lengths(T):
+    """128 heads select the fused kernel with 64-column value slices (two
+    workgroups per head): every output and state entry, ragged tails."""
+    print(f"prefill 128 heads B=2 H=64 T={T}", flush=True)
+    inp = inputs.prefill_inputs(2, T, 64, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=100 + T)
+    o, S = run(to_dev(inp))
+    check(inp, o, S, TOL["bfloat16"])
+
+
+def test_128_heads_strong_decay():
+    """Chunk sums of the log-decay down to about -65 with 64-column slices."""
+    print("prefill 128 heads strong decay", flush=True)
+    inp = inputs.prefill_inputs(1, 200, 128, dtype="bfloat16", g_scale=1.0, s0_std=0.05, seed=8)
+    o, S = run(to_dev(inp))
+    check(inp, o, S, TOL["bfloat16"])
+
+
 @pytest.mark.parametrize("schedule", ["fused", "two_kernel"])
-@pytest.mark.parametrize("H", [1, 40, 100])
+@pytest.mark.parametrize("H", [1, 40, 100, 128])
 def test_bf16_slice_widths(H, schedule):
     """Head counts that select each value-slice width (16, 32, 64 columns)."""
     print(f"prefill slice widths H={H} schedule={schedule}", flush=True)
@@ -126,9 +144,12 @@ def test_schedules_agree_closely():
     assert max_rel_err(S2, S1.cpu().numpy()) <= 1e-2
 
 
-@pytest.mark.parametrize("schedule", ["fused", "two_kernel"])
+@pytest.mark.parametrize("schedule", ["fused", "two_kernel", "fused_128_heads"])
 def test_state_options_and_edge_cases(schedule):
-    inp = inputs.prefill_inputs(2, 77, 2, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=5)
+    # (128 heads without a workspace select 64-column slices)
+    H = 64 if schedule == "fused_128_heads" else 2
+    schedule = "fused" if schedule == "fused_128_heads" else schedule
+    inp = inputs.prefill_inputs(2, 77, H, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=5)
     d = to_dev(inp)
     go = lambda S0="inp", **kw: run(d, S0=S0, schedule=schedule, **kw)  # noqa: E731
     o_ref, S_ref = go()

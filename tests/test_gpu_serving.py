@@ -34,11 +34,11 @@ def packed(lengths, H, dtype, gate, seed):
 
 
 @pytest.mark.parametrize("gate", ["channel", "head", "none"])
-@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
-def test_varlen_prefill_matches_each_sequence(gate, dtype):
+@pytest.mark.parametrize("dtype,H", [("float32", 3), ("bfloat16", 3), ("bfloat16", 16)])
+def test_varlen_prefill_matches_each_sequence(gate, dtype, H):
+    """(8 sequences x 16 heads select 64-column slices.)"""
     lengths = [1, 63, 64, 65, 0, 130, 200, 7]
-    H = 3
-    print(f"varlen prefill gate={gate} dtype={dtype} lengths={lengths}", flush=True)
+    print(f"varlen prefill gate={gate} dtype={dtype} H={H} lengths={lengths}", flush=True)
     inp, S0, cu = packed(lengths, H, dtype, gate, seed=21)
     d = {n: (x[0].to(DEV) if x is not None and n != "S0" else None) for n, x in inp.items()}
     o, S = kda.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"],
