@@ -209,10 +209,18 @@ gemm_nt_large_kernel(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, 
     const int ln = lane & 15, lg = lane >> 4;
     const int wm = wave >> 2, wn = wave & 3;
 
-    // N strips fastest: workgroup i goes to XCD i % 8, which then keeps one
-    // strip of B in its L2
-    const int tiles_n = (N + LBN - 1) / LBN;
-    const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+    // Workgroups are dealt to the 8 XCDs round-robin.  When the tile rows split
+    // evenly, XCD x takes an eighth of the row blocks with all their column
+    // tiles, so that the workgroups running together on an XCD share A tiles
+    // in its L2 (A, the long operand, is then read about once, and the small B
+    // comes from the shared last-level cache); otherwise N strips go fastest.
+    const int tiles_n = (N + LBN - 1) / LBN, tiles_m = (M + LBM - 1) / LBM;
+    int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+    if (tiles_m % 8 == 0) {
+        const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+        tm = x * (tiles_m / 8) + j / tiles_n;
+        tn = j % tiles_n;
+    }
     const int m0 = tm * LBM, n0 = tn * LBN;
 
     // loads of one K-step: 32 segments of A, 32 of B, 8 per wave
