@@ -192,9 +192,14 @@ gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
 // with 16-byte global-to-LDS loads: one load instruction fills 1 KiB = 8
 // rows, and lane l fetches the 16-byte chunk (l % 8) ^ (row % 8) of its row,
 // so LDS rows hold their chunks XOR-swizzled and the MFMA fetches (16 rows,
-// one chunk column) touch distinct banks.  Two stages: the next K-step's
-// loads are in flight while the current one is multiplied; one barrier per
-// K-step.
+// one chunk column) touch distinct banks.  Two stages, one barrier per
+// K-step, software-pipelined: the barrier sits between the step's two 32-wide
+// halves.  Before it, the first half's MFMAs run while the second half's
+// operands are read; after it, the next step's loads go out into the stage
+// just released, and the second half's MFMAs hide the reads of the next
+// step's first-half operands.  Each step's loads have a whole step to land,
+// and no wave waits on LDS right after the barrier.  K must be a multiple of
+// 64 (the layer's feature sizes are).
 constexpr int LBM = 256, LBN = 256, LBK = 64;
 constexpr int LGT = 512;
 constexpr int LSTAGE = (LBM + LBN) * LBK * 2;      // 64 KiB
@@ -249,31 +254,56 @@ gemm_nt_large_kernel(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, 
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // operands of one 32-wide half step kk: 4 B and 8 A fragments
+    bf16x8 f0b[4], f0a[8], f1b[4], f1a[8];
+    auto rd = [&](int stage, int kk, bf16x8 (&fb)[4], bf16x8 (&fa)[8]) {
+        const char* sA = smem + stage * LSTAGE;
+        const char* sB = sA + LBM * LBK * 2;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) fb[nb] = frag(sB, 64 * wn + 16 * nb + ln, 4 * kk + lg);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) fa[mb] = frag(sA, 128 * wm + 16 * mb + ln, 4 * kk + lg);
+    };
+    auto mm = [&](bf16x8 (&fb)[4], bf16x8 (&fa)[8]) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+    };
+
     const int KT = K / LBK;
     issue(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     block_sync();
+    issue(min(1, KT - 1) * LBK, 1);
+    rd(0, 0, f0b, f0a);
     for (int kt = 0; kt < KT; ++kt) {
         const int stage = kt & 1;
-        if (kt + 1 < KT) issue((kt + 1) * LBK, stage ^ 1);
-        const char* sA = smem + stage * LSTAGE;
-        const char* sB = sA + LBM * LBK * 2;
+        // first half: its MFMAs, with one second-half operand read per two
+        rd(stage, 1, f1b, f1a);
+        mm(f0b, f0a);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {               // two 32-wide K slices
-            bf16x8 fb[4], fa[8];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) fb[nb] = frag(sB, 64 * wn + 16 * nb + ln, 4 * kk + lg);
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) fa[mb] = frag(sA, 128 * wm + 16 * mb + ln, 4 * kk + lg);
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
         }
-        __builtin_amdgcn_s_waitcnt(0);                 // next stage loaded (and this one's reads done)
-        block_sync();
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0);        // step kt+1 landed; this step's reads done
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // step kt+2 into the stage just released (clamped: at the end the last
+        // tile is reloaded into a stage that is not read again), the next
+        // step's first-half operands (after the last step: unused reads of the
+        // idle stage), then the second half's MFMAs
+        issue(min(kt + 2, KT - 1) * LBK, stage);
+        rd(stage ^ 1, 0, f0b, f0a);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(f1b, f1a);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
 
     // epilogue: lane holds C[m][n .. n+3] for m = .. + ln, n = .. + 4 lg
 #pragma unroll
