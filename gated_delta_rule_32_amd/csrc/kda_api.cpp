@@ -63,7 +63,7 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dty
 {
     if (B <= 0 || T <= 0 || H <= 0 || dk != kHeadDim || dv != kHeadDim || dtype != KDA_BF16) return 0;
     if (!kda::chunk_prefers_two_kernel(B, T, H, dtype)) return 0;
-    return kda::chunk_ws_bytes(B, T, H);
+    return kda::chunk_fwd_ws_bytes(B, T, H);
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v,
@@ -123,11 +123,14 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
 
     // two-kernel schedule when a large enough workspace is supplied (bf16)
     void* ws = nullptr;
+    bool seg = false;
     const long long grid_prep = (long long)heads * ((T + 63) / 64);
     if (T > 0 && workspace && dtype == KDA_BF16 && grid_prep <= INT_MAX &&
         workspace_bytes >= kda::chunk_ws_bytes(B, T, H)) {
         if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
-        const Range rw{workspace, kda::chunk_ws_bytes(B, T, H)};
+        // with room for the segment buffers too, the scan may run in segments
+        seg = workspace_bytes >= kda::chunk_fwd_ws_bytes(B, T, H);
+        const Range rw{workspace, seg ? kda::chunk_fwd_ws_bytes(B, T, H) : kda::chunk_ws_bytes(B, T, H)};
         const Range all[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, g_bytes},
                              {beta, tok * es}, rS0, rST, {o, n_qk * es}};
         for (const Range& r : all)
@@ -141,7 +144,7 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
         if (!S_T || (const void*)S0 == (const void*)S_T) return KDA_OK;
         e = kda::launch_state_copy(S0, S_T, (long long)heads, s);
     } else {
-        e = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dtype, ws, s, gate);
+        e = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dtype, ws, s, gate, nullptr, seg);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

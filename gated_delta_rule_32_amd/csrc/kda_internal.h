@@ -16,7 +16,9 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v,
 
 // Chunked prefill over B*H heads of T >= 1 tokens (d_k = d_v = 128).  With
 // `ws` non-null (bf16 only, at least chunk_ws_bytes(B, T, H) bytes) the
-// two-kernel schedule runs; otherwise the fused single kernel.  `gate` is a
+// two-kernel schedule runs; otherwise the fused single kernel.  With `seg`
+// (ws then holds chunk_fwd_ws_bytes(B, T, H) bytes) its state scan runs in
+// segments when chunk_seg_count(B, T, H) > 1.  `gate` is a
 // kda_gate_t: g is [B, T, H, 128] (per channel), [B, T, H] (per head) or
 // unused (no decay).  With cu_seqlens (device, B + 1 entries) the B
 // "batches" are sequences packed along one token axis of T tokens (fused
@@ -25,11 +27,20 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             const float* g, const void* beta, const float* S0,
                             void* o, float* S_T, int B, int T, int H, int dtype,
                             void* ws, hipStream_t stream, int gate = KDA_GATE_CHANNEL,
-                            const int* cu_seqlens = nullptr);
+                            const int* cu_seqlens = nullptr, bool seg = false);
 
-// Bytes of workspace the two-kernel schedule needs: one 72,704-byte block of
-// key-side operands per (batch, head, 64-token chunk).
+// Bytes of the key-side operand blocks of the two-kernel schedule: one
+// 72,704-byte block per (batch, head, 64-token chunk).
 size_t chunk_ws_bytes(long long B, long long T, long long H);
+
+// Segments per head of the two-kernel schedule's state scan (1: one pass over
+// all chunks; more with 16 heads or fewer, see chunk_scan_kernel).
+int chunk_seg_count(long long B, long long T, long long H);
+
+// Bytes of workspace the two-kernel forward schedule needs: the operand
+// blocks, then with segments the segment summaries [B*H][nseg-1][128][256]
+// and entry states [B*H][nseg-1][128][128] (fp32).
+size_t chunk_fwd_ws_bytes(long long B, long long T, long long H);
 
 // Whether the two-kernel schedule is expected to be faster for this shape.
 bool chunk_prefers_two_kernel(long long B, long long T, long long H, int dtype);

@@ -191,7 +191,7 @@ size_t layer_ws_layout(long long B, long long T, long long H, long long rank, si
     const size_t sizes[KDA_LAYER_WS_REGIONS] = {
         R * 4 * HDm * 2, R * ldz * 4, R * HDm * 2, R * HDm * 2, R * HDm * 2,
         R * HDm * 4,     R * (size_t)H * 2, R * HDm * 2, R * HDm * 2,
-        two ? chunk_ws_bytes(B, T, H) : 0};
+        two ? chunk_fwd_ws_bytes(B, T, H) : 0};
     size_t p = 0;
     for (int i = 0; i < KDA_LAYER_WS_REGIONS; ++i) {
         if (off) off[i] = p;
@@ -239,7 +239,8 @@ hipError_t launch_layer_fwd(const LayerWeights& W, const bf16_t* x, bf16_t* y, i
                              B, T, H, stream)))
         return e;
     // 4. the KDA operator, zero initial state
-    if ((e = launch_chunk_fwd(q, k, v, g, beta, nullptr, o, nullptr, B, T, H, 1, kws, stream)))
+    if ((e = launch_chunk_fwd(q, k, v, g, beta, nullptr, o, nullptr, B, T, H, 1, kws, stream,
+                              KDA_GATE_CHANNEL, nullptr, true)))
         return e;
     // 5. RMSNorm(o) * sigmoid(W_g x), then W_o
     if ((e = launch_out_gate(o, pre + 3 * (size_t)HDm, NY, zg, R, H, stream))) return e;

@@ -44,6 +44,7 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace kda {
@@ -742,6 +743,8 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 // each), reading the A-operand with the same split, so each product is a
 // plain sum over k.
 constexpr int SC_KIB = WS_CHUNK / 1024;                   // 1 KiB pieces per block
+constexpr int SEG_NONE = 0, SEG_SUMMARY = 1, SEG_OUTPUT = 2;   // chunk_scan_kernel segment modes
+
 template <int NCW, bool SAVE = false> struct ScanCfg {   // NCW consumer waves
     static constexpr int DV = 16 * NCW;                   // value columns per workgroup
     static constexpr int NLW = 8 - NCW;                   // loader waves (two waves per SIMD)
@@ -771,15 +774,30 @@ template <int NCW, bool SAVE = false> struct ScanCfg {   // NCW consumer waves
 // H0 [head, chunk][128][128] (bf16) from the DPLR prep kernel: H0's slice of
 // this workgroup's value columns is loaded into the Tm slot, and O0 is added
 // by the loader lanes when they store the output.
-template <int NCW, bool SAVE, bool DPLR = false>
+//
+// SEG (few heads: the chunks of a head are split into segments of seg_len
+// chunks that run in parallel).  The chunk-to-chunk map is affine in the
+// state, S' = A_n S + B_n, and acts on each state column alike, so a segment
+// is summarised by its end state E from a zero entry state and its transition
+// P = A_last ... A_first, the end state of the identity matrix run with zero
+// values (the page's proposition S_r = P_r S_0 + H_r, taken per segment):
+//   SEG_SUMMARY: every segment but the last, 2 x 128 columns per head: value
+//     columns from S = 0, then identity columns with V = 0.  No output; the
+//     end state goes to segbuf [head][segment][128][256] fp32 (E | P).
+//   SEG_OUTPUT: every segment from its entry state (S0 for the first, else
+//     segbuf [head][segment - 1][128][128], written by seg_combine_kernel),
+//     with the output; the last segment writes S_T.
+template <int NCW, bool SAVE, bool DPLR = false, int SEG = SEG_NONE>
 __global__ void __launch_bounds__(512)
 chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
                   int T, int H, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
-                  const bf16_t* h0, const bf16_t* o0)
+                  const bf16_t* h0, const bf16_t* o0, int seg_len, float* segbuf)
 {
     static_assert(!(SAVE && DPLR), "the backward pass is KDA only");
+    static_assert(SEG == SEG_NONE || !(SAVE || DPLR), "segments: KDA forward only");
     typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-    using SC = ScanCfg<NCW, SAVE>;
+    constexpr bool NOOUT = SAVE || SEG == SEG_SUMMARY;      // no output products or stores
+    using SC = ScanCfg<NCW, NOOUT>;
     static_assert(SC::NT == 512, "eight waves (the launch bounds)");
     __shared__ __attribute__((aligned(1024))) char smem[SC::TOTAL];
 
@@ -788,13 +806,18 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     const bool loader = wave < SC::NLW;
     const int ln = lane & 15, lg = lane >> 4;
     const int cw = wave - SC::NLW;
-    constexpr int nsplit = DK / SC::DV;
+    constexpr int nsplit = (SEG == SEG_SUMMARY ? 2 * DK : DK) / SC::DV;
     const int nchunks = (T + C - 1) / C;
     const int nwg = gridDim.x, w = blockIdx.x;
     const int lid = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;   // slices of a head on one XCD
-    const int head = lid / nsplit, slice = lid % nsplit;
+    // segments per head in this launch (1 without SEG)
+    const int nsegs = SEG == SEG_NONE ? 1 : (nchunks + seg_len - 1) / seg_len - (SEG == SEG_SUMMARY ? 1 : 0);
+    const int head = lid / (nsplit * nsegs), seg = lid / nsplit % nsegs, slice = lid % nsplit;
+    const int c0 = SEG == SEG_NONE ? 0 : seg * seg_len;                  // chunks c0 .. c1-1
+    const int c1 = SEG == SEG_NONE ? nchunks : min(nchunks, c0 + seg_len);
+    const bool ident = SEG == SEG_SUMMARY && slice * SC::DV >= DK;       // identity columns, V = 0
     const int b = head / H, h = head % H;
-    const int j0 = slice * SC::DV;
+    const int j0 = slice * SC::DV % DK;
     const size_t tokstride = (size_t)H * DK;
     const size_t hbase = ((size_t)b * T * H + h) * DK;
     const size_t sbase = (size_t)head * DK * DK;
@@ -831,7 +854,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
         }
     };
     auto load_v = [&](int n) {
-        if (t >= 256) return;
+        if (t >= 256 || ident) return;
 #pragma unroll
         for (int i = 0; i < SC::VPL; ++i) {
             const int u = pt + 256 * i, uu = u / SC::VG, ug2 = u % SC::VG;
@@ -847,7 +870,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
         for (int i = 0; i < SC::VPL; ++i) {
             const int u = pt + 256 * i, uu = u / SC::VG, ug2 = u % SC::VG;
             if (uu >= C) continue;
-            const bool ok = n * C + uu < T;
+            const bool ok = !ident && n * C + uu < T;
 #pragma unroll
             for (int c = 0; c < 8; ++c) vt[(8 * ug2 + c) * WS_P64 + uu] = ok ? vrow[i][c] : bf16_t{};
         }
@@ -873,26 +896,33 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     const int jc = 16 * cw + ln;
     f32x4 acc_s[8];
     if (!loader) {
+        // entry state: S0, zero or the identity (summary), or the segment's
+        // entry state from seg_combine_kernel
+        const float* sin = S0 ? S0 + sbase : nullptr;
+        if (SEG == SEG_OUTPUT && seg > 0) sin = segbuf + ((size_t)head * (nsegs - 1) + seg - 1) * DK * DK;
+        if (SEG == SEG_SUMMARY) sin = nullptr;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc_s[cb][e] = S0 ? S0[sbase + (size_t)(16 * cb + 4 * lg + e) * DK + j0 + jc] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * cb + 4 * lg + e;
+                acc_s[cb][e] = sin ? sin[(size_t)r * DK + j0 + jc] : (ident && r == j0 + jc ? 1.f : 0.f);
+            }
     } else {
-        load_block(0);
-        load_v(0);
+        load_block(c0);
+        load_v(c0);
         __builtin_amdgcn_s_waitcnt(0);        // vmcnt, lgkmcnt and expcnt all zero
-        write_vt(0);
+        write_vt(c0);
     }
     lds_barrier();
 
-    for (int n = 0; n < nchunks; ++n) {
+    for (int n = c0; n < c1; ++n) {
         if (loader) {
-            if (n + 1 < nchunks) { load_block(n + 1); load_v(n + 1); }
-            if (!SAVE && n > 0) store_out(n - 1);
+            if (n + 1 < c1) { load_block(n + 1); load_v(n + 1); }
+            if (!NOOUT && n > c0) store_out(n - 1);
             if constexpr (DPLR) load_o0(n);
             __builtin_amdgcn_s_waitcnt(0);    // the stage must be complete at the barrier
-            if (n + 1 < nchunks) write_vt(n + 1);
+            if (n + 1 < c1) write_vt(n + 1);
         } else {
             const char* st = smem + (n & 1) * SC::STAGE;
             const bf16_t* sQt = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_QT);
@@ -917,7 +947,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             bf16x8 sb[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) sb[p] = cat8(to_bf16x4(acc_s[2 * p]), to_bf16x4(acc_s[2 * p + 1]));
-            constexpr int NF = SAVE ? 4 : 8;          // Kh (and Qt) fragments per block
+            constexpr int NF = NOOUT ? 4 : 8;         // Kh (and Qt) fragments per block
             bf16x8 fa[2][NF];
             auto frags = [&](int Rb, bf16x8 (&f)[NF]) {
                 const bf16_t* kr = sKh + (16 * Rb + ln) * WS_P128;
@@ -925,7 +955,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     f[p] = a_pair(kr, p, lg, true);
-                    if constexpr (!SAVE) f[4 + p] = a_pair(qr, p, lg, true);
+                    if constexpr (!NOOUT) f[4 + p] = a_pair(qr, p, lg, true);
                 }
             };
             f32x4 pk[4], qs[4];
@@ -937,7 +967,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[Rb & 1][p], sb[p], a, 0, 0, 0);
-                    if constexpr (!SAVE)
+                    if constexpr (!NOOUT)
                         c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[Rb & 1][4 + p], sb[p], c2, 0, 0, 0);
                 }
                 pk[Rb] = a;
@@ -982,7 +1012,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             }
 
             // O = Qt S + Aqk Vn -> LDS staging (stored to HBM by the loaders)
-            if constexpr (!SAVE)
+            if constexpr (!NOOUT)
 #pragma unroll
             for (int Rb = 0; Rb < 4; ++Rb) {
                 f32x4 a = qs[Rb];
@@ -1028,13 +1058,56 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     }
 
     if (loader) {
-        if (!SAVE) store_out(nchunks - 1);
-    } else if (S_T) {
+        if (!NOOUT) store_out(c1 - 1);
+    } else if (SEG == SEG_SUMMARY) {
+        float* dst = segbuf + ((size_t)head * nsegs + seg) * DK * 2 * DK + slice * SC::DV + jc;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(size_t)(16 * cb + 4 * lg + e) * 2 * DK] = acc_s[cb][e];
+    } else if (S_T && (SEG == SEG_NONE || seg == nsegs - 1)) {
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 S_T[sbase + (size_t)(16 * cb + 4 * lg + e) * DK + j0 + jc] = acc_s[cb][e];
+    }
+}
+
+// Entry states of the segments of SEG_OUTPUT: with E_j | P_j the summary of
+// segment j (end state from zero, transition), S_{j+1} = P_j S_j + E_j from
+// S_0 = S0 (or zero), in fp32.  One workgroup per (head, 16 state columns);
+// thread t computes row t / 2, columns 8 (t % 2) .. +7.
+__global__ void __launch_bounds__(256)
+seg_combine_kernel(const float* summ, const float* S0, float* entry, int nseg)
+{
+    __shared__ float cur[DK][16];
+    const int head = blockIdx.x / (DK / 16), j0 = blockIdx.x % (DK / 16) * 16;
+    const int t = threadIdx.x, r = t >> 1, c8 = (t & 1) * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        cur[r][c8 + c] = S0 ? S0[((size_t)head * DK + r) * DK + j0 + c8 + c] : 0.f;
+    __syncthreads();
+    for (int j = 0; j + 1 < nseg; ++j) {
+        const float* sm = summ + (((size_t)head * (nseg - 1) + j) * DK + r) * 2 * DK;   // row r of E_j | P_j
+        float acc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = sm[j0 + c8 + c];
+        for (int kk = 0; kk < DK; kk += 4) {
+            const f32x4 p = *reinterpret_cast<const f32x4*>(sm + DK + kk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[c] = fmaf(p[i], cur[kk + i][c8 + c], acc[c]);
+        }
+        __syncthreads();
+        float* out = entry + (((size_t)head * (nseg - 1) + j) * DK + r) * DK + j0 + c8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            cur[r][c8 + c] = acc[c];
+            out[c] = acc[c];
+        }
+        __syncthreads();
     }
 }
 
@@ -1053,7 +1126,7 @@ void launch_one(const void* q, const void* k, const void* v, const float* g, con
 template <int GATE>
 void launch_gate(const void* q, const void* k, const void* v, const float* g, const void* beta,
                  const float* S0, void* o, float* S_T, int B, int T, int H, int dtype, void* ws,
-                 hipStream_t stream, const int* cu)
+                 hipStream_t stream, const int* cu, bool seg)
 {
     const long long heads = (long long)B * H;
     if (dtype == 0) {
@@ -1066,12 +1139,34 @@ void launch_gate(const void* q, const void* k, const void* v, const float* g, co
                            dim3(NT), 0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
                            (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws, (char*)nullptr,
                            (const int*)nullptr);
+        const int nseg0 = seg ? chunk_seg_count(B, T, H) : 1;
+        const int L = (nchunks + nseg0 - 1) / nseg0;          // chunks per segment
+        const int nseg = (nchunks + L - 1) / L;                // as the kernels count them (<= nseg0)
+        if (nseg > 1) {
+            // few heads: segments in parallel (summaries, combine, outputs)
+            float* summ = reinterpret_cast<float*>((char*)ws + chunk_ws_bytes(B, T, H));
+            float* entry = summ + (size_t)heads * (nseg - 1) * DK * 2 * DK;
+            hipLaunchKernelGGL((chunk_scan_kernel<4, false, false, SEG_SUMMARY>),
+                               dim3((unsigned)(heads * (nseg - 1) * (2 * DK / ScanCfg<4, true>::DV))),
+                               dim3(ScanCfg<4, true>::NT), 0, stream, (const char*)ws, (const bf16_t*)v,
+                               (const float*)nullptr, (bf16_t*)nullptr, (float*)nullptr, T, H, (bf16_t*)nullptr,
+                               (bf16_t*)nullptr, (bf16_t*)nullptr, (const bf16_t*)nullptr, (const bf16_t*)nullptr,
+                               L, summ);
+            hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(heads * (DK / 16))), dim3(256), 0, stream,
+                               (const float*)summ, S0, entry, nseg);
+            hipLaunchKernelGGL((chunk_scan_kernel<2, false, false, SEG_OUTPUT>),
+                               dim3((unsigned)(heads * nseg * (DK / ScanCfg<2>::DV))), dim3(ScanCfg<2>::NT), 0,
+                               stream, (const char*)ws, (const bf16_t*)v, S0, (bf16_t*)o, S_T, T, H,
+                               (bf16_t*)nullptr, (bf16_t*)nullptr, (bf16_t*)nullptr, (const bf16_t*)nullptr,
+                               (const bf16_t*)nullptr, L, entry);
+            return;
+        }
         // value columns per scan workgroup: enough workgroups to cover the machine
         const int ncw = heads * 4 >= 256 ? 2 : 1;
 #define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, false>), dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), \
                                          dim3(ScanCfg<NCW>::NT), 0, stream, (const char*)ws, (const bf16_t*)v, S0, \
                                          (bf16_t*)o, S_T, T, H, (bf16_t*)nullptr, (bf16_t*)nullptr, (bf16_t*)nullptr, \
-                                         (const bf16_t*)nullptr, (const bf16_t*)nullptr)
+                                         (const bf16_t*)nullptr, (const bf16_t*)nullptr, 0, (float*)nullptr)
         if (ncw == 2) KDA_SCAN(2);
         else KDA_SCAN(1);
 #undef KDA_SCAN
@@ -1089,6 +1184,28 @@ void launch_gate(const void* q, const void* k, const void* v, const float* g, co
 size_t chunk_ws_bytes(long long B, long long T, long long H)
 {
     return (size_t)B * (size_t)H * (size_t)((T + C - 1) / C) * (size_t)WS_CHUNK;
+}
+
+int chunk_seg_count(long long B, long long T, long long H)
+{
+    // With 16 heads or fewer, one workgroup per 16 value columns leaves CUs
+    // idle; segments of each head then run in parallel (4 value-column
+    // workgroups per segment, about 256 workgroups in all), each segment at
+    // least two chunks long.
+    const long long heads = B * H, nchunks = (T + C - 1) / C;
+    if (heads > 16) return 1;
+    long long nseg = std::min<long long>(16, 64 / heads);
+    nseg = std::min(nseg, nchunks / 2);
+    if (nseg < 2) return 1;
+    const long long L = (nchunks + nseg - 1) / nseg;
+    return (int)((nchunks + L - 1) / L);     // no empty trailing segment
+}
+
+size_t chunk_fwd_ws_bytes(long long B, long long T, long long H)
+{
+    const int nseg = chunk_seg_count(B, T, H);
+    const size_t seg = nseg > 1 ? (size_t)B * H * (nseg - 1) * DK * DK * 4 * 3 : 0;   // summaries + entry states
+    return chunk_ws_bytes(B, T, H) + seg;
 }
 
 bool chunk_prefers_two_kernel(long long B, long long T, long long H, int dtype)
@@ -1121,7 +1238,7 @@ hipError_t launch_bwd_forward_part(const void* q, const void* k, const void* v, 
 #define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, true>), dim3((unsigned)(heads * (DK / ScanCfg<NCW, true>::DV))), \
                                          dim3(ScanCfg<NCW, true>::NT), 0, stream, (const char*)ws_fwd, (const bf16_t*)v, S0, \
                                          (bf16_t*)nullptr, (float*)nullptr, T, H, svS, svY, svVn, \
-                                         (const bf16_t*)nullptr, (const bf16_t*)nullptr)
+                                         (const bf16_t*)nullptr, (const bf16_t*)nullptr, 0, (float*)nullptr)
     if (ncw == 4) KDA_SCAN(4);
     else if (ncw == 2) KDA_SCAN(2);
     else KDA_SCAN(1);
@@ -1137,7 +1254,7 @@ hipError_t launch_dplr_scan(const char* blocks, const bf16_t* u0, const bf16_t* 
 #define KDA_SCAN(NCW) hipLaunchKernelGGL((chunk_scan_kernel<NCW, false, true>),                                   \
                                          dim3((unsigned)(heads * (DK / ScanCfg<NCW>::DV))), dim3(ScanCfg<NCW>::NT), \
                                          0, stream, blocks, u0, S0, (bf16_t*)o, S_T, T, H, (bf16_t*)nullptr,       \
-                                         (bf16_t*)nullptr, (bf16_t*)nullptr, h0, o0)
+                                         (bf16_t*)nullptr, (bf16_t*)nullptr, h0, o0, 0, (float*)nullptr)
     if (ncw == 2) KDA_SCAN(2);
     else KDA_SCAN(1);
 #undef KDA_SCAN
@@ -1147,15 +1264,15 @@ hipError_t launch_dplr_scan(const char* blocks, const bf16_t* u0, const bf16_t* 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                             const void* beta, const float* S0, void* o, float* S_T,
                             int B, int T, int H, int dtype, void* ws, hipStream_t stream, int gate,
-                            const int* cu_seqlens)
+                            const int* cu_seqlens, bool seg)
 {
     if (cu_seqlens) ws = nullptr;   // packed sequences: fused kernel
     if (gate == GATE_HEAD)
-        launch_gate<GATE_HEAD>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens);
+        launch_gate<GATE_HEAD>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens, seg);
     else if (gate == GATE_NONE)
-        launch_gate<GATE_NONE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens);
+        launch_gate<GATE_NONE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens, seg);
     else
-        launch_gate<GATE_CHANNEL>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens);
+        launch_gate<GATE_CHANNEL>(q, k, v, g, beta, S0, o, S_T, B, T, H, dtype, ws, stream, cu_seqlens, seg);
     return hipGetLastError();
 }
 

@@ -95,6 +95,15 @@ enum {
  *                             kernels: the key-side operands of every chunk
  *                             are computed in parallel into the workspace,
  *                             then a serial scan applies them to the state.
+ *                             With 16 heads or fewer (B * H) and at least
+ *                             kda_chunk_fwd_workspace_size() bytes, the scan
+ *                             runs each head's chunks in segments in parallel
+ *                             (per-segment end state and transition, then
+ *                             each segment from its entry state: the state
+ *                             after r chunks is an affine map of the state
+ *                             before them, page "Kimi Linear：高效注意力机制在
+ *                             长序列处理中的创新应用", section 2.1); results
+ *                             agree with the one-pass scan to rounding.
  *                             Otherwise one fused kernel does both (no
  *                             workspace is touched).  The workspace must be
  *                             256-byte aligned and overlap no other buffer;
@@ -155,8 +164,11 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
 /*
  * Workspace bytes that kda_chunk_fwd should be given for the fastest schedule
  * on this shape: B * H * ceil(T / 64) * 72704 when the two-kernel schedule is
- * expected to win (bf16 with fewer than 128 heads in total), else 0 (the fused
- * kernel is used and no workspace is needed).  Invalid arguments return 0.
+ * expected to win (bf16 with fewer than 128 heads in total), plus, when its
+ * scan runs in nseg > 1 segments (16 heads or fewer, at least two chunks per
+ * segment), B * H * (nseg - 1) * 196608 for the segment summaries and entry
+ * states; else 0 (the fused kernel is used and no workspace is needed).
+ * Invalid arguments return 0.
  */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
 

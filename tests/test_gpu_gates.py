@@ -53,6 +53,23 @@ def test_prefill_gate_variants(gate, dtype, schedule, T):
 
 
 @pytest.mark.parametrize("gate", ["head", "none"])
+def test_segmented_scan_gate_variants(gate):
+    """8 heads, 1300 tokens with the library's workspace: the state scan runs
+    in 7 segments of 3 chunks; every output and state entry."""
+    print(f"gated prefill segmented scan gate={gate}", flush=True)
+    B, T, H = 1, 1300, 8
+    inp = inputs.prefill_inputs(B, T, H, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=400, gate=gate)
+    d = {n: (x.to(DEV) if x is not None else None) for n, x in inp.items()}
+    ws = torch.empty(kda.workspace_size(B, T, H, kda.KDA_BF16), dtype=torch.uint8, device=DEV)
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle(inp)
+    eo, es = max_rel_err(o, o_ref), max_rel_err(S, S_ref)
+    print(f"  o err {eo:.3e}  S err {es:.3e}", flush=True)
+    assert eo <= TOL["bfloat16"] and es <= TOL["bfloat16"]
+
+
+@pytest.mark.parametrize("gate", ["head", "none"])
 @pytest.mark.parametrize("T", [1, 65, 200])
 def test_128_heads_gate_variants(gate, T):
     """64-column slices (128 heads) with each gate layout: every output and state entry."""

@@ -65,6 +65,31 @@ def test_ragged_lengths_with_initial_state(dtype, schedule, T):
     check(inp, o, S, TOL[dtype])
 
 
+@pytest.mark.parametrize("B,H,T,s0_std,g_scale", [
+    (1, 16, 520, 0.05, 0.1),     # 3 segments of 3 chunks (ragged last chunk)
+    (1, 16, 1000, 0.0, 0.1),     # no initial state
+    (1, 16, 4096, 0.05, 0.05),   # 4 segments of 16 chunks
+    (2, 3, 2000, 0.05, 0.1),     # 6 heads: 8 segments of 4 chunks (ragged last chunk)
+    (1, 1, 777, 0.05, 0.1),      # one head: 5 segments of 3 chunks (the last of 1.1)
+    (1, 4, 1500, 0.05, 1.0),     # 12 segments of 2 chunks, strong decay
+])
+def test_segmented_scan(B, H, T, s0_std, g_scale):
+    """16 heads or fewer with the library's workspace: the two-kernel schedule
+    runs each head's state scan in segments (segment summaries, their combine,
+    then every segment from its entry state).  Every output and final-state
+    entry against the oracle."""
+    print(f"prefill segmented scan B={B} H={H} T={T} s0_std={s0_std} g_scale={g_scale}", flush=True)
+    ws = kda.workspace_size(B, T, H, kda.KDA_BF16)
+    assert ws > kda.scan_workspace_bytes(B, T, H)      # room for the segment buffers
+    inp = inputs.prefill_inputs(B, T, H, dtype="bfloat16", g_scale=g_scale, s0_std=s0_std, seed=300 + T)
+    d = to_dev(inp)
+    o, S = run(d, workspace=torch.empty(ws, dtype=torch.uint8, device=DEV))
+    check(inp, o, S, TOL["bfloat16"])
+    # the same call without the segment buffers (one pass per head) agrees to rounding
+    o2, S2 = run(d, schedule="two_kernel")
+    check(inp, o2, S2, TOL["bfloat16"])
+
+
 @pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 200])
 def test_128_heads_ragged_lengths(T):
     """128 heads select the fused kernel with 64-column value slices (two
