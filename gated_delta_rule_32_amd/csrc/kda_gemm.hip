@@ -9,9 +9,9 @@
 // Tiling (general kernel): a 256-thread workgroup computes a 128 x 128 tile
 // of C, each of its 4 waves a 64 x 64 sub-tile (4 x 4 MFMA tiles), over K in
 // steps of 64.  Large bf16 products use the 256 x 256-tile kernel below.
-// Operand tiles are staged through double-buffered LDS (rows padded by 16 B
-// against bank conflicts); the next K-step's global loads are in flight while
-// the current step's MFMAs run, with one barrier per step.  The MFMA computes
+// Operand tiles are staged through LDS (rows padded by 16 B against bank
+// conflicts), double-buffered for bf16 A; the next K-step's global loads are
+// in flight while the current step's MFMAs run.  The MFMA computes
 // C^T tiles (weights as the first operand) so that each lane ends up holding
 // 4 consecutive columns of one row of C, which it stores as one vector.
 //
@@ -61,17 +61,29 @@ gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
                int lda, int ldb, int ldc)
 {
     constexpr int NA = AF32 ? 2 : 1;     // A planes in LDS (hi, lo)
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][NA][BM * LDT];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDT];
+    // LDS stages: two for bf16 A; one for fp32 A (its K is the small gate
+    // rank), which halves the footprint to 55 KiB so two workgroups share a CU
+    constexpr int NBUF = AF32 ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) bf16_t sA[NBUF][NA][BM * LDT];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[NBUF][BN * LDT];
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int ln = lane & 15, lg = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;      // 64 x 64 sub-tile of the wave
 
-    // tile order: consecutive workgroups walk down M for a fixed N strip
-    const int tiles_m = (M + BM - 1) / BM;
-    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    // tile order: consecutive workgroups walk down M for a fixed N strip.
+    // With several N strips and tile rows that split evenly over the 8 XCDs
+    // (workgroups are dealt to them round-robin), XCD x instead takes an
+    // eighth of the tile rows with all their N tiles, so that the A tile of a
+    // row is fetched into that XCD's L2 once rather than once per N strip.
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    if (tiles_n > 1 && tiles_m % 8 == 0) {
+        const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+        tm = x * (tiles_m / 8) + j / tiles_n;
+        tn = j % tiles_n;
+    }
     const int m0 = tm * BM, n0 = tn * BN;
 
     // global -> register staging: 16-byte units, rows clamped into range (rows
@@ -144,7 +156,7 @@ gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
     lstore(0);
     block_sync();
     for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
+        const int buf = NBUF == 2 ? kt & 1 : 0;
         if (kt + 1 < KT) gload((kt + 1) * BK);
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 32) {
@@ -163,7 +175,10 @@ gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
                 }
             }
         }
-        if (kt + 1 < KT) lstore(buf ^ 1);
+        if (kt + 1 < KT) {
+            if (NBUF == 1) block_sync();      // every wave is done reading the stage
+            lstore(NBUF == 2 ? buf ^ 1 : 0);
+        }
         block_sync();
     }
 

@@ -1093,13 +1093,16 @@ seg_combine_kernel(const float* summ, const float* S0, float* entry, int nseg)
         float acc[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = sm[j0 + c8 + c];
-        for (int kk = 0; kk < DK; kk += 4) {
-            const f32x4 p = *reinterpret_cast<const f32x4*>(sm + DK + kk);
+        // the row of P_j in registers first (its 32 loads in flight together)
+        f32x4 prow[DK / 4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < DK / 4; ++i) prow[i] = *reinterpret_cast<const f32x4*>(sm + DK + 4 * i);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[c] = fmaf(p[i], cur[kk + i][c8 + c], acc[c]);
-        }
+        for (int i = 0; i < DK / 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[c] = fmaf(prow[i][e], cur[4 * i + e][c8 + c], acc[c]);
         __syncthreads();
         float* out = entry + (((size_t)head * (nseg - 1) + j) * DK + r) * DK + j0 + c8;
 #pragma unroll
