@@ -835,10 +835,15 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     constexpr int HPAGES = DK / HRPP;
     static_assert(!DPLR || (WS_TM % 1024 == 0 && WS_QK % 1024 == 0 && HPAGES <= TM_P1 - TM_P0),
                   "H0 slice fits the Tm slot");
+    constexpr int QT_P1 = WS_KH / 1024, QK_P0 = WS_QK / 1024, QK_P1 = WS_GAM / 1024;
+    static_assert(WS_QT == 0 && WS_KH % 1024 == 0 && WS_QK % 1024 == 0 && WS_GAM % 1024 == 0,
+                  "Qt and Aqk occupy whole pages");
     auto load_block = [&](int n) {            // workspace block n -> stage n % 2
         const char* src = wsh + (size_t)n * WS_CHUNK;
         char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
         for (int u = wave; u < SC_KIB; u += SC::NLW) {
+            // without output, the Qt and Aqk pages are not read: not copied
+            if (NOOUT && (u < QT_P1 || (u >= QK_P0 && u < QK_P1))) continue;
             const char* from = src + (size_t)u * 1024 + lane * 16;
             if constexpr (DPLR) {
                 if (u >= TM_P0 && u < TM_P1) {
