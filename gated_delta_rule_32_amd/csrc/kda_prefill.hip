@@ -595,10 +595,13 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                 for (int u = t; u < bytes / 16; u += NT)
                     reinterpret_cast<i32x4*>(blk + dst)[u] = reinterpret_cast<const i32x4*>(smem + src)[u];
             };
-            copy(WS_QT, L::OFF_QT, WS_KBT - WS_QT);       // Qt and Kh
+            // (for the backward pass, whose save-mode scan reads neither Qt
+            // nor Aqk from this block, only Kh, Kb^T, Tm and gamma)
+            if constexpr (BWD) copy(WS_KH, L::OFF_KH, WS_KBT - WS_KH);
+            else copy(WS_QT, L::OFF_QT, WS_KBT - WS_QT);  // Qt and Kh
             copy(WS_KBT, L::OFF_KBT, WS_TM - WS_KBT);
             copy(WS_TM, L::OFF_RT, WS_QK - WS_TM);
-            copy(WS_QK, L::OFF_QK, WS_GAM - WS_QK);
+            if constexpr (!BWD) copy(WS_QK, L::OFF_QK, WS_GAM - WS_QK);
             copy(WS_GAM, L::OFF_GAM, WS_USED - WS_GAM);
             if constexpr (BWD) {
                 // operands of the backward state scan: transposes read from LDS
