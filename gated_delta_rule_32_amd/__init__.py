@@ -58,7 +58,9 @@ def workspace_size(B, T, H, dtype_code, d=128):
 
 
 def scan_workspace_bytes(B, T, H):
-    """Workspace that selects the two-kernel schedule for any bf16 shape."""
+    """Workspace that selects the two-kernel schedule with a one-pass state
+    scan for any bf16 shape (:func:`workspace_size` adds, for 16 heads or
+    fewer, the buffers of the segmented scan)."""
     return B * H * ((T + 63) // 64) * 72704
 
 

@@ -241,6 +241,32 @@ def test_split_and_resume():
     assert relerr(np.concatenate([oa, ob], axis=1), o) < 1e-13 and relerr(Sb, S) < 1e-13
 
 
+def test_segment_summaries_compose():
+    """The state after a run of tokens is an affine map of the state before it
+    (the Proposition S_r = P_r S_0 + H_r of page "Kimi Linear：高效注意力机制
+    在长序列处理中的创新应用", section 2.1, taken over a whole segment): its
+    offset E is the end state from zero, and its matrix P is the end state of
+    the identity run with zero values.  Composing S_{j+1} = P_j S_j + E_j over
+    segments, then running every segment from its entry state, reproduces the
+    one-pass outputs and final state (the segmented state scan's plan)."""
+    rng = np.random.default_rng(16)
+    B, T, H, dk, dv = 1, 70, 2, 16, 8
+    q, k, v, g, beta, S0 = rand_inputs(rng, B, T, H, dk, dv)
+    o, S = kda_ref.recurrent(q, k, v, g, beta, S0)
+    cuts = [0, 17, 40, 52, T]
+    Sj, outs = S0, []
+    eye = np.broadcast_to(np.eye(dk), (B, H, dk, dk)).copy()
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sl = lambda x: x[:, a:b]
+        oj, _ = kda_ref.recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), Sj)
+        outs.append(oj)
+        _, E = kda_ref.recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), None)
+        zero_v = np.zeros((B, b - a, H, dk))
+        _, P = kda_ref.recurrent(sl(q), sl(k), zero_v, sl(g), sl(beta), eye)
+        Sj = P @ Sj + E
+    assert relerr(np.concatenate(outs, axis=1), o) < 1e-12 and relerr(Sj, S) < 1e-12
+
+
 def test_padding_tokens_are_identity():
     rng = np.random.default_rng(13)
     q, k, v, g, beta, S0 = rand_inputs(rng, 1, 20, 1, 16, 8)
