@@ -39,7 +39,7 @@ int chunk_seg_count(long long B, long long T, long long H);
 
 // Bytes of workspace the two-kernel forward schedule needs: the operand
 // blocks, then with segments the segment summaries [B*H][nseg-1][128][256]
-// and entry states [B*H][nseg-1][128][128] (fp32).
+// and entry states [B*H][nseg][128][128] (fp32).
 size_t chunk_fwd_ws_bytes(long long B, long long T, long long H);
 
 // Whether the two-kernel schedule is expected to be faster for this shape.

@@ -787,9 +787,10 @@ template <int NCW, bool SAVE = false> struct ScanCfg {   // NCW consumer waves
 //   SEG_SUMMARY: every segment but the last, 2 x 128 columns per head: value
 //     columns from S = 0, then identity columns with V = 0.  No output; the
 //     end state goes to segbuf [head][segment][128][256] fp32 (E | P).
-//   SEG_OUTPUT: every segment from its entry state (S0 for the first, else
-//     segbuf [head][segment - 1][128][128], written by seg_combine_kernel),
-//     with the output; the last segment writes S_T.
+//   SEG_OUTPUT: every segment from its entry state segbuf [head][segment]
+//     [128][128] (written by seg_combine_kernel, the first a copy of S0, so
+//     that S_T may overwrite S0 in place), with the output; the last segment
+//     writes S_T.
 template <int NCW, bool SAVE, bool DPLR = false, int SEG = SEG_NONE>
 __global__ void __launch_bounds__(512)
 chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
@@ -907,7 +908,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
         // entry state: S0, zero or the identity (summary), or the segment's
         // entry state from seg_combine_kernel
         const float* sin = S0 ? S0 + sbase : nullptr;
-        if (SEG == SEG_OUTPUT && seg > 0) sin = segbuf + ((size_t)head * (nsegs - 1) + seg - 1) * DK * DK;
+        if (SEG == SEG_OUTPUT) sin = segbuf + ((size_t)head * nsegs + seg) * DK * DK;
         if (SEG == SEG_SUMMARY) sin = nullptr;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
@@ -1082,10 +1083,11 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     }
 }
 
-// Entry states of the segments of SEG_OUTPUT: with E_j | P_j the summary of
-// segment j (end state from zero, transition), S_{j+1} = P_j S_j + E_j from
-// S_0 = S0 (or zero), in fp32.  One workgroup per (head, 16 state columns);
-// thread t computes row t / 2, columns 8 (t % 2) .. +7.
+// Entry states of the segments of SEG_OUTPUT, entry [head][j][128][128]:
+// with E_j | P_j the summary of segment j (end state from zero, transition),
+// S_{j+1} = P_j S_j + E_j from S_0 = S0 (or zero), in fp32.  One workgroup
+// per (head, 16 state columns); thread t computes row t / 2, columns
+// 8 (t % 2) .. +7.
 __global__ void __launch_bounds__(256)
 seg_combine_kernel(const float* summ, const float* S0, float* entry, int nseg)
 {
@@ -1093,8 +1095,11 @@ seg_combine_kernel(const float* summ, const float* S0, float* entry, int nseg)
     const int head = blockIdx.x / (DK / 16), j0 = blockIdx.x % (DK / 16) * 16;
     const int t = threadIdx.x, r = t >> 1, c8 = (t & 1) * 8;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        cur[r][c8 + c] = S0 ? S0[((size_t)head * DK + r) * DK + j0 + c8 + c] : 0.f;
+    for (int c = 0; c < 8; ++c) {
+        const float x = S0 ? S0[((size_t)head * DK + r) * DK + j0 + c8 + c] : 0.f;
+        cur[r][c8 + c] = x;
+        entry[((size_t)head * nseg * DK + r) * DK + j0 + c8 + c] = x;
+    }
     __syncthreads();
     for (int j = 0; j + 1 < nseg; ++j) {
         const float* sm = summ + (((size_t)head * (nseg - 1) + j) * DK + r) * 2 * DK;   // row r of E_j | P_j
@@ -1112,7 +1117,7 @@ seg_combine_kernel(const float* summ, const float* S0, float* entry, int nseg)
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc[c] = fmaf(prow[i][e], cur[4 * i + e][c8 + c], acc[c]);
         __syncthreads();
-        float* out = entry + (((size_t)head * (nseg - 1) + j) * DK + r) * DK + j0 + c8;
+        float* out = entry + (((size_t)head * nseg + j + 1) * DK + r) * DK + j0 + c8;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             cur[r][c8 + c] = acc[c];
@@ -1215,7 +1220,8 @@ int chunk_seg_count(long long B, long long T, long long H)
 size_t chunk_fwd_ws_bytes(long long B, long long T, long long H)
 {
     const int nseg = chunk_seg_count(B, T, H);
-    const size_t seg = nseg > 1 ? (size_t)B * H * (nseg - 1) * DK * DK * 4 * 3 : 0;   // summaries + entry states
+    // summaries [nseg - 1][128][256] and entry states [nseg][128][128] per head
+    const size_t seg = nseg > 1 ? (size_t)B * H * (3 * (nseg - 1) + 1) * DK * DK * 4 : 0;
     return chunk_ws_bytes(B, T, H) + seg;
 }
 

@@ -166,8 +166,9 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
  * on this shape: B * H * ceil(T / 64) * 72704 when the two-kernel schedule is
  * expected to win (bf16 with fewer than 128 heads in total), plus, when its
  * scan runs in nseg > 1 segments (16 heads or fewer, at least two chunks per
- * segment), B * H * (nseg - 1) * 196608 for the segment summaries and entry
- * states; else 0 (the fused kernel is used and no workspace is needed).
+ * segment), B * H * (3 * (nseg - 1) + 1) * 65536 for the segment summaries
+ * and entry states; else 0 (the fused kernel is used and no workspace is
+ * needed).
  * Invalid arguments return 0.
  */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);

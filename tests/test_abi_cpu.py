@@ -106,13 +106,13 @@ def test_workspace_size_query(lib):
     # few heads, bf16: two-kernel schedule, one 72,704-byte block per chunk
     assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 72704
     assert f(1, 100, 3, 128, 128, BF16) == 3 * 2 * 72704
-    # 16 heads or fewer over enough chunks: the state scan runs in segments,
-    # each but the last with a fp32 summary [128][256] and entry state [128][128]
-    SEG = 128 * 128 * 4 * 3
-    assert f(1, 32768, 16, 128, 128, BF16) == 16 * 512 * 72704 + 16 * 3 * SEG      # 4 segments
-    assert f(1, 4096, 1, 128, 128, BF16) == 64 * 72704 + 15 * SEG                  # 16 segments
-    assert f(2, 1300, 4, 128, 128, BF16) == 8 * 21 * 72704 + 8 * 6 * SEG           # 7 segments of 3 chunks
-    assert f(1, 256, 16, 128, 128, BF16) == 16 * 4 * 72704 + 16 * 1 * SEG          # 2 segments of 2 chunks
+    # 16 heads or fewer over enough chunks: the state scan runs in nseg
+    # segments: fp32 summaries [nseg - 1][128][256], entry states [nseg][128][128]
+    SEG = lambda n: (3 * (n - 1) + 1) * 128 * 128 * 4
+    assert f(1, 32768, 16, 128, 128, BF16) == 16 * 512 * 72704 + 16 * SEG(4)      # 4 segments
+    assert f(1, 4096, 1, 128, 128, BF16) == 64 * 72704 + SEG(16)                  # 16 segments
+    assert f(2, 1300, 4, 128, 128, BF16) == 8 * 21 * 72704 + 8 * SEG(7)           # 7 segments of 3 chunks
+    assert f(1, 256, 16, 128, 128, BF16) == 16 * 4 * 72704 + 16 * SEG(2)          # 2 segments of 2 chunks
     # many heads, fp32, tiny T or bad arguments: fused kernel, no workspace
     assert f(8, 4096, 16, 128, 128, BF16) == 0
     assert f(1, 256, 1, 128, 128, F32) == 0
@@ -151,7 +151,7 @@ def test_layer_workspace_layout(lib):
     total = lib.kda_layer_workspace_layout(B, T, dm, H, r, offs)
     R, hd = B * T, H * 128
     sizes = [R * 4 * hd * 2, R * 144 * 4, R * hd * 2, R * hd * 2, R * hd * 2, R * hd * 4,
-             R * H * 2, R * hd * 2, R * hd * 2, H * 512 * 72704 + H * 3 * 128 * 128 * 4 * 3]
+             R * H * 2, R * hd * 2, R * hd * 2, H * 512 * 72704 + H * 10 * 128 * 128 * 4]
     assert list(offs)[0] == 0
     for i in range(9):
         assert offs[i + 1] - offs[i] == (sizes[i] + 255) // 256 * 256

@@ -90,6 +90,20 @@ def test_segmented_scan(B, H, T, s0_std, g_scale):
     check(inp, o2, S2, TOL["bfloat16"])
 
 
+def test_segmented_scan_in_place_state():
+    """The segmented scan with S_T written over S0 (the same tensor)."""
+    print("prefill segmented scan, S_T in place of S0", flush=True)
+    B, T, H = 1, 1000, 16
+    inp = inputs.prefill_inputs(B, T, H, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=350)
+    d = to_dev(inp)
+    ws = torch.empty(kda.workspace_size(B, T, H, kda.KDA_BF16), dtype=torch.uint8, device=DEV)
+    state = d["S0"].clone()
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], state, S_T=state, workspace=ws)
+    torch.cuda.synchronize()
+    assert S.data_ptr() == state.data_ptr()
+    check(inp, o, state, TOL["bfloat16"])
+
+
 @pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 200])
 def test_128_heads_ragged_lengths(T):
     """128 heads select the fused kernel with 64-column value slices (two
