@@ -58,7 +58,7 @@ __device__ __forceinline__ float neg_softplus(float x) {
 template <bool AF32, typename OutT, int EPI>
 __global__ void __launch_bounds__(GT)
 gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
-               int lda, int ldb, int ldc)
+               int lda, int ldb, int ldc, const bf16_t* B2, int n_split)
 {
     constexpr int NA = AF32 ? 2 : 1;     // A planes in LDS (hi, lo)
     // LDS stages: two for bf16 A; one for fp32 A (its K is the small gate
@@ -112,7 +112,8 @@ gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
         for (int i = 0; i < 4; ++i) {
             const int u = t + GT * i, row = u >> 3, cu = u & 7;
             const int gr = min(n0 + row, N - 1);
-            rb[i] = *reinterpret_cast<const i32x4*>(B + (size_t)gr * ldb + k0 + 8 * cu);
+            const bf16_t* brow = gr < n_split ? B + (size_t)gr * ldb : B2 + (size_t)(gr - n_split) * ldb;
+            rb[i] = *reinterpret_cast<const i32x4*>(brow + k0 + 8 * cu);
         }
     };
     auto lstore = [&](int buf) {
@@ -335,10 +336,10 @@ gemm_nt_large_kernel(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, 
 
 hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, bool c_f32,
                           int epilogue, int M, int N, int K, int lda, int ldb, int ldc,
-                          hipStream_t stream)
+                          hipStream_t stream, const bf16_t* B2, int n_split)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
-    if (!a_f32 && !c_f32 && epilogue == 0 && M >= LBM && N >= LBN) {
+    if (!B2 && !a_f32 && !c_f32 && epilogue == 0 && M >= LBM && N >= LBN) {
         const unsigned tiles = (unsigned)(((M + LBM - 1) / LBM) * ((N + LBN - 1) / LBN));
         hipLaunchKernelGGL(gemm_nt_large_kernel, dim3(tiles), dim3(LGT), 0, stream,
                            (const bf16_t*)A, B, (bf16_t*)C, M, N, K, lda, ldb, ldc);
@@ -346,7 +347,8 @@ hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, b
     }
     const dim3 grid((unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN))), block(GT);
 #define KDA_GEMM(AF, OT, EP) \
-    hipLaunchKernelGGL((gemm_nt_kernel<AF, OT, EP>), grid, block, 0, stream, A, B, (OT*)C, M, N, K, lda, ldb, ldc)
+    hipLaunchKernelGGL((gemm_nt_kernel<AF, OT, EP>), grid, block, 0, stream, A, B, (OT*)C, M, N, K, lda, ldb, ldc, \
+                       B2 ? B2 : B, B2 ? n_split : N)
     if (a_f32) {
         if (c_f32 && epilogue == 1) KDA_GEMM(true, float, 1);
         else if (c_f32) KDA_GEMM(true, float, 0);

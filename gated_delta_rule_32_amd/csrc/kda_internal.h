@@ -103,10 +103,11 @@ hipError_t launch_state_copy(const float* S0, float* S_T, long long heads,
 // C[M, N] = A[M, K] B[N, K]^T (both K-contiguous, K % 64 == 0, leading
 // dimensions in elements, multiples of 8).  A is bf16 or, with a_f32, fp32
 // (split into bf16 hi + lo parts); B is bf16; C is fp32 (c_f32) or bf16.
-// epilogue 0: none, 1: c -> -softplus(c).
+// epilogue 0: none, 1: c -> -softplus(c).  With B2, rows n >= n_split of B
+// are rows n - n_split of B2 (two weight matrices stacked, one pass over A).
 hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, bool c_f32,
                           int epilogue, int M, int N, int K, int lda, int ldb, int ldc,
-                          hipStream_t stream);
+                          hipStream_t stream, const bf16_t* B2 = nullptr, int n_split = 0);
 
 // Weights of one KDA token-mixing layer, all bf16, [out_features, in_features]
 // (conv taps [H*128, 4]).

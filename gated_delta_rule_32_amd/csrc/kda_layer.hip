@@ -225,11 +225,9 @@ hipError_t launch_layer_fwd(const LayerWeights& W, const bf16_t* x, bf16_t* y, i
         if ((e = launch_gemm_nt(x, false, Win[i], pre + (size_t)i * HDm, false, 0, R, HDm, d_model,
                                 d_model, d_model, NY, stream)))
             return e;
-    if ((e = launch_gemm_nt(x, false, W.W_down, low, true, 0, R, rank, d_model, d_model, d_model,
-                            ldz, stream)))
-        return e;
-    if ((e = launch_gemm_nt(x, false, W.W_beta, low + rank, true, 0, R, H, d_model, d_model,
-                            d_model, ldz, stream)))
+    //    ([W_down; W_beta] stacked: one pass over x writes both)
+    if ((e = launch_gemm_nt(x, false, W.W_down, low, true, 0, R, rank + H, d_model, d_model, d_model,
+                            ldz, stream, W.W_beta, rank)))
         return e;
     // 2. log alpha = -softplus(W_up (W_down x)); fp32 A operand (hi/lo split)
     if ((e = launch_gemm_nt(low, true, W.W_up, g, true, 1, R, HDm, rank, ldz, rank, HDm, stream)))
