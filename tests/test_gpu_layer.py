@@ -57,6 +57,8 @@ def check(inp, y, iv, H, full_intermediates=True):
     (3, 77, 192, 1, 64),       # d_model not a multiple of the 128-wide GEMM tile
     (1, 1, 256, 2, 64),        # single token
     (8, 130, 256, 16, 128),    # 128 heads: fused KDA kernel, H * 128 = 2048 channels
+    (1, 1000, 256, 4, 128),    # segmented state scan (8 segments of 2 chunks); W_down with W_beta
+                               # over 132 rows, the second 128-row tile holding 4
 ])
 def test_layer_small_shapes(B, T, d_model, H, rank):
     inp, y, iv = run_layer(B, T, d_model, H, rank, seed=11)
