@@ -1,29 +1,38 @@
 """KDA benchmark on one MI355X.
 
-One step = one kda_chunk_fwd call over the prefill workload B = 8, H = 16,
-T = 4096, d_k = d_v = 128, C = 64, bf16 q/k/v/beta, fp32 log-decay, S0 = 0,
-returning o and S_T (inputs already resident in HBM).  The headline value is
-head-tokens per second (B*T*H / time).  The JSON line also carries:
-  * roofline: the fused prefill kernel against HBM bandwidth (the pages' cost
-    model puts the workload below the bf16 ridge point), its measured average
-    launch time from HIP events on the launch stream, and the HBM traffic
-    measured with rocprofv3 counters (stored under profiles/);
-  * mfma: the pages' cost-model FLOPs as a fraction of the bf16 MFMA peak;
+One step = one kda_chunk_fwd call over the long-context prefill workload
+B = 1, H = 32, T = 65536, d_k = d_v = 128, C = 64, bf16 q/k/v/beta, fp32
+log-decay, S0 ~ N(0, 0.02^2), returning o and S_T (inputs already resident in
+HBM).  The headline value is head-tokens per second (B*T*H / time).  The JSON
+line also carries:
+  * roofline: the call against HBM bandwidth (the pages' cost model puts the
+    workload below the bf16 ridge point), its measured average launch time
+    from HIP events on the launch stream, and the HBM traffic measured with
+    rocprofv3 counters (stored under profiles/);
+  * mfma: the pages' cost-model FLOPs as a fraction of the bf16 MFMA peak, and
+    the counter-derived MFMA figures (executed bf16 MFMA operations, MFMA busy
+    cycles) of the kernels, from rocprofv3 runs stored under profiles/;
+  * prefill_c2: the B = 8, H = 16, T = 4096 prefill (S0 = 0) with its own
+    roofline, MFMA figures and oracle timings (all host threads on the whole
+    workload; one thread on a sample);
+  * prefill_c1: the one-head fp32 T = 256 prefill, latency per call, and the
+    one-thread oracle time of the same call;
   * decode: the recurrent decode step over 256 x 32 heads, state GB/s and %
     of HBM peak;
   * layer: the full token-mixing layer (d_model 2048, 16 heads, 32768
     tokens), its time, the KDA operator's share and the achieved TFLOP/s;
-  * gate_variants: the same prefill with one decay per head and token (Gated
+  * gate_variants: the B = 8 prefill with one decay per head and token (Gated
     DeltaNet) and with no decay (DeltaNet), through kda_chunk_fwd_gated;
   * full_attention_decode: the decode step of a NoPE MLA layer (MQA over a
     512-wide latent) at 1M tokens, and per sequence and layer against KDA's;
-  * backward: kda_chunk_bwd on the prefill workload (incoming gradients dL/do
-    ~ N(0,1), dL/dS_T = 0), head-tokens/s, compulsory-HBM-bytes rate, and the
-    gradient oracle timed on the host cores on the same workload;
-  * cpu_baseline: the fp64 oracle timed on the host cores on the same workload.
+  * backward: kda_chunk_bwd on the B = 8 prefill workload (incoming gradients
+    dL/do ~ N(0,1), dL/dS_T = 0), head-tokens/s, compulsory-HBM-bytes rate,
+    and the gradient oracle timed on the host cores on the same workload;
+  * cpu_baseline: the fp64 oracle timed on the host cores on the headline
+    workload (thread count and host CPU model stated).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload c3|c1|decode|layer|bwd|gdn|deltanet|mqa|dplr  (single-workload lines, for profiling)
+       python bench.py --workload c3|c2|c1|decode|layer|bwd|gdn|deltanet|mqa|dplr  (single-workload lines, for profiling)
        python bench.py --copy-calibration       (plain copy kernel for counter scaling)
 """
 from __future__ import annotations
@@ -62,6 +71,7 @@ DECODE_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_d
 BACKWARD_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_backward.hip")
 DPLR_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_dplr.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 WORKLOADS = {
     "c2": "c2_bf16_B8_H16_T4096",
@@ -93,6 +103,48 @@ def measured_traffic(kernel_key, src_path):
     if not rec or rec.get("src_sha256_16") != src_hash(src_path):
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_counters(kernel_keys, src_path):
+    """Counter-derived MFMA and LDS figures per launch (executed bf16 MFMA
+    FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16, MFMA busy fraction =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs), LDS bank
+    conflicts per LDS instruction), summed over the kernels of one call, from
+    committed rocprofv3 runs; None if absent or taken on other sources."""
+    try:
+        with open(COUNTER_FILE) as f:
+            recs = json.load(f)
+    except (OSError, ValueError):
+        return None
+    parts = [recs.get(k) for k in kernel_keys]
+    if any(p is None or p.get("src_sha256_16") != src_hash(src_path) for p in parts):
+        return None
+    us = sum(p["kernel_us"] for p in parts)
+    flops = sum(p["mfma_bf16_flops"] for p in parts)
+    busy = sum(p["mfma_busy_frac"] * p["kernel_us"] for p in parts) / us
+    out = {"kernels": list(kernel_keys),
+           "kernel_us": round(us, 2),
+           "executed_mfma_bf16_flops": flops,
+           "executed_mfma_tflops": round(flops / us / 1e6, 1),
+           "executed_frac_of_bf16_peak": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4),
+           "mfma_busy_frac": round(busy, 4),
+           "source": sorted({p["source"] for p in parts})}
+    if all("lds_bank_conflict_per_lds_inst" in p for p in parts):
+        out["lds_bank_conflict_cycles_per_lds_inst"] = {k: p["lds_bank_conflict_per_lds_inst"]
+                                                        for k, p in zip(kernel_keys, parts)}
+    return out
+
+
+def host_cpu():
+    """Model name of the host CPU (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def time_launches(fn, steps, warmup):
@@ -147,7 +199,11 @@ def prefill_line(name, steps, warmup, schedule="auto"):
     alg_bytes = head_tokens * per_ht + STATE_BYTES * B * H + s0_bytes
     flops = head_tokens * FLOP_PER_HEAD_TOKEN
     t_floor = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
-    traffic = measured_traffic(f"chunk_fwd_{name}", PREFILL_KERNEL_SRC)
+    # kernels of one call: their rocprofv3 counter records under profiles/
+    keys = [f"chunk_fwd_{name}"] if sched == "fused" else [f"chunk_fwd_{name}_prep", f"chunk_fwd_{name}_scan"]
+    parts = [measured_traffic(key, PREFILL_KERNEL_SRC) for key in keys]
+    traffic = sum(parts) if all(p is not None for p in parts) else None
+    counters = measured_counters(keys, PREFILL_KERNEL_SRC)
     achieved = alg_bytes / t_kernel / 1e9
     return dict(
         inp=inp, t=t_kernel, wall=wall, head_tokens=head_tokens,
@@ -163,7 +219,8 @@ def prefill_line(name, steps, warmup, schedule="auto"):
               "achieved_tflops": round(flops / t_kernel / 1e12, 2),
               "peak_tflops": BF16_PEAK_TFLOPS,
               "frac_of_bf16_peak": round(flops / t_kernel / 1e12 / BF16_PEAK_TFLOPS, 4),
-              "frac_of_roofline": round(t_floor / t_kernel, 4)},
+              "frac_of_roofline": round(t_floor / t_kernel, 4),
+              "counters": counters},
         config={"workload": f"kda_chunk_fwd {name}", "schedule": sched, "gate": gate,
                 "B": B, "T": T, "H": H, "d_k": D, "d_v": D,
                 "chunk": C, "dtype": cfg["dtype"], "S0": "N(0,%g)" % cfg["s0_std"] if d["S0"] is not None else "zero",
@@ -402,7 +459,7 @@ def backward_line(steps, warmup, with_cpu=False, wl="c2"):
         kda_ref.recurrent_grad(*args, None, kda_ref._f64(gr["dO"]), None, nthreads=threads)
         dt = time.perf_counter() - t0
         out["cpu_oracle"] = {"value": round(ht / dt, 1), "unit": "head-tokens/s", "cores": threads,
-                             "kind": "oracle",
+                             "kind": "oracle", "cpu_model": host_cpu(),
                              "sample": f"whole workload: {B}x{H} heads x {T} tokens, fp64 reverse-mode "
                                        f"recurrence (C, -O2, OpenMP over heads), {dt:.2f} s wall"}
     return out
@@ -419,7 +476,7 @@ def _oracle_timing(fn, units, unit, cores, sample):
     fn()
     dt = time.perf_counter() - t0
     return {"value": round(units / dt, 1), "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{sample}, {dt:.2f} s wall"}
+            "cpu_model": host_cpu(), "sample": f"{sample}, {dt:.2f} s wall"}
 
 
 def oracle_timings():
@@ -477,23 +534,54 @@ def oracle_timings():
     return out
 
 
-def cpu_baseline(inp):
-    """The fp64 oracle as it stands, on the host cores, on the whole workload."""
-    import numpy as np
+def cpu_baseline(inp, threads=None, batches=None, label="whole workload"):
+    """The fp64 oracle as it stands, on the host cores (``threads``: all of
+    them by default), over the workload's batches ``batches`` (all by
+    default): head-tokens per second."""
     from oracle import kda_ref
+    if batches is not None:
+        inp = {n: (None if x is None else x[batches]) for n, x in inp.items()}
     B, T, H, _ = inp["q"].shape
     arrs = [kda_ref._f64(inp[n]) for n in ("q", "k", "v", "g", "beta")]
     S0 = kda_ref._f64(inp["S0"])
-    threads = kda_ref.max_threads()
-    log(f"[bench] cpu baseline: oracle on {B}x{H} heads x {T} tokens, {threads} threads")
+    threads = threads or kda_ref.max_threads()
+    reps = max(1, int(2e5 // (B * T * H)))      # tiny workloads: repeat to reach ~a second
+    log(f"[bench] cpu oracle: {B}x{H} heads x {T} tokens, {threads} threads, {reps} rep(s)")
     t0 = time.perf_counter()
-    kda_ref.recurrent(*arrs, S0, nthreads=threads)
-    dt = time.perf_counter() - t0
-    del np
+    for _ in range(reps):
+        kda_ref.recurrent(*arrs, S0, nthreads=threads)
+    dt = (time.perf_counter() - t0) / reps
     return {"value": round(B * T * H / dt, 1), "unit": "head-tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"whole workload: {B}x{H} heads x {T} tokens, fp64 sequential recurrence "
-                      f"(C, -O2, OpenMP over heads), {dt:.2f} s wall"}
+            "kind": "oracle", "cpu_model": host_cpu(),
+            "sample": f"{label}: {B}x{H} heads x {T} tokens, fp64 sequential recurrence "
+                      f"(C, -O2, OpenMP over heads), {dt:.3f} s wall per call"
+                      + (f" (mean of {reps} calls)" if reps > 1 else "")}
+
+
+def c2_entry(args):
+    """The B = 8, H = 16, T = 4096 prefill (S0 = 0) with its own roofline,
+    counters and oracle timings."""
+    pre = prefill_line(WORKLOADS["c2"], args.steps, args.warmup, args.schedule)
+    out = {"workload": pre["config"]["workload"], "config": pre["config"],
+           "ms_per_step": round(pre["t"] * 1e3, 4), "head_tokens_per_s": round(pre["value"], 1),
+           "roofline": pre["roofline"], "mfma": pre["mfma"]}
+    if not args.no_cpu:
+        out["cpu_oracle"] = cpu_baseline(pre["inp"])
+        # one thread on one of the 8 batches (16 heads x 4096 tokens)
+        out["cpu_oracle_1thread"] = cpu_baseline(pre["inp"], threads=1, batches=slice(0, 1),
+                                                 label="batch 0 of 8 (1/8 of the workload)")
+    return out, pre
+
+
+def c1_entry(args):
+    """The one-head fp32 T = 256 prefill: latency of one call (a parity
+    workload; it occupies one workgroup of the GPU)."""
+    pre = prefill_line(WORKLOADS["c1"], max(args.steps, 200), args.warmup)
+    out = {"workload": pre["config"]["workload"], "config": pre["config"],
+           "us_per_call": round(pre["t"] * 1e6, 2), "head_tokens_per_s": round(pre["value"], 1)}
+    if not args.no_cpu:
+        out["cpu_oracle_1thread"] = cpu_baseline(pre["inp"], threads=1)
+    return out
 
 
 def main():
@@ -508,7 +596,7 @@ def main():
     ap.add_argument("--no-gates", action="store_true")
     ap.add_argument("--no-mqa", action="store_true")
     ap.add_argument("--no-dplr", action="store_true")
-    ap.add_argument("--workload", choices=["c2", "c3", "c1", "decode", "layer", "bwd", "gdn", "deltanet", "mqa", "dplr"],
+    ap.add_argument("--workload", choices=["c3", "c2", "c1", "decode", "layer", "bwd", "gdn", "deltanet", "mqa", "dplr"],
                     default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--schedule", choices=["auto", "fused", "two_kernel"], default="auto",
@@ -559,7 +647,7 @@ def main():
         print(json.dumps({"metric": "KDA layer tokens/s", **lay}))
         return
 
-    name = WORKLOADS[args.workload or "c2"]
+    name = WORKLOADS[args.workload or "c3"]
     pre = prefill_line(name, args.steps, args.warmup, args.schedule)
     line = {
         "metric": "KDA prefill tokens/s/head-layer (% MFMA peak); decode state GB/s (% HBM)",
@@ -574,6 +662,10 @@ def main():
         "roofline": pre["roofline"],
         "mfma": pre["mfma"],
     }
+    c2 = None
+    if args.workload is None:
+        line["prefill_c2"], c2 = c2_entry(args)
+        line["prefill_c1"] = c1_entry(args)
     if args.workload is None and not args.no_decode:
         line["decode"] = decode_line(max(args.steps, 20), args.warmup)
         line["decode"]["small_batch"] = decode_latency_line(max(args.steps, 20), args.warmup)
@@ -594,11 +686,12 @@ def main():
             if not args.no_bwd:
                 line["gate_variants"][wl]["backward"] = backward_line(min(args.steps, 20), args.warmup, wl=wl)
     if args.workload is None and not args.no_dplr:
-        line["dplr_comparison"] = dplr_line(args.steps, args.warmup, pre["t"] * 1e3)
+        line["dplr_comparison"] = dplr_line(args.steps, args.warmup, c2["t"] * 1e3)
     if args.workload is None and not args.no_bwd:
         line["backward"] = backward_line(min(args.steps, 20), args.warmup, with_cpu=not args.no_cpu)
     if not args.no_cpu and args.workload is None:
         line["cpu_baseline"] = cpu_baseline(pre["inp"])
+        del pre["inp"]
         orc = oracle_timings()
         for key, target in (("decode", line.get("decode")), ("full_attention_decode", line.get("full_attention_decode")),
                             ("layer", line.get("layer")), ("dplr", line.get("dplr_comparison"))):

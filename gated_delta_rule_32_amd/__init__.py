@@ -15,7 +15,7 @@ from ._binding import (KDA_BF16, KDA_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,  # no
 
 __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "bwd_workspace_size", "dplr_chunk_fwd",
            "dplr_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
-           "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS", "mqa_decode",
+           "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS", "mqa_decode", "release_workspaces",
            "status_string", "version", "KDAError",
            "KDA_F32", "KDA_BF16", "lib"]
 
@@ -57,27 +57,37 @@ def workspace_size(B, T, H, dtype_code, d=128):
     return int(lib().kda_chunk_fwd_workspace_size(B, T, H, d, d, dtype_code))
 
 
-def scan_workspace_bytes(B, T, H):
+def scan_workspace_bytes(B, T, H, d=128):
     """Workspace that selects the two-kernel schedule with a one-pass state
     scan for any bf16 shape (:func:`workspace_size` adds, for 16 heads or
-    fewer, the buffers of the segmented scan)."""
-    return B * H * ((T + 63) // 64) * 72704
+    fewer, the buffers of the segmented scan); asked of the library."""
+    return int(lib().kda_chunk_fwd_scan_workspace_size(B, T, H, d, d, KDA_BF16))
 
 
 def _workspace(device, nbytes):
-    """The "auto" workspace: one growing buffer per (device, stream), so calls
-    on different streams never share scratch memory.  It is allocated while
-    that stream is current, so torch's allocator orders its reuse after the
-    stream's pending work when it is replaced by a larger one."""
+    """The "auto" workspace: at most one buffer per (device, stream), so calls
+    on different streams never share scratch memory.  A cached buffer is
+    reused when it holds the request and is at most twice its size; otherwise
+    it is replaced by one of the requested size, so the cache never keeps much
+    more than the last call needed.  It is allocated while that stream is
+    current, so torch's allocator orders its reuse after the stream's pending
+    work when it is replaced.  :func:`release_workspaces` drops the cache."""
     import torch
     if nbytes <= 0:
         return None
     key = (torch.device(device), _stream(device))
     buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
+    if buf is None or buf.numel() < nbytes or buf.numel() > 2 * nbytes:
+        _ws_cache.pop(key, None)
         buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
+
+
+def release_workspaces():
+    """Drop every cached "auto" workspace (their memory returns to torch's
+    allocator once the streams' pending work no longer uses it)."""
+    _ws_cache.clear()
 
 
 def _gate(log_alpha, per_channel_dim):

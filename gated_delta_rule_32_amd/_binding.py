@@ -19,7 +19,7 @@ KDA_OK = 0
 # workspace regions of kda_layer_fwd, in the order of the KDA_LAYER_WS_* enum
 LAYER_REGIONS = ("pre", "low", "q", "k", "v", "g", "beta", "o", "zg", "chunk")
 STATUS_NAMES = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
-                -3: "KDA_ERR_ALIGNMENT", -4: "KDA_ERR_HIP"}
+                -3: "KDA_ERR_ALIGNMENT", -4: "KDA_ERR_HIP", -5: "KDA_ERR_WORKSPACE"}
 
 # name -> (restype, argtypes) for every symbol declared in include/kda.h
 _VP, _I, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -27,6 +27,8 @@ SIGNATURES = {
     "kda_chunk_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                            _I, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
     "kda_chunk_fwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "kda_chunk_fwd_scan_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "kda_chunk_fwd_block_bytes": (_SZ, []),
     "kda_chunk_fwd_gated": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP,
                                  _I, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
     "kda_chunk_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _I, _VP, _VP, _VP,

@@ -53,6 +53,7 @@ const char* kda_status_string(int status) {
         case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k and d_v must be 128; dtype must be KDA_F32 or KDA_BF16)";
         case KDA_ERR_ALIGNMENT: return "misaligned pointer (data pointers need 16-byte alignment, beta its element size)";
         case KDA_ERR_HIP: return "HIP runtime or launch error";
+        case KDA_ERR_WORKSPACE: return "workspace too small for this call (see the *_workspace_size queries)";
         default: return "unknown status";
     }
 }
@@ -65,6 +66,14 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dty
     if (!kda::chunk_prefers_two_kernel(B, T, H, dtype)) return 0;
     return kda::chunk_fwd_ws_bytes(B, T, H);
 }
+
+size_t kda_chunk_fwd_scan_workspace_size(int B, int T, int H, int dk, int dv, int dtype)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || dk != kHeadDim || dv != kHeadDim || dtype != KDA_BF16) return 0;
+    return kda::chunk_ws_bytes(B, T, H);
+}
+
+size_t kda_chunk_fwd_block_bytes(void) { return kda::chunk_ws_bytes(1, 1, 1); }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* log_alpha, const void* beta, const float* S0,
@@ -125,8 +134,9 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
     void* ws = nullptr;
     bool seg = false;
     const long long grid_prep = (long long)heads * ((T + 63) / 64);
-    if (T > 0 && workspace && dtype == KDA_BF16 && grid_prep <= INT_MAX &&
-        workspace_bytes >= kda::chunk_ws_bytes(B, T, H)) {
+    if (T > 0 && workspace && dtype == KDA_BF16) {
+        if (workspace_bytes < kda::chunk_ws_bytes(B, T, H)) return KDA_ERR_WORKSPACE;
+        if (grid_prep > INT_MAX) return KDA_ERR_UNSUPPORTED;
         if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
         // with room for the segment buffers too, the scan may run in segments
         seg = workspace_bytes >= kda::chunk_fwd_ws_bytes(B, T, H);
@@ -220,7 +230,8 @@ int kda_chunk_bwd_gated(const void* q, const void* k, const void* v,
             return rc;
     }
     const size_t need = kda::chunk_bwd_ws_layout(B, T, H, nullptr);
-    if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    if (!workspace) return KDA_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
     if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
 
     const Range in[] = {{q, n_qk * es}, {k, n_qk * es}, {v, n_qk * es}, {log_alpha, g_bytes},
@@ -359,7 +370,8 @@ int kda_mqa_decode(const void* q, const void* cache, void* o, int B, int T, int 
     int rc;
     if ((rc = check_ptr(q, 16)) || (rc = check_ptr(cache, 16)) || (rc = check_ptr(o, 16))) return rc;
     const size_t need = kda::mqa_ws_bytes(B, T, H);
-    if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    if (!workspace) return KDA_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
     if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
     const Range rq{q, nq}, rc_{cache, nc}, ro{o, nq}, rw{workspace, need};
     if (overlap(ro, rq) || overlap(ro, rc_) || overlap(ro, rw) || overlap(rw, rq) || overlap(rw, rc_))
@@ -409,7 +421,8 @@ int kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* 
     for (const void* p : ptrs)
         if ((rc = check_ptr(p, 16)) != KDA_OK) return rc;
     const size_t need = kda::dplr_ws_layout(B, T, H, nullptr);
-    if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    if (!workspace) return KDA_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
     if ((rc = check_ptr(workspace, 256)) != KDA_OK) return rc;
     const Range in[] = {{q, n_qk * 2}, {k, n_qk * 2}, {v, n_qk * 2}, {a, n_qk * 2},
                         {b, n_qk * 2}, {log_alpha, n_qk * 4}, rS0};
@@ -447,7 +460,8 @@ int kda_layer_fwd(const void* x, const void* W_q, const void* W_k, const void* W
     if (R == 0) return KDA_OK;
 
     const size_t need = kda::layer_ws_layout(B, T, H, rank, nullptr);
-    if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    if (!workspace) return KDA_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
     int rc;
     const void* ptrs[] = {x, W_q, W_k, W_v, W_g, conv_q, conv_k, conv_v, W_down, W_up, W_beta, W_o, y};
     for (const void* p : ptrs)

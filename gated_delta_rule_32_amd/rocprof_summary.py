@@ -12,6 +12,17 @@ Usage:
       HBM bytes per launch of the matching kernel: FETCH_SIZE and WRITE_SIZE
       (KiB per dispatch) scaled by what the same counters read for a plain
       copy kernel that reads and writes N bytes.
+  python -m gated_delta_rule_32_amd.rocprof_summary mfma PMC_DIR [PMC_DIR ...]
+      --match SUBSTR --trace TRACE_DIR [--record KEY --src FILE --source NAME]
+      counter-derived MFMA and LDS figures of the matching kernel from `--pmc`
+      runs holding SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES,
+      GRBM_GUI_ACTIVE, SQ_INSTS_LDS and SQ_LDS_BANK_CONFLICT (any split over
+      the runs), with the mean kernel duration from a kernel-trace run:
+        executed bf16 MFMA FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16
+        MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4)
+        LDS bank-conflict cycles per LDS instruction
+      With --record, the figures are also stored under KEY in
+      profiles/counters.json together with the sha256 of FILE.
 Output is Markdown on stdout.
 """
 from __future__ import annotations
@@ -107,6 +118,61 @@ def traffic(fetch_dir, write_dir, match, cf_dir, cw_dir, copy_bytes, copy_match)
     return fetch_b + write_b
 
 
+N_CU = 256          # MI355X compute units (4 SIMDs each)
+
+
+def mfma(pmc_dirs, match, trace_dir, key=None, src=None, source=None):
+    import hashlib
+    import json
+    vals = {}
+    for d in pmc_dirs:
+        for r in _rows(d, "*counter_collection.csv"):
+            if match in r.get("Kernel_Name", ""):
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = {c: statistics.mean(v) for c, v in vals.items()}
+    durs = []
+    for r in _rows(trace_dir, "*kernel_trace.csv"):
+        if match in r.get("Kernel_Name", ""):
+            durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if not durs or "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in mean:
+        raise SystemExit(f"no trace rows or MFMA counters for kernels matching {match!r}")
+    us = statistics.mean(durs)
+    flops = 512.0 * mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+    rec = {"kernel_us": round(us, 2), "mfma_bf16_flops": flops,
+           "mfma_tflops": round(flops / us / 1e6, 2)}
+    print("| quantity | value |\n|---|---|")
+    print(f"| kernel match | `{match}` ({len(durs)} traced dispatches) |")
+    for c in sorted(mean):
+        print(f"| {c} per dispatch | {mean[c]:.4g} ({len(vals[c])} dispatches) |")
+    print(f"| mean kernel duration (trace) | {us:.2f} us |")
+    print(f"| executed bf16 MFMA FLOPs per dispatch (512 x MOPS) | {flops:.4e} |")
+    print(f"| executed bf16 MFMA rate | {flops / us / 1e6:.1f} TFLOP/s |")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+        busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (mean["GRBM_GUI_ACTIVE"] * N_CU * 4)
+        rec["mfma_busy_frac"] = round(busy, 4)
+        print(f"| MFMA busy fraction, BUSY_CYCLES / (GUI_ACTIVE x {N_CU} x 4) | {busy:.4f} |")
+    if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_INSTS_LDS"):
+        per = mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_INSTS_LDS"]
+        rec["lds_bank_conflict_per_lds_inst"] = round(per, 3)
+        print(f"| LDS bank-conflict cycles per LDS instruction | {per:.3f} |")
+    if key:
+        with open(src, "rb") as f:
+            rec["src_sha256_16"] = hashlib.sha256(f.read()).hexdigest()[:16]
+        rec["source"] = source
+        path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "profiles", "counters.json")
+        try:
+            with open(path) as f:
+                allr = json.load(f)
+        except (OSError, ValueError):
+            allr = {}
+        allr[key] = rec
+        with open(path, "w") as f:
+            json.dump(allr, f, indent=1, sort_keys=True)
+            f.write("\n")
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -118,7 +184,14 @@ def main(argv=None):
     x.add_argument("--copy-fetch", required=True); x.add_argument("--copy-write", required=True)
     x.add_argument("--copy-bytes", type=float, required=True)
     x.add_argument("--copy-match", default="copy")
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_dirs", nargs="+")
+    m.add_argument("--match", required=True); m.add_argument("--trace", required=True)
+    m.add_argument("--record"); m.add_argument("--src"); m.add_argument("--source")
     a = ap.parse_args(argv)
+    if a.cmd == "mfma":
+        mfma(a.pmc_dirs, a.match, a.trace, a.record, a.src, a.source)
+        return 0
     if a.cmd == "trace":
         trace(a.dir, a.match)
     elif a.cmd == "counters":

@@ -27,6 +27,9 @@
  *    failed check returns a negative status and touches no memory.  Values
  *    are not inspected: NaN and Inf pass through.
  *  - Calls keep no state between them and are safe from several host threads.
+ *  - A `workspace` is caller-owned device scratch.  Where one is required, a
+ *    NULL workspace returns KDA_ERR_INVALID_ARG and one of fewer bytes than
+ *    the call needs returns KDA_ERR_WORKSPACE, before anything is launched.
  *
  * Numeric range of the gate: g (= log alpha) must be finite and <= 0.  The
  * chunked prefill factorises exp(G_r - G_i) over 64-token chunks, so it needs
@@ -69,7 +72,8 @@ enum {
     KDA_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, overlapping buffers */
     KDA_ERR_UNSUPPORTED = -2, /* d_k or d_v != 128, unknown dtype, size overflow */
     KDA_ERR_ALIGNMENT = -3,   /* pointer not aligned as documented above */
-    KDA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+    KDA_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+    KDA_ERR_WORKSPACE = -5    /* a workspace smaller than the call needs */
 };
 
 /*
@@ -104,10 +108,17 @@ enum {
  *                             before them, page "Kimi Linear：高效注意力机制在
  *                             长序列处理中的创新应用", section 2.1); results
  *                             agree with the one-pass scan to rounding.
- *                             Otherwise one fused kernel does both (no
- *                             workspace is touched).  The workspace must be
- *                             256-byte aligned and overlap no other buffer;
- *                             its contents on entry and exit are unspecified.
+ *                             With workspace NULL (or dtype KDA_F32, where
+ *                             the workspace is ignored) one fused kernel does
+ *                             both and no workspace is touched.  A non-NULL
+ *                             workspace of fewer bytes than
+ *                             kda_chunk_fwd_scan_workspace_size() returns
+ *                             KDA_ERR_WORKSPACE (bf16, T >= 1), and with a
+ *                             workspace B * H * ceil(T / 64) must stay below
+ *                             2^31 (else KDA_ERR_UNSUPPORTED).  The
+ *                             workspace must be 256-byte aligned and overlap
+ *                             no other buffer; its contents on entry and exit
+ *                             are unspecified.
  * T may be any value >= 0 (a partial last chunk is handled exactly); T = 0
  * copies S0 (or zeros) to S_T.  B*H = 0 is a no-op.  `o` must not overlap any
  * input.  Returns KDA_OK or a negative status.
@@ -172,6 +183,18 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
  * Invalid arguments return 0.
  */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
+
+/*
+ * Smallest workspace with which kda_chunk_fwd runs the two-kernel schedule
+ * (with a one-pass state scan) on this shape, whatever the fastest schedule
+ * is: B * H * ceil(T / 64) * kda_chunk_fwd_block_bytes() for dtype KDA_BF16
+ * and T >= 1; 0 for fp32 (no workspace is used) or invalid arguments.
+ */
+size_t kda_chunk_fwd_scan_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
+
+/* Bytes of one per-(batch, head, 64-token chunk) operand block of the
+ * two-kernel schedule's workspace. */
+size_t kda_chunk_fwd_block_bytes(void);
 
 /*
  * Backward pass of kda_chunk_fwd: for a scalar loss L, given dL/do (grad_o)

@@ -17,6 +17,19 @@ def max_rel_err(x, ref):
     return float(np.max(np.abs(x - ref)) / den) if den > 0 else float(np.max(np.abs(x)))
 
 
+def max_rel_err_per_head(x, ref, head_axes):
+    """Worst per-head normwise error: for every head (the index over
+    ``head_axes``), max |x - ref| / max |ref| over that head's entries; the
+    maximum over heads.  A head with small outputs is then judged on its own
+    scale, not on the largest head's."""
+    x = x.detach().cpu().double().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    red = tuple(a for a in range(ref.ndim) if a not in head_axes)
+    num = np.abs(x - ref).max(axis=red)
+    den = np.abs(ref).max(axis=red)
+    return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1.0), num)))
+
+
 def oracle_prefill(inp, heads=None):
     """Oracle on a prefill input dict; ``heads`` = list of (b, h) to restrict to."""
     q, k, v, g, beta, S0 = (inp[n] for n in ("q", "k", "v", "g", "beta", "S0"))

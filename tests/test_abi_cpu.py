@@ -14,7 +14,7 @@ kda = pytest.importorskip("gated_delta_rule_32_amd")
 from gated_delta_rule_32_amd import _binding  # noqa: E402
 
 F32, BF16 = 0, 1
-OK, INVALID, UNSUP, ALIGN = 0, -1, -2, -3
+OK, INVALID, UNSUP, ALIGN, WSERR = 0, -1, -2, -3, -5
 P = 0x10000000  # fake, 16-byte aligned "device" addresses; never dereferenced
 
 
@@ -33,7 +33,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_bwd", "kda_chunk_bwd_gated",
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_scan_workspace_size",
+                          "kda_chunk_fwd_block_bytes", "kda_chunk_bwd", "kda_chunk_bwd_gated",
                           "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated", "kda_chunk_fwd_varlen",
                           "kda_mqa_decode", "kda_mqa_decode_workspace_size",
                           "kda_dplr_chunk_fwd", "kda_dplr_chunk_fwd_workspace_size",
@@ -46,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, INVALID, UNSUP, ALIGN, -4, 12345):
+    for code in (OK, INVALID, UNSUP, ALIGN, -4, WSERR, 12345):
         assert isinstance(lib.kda_status_string(code), bytes)
     assert lib.kda_version().decode().count(".") == 2
 
@@ -74,6 +75,9 @@ def step(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S=P + 
     (dict(B=2**30, H=2**30), UNSUP),            # size overflow
     (dict(ws=P + 2**31 + 16, wsb=72704), ALIGN),           # workspace needs 256-byte alignment
     (dict(ws=P + 2**24, wsb=72704), INVALID),               # workspace overlaps k
+    (dict(ws=P + 2**31, wsb=72703), WSERR),                 # bf16 workspace below one block
+    (dict(ws=P + 2**31, wsb=0), WSERR),                     # a non-NULL workspace of zero bytes
+    (dict(ws=P + 2**31, wsb=72704, T=65), WSERR),           # two chunks need two blocks
 ])
 def test_chunk_fwd_rejects(lib, kw, code):
     assert chunk(lib, **kw) == code
@@ -101,6 +105,21 @@ def test_recurrent_step_rejects(lib, kw, code):
     assert step(lib, **kw) == code
 
 
+def test_block_and_scan_workspace_queries(lib):
+    assert lib.kda_chunk_fwd_block_bytes() == 72704
+    f = lib.kda_chunk_fwd_scan_workspace_size
+    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 72704
+    assert f(2, 65, 3, 128, 128, BF16) == 6 * 2 * 72704
+    assert f(1, 64, 1, 128, 128, F32) == 0            # fp32 uses no workspace
+    assert f(1, 0, 1, 128, 128, BF16) == 0 and f(1, 64, 1, 64, 128, BF16) == 0
+
+
+def test_fp32_ignores_a_small_workspace(lib):
+    # the workspace only serves the bf16 two-kernel schedule; validation of an
+    # fp32 call then fails on the (bogus) data pointers' overlap, not on size
+    assert chunk(lib, dt=F32, ws=P + 2**31, wsb=16, o=P) == INVALID
+
+
 def test_workspace_size_query(lib):
     f = lib.kda_chunk_fwd_workspace_size
     # few heads, bf16: two-kernel schedule, one 72,704-byte block per chunk
@@ -118,7 +137,7 @@ def test_workspace_size_query(lib):
     assert f(1, 256, 1, 128, 128, F32) == 0
     assert f(1, 64, 1, 128, 128, BF16) == 0
     assert f(1, 100, 3, 64, 128, BF16) == 0 and f(-1, 100, 3, 128, 128, BF16) == 0
-    # a workspace too small is simply not used (fused kernel): no error
+    # T = 0 needs no workspace: any size is accepted
     assert chunk(lib, ws=P + 2**31, wsb=100, T=0, q=None, k=None, v=None, g=None, beta=None,
                  o=None, ST=None) == OK
 
@@ -167,7 +186,7 @@ def test_layer_workspace_layout(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(ws=None), INVALID),
-    (dict(wsb=1000), INVALID),                  # workspace too small
+    (dict(wsb=1000), WSERR),                    # workspace too small
     (dict(B=-1), INVALID), (dict(H=0), INVALID), (dict(rank=0), INVALID),
     (dict(dm=100), UNSUP), (dict(rank=96), UNSUP), (dict(T=2**20, dm=2048, H=16), UNSUP),
     (dict(x=P + 8), ALIGN), (dict(ws=P + 2**32 + 128), ALIGN),
@@ -213,7 +232,7 @@ def test_bwd_workspace_size(lib):
     (dict(dt=F32), UNSUP), (dict(dt=5), UNSUP), (dict(kd=64), UNSUP), (dict(vd=32), UNSUP),
     (dict(q=P + 2), ALIGN), (dict(dk=P + 2**30 + 8), ALIGN), (dict(dbeta=P + 2**33 + 1), ALIGN),
     (dict(ws=P + 2**34 + 16), ALIGN), (dict(dS0=P + 2**35 + 4), ALIGN),
-    (dict(wsb=BWD_UNIT - 1), INVALID),           # workspace too small
+    (dict(wsb=BWD_UNIT - 1), WSERR),             # workspace too small
     (dict(dq=P + 2**24), INVALID),               # dq overlaps k
     (dict(dv=P + 2**29 + 64), INVALID),          # dv overlaps dq
     (dict(ws=P + 2**26), INVALID),               # workspace overlaps g
@@ -330,7 +349,7 @@ def test_mqa_workspace_size(lib):
     (dict(q=None), INVALID), (dict(c=None), INVALID), (dict(o=None), INVALID), (dict(ws=None), INVALID),
     (dict(B=-1), INVALID), (dict(T=0), INVALID), (dict(H=24), UNSUP), (dict(D=128), UNSUP),
     (dict(T=(1 << 22) + 1), UNSUP),
-    (dict(q=P + 4), ALIGN), (dict(ws=P + 2**35 + 64), ALIGN), (dict(wsb=100), INVALID),
+    (dict(q=P + 4), ALIGN), (dict(ws=P + 2**35 + 64), ALIGN), (dict(wsb=100), WSERR),
     (dict(o=P + 2**24 + 64), INVALID),           # o inside the cache
     (dict(ws=P), INVALID),                       # workspace overlaps q
 ])
@@ -366,7 +385,7 @@ def test_dplr_workspace_size(lib):
     (dict(o=None), INVALID), (dict(ws=None), INVALID), (dict(B=-1), INVALID), (dict(T=-1), INVALID),
     (dict(dt=F32), UNSUP), (dict(kd=64), UNSUP), (dict(vd=256), UNSUP),
     (dict(a=P + 2**26 + 8), ALIGN), (dict(g=P + 2**28 + 4), ALIGN), (dict(ws=P + 2**34 + 16), ALIGN),
-    (dict(wsb=1000), INVALID),                   # workspace too small
+    (dict(wsb=1000), WSERR),                     # workspace too small
     (dict(o=P + 2**27 + 64), INVALID),           # o overlaps b
     (dict(ws=P + 2**28), INVALID),               # workspace overlaps the log-decay
     (dict(S0=P + 2**35, ST=P + 2**35 + 16), INVALID),   # S_T overlaps S0 partially

@@ -73,10 +73,12 @@ def test_layer_full_width_short_sequence():
 @pytest.mark.timeout(900)
 def test_layer_full_workload():
     """The 32768-token, d_model 2048, 16-head layer in full, against the
-    complete fp64 oracle (about half a minute of host time)."""
+    complete fp64 oracle (about half a minute of host time): y, o and every
+    intermediate (q, k, v, log alpha, beta, the gate pre-activation, the gated
+    norm)."""
     cfg = {k: v for k, v in inputs.LAYER_CONFIG.items() if k != "dtype"}
     inp, y, iv = run_layer(cfg["B"], cfg["T"], cfg["d_model"], cfg["H"], 128, cfg["seed"])
-    check(inp, y, iv, cfg["H"], full_intermediates=False)
+    check(inp, y, iv, cfg["H"], full_intermediates=True)
 
 
 def test_layer_validates_tensors():
