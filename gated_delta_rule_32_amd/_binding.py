@@ -31,6 +31,8 @@ SIGNATURES = {
     "kda_chunk_fwd_block_bytes": (_SZ, []),
     "kda_chunk_fwd_gated": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP,
                                  _I, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
+    "kda_chunk_fwd_noalloc": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP,
+                                   _I, _I, _I, _I, _I, _I, _VP]),
     "kda_chunk_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _I, _VP, _VP, _VP,
                                   _I, _I, _I, _I, _I, _VP]),
     "kda_recurrent_step_gated": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP,

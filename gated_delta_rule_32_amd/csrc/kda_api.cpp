@@ -91,6 +91,22 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
                         int B, int T, int H, int dk, int dv, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream)
 {
+    return kda::chunk_fwd_entry(q, k, v, log_alpha, gate, beta, S0, o, S_T, B, T, H, dk, dv, dtype, workspace,
+                                workspace_bytes, 0, stream);
+}
+
+}  // extern "C"
+
+// The body of kda_chunk_fwd_gated.  With scratch_bytes > 0 (the
+// allocation-free entry point) `workspace` is ignored: once the arguments
+// have passed validation, a schedule that wants scratch takes scratch_bytes
+// of the library's static array (kda::noalloc_scratch) instead.
+int kda::chunk_fwd_entry(const void* q, const void* k, const void* v,
+                         const float* log_alpha, int gate, const void* beta, const float* S0,
+                         void* o, float* S_T,
+                         int B, int T, int H, int dk, int dv, int dtype,
+                         void* workspace, size_t workspace_bytes, size_t scratch_bytes, void* stream)
+{
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED;
@@ -134,6 +150,17 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
     void* ws = nullptr;
     bool seg = false;
     const long long grid_prep = (long long)heads * ((T + 63) / 64);
+    if (scratch_bytes > 0) {
+        workspace = nullptr;
+        if (T > 0 && dtype == KDA_BF16) {
+            if (scratch_bytes < kda::chunk_ws_bytes(B, T, H)) return KDA_ERR_WORKSPACE;
+            if (grid_prep > INT_MAX) return KDA_ERR_UNSUPPORTED;
+            hipError_t e;
+            ws = kda::noalloc_scratch(&e);
+            if (!ws) return KDA_ERR_HIP;
+            seg = scratch_bytes >= kda::chunk_fwd_ws_bytes(B, T, H);
+        }
+    }
     if (T > 0 && workspace && dtype == KDA_BF16) {
         if (workspace_bytes < kda::chunk_ws_bytes(B, T, H)) return KDA_ERR_WORKSPACE;
         if (grid_prep > INT_MAX) return KDA_ERR_UNSUPPORTED;
@@ -158,6 +185,8 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v,
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
+
+extern "C" {
 
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype)
 {

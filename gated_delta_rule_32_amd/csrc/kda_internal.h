@@ -29,6 +29,19 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             void* ws, hipStream_t stream, int gate = KDA_GATE_CHANNEL,
                             const int* cu_seqlens = nullptr, bool seg = false);
 
+// kda_chunk_fwd_gated's validation and launch; with scratch_bytes > 0 the
+// two-kernel schedule takes scratch_bytes of the static scratch array of
+// kda_noalloc.hip instead of `workspace` (the allocation-free entry point).
+int chunk_fwd_entry(const void* q, const void* k, const void* v, const float* log_alpha, int gate,
+                    const void* beta, const float* S0, void* o, float* S_T, int B, int T, int H, int dk,
+                    int dv, int dtype, void* workspace, size_t workspace_bytes, size_t scratch_bytes,
+                    void* stream);
+
+// Device address of the current device's copy of the library's static
+// scratch array (KDA_NOALLOC_SCRATCH_BYTES; looked up once per device), or
+// nullptr with *err set.
+void* noalloc_scratch(hipError_t* err);
+
 // Bytes of the key-side operand blocks of the two-kernel schedule: one
 // 72,704-byte block per (batch, head, 64-token chunk).
 size_t chunk_ws_bytes(long long B, long long T, long long H);

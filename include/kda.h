@@ -197,6 +197,28 @@ size_t kda_chunk_fwd_scan_workspace_size(int B, int T, int H, int dk, int dv, in
 size_t kda_chunk_fwd_block_bytes(void);
 
 /*
+ * kda_chunk_fwd_gated for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Instead of a caller-supplied workspace, the two-kernel
+ * schedule's scratch is a static device array inside the library,
+ * KDA_NOALLOC_SCRATCH_BYTES on each GPU, held until the process ends.  The
+ * call allocates and frees nothing.  It runs the schedule kda_chunk_fwd_gated
+ * runs with kda_chunk_fwd_workspace_size() bytes of workspace (or, when that
+ * exceeds the array, with kda_chunk_fwd_scan_workspace_size() bytes); shapes
+ * whose scratch exceeds the array even then return KDA_ERR_WORKSPACE.  Shapes
+ * served by the fused kernel use no scratch.  Arguments, results and other
+ * errors are those of kda_chunk_fwd_gated.  The device is the current HIP
+ * device.  Every call on one GPU uses that GPU's one array: calls that can
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller; calls on one stream are ordered.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                          const float* log_alpha, int gate, const void* beta, const float* S0,
+                          void* o, float* S_T,
+                          int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
+/*
  * Backward pass of kda_chunk_fwd: for a scalar loss L, given dL/do (grad_o)
  * and dL/dS_T (grad_S_T), the gradient of L with respect to every input of the
  * forward call.  The chunkwise algorithm (same pages and sections as

@@ -34,6 +34,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_scan_workspace_size",
+                          "kda_chunk_fwd_noalloc",
                           "kda_chunk_fwd_block_bytes", "kda_chunk_bwd", "kda_chunk_bwd_gated",
                           "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated", "kda_chunk_fwd_varlen",
                           "kda_mqa_decode", "kda_mqa_decode_workspace_size",
@@ -112,6 +113,17 @@ def test_block_and_scan_workspace_queries(lib):
     assert f(2, 65, 3, 128, 128, BF16) == 6 * 2 * 72704
     assert f(1, 64, 1, 128, 128, F32) == 0            # fp32 uses no workspace
     assert f(1, 0, 1, 128, 128, BF16) == 0 and f(1, 64, 1, 64, 128, BF16) == 0
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    # the scratch array holds 128 MiB: the 32-head 65536-token prefill needs
+    # 2.4 GB of operand blocks and is rejected before any HIP call
+    assert lib.kda_chunk_fwd_noalloc(P, P + 2**24, P + 2**25, P + 2**26, 0, P + 2**27, None, P + 2**28,
+                                     P + 2**29, 1, 65536, 32, 128, 128, BF16, None) == WSERR
+    # argument errors as for kda_chunk_fwd_gated (checked before the scratch lookup
+    # only when no scratch is needed: fused-kernel shapes)
+    assert lib.kda_chunk_fwd_noalloc(None, P, P, P, 0, P, None, P, P, 2, 100, 64, 128, 128, BF16, None) == INVALID
+    assert lib.kda_chunk_fwd_noalloc(P, P, P, P, 0, P, None, P, P, 1, 64, 1, 64, 128, BF16, None) == UNSUP
 
 
 def test_fp32_ignores_a_small_workspace(lib):
