@@ -70,6 +70,7 @@ PREFILL_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_
 DECODE_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_decode.hip")
 BACKWARD_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_backward.hip")
 DPLR_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_dplr.hip")
+GEMM_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_32_amd", "csrc", "kda_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -107,10 +108,12 @@ def measured_traffic(kernel_key, src_path):
 
 def measured_counters(kernel_keys, src_path):
     """Counter-derived MFMA and LDS figures per launch (executed bf16 MFMA
-    FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16, MFMA busy fraction =
-    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs), LDS bank
-    conflicts per LDS instruction), summed over the kernels of one call, from
-    committed rocprofv3 runs; None if absent or taken on other sources."""
+    FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16; MFMA busy fraction =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 256 CUs x 4 SIMDs),
+    where rocprofv3 reports GRBM_GUI_ACTIVE summed over the 8 XCDs; LDS
+    bank-conflict cycles per LDS instruction), summed over the kernels of one
+    call, from committed rocprofv3 runs; None if absent or taken on other
+    sources."""
     try:
         with open(COUNTER_FILE) as f:
             recs = json.load(f)
@@ -403,7 +406,8 @@ def layer_line(steps, warmup):
             "rest_ms": round((t_layer - t_kda) * 1e3, 4),
             "model_flops": gemm_flops + kda_flops,
             "achieved_tflops": round((gemm_flops + kda_flops) / t_layer / 1e12, 1),
-            "frac_of_bf16_peak": round((gemm_flops + kda_flops) / t_layer / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            "frac_of_bf16_peak": round((gemm_flops + kda_flops) / t_layer / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "projection_gemm_counters": measured_counters(["kda_layer_gemm_large"], GEMM_KERNEL_SRC)}
 
 
 def backward_line(steps, warmup, with_cpu=False, wl="c2"):

@@ -189,12 +189,13 @@ __device__ __forceinline__ bf16x8 a_pair(const bf16_t* row, int p, int lg, bool 
 // ---- forward state scan: per-chunk operand block -------------------------------
 // Workspace block of one chunk, written by a prep kernel and read by
 // chunk_scan_kernel (bf16 only).  It is the image of the scan's LDS stage:
-// rows keep their 16-byte padding and Kb^T its swizzle (kbt_swz), so the scan
+// rows keep their 16-byte padding and Kt^T its swizzle (kbt_swz), so the scan
 // copies it linearly in 1 KiB pieces.  Byte offsets:
 constexpr int WS_P128 = DK + 8, WS_P64 = C + 8;    // padded row pitches (elements)
 constexpr int WS_QT = 0;                            // Qt   [64][136] bf16, token-major
 constexpr int WS_KH = WS_QT + C * WS_P128 * 2;      // Kh   [64][136] bf16, token-major
-constexpr int WS_KBT = WS_KH + C * WS_P128 * 2;     // Kb^T [128][72] bf16, channel-major, swizzled
+constexpr int WS_KBT = WS_KH + C * WS_P128 * 2;     // Kt^T [128][72] bf16, channel-major, swizzled
+                                                    //   (Kt = e^{G_64 - G} k; DPLR: (e^{-G} a)^T)
 constexpr int WS_TM = WS_KBT + DK * WS_P64 * 2;     // Tm Diag(beta) [64][72] bf16
 constexpr int WS_QK = WS_TM + C * WS_P64 * 2;       // Aqk  [64][72] bf16
 constexpr int WS_GAM = WS_QK + C * WS_P64 * 2;      // e^{G_64} [128] fp32

@@ -7,20 +7,29 @@
 // For a chunk of C = 64 tokens with entry state S (d_k x d_v, fp32), and
 // G = in-chunk cumulative sum of g = log(alpha):
 //
-//   Qt = e^{G} * Q,  Kh = e^{G} * K,  Kb = e^{-G} * K                  [64 x 128]
-//   Aqk = Qt Kb^T   (kept for i <= r)                                  [64 x 64]
-//   Akk = Diag(beta) Kh Kb^T   (kept for i < r)
+//   Qt = e^{G} * Q,  Kh = e^{G} * K,  Kt = e^{G_64 - G} * K             [64 x 128]
+//   Aqk[r,i] = sum_c q_r[c] k_i[c] e^{G_r[c] - G_i[c]}   (kept for i <= r) [64 x 64]
+//   Akk[r,i] = beta_r sum_c k_r[c] k_i[c] e^{G_r[c] - G_i[c]}   (kept for i < r)
 //   Tm  = (I + Akk)^{-1}                         (UT transform)
 //   Vn  = Tm Diag(beta) (V - Kh S)               (= U - W S with the WY factors
 //                                                  W = Tm Diag(beta) Kh, U = Tm Diag(beta) V)
 //   O   = Qt S + Aqk Vn
-//   S  <- Diag(e^{G_64}) (S + Kb^T Vn)           (= Diag(e^{G_64}) S + (e^{G_64 - G} * K)^T Vn)
+//   S  <- Diag(e^{G_64}) S + Kt^T Vn
 //
-// The decay e^{G_r - G_i} is split into a row factor e^{G_r} and a column
-// factor e^{-G_i} (reference point: the chunk start); this is exact up to
-// rounding while every |G| in a chunk stays below ~80.  The WY factor W is
-// never formed: Tm is applied to the residual V - Kh S instead, which is the
-// same product reassociated and saves one 64x64x128 product and its buffer.
+// Aqk and Akk are products of decay-scaled operands: the decay e^{G_r - G_i}
+// is split at a reference point into a row factor and a column factor.  A
+// chunk whose decay stays in range (every channel's G_64 above -FAST_LIM in
+// log2 units) takes the chunk start: Aqk = Qt Kb^T, Akk = Diag(beta) Kh Kb^T
+// with Kb = e^{-G} * K.  Any other chunk takes the ends of its four 16-token
+// sub-chunks (the secondary chunking of page "Kimi K3论文：Kimi Linear",
+// section 4): its 16 x 16 blocks are products of operands referenced to the
+// end of their own sub-chunk, the blocks below the diagonal scaled by the
+// decay between the two sub-chunk ends (m1_subchunk), so that no factor grows
+// with the chunk's total decay; only each sub-chunk's decay must stay in fp32
+// range.  Kt, the state update's operand, is bounded by one on both paths.
+// The WY factor W is never formed: Tm is applied to the residual V - Kh S
+// instead, which is the same product reassociated and saves one 64x64x128
+// product and its buffer.
 //
 // Tm is built blockwise: the four 16x16 diagonal blocks by forward
 // substitution in registers (one column per lane), then the off-diagonal
@@ -68,7 +77,7 @@ struct Layout {
     static constexpr int OFF_QT = 0;                                  // Qt = e^G q
     static constexpr int OFF_KH = OFF_QT + SZ_TOK;                    // Kh = e^G k (right after Qt)
     static constexpr int OFF_KB = OFF_KH + SZ_TOK;                    // Kb = e^-G k
-    static constexpr int OFF_KBT = OFF_KB + SZ_TOK;                   // Kb^T (bf16 only)
+    static constexpr int OFF_KBT = OFF_KB + SZ_TOK;                   // Kt^T (bf16 only)
     static constexpr int OFF_RA = OFF_KBT + (kF32 ? 0 : DK * P64 * ES);   // Akk -> Tm (fp32)
     static constexpr int OFF_RT = OFF_RA + C * PA * 4;               // Tm Diag(beta) in E (bf16 only)
     static constexpr int OFF_QK = OFF_RT + (kF32 ? 0 : C * P64 * ES);    // Aqk
@@ -80,10 +89,11 @@ struct Layout {
     static constexpr int OFF_GAM = OFF_VN + DV * P64 * ES;           // e^{G_64}
     static constexpr int OFF_BETA = OFF_GAM + DK * 4;
     static constexpr int OFF_TOT = OFF_BETA + C * 4;                 // per-wave column sums of g
-    static constexpr int TOTAL = OFF_TOT + NW * DK * 4;
+    static constexpr int OFF_GTOT = OFF_TOT + NW * DK * 4;           // G_64 per channel (log2)
+    static constexpr int TOTAL = OFF_GTOT + DK * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static_assert(!kF32 || P64 == PA, "fp32 Tm aliases Akk");
-    // Kb^T (channel-major, 64 tokens per row) is stored with its 8-token
+    // Kt^T (channel-major, 64 tokens per row) is stored with its 8-token
     // blocks XOR-swizzled by bits 3..5 of the channel, so that the elementwise
     // phase (lanes 8 channels apart) writes it without bank conflicts while the
     // MFMA fetch (8 consecutive channels, one 8-token block) stays conflict-free.
@@ -112,12 +122,122 @@ struct ChunkIn {
 
 constexpr int PREP_CHUNKS = 4;                      // chunks per prep workgroup
 
+// Largest log2-decay magnitude over one chunk (per channel) for which the
+// chunk-start factorisation 2^{G_r} 2^{-G_i} keeps every factor a normal
+// number with room to spare (fp32 and bf16 share the 8-bit exponent).
+constexpr float FAST_LIM = 96.f;
+
+// Intra-chunk matrices of a chunk whose decay exceeds the fast path's range
+// (secondary chunking; page "Kimi K3论文：Kimi Linear", section 4, on chunking
+// below the chunk because of the cumulative decay's reciprocal).  On entry the
+// LDS holds, for row r of sub-chunk s = r / 16 with B_{s+1} the cumulative
+// log2-decay at the end of that sub-chunk (prefix totals in s_tot, G_64 in
+// s_gtot):
+//   Qt = 2^{G_r - B_{s+1}} q_r, Kh = 2^{G_r - B_{s+1}} k_r   (>= 1, bounded by
+//   the sub-chunk's decay),  Kb = 2^{B_{s+1} - G_r} k_r   (<= 1).
+// Tile (I, R), R >= I, of Aqk^T / Akk^T takes A = Kb rows of block I and B =
+// the Qt / Kh rows of block R; their product carries 2^{G_r - G_i} times
+// 2^{B_{I+1} - B_{R+1}}, so for R > I the B fragment is scaled by
+// F = 2^{B_{R+1} - B_{I+1}} (<= 1, per channel) first: every operand then
+// stays at or below one off the diagonal, and the diagonal tiles need no
+// factor.  The tiles are written as the fast path writes them (Akk in RA with
+// beta, Aqk in sQK, the transposed diagonal Akk blocks in sDT, zero upper
+// tiles).  Then Qt and Kh are rebased to the chunk start (times 2^{B_{s+1}} <=
+// 1), and for fp32, which keeps no Kt^T tile, Kb becomes Kt = 2^{G_64 - G_r}
+// k_r.
+template <typename E, int DV>
+__device__ __forceinline__ void m1_subchunk(char* smem, int t)
+{
+    using L = Layout<E, DV>;
+    using M = Mma<E>;
+    const int lane = t & 63, wave = t >> 6, ln = lane & 15, lg = lane >> 4;
+    E* sQt = reinterpret_cast<E*>(smem + L::OFF_QT);
+    E* sKh = reinterpret_cast<E*>(smem + L::OFF_KH);
+    E* sKb = reinterpret_cast<E*>(smem + L::OFF_KB);
+    float* RA = reinterpret_cast<float*>(smem + L::OFF_RA);
+    float* sDT = reinterpret_cast<float*>(smem + L::OFF_RT);
+    E* sQK = reinterpret_cast<E*>(smem + L::OFF_QK);
+    const float* s_beta = reinterpret_cast<const float*>(smem + L::OFF_BETA);
+    const float* s_tot = reinterpret_cast<const float*>(smem + L::OFF_TOT);
+    const float* s_gtot = reinterpret_cast<const float*>(smem + L::OFF_GTOT);
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    auto bnd_of = [&](int j, int c) { return j < 4 ? s_tot[2 * j * DK + c] : s_gtot[c]; };   // B_j, j = 1..4
+    // 20 product tiles (10 of Aqk, 10 of Akk) and 6 zero upper tiles over the 8 waves
+#pragma unroll 1
+    for (int u = wave; u < 26; u += NW) {
+        if (u < 20) {
+            const bool kk = u >= 10;
+            const int v10 = u % 10;   // (I, R): (0,0..3), (1,1..3), (2,2..3), (3,3)
+            const int I = v10 < 4 ? 0 : (v10 < 7 ? 1 : (v10 < 9 ? 2 : 3));
+            const int R = I + (v10 < 4 ? v10 : (v10 < 7 ? v10 - 4 : (v10 < 9 ? v10 - 7 : 0)));
+            const E* Bm = kk ? sKh : sQt;
+            f32x4 acc = z4;
+#pragma unroll 1
+            for (int k0 = 0; k0 < DK; k0 += M::KS) {
+                const auto fa = M::frag_kc(sKb, L::P128, 16 * I, k0, lane);
+                auto fb = M::frag_kc(Bm, L::P128, 16 * R, k0, lane);
+                if (R > I) {
+                    if constexpr (L::kF32) {
+                        const int c = k0 + (lane >> 4);
+                        fb *= __builtin_amdgcn_exp2f(bnd_of(R + 1, c) - bnd_of(I + 1, c));
+                    } else {
+                        const int c0 = k0 + 8 * (lane >> 4);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            fb[e] = (bf16_t)((float)fb[e] *
+                                             __builtin_amdgcn_exp2f(bnd_of(R + 1, c0 + e) - bnd_of(I + 1, c0 + e)));
+                    }
+                }
+                acc = M::mma(fa, fb, acc);
+            }
+            // epilogue: mask, beta of the row for Akk, store (as the fast path)
+            const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
+            f32x4 val;
+            const float bt = kk ? s_beta[r] : 1.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] = (kk ? (i0 + e < r) : (i0 + e <= r)) ? bt * acc[e] : 0.f;
+            if (kk) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = val;
+            else store_vec4<E>(sQK + r * L::P64 + i0, val);
+            if constexpr (!L::kF32) {
+                if (kk && I == R) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sDT[(16 * R + 4 * lg + e) * L::PDT + ln] = val[e];
+                }
+            }
+        } else {
+            const int v6 = u - 20;
+            const int I = v6 < 3 ? v6 + 1 : (v6 < 5 ? v6 - 1 : 3);
+            const int R = v6 < 3 ? 0 : (v6 < 5 ? 1 : 2);
+            const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
+            if constexpr (L::kF32) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = z4;
+            store_vec4<E>(sQK + r * L::P64 + i0, z4);
+        }
+    }
+    lds_barrier();
+    // rebase: Qt, Kh times 2^{B_{s+1}}; fp32 Kb times 2^{G_64 - B_{s+1}}
+    constexpr int NTILE = L::kF32 ? 3 : 2;
+#pragma unroll 1
+    for (int gi = t; gi < NTILE * C * 16; gi += NT) {
+        const int tile = gi / (C * 16), r = (gi / 16) % C, c0 = 8 * (gi % 16);
+        E* row = (tile == 0 ? sQt : tile == 1 ? sKh : sKb) + r * L::P128 + c0;
+        const int s = r >> 4;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float bs = bnd_of(s + 1, c0 + e);
+            x[e] = to_f32(row[e]) * __builtin_amdgcn_exp2f(tile < 2 ? bs : s_gtot[c0 + e] - bs);
+        }
+        store8<E>(row, x);
+    }
+    lds_barrier();
+}
+
 // The fused kernel (PREP = false): one workgroup per (head, value slice)
 // walks all chunks of its head.  The prep instantiation (PREP = true): one
 // workgroup per (head, chunk) runs only the key-side work -- decay, Aqk, Akk,
 // Tm -- and exports it to the workspace for chunk_scan_kernel; with BWD it
 // also exports to `wsb` the operands of the backward state scan (the
-// transposes Aqk^T, Tm^T, Qt^T, Kh^T and Kt = Diag(e^{G_64}) Kb, layout
+// transposes Aqk^T, Tm^T, Qt^T, Kh^T and Kt = e^{G_64 - G} k, layout
 // WSB_* in kda_chunk_common.h).
 //
 // With cu_seqlens (fused kernel only), batch index b is a sequence packed
@@ -167,6 +287,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     float* s_gam = reinterpret_cast<float*>(smem + L::OFF_GAM);
     float* s_beta = reinterpret_cast<float*>(smem + L::OFF_BETA);
     float* s_tot = reinterpret_cast<float*>(smem + L::OFF_TOT);
+    float* s_gtot = reinterpret_cast<float*>(smem + L::OFF_GTOT);
     // prep for the backward pass: Tm^T, unscaled, in the (unused) value-side
     // buffers; null otherwise
     static_assert(!BWD || (PREP && L::OFF_VN - L::OFF_V >= C * WSB_P64 * 2), "Tm^T fits in the value-side buffers");
@@ -311,8 +432,19 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     acc += a;
                 }
                 s_gam[t] = __builtin_amdgcn_exp2f(acc);
+                s_gtot[t] = acc;
             }
             lds_barrier();
+            // Decay range of this chunk (the same verdict in every wave).
+            // While every channel's log2-decay over the chunk stays above
+            // -FAST_LIM, the row and column factors 2^{G} and 2^{-G} referenced
+            // to the chunk start are normal fp32 / bf16 numbers and the chunk
+            // takes the fast path.  Otherwise its intra-chunk products are
+            // referenced to the ends of the four 16-token sub-chunks (slow
+            // path below), which needs only each sub-chunk's decay in range.
+            bool slow_chunk = false;
+            if constexpr (GATE != GATE_NONE)
+                slow_chunk = __builtin_amdgcn_ballot_w64(s_gtot[lane] < -FAST_LIM || s_gtot[lane + 64] < -FAST_LIM) != 0;
             {
                 if constexpr (NG == 8) {
                     const f32x4 o0 = *reinterpret_cast<const f32x4*>(s_tot + wave * DK + 8 * cg);
@@ -327,33 +459,62 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     for (int i = 0; i < RPL; ++i) G[i][0] += o;
                 }
             }
-            float kb[RPL][8];
+            // Operands, per row r and channel c, from factors a, b, c':
+            //   Qt = a q, Kh = a k, Kb = b k, Kt = c' k  (Kt^T is the bf16 Kb^T tile)
+            // with a = 2^{G_r - ref}, b = 2^{ref - G_r}, c' = 2^{G_64 - G_r}
+            // = 2^{G_64 - ref} b.  Fast path: ref = 0 (the chunk start).  Slow
+            // path: ref = B_{s+1}, the end of the row's sub-chunk s = r / 16
+            // (a >= 1 and b <= 1 within the sub-chunk); its Qt and Kh are
+            // rebased to the chunk start after the intra-chunk products, and Kt
+            // is the same on both paths.  Both paths run the same code on G
+            // shifted by ref.
+            float mult[8];                       // 2^{G_64 - ref} per channel
+            if (slow_chunk) {
+                // sub-chunk s = wave / 2 (16 rows = two waves): its end is the
+                // exclusive prefix at wave 2s + 2, or G_64 for the last one
+                const float* bsrc = (wave >> 1) < 3 ? s_tot + ((wave >> 1) * 2 + 2) * DK + 8 * cg : s_gtot + 8 * cg;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float ref = bsrc[c];
+                    mult[c] = __builtin_amdgcn_exp2f(s_gtot[8 * cg + c] - ref);
+                    if (c < NG) {
+#pragma unroll
+                        for (int i = 0; i < RPL; ++i) G[i][c] -= ref;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) mult[c] = s_gam[8 * cg + c];
+            }
+            float kt[RPL][8];
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 const int r = r0 + i;
                 const bool ok = row_ok(r);
-                float qe[8], ke[8], eg[NG], neg[NG];
+                float qe[8], ke[8], kb[8], fa[NG], fb[NG];
 #pragma unroll
                 for (int c = 0; c < NG; ++c) {
-                    eg[c] = GATE == GATE_NONE ? 1.f : __builtin_amdgcn_exp2f(G[i][c]);
-                    neg[c] = GATE == GATE_NONE ? 1.f : __builtin_amdgcn_exp2f(-G[i][c]);
+                    fa[c] = GATE == GATE_NONE ? 1.f : __builtin_amdgcn_exp2f(G[i][c]);
+                    fb[c] = GATE == GATE_NONE ? 1.f : __builtin_amdgcn_exp2f(-G[i][c]);
                 }
 #pragma unroll
+                for (int c = 0; c < 8; ++c) kt[i][c] = mult[c] * fb[NG == 8 ? c : 0];
+#pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const float e = eg[NG == 8 ? c : 0], ne = neg[NG == 8 ? c : 0];
+                    const float e = fa[NG == 8 ? c : 0], ne = fb[NG == 8 ? c : 0];
                     const float qv = ok ? in.q[i][c] : 0.f, kv = ok ? in.k[i][c] : 0.f;
-                    qe[c] = qv * e; ke[c] = kv * e; kb[i][c] = kv * ne;
+                    qe[c] = qv * e; ke[c] = kv * e; kb[c] = kv * ne; kt[i][c] *= kv;
                 }
                 store8<E>(sQt + r * L::P128 + 8 * cg, qe);
                 store8<E>(sKh + r * L::P128 + 8 * cg, ke);
-                store8<E>(sKb + r * L::P128 + 8 * cg, kb[i]);
+                store8<E>(sKb + r * L::P128 + 8 * cg, kb);
             }
             if constexpr (!L::kF32) {
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     float col[RPL];
 #pragma unroll
-                    for (int i = 0; i < RPL; ++i) col[i] = kb[i][c];
+                    for (int i = 0; i < RPL; ++i) col[i] = kt[i][c];
                     store_run<E, RPL>(sKbT + L::kbt(8 * cg + c, r0), col);
                 }
             }
@@ -367,9 +528,9 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     store8<E>(sV + (RVR * vr + i) * L::PV + 8 * vg, row);
                 }
             }
+            return slow_chunk;
         };
-        if (full) ephase(std::false_type{});
-        else ephase(std::true_type{});
+        const bool slow = full ? ephase(std::false_type{}) : ephase(std::true_type{});
         lds_barrier();
 
         // ===== M1: Aqk, Akk (waves 0-3) | P = Kh S, Z = V - P (waves 4-7) =====
@@ -393,56 +554,6 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     }
                 }
             };
-            // 20 tiles over waves 0-3 (Kh row r is row 64 + r of the Qt base).
-            if (wave == 0) {          // I = 0: Aqk R = 0..3, Akk R = 0
-                f32x4 acc[5] = {z4, z4, z4, z4, z4};
-                const int br[5] = {0, 16, 32, 48, 64};
-                mma_rows<E, DK, 5>(acc, sKb, L::P128, 0, sQt, L::P128, br, lane);
-#pragma unroll
-                for (int R = 0; R < 4; ++R) epilogue(acc[R], 0, R, false);
-                epilogue(acc[4], 0, 0, true);
-            } else if (wave == 1) {   // I = 0: Akk R = 1..3;  I = 1: Aqk R = 1, 2
-                f32x4 acc[3] = {z4, z4, z4};
-                const int br[3] = {80, 96, 112};
-                mma_rows<E, DK, 3>(acc, sKb, L::P128, 0, sQt, L::P128, br, lane);
-                f32x4 acc2[2] = {z4, z4};
-                const int br2[2] = {16, 32};
-                mma_rows<E, DK, 2>(acc2, sKb, L::P128, 16, sQt, L::P128, br2, lane);
-#pragma unroll
-                for (int R = 1; R < 4; ++R) epilogue(acc[R - 1], 0, R, true);
-                epilogue(acc2[0], 1, 1, false); epilogue(acc2[1], 1, 2, false);
-            } else if (wave == 2) {   // I = 1: Aqk R = 3, Akk R = 1..3;  I = 3: Akk R = 3
-                f32x4 acc[4] = {z4, z4, z4, z4};
-                const int br[4] = {48, 80, 96, 112};
-                mma_rows<E, DK, 4>(acc, sKb, L::P128, 16, sQt, L::P128, br, lane);
-                f32x4 acc3[1] = {z4};
-                const int br3[1] = {112};
-                mma_rows<E, DK, 1>(acc3, sKb, L::P128, 48, sQt, L::P128, br3, lane);
-                epilogue(acc[0], 1, 3, false);
-#pragma unroll
-                for (int R = 1; R < 4; ++R) epilogue(acc[R], 1, R, true);
-                epilogue(acc3[0], 3, 3, true);
-            } else if (wave == 3) {   // I = 2 for both, I = 3: Aqk R = 3, and the zero upper tiles
-                f32x4 acc[4] = {z4, z4, z4, z4};
-                const int br[4] = {32, 48, 96, 112};
-                mma_rows<E, DK, 4>(acc, sKb, L::P128, 32, sQt, L::P128, br, lane);
-                f32x4 acc3[1] = {z4};
-                const int br3[1] = {48};
-                mma_rows<E, DK, 1>(acc3, sKb, L::P128, 48, sQt, L::P128, br3, lane);
-                epilogue(acc[0], 2, 2, false); epilogue(acc[1], 2, 3, false);
-                epilogue(acc[2], 2, 2, true); epilogue(acc[3], 2, 3, true);
-                epilogue(acc3[0], 3, 3, false);
-#pragma unroll
-                for (int u = 0; u < 6; ++u) {       // zero the upper tiles (I > R)
-                    const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
-                    const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
-                    const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
-                    // (bf16: only the lower blocks of Akk are ever read; fp32
-                    // turns Akk into Tm in place, whose upper blocks are read)
-                    if constexpr (L::kF32) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = z4;
-                    store_vec4<E>(sQK + r * L::P64 + i0, z4);
-                }
-            }
             // P tiles for token block R = wave - 4 (waves 4-7)
             auto p_block = [&](int R) {
                 f32x4 pacc[NJ];
@@ -459,7 +570,62 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     store_vec4<E>(sZT + j * L::P64 + r, vv - pacc[jb]);
                 }
             };
-            if (!PREP && wave >= 4) p_block(wave - 4);
+            if (!slow) {
+                // 20 tiles over waves 0-3 (Kh row r is row 64 + r of the Qt base).
+                if (wave == 0) {          // I = 0: Aqk R = 0..3, Akk R = 0
+                    f32x4 acc[5] = {z4, z4, z4, z4, z4};
+                    const int br[5] = {0, 16, 32, 48, 64};
+                    mma_rows<E, DK, 5>(acc, sKb, L::P128, 0, sQt, L::P128, br, lane);
+    #pragma unroll
+                    for (int R = 0; R < 4; ++R) epilogue(acc[R], 0, R, false);
+                    epilogue(acc[4], 0, 0, true);
+                } else if (wave == 1) {   // I = 0: Akk R = 1..3;  I = 1: Aqk R = 1, 2
+                    f32x4 acc[3] = {z4, z4, z4};
+                    const int br[3] = {80, 96, 112};
+                    mma_rows<E, DK, 3>(acc, sKb, L::P128, 0, sQt, L::P128, br, lane);
+                    f32x4 acc2[2] = {z4, z4};
+                    const int br2[2] = {16, 32};
+                    mma_rows<E, DK, 2>(acc2, sKb, L::P128, 16, sQt, L::P128, br2, lane);
+    #pragma unroll
+                    for (int R = 1; R < 4; ++R) epilogue(acc[R - 1], 0, R, true);
+                    epilogue(acc2[0], 1, 1, false); epilogue(acc2[1], 1, 2, false);
+                } else if (wave == 2) {   // I = 1: Aqk R = 3, Akk R = 1..3;  I = 3: Akk R = 3
+                    f32x4 acc[4] = {z4, z4, z4, z4};
+                    const int br[4] = {48, 80, 96, 112};
+                    mma_rows<E, DK, 4>(acc, sKb, L::P128, 16, sQt, L::P128, br, lane);
+                    f32x4 acc3[1] = {z4};
+                    const int br3[1] = {112};
+                    mma_rows<E, DK, 1>(acc3, sKb, L::P128, 48, sQt, L::P128, br3, lane);
+                    epilogue(acc[0], 1, 3, false);
+    #pragma unroll
+                    for (int R = 1; R < 4; ++R) epilogue(acc[R], 1, R, true);
+                    epilogue(acc3[0], 3, 3, true);
+                } else if (wave == 3) {   // I = 2 for both, I = 3: Aqk R = 3, and the zero upper tiles
+                    f32x4 acc[4] = {z4, z4, z4, z4};
+                    const int br[4] = {32, 48, 96, 112};
+                    mma_rows<E, DK, 4>(acc, sKb, L::P128, 32, sQt, L::P128, br, lane);
+                    f32x4 acc3[1] = {z4};
+                    const int br3[1] = {48};
+                    mma_rows<E, DK, 1>(acc3, sKb, L::P128, 48, sQt, L::P128, br3, lane);
+                    epilogue(acc[0], 2, 2, false); epilogue(acc[1], 2, 3, false);
+                    epilogue(acc[2], 2, 2, true); epilogue(acc[3], 2, 3, true);
+                    epilogue(acc3[0], 3, 3, false);
+    #pragma unroll
+                    for (int u = 0; u < 6; ++u) {       // zero the upper tiles (I > R)
+                        const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
+                        const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
+                        const int r = 16 * R + ln, i0 = 16 * I + 4 * lg;
+                        // (bf16: only the lower blocks of Akk are ever read; fp32
+                        // turns Akk into Tm in place, whose upper blocks are read)
+                        if constexpr (L::kF32) *reinterpret_cast<f32x4*>(RA + r * L::PA + i0) = z4;
+                        store_vec4<E>(sQK + r * L::P64 + i0, z4);
+                    }
+                }
+                if (!PREP && wave >= 4) p_block(wave - 4);
+            } else {
+                m1_subchunk<E, DV>(smem, t);
+                if (!PREP && wave >= 4) p_block(wave - 4);
+            }
         }
         lds_barrier();
 
@@ -596,7 +762,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                     reinterpret_cast<i32x4*>(blk + dst)[u] = reinterpret_cast<const i32x4*>(smem + src)[u];
             };
             // (for the backward pass, whose save-mode scan reads neither Qt
-            // nor Aqk from this block, only Kh, Kb^T, Tm and gamma)
+            // nor Aqk from this block, only Kh, Kt^T, Tm and gamma)
             if constexpr (BWD) copy(WS_KH, L::OFF_KH, WS_KBT - WS_KH);
             else copy(WS_QT, L::OFF_QT, WS_KBT - WS_QT);  // Qt and Kh
             copy(WS_KBT, L::OFF_KBT, WS_TM - WS_KBT);
@@ -621,12 +787,11 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                 transpose(reinterpret_cast<bf16_t*>(bb + WSB_KHT), sKh, L::P128, DK);
                 for (int u = t; u < C * WSB_P64 * 2 / 16; u += NT)
                     reinterpret_cast<i32x4*>(bb + WSB_TMT)[u] = reinterpret_cast<const i32x4*>(sTmT)[u];
-                for (int u = t; u < C * (DK / 8); u += NT) {           // Kt = Diag(e^{G_64}) Kb
+                for (int u = t; u < C * (DK / 8); u += NT) {           // Kt, token-major, from Kt^T
                     const int r = u >> 4, c8 = 8 * (u & 15);
-                    const bf16x8 kb = *reinterpret_cast<const bf16x8*>(sKb + r * L::P128 + c8);
                     bf16x8 x;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] = (bf16_t)(s_gam[c8 + i] * (float)kb[i]);
+                    for (int i = 0; i < 8; ++i) x[i] = sKbT[L::kbt(c8 + i, r)];
                     *reinterpret_cast<bf16x8*>(bb + WSB_KT + (r * WSB_P128 + c8) * 2) = x;
                 }
                 if (t < DK) reinterpret_cast<float*>(bb + WSB_GAM)[t] = s_gam[t];
@@ -662,7 +827,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         lds_barrier();
 
         // ===== O += Aqk Vn (to HBM; the parked Qt S tiles, spread over all
-        // waves) | S <- Diag(gamma) (S + Kb^T Vn) =====
+        // waves) | S <- Diag(gamma) S + Kt^T Vn =====
         {
 #pragma unroll
             for (int m = 0; m < (NO + NW - 1) / NW; ++m) {
@@ -683,6 +848,17 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 #pragma unroll
             for (int jb = 0; jb < NJ; ++jb) br[jb] = 16 * jb;
             const int Cb = wave;
+            const int c = 16 * Cb + 4 * lg;
+            // S <- Diag(gamma) S + Kt^T Vn, Kt = 2^{G_64 - G} k (bf16: the Kb^T
+            // tile holds Kt^T; fp32: Kb holds Kt on the slow path, while the
+            // fast path keeps Kb = 2^{-G} k and applies gamma after the sum)
+            const bool gamma_first = !L::kF32 || slow;
+            if (gamma_first) {
+#pragma unroll
+                for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc_s[jb][e] *= s_gam[c + e];
+            }
             if constexpr (L::kF32) {
                 // A operand Kb^T read from the token-major Kb
 #pragma unroll 4
@@ -703,11 +879,12 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
                         acc_s[jb] = M::mma(a, M::frag_kc(sVN, L::P64, br[jb], kk, lane), acc_s[jb]);
                 }
             }
-            const int c = 16 * Cb + 4 * lg;
+            if (!gamma_first) {
 #pragma unroll
-            for (int jb = 0; jb < NJ; ++jb)
+                for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc_s[jb][e] *= s_gam[c + e];
+                    for (int e = 0; e < 4; ++e) acc_s[jb][e] *= s_gam[c + e];
+            }
         }
         // S^T for the next chunk: nobody reads S^T in this phase, and the next
         // chunk's first barrier orders these writes before its readers.
@@ -728,7 +905,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 // ---- serial scan over chunks from the workspace (bf16) --------------------
 // One workgroup per (head, 16 NCW value columns), eight waves:
 //   waves 0 .. 7-NCW (loaders) move data: the next chunk's workspace block -- the
-//     key-side operands Qt, Kh, Kb^T, Tm Diag(beta), Aqk, e^{G_64} of that
+//     key-side operands Qt, Kh, Kt^T, Tm Diag(beta), Aqk, e^{G_64} of that
 //     chunk, laid out as this kernel's LDS image -- is copied global -> LDS
 //     directly (16-byte LDS-destination loads) into the other of two stages,
 //     the V slice is written transposed next to it, and the previous chunk's
@@ -736,7 +913,7 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 //   the last NCW waves (consumers) each own 16 value columns and keep their 128 x 16
 //     slice of the state in MFMA accumulators.  For chunk n they form
 //       P = Kh S,  Qt S,  Z = V - P,  Vn = Tm Z,  O = Qt S + Aqk Vn (to LDS),
-//       S <- Diag(e^{G_64}) (S + Kb^T Vn)
+//       S <- Diag(e^{G_64}) S + Kt^T Vn
 //     chaining every product through registers: the accumulator layout of one
 //     product (lane holds rows 4*(lane/16)+e of column lane%16) is the
 //     B-operand layout of the next.  Only A-operands are read from LDS, and
@@ -1036,7 +1213,9 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
                 for (int e = 0; e < 4; ++e) sO[(16 * Rb + 4 * lg + e) * SC::DV + jc] = (bf16_t)a[e];
             }
 
-            // S <- Diag(gamma) (S + Kb^T Vn).  kbt(16cb + ln, 32p + 16hh + 4lg)
+            // KDA: S <- Diag(gamma) S + Kt^T Vn with Kt = e^{G_64 - G} k (the
+            // block's Kb^T slot holds Kt^T); DPLR: S <- Diag(gamma) (S + Ab^T Vn)
+            // + H0 (the slot holds (e^{-G} a)^T).  kbt(16cb + ln, 32p + 16hh + 4lg)
             // splits into a lane part and a compile-time part: the swizzle bits
             // 1-2 depend on (cb, p, hh) only.
             bf16x8 vb[2];
@@ -1048,14 +1227,20 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             };
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(sGam + 16 * cb + 4 * lg);
+                if constexpr (!DPLR) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc_s[cb][e] *= gv[e];
+                }
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     const bf16x8 a = cat8(ld4(kbt_at(cb, p, 0)), ld4(kbt_at(cb, p, 1)));
                     acc_s[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vb[p], acc_s[cb], 0, 0, 0);
                 }
-                const f32x4 gv = *reinterpret_cast<const f32x4*>(sGam + 16 * cb + 4 * lg);
+                if constexpr (DPLR) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc_s[cb][e] *= gv[e];
+                    for (int e = 0; e < 4; ++e) acc_s[cb][e] *= gv[e];
+                }
                 if constexpr (DPLR) {
                     const bf16_t* sH0 = sTm;          // [128][DV] in the Tm slot
 #pragma unroll

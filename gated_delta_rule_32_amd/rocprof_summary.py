@@ -19,7 +19,10 @@ Usage:
       GRBM_GUI_ACTIVE, SQ_INSTS_LDS and SQ_LDS_BANK_CONFLICT (any split over
       the runs), with the mean kernel duration from a kernel-trace run:
         executed bf16 MFMA FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16
-        MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4)
+        MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x CUs x 4)
+          (rocprofv3 reports GRBM_GUI_ACTIVE summed over the 8 XCDs; the
+          busy fraction takes its per-XCD value, as the MfmaUtil expression's
+          reduce(GRBM_GUI_ACTIVE, max) does)
         LDS bank-conflict cycles per LDS instruction
       With --record, the figures are also stored under KEY in
       profiles/counters.json together with the sha256 of FILE.
@@ -119,6 +122,7 @@ def traffic(fetch_dir, write_dir, match, cf_dir, cw_dir, copy_bytes, copy_match)
 
 
 N_CU = 256          # MI355X compute units (4 SIMDs each)
+N_XCD = 8           # accelerator complex dies (GRBM_GUI_ACTIVE is summed over them)
 
 
 def mfma(pmc_dirs, match, trace_dir, key=None, src=None, source=None):
@@ -148,9 +152,12 @@ def mfma(pmc_dirs, match, trace_dir, key=None, src=None, source=None):
     print(f"| executed bf16 MFMA FLOPs per dispatch (512 x MOPS) | {flops:.4e} |")
     print(f"| executed bf16 MFMA rate | {flops / us / 1e6:.1f} TFLOP/s |")
     if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
-        busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (mean["GRBM_GUI_ACTIVE"] * N_CU * 4)
+        gui = mean["GRBM_GUI_ACTIVE"] / N_XCD
+        busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * N_CU * 4)
         rec["mfma_busy_frac"] = round(busy, 4)
-        print(f"| MFMA busy fraction, BUSY_CYCLES / (GUI_ACTIVE x {N_CU} x 4) | {busy:.4f} |")
+        rec["gpu_clock_ghz"] = round(gui / us / 1e3, 3)
+        print(f"| GPU busy cycles per XCD (GRBM_GUI_ACTIVE / {N_XCD}) | {gui:.4g} ({gui / us / 1e3:.2f} GHz over the traced duration) |")
+        print(f"| MFMA busy fraction, BUSY_CYCLES / (GUI_ACTIVE / {N_XCD} x {N_CU} x 4) | {busy:.4f} |")
     if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_INSTS_LDS"):
         per = mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_INSTS_LDS"]
         rec["lds_bank_conflict_per_lds_inst"] = round(per, 3)

@@ -32,10 +32,16 @@
  *    the call needs returns KDA_ERR_WORKSPACE, before anything is launched.
  *
  * Numeric range of the gate: g (= log alpha) must be finite and <= 0.  The
- * chunked prefill factorises exp(G_r - G_i) over 64-token chunks, so it needs
- * the cumulative log-decay of every channel over one chunk to stay above -80
- * (alpha products above e^-80); gates stronger than that are outside the
- * supported range.  The decode step has no such limit.
+ * chunked prefill splits each in-chunk decay exp(G_r - G_i) at a reference
+ * point (page "Kimi K3论文：Kimi Linear", section 4: chunking below the chunk
+ * because of the reciprocal of the cumulative decay).  A 64-token chunk whose
+ * cumulative log-decay stays above -66 in every channel uses the chunk start;
+ * any other chunk uses the ends of its four 16-token sub-chunks, which only
+ * needs every channel's log-decay over each such sub-chunk to stay above -87
+ * (chunk totals down to about -350).  Stronger gates are outside the
+ * supported range.  The backward pass (kda_chunk_bwd*) recomputes the decay
+ * factors from the chunk start and needs every chunk's per-channel log-decay
+ * above -80.  The decode step has no limit.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -342,7 +348,8 @@ int kda_recurrent_step_gated(const void* q, const void* k, const void* v,
  * 128 < 2^31.  T = 0 or B = 0 is a no-op.  Errors as for kda_chunk_fwd; y
  * must not overlap any input or the workspace.  The intermediate activations
  * are rounded to bf16 between steps (log alpha and the low-rank gate input
- * stay fp32); the KDA step runs the same kernels as kda_chunk_fwd.
+ * stay fp32); the KDA step runs the same kernels as kda_chunk_fwd, with the
+ * same range of the decay (see the top of this header).
  */
 enum {
     KDA_LAYER_WS_PRE = 0,  /* [B*T, 4*H*128] bf16: W_q x | W_k x | W_v x | W_g x   */

@@ -23,10 +23,10 @@ def channel_gate(g, like):
     return g if g.shape == like.shape else g[..., None].expand(like.shape).contiguous()
 
 
-def packed(lengths, H, dtype, gate, seed):
+def packed(lengths, H, dtype, gate, seed, g_scale=0.1):
     """Sequences of the given lengths packed along one token axis."""
     total = int(sum(lengths))
-    inp = inputs.prefill_inputs(1, total, H, dtype=dtype, g_scale=0.1, s0_std=0.0, seed=seed, gate=gate)
+    inp = inputs.prefill_inputs(1, total, H, dtype=dtype, g_scale=g_scale, s0_std=0.0, seed=seed, gate=gate)
     S0 = torch.from_numpy(0.05 * np.random.default_rng([seed, 2]).standard_normal(
         (len(lengths), H, 128, 128), dtype=np.float32))
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
