@@ -187,6 +187,10 @@ def prefill_line(name, steps, warmup, schedule="auto"):
         nbytes = kda.scan_workspace_bytes(B, T, H) if schedule == "two_kernel" else 0
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0") if nbytes else None
     sched = "two_kernel" if ws is not None and cfg["dtype"] == "bfloat16" else "fused"
+    if sched == "two_kernel" and nbytes > kda.scan_workspace_bytes(B, T, H):
+        # the library's full workspace: segmented scan (16 heads or fewer) or,
+        # for 24 to 48 heads (a multiple of 8), prep and scan in one launch
+        sched = "pipelined" if B * H % 8 == 0 and 24 <= B * H <= 48 else "two_kernel_segmented"
 
     def step():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], out=o, S_T=S_T,
@@ -203,7 +207,8 @@ def prefill_line(name, steps, warmup, schedule="auto"):
     flops = head_tokens * FLOP_PER_HEAD_TOKEN
     t_floor = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
     # kernels of one call: their rocprofv3 counter records under profiles/
-    keys = [f"chunk_fwd_{name}"] if sched == "fused" else [f"chunk_fwd_{name}_prep", f"chunk_fwd_{name}_scan"]
+    keys = ([f"chunk_fwd_{name}"] if sched in ("fused", "pipelined")
+            else [f"chunk_fwd_{name}_prep", f"chunk_fwd_{name}_scan"])
     parts = [measured_traffic(key, PREFILL_KERNEL_SRC) for key in keys]
     traffic = sum(parts) if all(p is not None for p in parts) else None
     counters = measured_counters(keys, PREFILL_KERNEL_SRC)
@@ -214,8 +219,9 @@ def prefill_line(name, steps, warmup, schedule="auto"):
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": traffic,
-                  "kernel": ("chunk_fwd_kernel (fused)" if sched == "fused"
-                             else "chunk_fwd_kernel (prep) + chunk_scan_kernel"),
+                  "kernel": {"fused": "chunk_fwd_kernel (fused)",
+                             "pipelined": "chunk_pipe_kernel (prep and scan roles in one launch)"}.get(
+                                 sched, "chunk_fwd_kernel (prep) + chunk_scan_kernel"),
                   "alg_bytes_per_launch": alg_bytes,
                   "avg_launch_us": round(t_kernel * 1e6, 2)},
         mfma={"model_flops_per_launch": flops,

@@ -50,9 +50,14 @@ size_t chunk_ws_bytes(long long B, long long T, long long H);
 // all chunks; more with 16 heads or fewer, see chunk_scan_kernel).
 int chunk_seg_count(long long B, long long T, long long H);
 
+// Whether the two-kernel schedule with its full workspace runs prep and scan
+// in one pipelined launch (24 to 48 heads, a multiple of 8).
+bool chunk_uses_pipe(long long B, long long T, long long H);
+
 // Bytes of workspace the two-kernel forward schedule needs: the operand
 // blocks, then with segments the segment summaries [B*H][nseg-1][128][256]
-// and entry states [B*H][nseg][128][128] (fp32).
+// and entry states [B*H][nseg][128][128] (fp32), or for the pipelined launch
+// one int32 ready flag per block and 8 arrival counters.
 size_t chunk_fwd_ws_bytes(long long B, long long T, long long H);
 
 // Whether the two-kernel schedule is expected to be faster for this shape.

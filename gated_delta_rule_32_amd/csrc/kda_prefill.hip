@@ -248,11 +248,16 @@ __device__ __forceinline__ void m1_subchunk(char* smem, int t)
 // GATE_HEAD (one decay per head and token, g [B, T, H]: Gated DeltaNet) or
 // GATE_NONE (alpha = 1: DeltaNet, g unused).  With one decay per row the
 // decay factors are computed once per row instead of once per channel.
+//
+// The body runs on LDS `smem` for the work item `lid` (a (head, slice) or
+// (head, chunk group) index); with `flags` (prep only, the pipelined
+// schedule) each exported block is followed by a ready flag, see
+// chunk_pipe_kernel.
 template <typename E, int DV, bool PREP, bool BWD = false, int GATE = GATE_CHANNEL>
-__global__ void __launch_bounds__(NT)
-chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* beta,
-                 const float* S0, E* o, float* S_T, int T_axis, int H, int nsplit, char* ws,
-                 char* wsb, const int* cu_seqlens)
+__device__ __forceinline__ void
+chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta,
+               const float* S0, E* o, float* S_T, int T_axis, int H, int nsplit, char* ws,
+               char* wsb, const int* cu_seqlens, char* smem, const int lid, int* flags)
 {
     // (No __restrict__ on the inputs: the LDS barriers are asm statements with
     // a memory clobber, and without restrict the compiler keeps the prefetch
@@ -266,7 +271,6 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     constexpr int NO = 4 * NJ;              // output tiles (jb, R)
     constexpr int MO = (NO + NW - 2) / (NW - 1);   // output tiles per wave (waves 1..NW-1)
 
-    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
     E* sQt = reinterpret_cast<E*>(smem + L::OFF_QT);
     E* sKh = reinterpret_cast<E*>(smem + L::OFF_KH);
     E* sKb = reinterpret_cast<E*>(smem + L::OFF_KB);
@@ -299,10 +303,6 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     const int vg = t % In::VL, vr = t / In::VL; // 8-channel group and row group for v
     const int ln = lane & 15, lg = lane >> 4;
 
-    // Workgroup -> (head, slice), keeping the slices of a head on one XCD
-    // (workgroups are dealt to the 8 XCDs round-robin); prep: (head, chunk).
-    const int nwg = gridDim.x, w = blockIdx.x;
-    const int lid = (!PREP && nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
     const int nblk = ((T_axis + C - 1) / C + PREP_CHUNKS - 1) / PREP_CHUNKS;   // prep: chunk groups per head
     const int head = PREP ? lid / nblk : lid / nsplit;
     const int slice = PREP ? 0 : lid % nsplit;
@@ -891,6 +891,18 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
         write_state_lds();
     }
 
+    if (PREP && !BWD && flags && n_first < n_end) {
+        // the blocks of this work item complete in L2 (every store is
+        // acknowledged there), then their ready flags: one wait per item,
+        // not per chunk.  The reader sits on the same XCD, so that L2 is
+        // where it looks.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (t < n_end - n_first)
+            __hip_atomic_store(flags + (size_t)head * nchunks + n_first + t, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     if (!PREP && S_T) {
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) {
@@ -901,6 +913,21 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
     }
 }
 
+
+template <typename E, int DV, bool PREP, bool BWD = false, int GATE = GATE_CHANNEL>
+__global__ void __launch_bounds__(NT)
+chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* beta,
+                 const float* S0, E* o, float* S_T, int T_axis, int H, int nsplit, char* ws,
+                 char* wsb, const int* cu_seqlens)
+{
+    __shared__ __attribute__((aligned(16))) char smem[Layout<E, DV>::TOTAL];
+    // Workgroup -> (head, slice), keeping the slices of a head on one XCD
+    // (workgroups are dealt to the 8 XCDs round-robin); prep: (head, chunk group).
+    const int nwg = gridDim.x, w = blockIdx.x;
+    const int lid = (!PREP && nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
+    chunk_fwd_body<E, DV, PREP, BWD, GATE>(q, k, v, g, beta, S0, o, S_T, T_axis, H, nsplit, ws, wsb,
+                                           cu_seqlens, smem, lid, nullptr);
+}
 
 // ---- serial scan over chunks from the workspace (bf16) --------------------
 // One workgroup per (head, 16 NCW value columns), eight waves:
@@ -968,11 +995,16 @@ template <int NCW, bool SAVE = false> struct ScanCfg {   // NCW consumer waves
 //     [128][128] (written by seg_combine_kernel, the first a copy of S0, so
 //     that S_T may overwrite S0 in place), with the output; the last segment
 //     writes S_T.
+//
+// The body runs on LDS `smem` for the work item `lid` ((head, segment,
+// slice) index); with `flags` (the pipelined schedule) the loaders wait for
+// each block's ready flag before copying it (see chunk_pipe_kernel).
 template <int NCW, bool SAVE, bool DPLR = false, int SEG = SEG_NONE>
-__global__ void __launch_bounds__(512)
-chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
-                  int T, int H, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
-                  const bf16_t* h0, const bf16_t* o0, int seg_len, float* segbuf)
+__device__ __forceinline__ void
+chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
+                int T, int H, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
+                const bf16_t* h0, const bf16_t* o0, int seg_len, float* segbuf, char* smem, const int lid,
+                const int* flags)
 {
     static_assert(!(SAVE && DPLR), "the backward pass is KDA only");
     static_assert(SEG == SEG_NONE || !(SAVE || DPLR), "segments: KDA forward only");
@@ -980,7 +1012,6 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     constexpr bool NOOUT = SAVE || SEG == SEG_SUMMARY;      // no output products or stores
     using SC = ScanCfg<NCW, NOOUT>;
     static_assert(SC::NT == 512, "eight waves (the launch bounds)");
-    __shared__ __attribute__((aligned(1024))) char smem[SC::TOTAL];
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -989,8 +1020,6 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     const int cw = wave - SC::NLW;
     constexpr int nsplit = (SEG == SEG_SUMMARY ? 2 * DK : DK) / SC::DV;
     const int nchunks = (T + C - 1) / C;
-    const int nwg = gridDim.x, w = blockIdx.x;
-    const int lid = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;   // slices of a head on one XCD
     // segments per head in this launch (1 without SEG)
     const int nsegs = SEG == SEG_NONE ? 1 : (nchunks + seg_len - 1) / seg_len - (SEG == SEG_SUMMARY ? 1 : 0);
     const int head = lid / (nsplit * nsegs), seg = lid / nsplit % nsegs, slice = lid % nsplit;
@@ -1037,6 +1066,21 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
             }
             __builtin_amdgcn_global_load_lds(from, (__attribute__((address_space(3))) void*)(dst + u * 1024),
                                              16, 0, 0);
+        }
+    };
+    // pipelined schedule: block n is copied only once its ready flag is set.
+    // The producers never wait, so every wait ends; the spin budget (shared
+    // by all waits of the wave, about a second in all) only guards against a
+    // launch that cannot make progress: once spent, the wave stops waiting.
+    int spin_budget = 1 << 20;
+    auto wait_ready = [&](int n) {
+        if (!flags) return;
+        const int* f = flags + (size_t)head * nchunks + n;
+        while (spin_budget > 0) {
+            if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+                break;
+            __builtin_amdgcn_s_sleep(1);
+            --spin_budget;
         }
     };
     auto load_v = [&](int n) {
@@ -1095,6 +1139,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
                 acc_s[cb][e] = sin ? sin[(size_t)r * DK + j0 + jc] : (ident && r == j0 + jc ? 1.f : 0.f);
             }
     } else {
+        wait_ready(c0);
         load_block(c0);
         load_v(c0);
         __builtin_amdgcn_s_waitcnt(0);        // vmcnt, lgkmcnt and expcnt all zero
@@ -1104,7 +1149,7 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
 
     for (int n = c0; n < c1; ++n) {
         if (loader) {
-            if (n + 1 < c1) { load_block(n + 1); load_v(n + 1); }
+            if (n + 1 < c1) { wait_ready(n + 1); load_block(n + 1); load_v(n + 1); }
             if (!NOOUT && n > c0) store_out(n - 1);
             if constexpr (DPLR) load_o0(n);
             __builtin_amdgcn_s_waitcnt(0);    // the stage must be complete at the barrier
@@ -1268,6 +1313,19 @@ chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, f
     }
 }
 
+template <int NCW, bool SAVE, bool DPLR = false, int SEG = SEG_NONE>
+__global__ void __launch_bounds__(512)
+chunk_scan_kernel(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, float* S_T,
+                  int T, int H, bf16_t* svS, bf16_t* svY, bf16_t* svVn,
+                  const bf16_t* h0, const bf16_t* o0, int seg_len, float* segbuf)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[ScanCfg<NCW, SAVE || SEG == SEG_SUMMARY>::TOTAL];
+    const int nwg = gridDim.x, w = blockIdx.x;
+    const int lid = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;   // slices of a head on one XCD
+    chunk_scan_body<NCW, SAVE, DPLR, SEG>(ws, v, S0, o, S_T, T, H, svS, svY, svVn, h0, o0, seg_len, segbuf, smem,
+                                          lid, nullptr);
+}
+
 // Entry states of the segments of SEG_OUTPUT, entry [head][j][128][128]:
 // with E_j | P_j the summary of segment j (end state from zero, transition),
 // S_{j+1} = P_j S_j + E_j from S_0 = S0 (or zero), in fp32.  One workgroup
@@ -1312,6 +1370,71 @@ seg_combine_kernel(const float* summ, const float* S0, float* entry, int nseg)
     }
 }
 
+// ---- prep and scan in one launch (pipelined two-kernel schedule) -------------
+// For 24 to 48 heads (a multiple of 8, bf16): the prep role's chunk blocks are
+// consumed by the scan role while the prep is still running, so the key-side
+// work of later chunks overlaps the serial state scan, and each block is read
+// from the L2 it was just written to instead of from HBM.  One workgroup per
+// CU, 32 per XCD: on each XCD the first `nprep` workgroups to arrive become
+// producers, the others consumers (one per head of that XCD and 32 value
+// columns).  The heads of XCD x are x, x + 8, ...; producers walk their
+// XCD's chunk groups group-major (all heads' group 0, then group 1, ...) and
+// set a ready flag per block; consumers run chunk_scan_body, whose loaders
+// wait for each block's flag.  Producer and consumer of a block share the
+// XCD's L2, where the flag and the block meet (the producer waits for its
+// stores' acknowledgements before setting the flag).  Roles come from the
+// hardware XCD id and a per-XCD arrival counter, so the pairing does not
+// depend on how workgroups are dealt to XCDs; producers never wait, and
+// consumers arrive after them, so the launch always progresses.  The flags
+// and counters are cleared by pipe_clear_kernel before the launch.
+constexpr int PIPE_NCW = 2;                                // consumer: 32 value columns
+constexpr int PIPE_LDS = Layout<bf16_t, 16>::TOTAL > ScanCfg<PIPE_NCW>::TOTAL ? Layout<bf16_t, 16>::TOTAL
+                                                                               : ScanCfg<PIPE_NCW>::TOTAL;
+constexpr int PIPE_PER_XCD = 32;                           // workgroups per XCD (256 CUs / 8)
+
+__device__ __forceinline__ int xcc_id() {
+    // HW_REG_XCC_ID (hardware register 20), bits 3:0
+    return __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7;
+}
+
+__global__ void __launch_bounds__(256)
+pipe_clear_kernel(int* p, int n)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+template <int GATE>
+__global__ void __launch_bounds__(512)
+chunk_pipe_kernel(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* g, const bf16_t* beta,
+                  const float* S0, bf16_t* o, float* S_T, int T, int H, int heads, char* ws, int* flags,
+                  int* counters)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[PIPE_LDS];
+    constexpr int NSL = DK / ScanCfg<PIPE_NCW>::DV;        // consumers per head
+    const int x = xcc_id();
+    // arrival index on this XCD (passed through the first LDS word, which the
+    // roles overwrite only after the second barrier)
+    if (threadIdx.x == 0) *reinterpret_cast<int*>(smem) = atomicAdd(counters + x, 1);
+    __syncthreads();
+    const int j = *reinterpret_cast<const int*>(smem);
+    __syncthreads();
+    const int hx = heads / 8;                              // heads per XCD
+    const int nprep = PIPE_PER_XCD - NSL * hx;
+    const int nchunks = (T + C - 1) / C;
+    const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
+    if (j < nprep) {
+        for (int i = j; i < hx * nblk; i += nprep) {
+            const int grp = i / hx, head = x + 8 * (i % hx);
+            chunk_fwd_body<bf16_t, 16, true, false, GATE>(q, k, v, g, beta, S0, nullptr, nullptr, T, H, 1, ws,
+                                                          nullptr, nullptr, smem, head * nblk + grp, flags);
+        }
+    } else if (j < PIPE_PER_XCD) {
+        const int js = j - nprep, head = x + 8 * (js / NSL), slice = js % NSL;
+        chunk_scan_body<PIPE_NCW, false>(ws, v, S0, o, S_T, T, H, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                                         nullptr, smem, head * NSL + slice, flags);
+    }
+}
+
 template <typename E, int DV, int GATE>
 void launch_one(const void* q, const void* k, const void* v, const float* g, const void* beta,
                 const float* S0, void* o, float* S_T, int B, int T, int H, hipStream_t stream,
@@ -1336,6 +1459,18 @@ void launch_gate(const void* q, const void* k, const void* v, const float* g, co
     } else if (ws) {
         const int nchunks = (T + C - 1) / C;
         const int nblk = (nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS;
+        if (seg && chunk_uses_pipe(B, T, H)) {
+            // prep and scan in one launch; flags and arrival counters after the blocks
+            int* flags = reinterpret_cast<int*>((char*)ws + chunk_ws_bytes(B, T, H));
+            int* counters = flags + heads * nchunks;
+            const int nclear = (int)(heads * nchunks + 8);
+            hipLaunchKernelGGL(pipe_clear_kernel, dim3((unsigned)std::min(1024, (nclear + 255) / 256)), dim3(256),
+                               0, stream, flags, nclear);
+            hipLaunchKernelGGL((chunk_pipe_kernel<GATE>), dim3(8 * PIPE_PER_XCD), dim3(512), 0, stream,
+                               (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g, (const bf16_t*)beta, S0,
+                               (bf16_t*)o, S_T, T, H, (int)heads, (char*)ws, flags, counters);
+            return;
+        }
         hipLaunchKernelGGL((chunk_fwd_kernel<bf16_t, 16, true, false, GATE>), dim3((unsigned)(heads * nblk)),
                            dim3(NT), 0, stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, g,
                            (const bf16_t*)beta, S0, (bf16_t*)o, S_T, T, H, 1, (char*)ws, (char*)nullptr,
@@ -1402,8 +1537,18 @@ int chunk_seg_count(long long B, long long T, long long H)
     return (int)((nchunks + L - 1) / L);     // no empty trailing segment
 }
 
+bool chunk_uses_pipe(long long B, long long T, long long H)
+{
+    // 24 to 48 heads, a multiple of 8 (whole heads per XCD): 12 to 24 scan
+    // workgroups of 32 columns per XCD, the rest producers
+    const long long heads = B * H;
+    return heads % 8 == 0 && heads >= 24 && heads <= 48 && (T + C - 1) / C >= 2;
+}
+
 size_t chunk_fwd_ws_bytes(long long B, long long T, long long H)
 {
+    if (chunk_uses_pipe(B, T, H))   // blocks, then a ready flag per block and 8 arrival counters
+        return chunk_ws_bytes(B, T, H) + ((size_t)B * H * ((T + C - 1) / C) + 8) * 4;
     const int nseg = chunk_seg_count(B, T, H);
     // summaries [nseg - 1][128][256] and entry states [nseg][128][128] per head
     const size_t seg = nseg > 1 ? (size_t)B * H * (3 * (nseg - 1) + 1) * DK * DK * 4 : 0;

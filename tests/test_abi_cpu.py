@@ -135,7 +135,12 @@ def test_fp32_ignores_a_small_workspace(lib):
 def test_workspace_size_query(lib):
     f = lib.kda_chunk_fwd_workspace_size
     # few heads, bf16: two-kernel schedule, one 72,704-byte block per chunk
-    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 72704
+    # 24 to 48 heads (a multiple of 8): prep and scan pipelined in one launch,
+    # one int32 ready flag per block and 8 arrival counters after the blocks
+    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 72704 + (32 * 1024 + 8) * 4
+    assert f(2, 1000, 20, 128, 128, BF16) == 40 * 16 * 72704 + (40 * 16 + 8) * 4
+    assert f(1, 1000, 36, 128, 128, BF16) == 36 * 16 * 72704            # not a multiple of 8: one pass
+    assert f(1, 64, 32, 128, 128, BF16) == 0                            # one chunk: fused kernel
     assert f(1, 100, 3, 128, 128, BF16) == 3 * 2 * 72704
     # 16 heads or fewer over enough chunks: the state scan runs in nseg
     # segments: fp32 summaries [nseg - 1][128][256], entry states [nseg][128][128]

@@ -95,6 +95,39 @@ def test_segmented_scan(B, H, T, s0_std, g_scale):
     check(inp, o2, S2, TOL["bfloat16"])
 
 
+@pytest.mark.parametrize("B,H,T,gate", [
+    (1, 24, 1000, "channel"),   # 3 heads per XCD, ragged last chunk
+    (2, 16, 777, "channel"),    # 32 heads
+    (1, 40, 300, "channel"),
+    (1, 48, 130, "channel"),    # 6 heads per XCD: 8 producers per XCD
+    (3, 8, 65, "channel"),      # two chunks
+    (1, 32, 500, "head"),
+    (1, 32, 500, "none"),
+])
+def test_pipelined_schedule(B, H, T, gate):
+    """24 to 48 heads (a multiple of 8) with the library's workspace: prep and
+    scan in one launch, the scan waiting on per-block ready flags.  Every
+    output and final-state entry against the oracle, and bitwise equal to the
+    one-pass two-kernel schedule (the same products in the same order)."""
+    print(f"prefill pipelined B={B} H={H} T={T} gate={gate}", flush=True)
+    ws = kda.workspace_size(B, T, H, kda.KDA_BF16)
+    assert ws > kda.scan_workspace_bytes(B, T, H)      # room for the flags
+    inp = inputs.prefill_inputs(B, T, H, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=400 + T, gate=gate)
+    d = to_dev(inp)
+    o, S = run(d, workspace=torch.empty(ws, dtype=torch.uint8, device=DEV))
+    g = inp["g"] if gate == "channel" else (torch.zeros(inp["q"].shape) if inp["g"] is None
+                                             else inp["g"][..., None].expand(inp["q"].shape).contiguous())
+    check({**inp, "g": g}, o, S, TOL["bfloat16"])
+    o2, S2 = run(d, schedule="two_kernel")
+    assert torch.equal(o, o2) and torch.equal(S, S2)
+    # twice more on the same workspace (flags cleared per call), S_T in place of S0
+    state = d["S0"].clone()
+    o3, _ = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], state, S_T=state,
+                          workspace=torch.empty(ws, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o) and torch.equal(state, S)
+
+
 def test_segmented_scan_in_place_state():
     """The segmented scan with S_T written over S0 (the same tensor)."""
     print("prefill segmented scan, S_T in place of S0", flush=True)
