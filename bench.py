@@ -18,7 +18,7 @@ line also carries:
   * prefill_c1: the one-head fp32 T = 256 prefill, latency per call, and the
     one-thread oracle time of the same call;
   * decode: the recurrent decode step over 256 x 32 heads, state GB/s and %
-    of HBM peak;
+    of HBM peak, plus four tokens per call through kda_recurrent_steps;
   * layer: the full token-mixing layer (d_model 2048, 16 heads, 32768
     tokens), its time, the KDA operator's share and the achieved TFLOP/s;
   * gate_variants: the B = 8 prefill with one decay per head and token (Gated
@@ -295,6 +295,29 @@ def decode_latency_line(steps, warmup, N=1, H=32, per_graph=32):
             "eager_us_per_step": round(t_eager * 1e6, 2),
             "graph_us_per_step": round(t_graph / per_graph * 1e6, 2),
             "steps_per_graph": per_graph}
+
+
+def multi_token_line(steps, warmup, m=4):
+    """kda_recurrent_steps: m tokens per sequence in one call over 256 x 32
+    heads (speculative or multi-token decoding; every token applied), against
+    m single-token steps."""
+    import torch
+    import gated_delta_rule_32_amd as kda
+    from gated_delta_rule_32_amd import inputs
+
+    cfg = inputs.DECODE_CONFIG
+    N, H = cfg["N"], cfg["H"]
+    S = inputs.decode_state(N, H, s_std=cfg["s_std"], seed=cfg["seed"], device="cuda:0")
+    tk = inputs.decode_tokens(N, H, m, dtype=cfg["dtype"], seed=cfg["seed"], device="cuda:0")
+    seq = {n: tk[n].transpose(0, 1).contiguous() for n in ("q", "k", "v", "g", "beta")}   # [N, m, H, .]
+    o = torch.empty((N, m, H, D), dtype=torch.bfloat16, device="cuda:0")
+    t, _ = time_launches(lambda: kda.recurrent_steps(seq["q"], seq["k"], seq["v"], seq["g"], seq["beta"], S,
+                                                     out=o), steps, warmup)
+    alg = N * H * (2 * STATE_BYTES + m * (DECODE_BYTES_PER_HEAD - 2 * STATE_BYTES))
+    return {"workload": f"kda_recurrent_steps {N}x{H} heads, m = {m} tokens per call (all applied)",
+            "us_per_call": round(t * 1e6, 2), "us_per_token": round(t * 1e6 / m, 2),
+            "alg_bytes_per_call": alg, "gb_s": round(alg / t / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def mqa_line(steps, warmup, kda_decode=None):
@@ -679,6 +702,7 @@ def main():
     if args.workload is None and not args.no_decode:
         line["decode"] = decode_line(max(args.steps, 20), args.warmup)
         line["decode"]["small_batch"] = decode_latency_line(max(args.steps, 20), args.warmup)
+        line["decode"]["multi_token"] = multi_token_line(max(args.steps, 20), args.warmup)
     if args.workload is None and not args.no_mqa:
         line["full_attention_decode"] = mqa_line(max(args.steps, 20), args.warmup, line.get("decode"))
     if args.workload is None and not args.no_layer:

@@ -13,7 +13,7 @@ import ctypes
 from ._binding import (KDA_BF16, KDA_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,  # noqa: F401
                        KDA_GATE_NONE, LAYER_REGIONS, KDAError, lib, status_string, version, _check)
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "bwd_workspace_size", "dplr_chunk_fwd",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "bwd_workspace_size", "dplr_chunk_fwd", "recurrent_steps",
            "dplr_workspace_size", "recurrent_step", "workspace_size", "scan_workspace_bytes",
            "layer_fwd", "layer_workspace_layout", "LAYER_WEIGHTS", "mqa_decode", "release_workspaces",
            "status_string", "version", "KDAError",
@@ -320,6 +320,37 @@ def recurrent_step(q, k, v, log_alpha, beta, S, *, out=None):
     st = lib().kda_recurrent_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), gate, _ptr(beta),
                                         _ptr(S), _ptr(out), N, H, dk, dv, code, _stream(dev))
     _check("kda_recurrent_step_gated", st)
+    return out
+
+
+def recurrent_steps(q, k, v, log_alpha, beta, S, accept=None, *, out=None, return_output=True):
+    """m decode steps per sequence in one call, state updated in place
+    (multi-token or speculative decoding).  q, k, v: [N, m, H, 128];
+    log_alpha: [N, m, H, 128] fp32, [N, m, H] fp32 or None; beta: [N, m, H];
+    S: [N, H, 128, 128] fp32; accept: None (all m tokens) or an int32 device
+    tensor [N] (sequence n applies its first accept[n] tokens).  Returns o
+    [N, m, H, 128] (entries of tokens not applied are left as allocated) or
+    None with return_output=False."""
+    import torch
+    N, m, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for t, n, shp in ((k, "k", q.shape), (v, "v", (N, m, H, dv)), (beta, "beta", (N, m, H))):
+        _need(t, n, dt, shp, dev)
+    gate = _gate(log_alpha, 4)
+    if gate != KDA_GATE_NONE:
+        _need(log_alpha, "log_alpha", torch.float32, q.shape if gate == KDA_GATE_CHANNEL else (N, m, H), dev)
+    _need(S, "S", torch.float32, (N, H, dk, dv), dev)
+    if accept is not None:
+        _need(accept, "accept", torch.int32, (N,), dev)
+    if out is None and return_output:
+        out = torch.empty((N, m, H, dv), dtype=dt, device=dev)
+    elif out is not None:
+        _need(out, "out", dt, (N, m, H, dv), dev)
+    st = lib().kda_recurrent_steps(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), gate, _ptr(beta), _ptr(accept),
+                                   _ptr(S), _ptr(out), N, m, H, dk, dv, code, _stream(dev))
+    _check("kda_recurrent_steps", st)
     return out
 
 

@@ -44,6 +44,8 @@ SIGNATURES = {
     "kda_chunk_bwd_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "kda_recurrent_step": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                 _I, _I, _I, _I, _I, _VP]),
+    "kda_recurrent_steps": (_I, [_VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP,
+                                 _I, _I, _I, _I, _I, _I, _VP]),
     "kda_layer_fwd": (_I, [_VP] * 13 + [_I] * 5 + [_VP, _SZ, _VP]),
     "kda_layer_workspace_layout": (_SZ, [_I] * 5 + [ctypes.POINTER(_SZ)]),
     "kda_mqa_decode": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _VP, _SZ, _VP]),

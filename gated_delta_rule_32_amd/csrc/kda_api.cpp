@@ -379,6 +379,45 @@ int kda_recurrent_step_gated(const void* q, const void* k, const void* v,
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_recurrent_steps(const void* q, const void* k, const void* v,
+                        const float* log_alpha, int gate, const void* beta, const int32_t* accept,
+                        float* S, void* o, int N, int m, int H, int dk, int dv, int dtype, void* stream)
+{
+    if (N < 0 || m < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED;
+    if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if ((long long)N * H == 0 || m == 0) return KDA_OK;
+
+    bool ok = true;
+    const size_t es = elem_size(dtype);
+    const size_t heads = mul3(N, H, 1, &ok);
+    const size_t toks = mul3(N, m, H, &ok);                 // (sequence, token, head) entries
+    const size_t n_vec = mul3((long long)toks, kHeadDim, 1, &ok);
+    const size_t n_state = mul3((long long)heads, kHeadDim, kHeadDim, &ok);
+    if (!ok || heads > (size_t)INT_MAX) return KDA_ERR_UNSUPPORTED;
+
+    int rc;
+    if (gate == KDA_GATE_NONE && log_alpha) return KDA_ERR_INVALID_ARG;
+    if ((rc = check_ptr(q, 16)) || (rc = check_ptr(k, 16)) || (rc = check_ptr(v, 16)) ||
+        (gate != KDA_GATE_NONE && (rc = check_ptr(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4))) ||
+        (rc = check_ptr(beta, es)) || (rc = check_ptr(S, 16)))
+        return rc;
+    if (o && (rc = check_ptr(o, 16))) return rc;
+    if (accept && (rc = check_ptr(accept, 4))) return rc;
+    const size_t g_bytes = gate == KDA_GATE_CHANNEL ? n_vec * 4 : gate == KDA_GATE_HEAD ? toks * 4 : 0;
+    const Range in[] = {{q, n_vec * es}, {k, n_vec * es}, {v, n_vec * es},
+                        {log_alpha, g_bytes}, {beta, toks * es}, {accept, accept ? (size_t)N * 4 : 0}};
+    const Range rS{S, n_state * 4}, ro{o, o ? n_vec * es : 0};
+    for (const Range& r : in)
+        if (overlap(rS, r) || overlap(ro, r)) return KDA_ERR_INVALID_ARG;
+    if (overlap(rS, ro)) return KDA_ERR_INVALID_ARG;
+
+    hipError_t e = kda::launch_decode_steps(q, k, v, log_alpha, beta, accept, S, o, (long long)heads, m, H, dtype,
+                                            (hipStream_t)stream, gate);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 size_t kda_mqa_decode_workspace_size(int B, int T, int H, int D)
 {
     if (B < 0 || T < 1 || T > (1 << 22) || (H != 16 && H != 32) || D != 512) return 0;

@@ -14,6 +14,13 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v,
                               long long heads, int dtype, hipStream_t stream,
                               int gate = KDA_GATE_CHANNEL);
 
+// m decode steps per head, tokens [N, m, H, .]; with `accept` (device,
+// [N]) sequence n applies only its first accept[n] tokens (clamped to
+// [0, m]).  `o` may be null.  heads = N * H.
+hipError_t launch_decode_steps(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                               const int* accept, float* S, void* o, long long heads, int m, int H, int dtype,
+                               hipStream_t stream, int gate = KDA_GATE_CHANNEL);
+
 // Chunked prefill over B*H heads of T >= 1 tokens (d_k = d_v = 128).  With
 // `ws` non-null (bf16 only, at least chunk_ws_bytes(B, T, H) bytes) the
 // two-kernel schedule runs; otherwise the fused single kernel.  With `seg`

@@ -317,6 +317,33 @@ int kda_recurrent_step_gated(const void* q, const void* k, const void* v,
                              void* stream);
 
 /*
+ * m recurrent steps per head in one call: multi-token and speculative
+ * decoding (page "Kimi K3论文：Kimi Linear", section 8: the KDA kernel inside a
+ * serving engine; section 3 eq. (1) applied token after token).  Sequence n
+ * brings m tokens (drafted tokens, or several known ones); with `accept`
+ * NULL all m are applied, otherwise only its first accept[n] (clamped to
+ * [0, m]; 0 leaves the state untouched) -- the accepted prefix once a
+ * verifier has checked the drafted tokens, e.g. from the outputs of
+ * kda_chunk_fwd run on them with S_T = NULL.  The state stays on chip between
+ * the tokens, so it crosses HBM once in and once out per call.
+ *
+ *   q, k      [N, m, H, dk]   dtype        token i of sequence n at [n, i]
+ *   v         [N, m, H, dv]   dtype
+ *   log_alpha [N, m, H, dk] / [N, m, H] fp32 / NULL, by gate (kda_gate_t)
+ *   beta      [N, m, H]       dtype
+ *   accept    [N]             int32, DEVICE memory, or NULL (all m)
+ *   S         [N, H, dk, dv]  fp32   in/out  state before, then after the
+ *                                            applied tokens
+ *   o         [N, m, H, dv]   dtype  out     outputs of the applied tokens
+ *                                            (others untouched), or NULL
+ * N*H = 0 or m = 0 is a no-op.  S and o must not overlap each other or any
+ * input; accept must be 4-byte aligned.  Errors as for kda_recurrent_step.
+ */
+int kda_recurrent_steps(const void* q, const void* k, const void* v,
+                        const float* log_alpha, int gate, const void* beta, const int32_t* accept,
+                        float* S, void* o, int N, int m, int H, int dk, int dv, int dtype, void* stream);
+
+/*
  * One KDA token-mixing layer (page "Kimi K3论文：Kimi Linear", section 3:
  * input parameterisation of q, k, v, alpha, beta, the KDA recurrence and the
  * gated output path), for B sequences of T tokens, all bf16 except where noted:

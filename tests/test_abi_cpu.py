@@ -34,7 +34,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_scan_workspace_size",
-                          "kda_chunk_fwd_noalloc",
+                          "kda_chunk_fwd_noalloc", "kda_recurrent_steps",
                           "kda_chunk_fwd_block_bytes", "kda_chunk_bwd", "kda_chunk_bwd_gated",
                           "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_gated", "kda_chunk_fwd_varlen",
                           "kda_mqa_decode", "kda_mqa_decode_workspace_size",
@@ -113,6 +113,29 @@ def test_block_and_scan_workspace_queries(lib):
     assert f(2, 65, 3, 128, 128, BF16) == 6 * 2 * 72704
     assert f(1, 64, 1, 128, 128, F32) == 0            # fp32 uses no workspace
     assert f(1, 0, 1, 128, 128, BF16) == 0 and f(1, 64, 1, 64, 128, BF16) == 0
+
+
+def steps(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, gate=0, beta=P + 2**27, accept=None, S=P + 2**28,
+          o=P + 2**29, N=2, m=3, H=4, dk=128, dv=128, dt=BF16):
+    return lib.kda_recurrent_steps(q, k, v, g, gate, beta, accept, S, o, N, m, H, dk, dv, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(S=None), INVALID), (dict(N=-1), INVALID), (dict(m=-1), INVALID),
+    (dict(dk=64), UNSUP), (dict(dt=5), UNSUP), (dict(gate=7), UNSUP),
+    (dict(gate=2), INVALID),                    # no gate: log_alpha must be NULL
+    (dict(accept=P + 2**30 + 2), ALIGN), (dict(o=P + 2**29 + 8), ALIGN),
+    (dict(S=P + 2**24 + 64), INVALID),          # S overlaps k
+    (dict(o=P + 2**28 + 1024), INVALID),        # o inside S
+    (dict(accept=P + 2**28 + 64), INVALID),     # accept inside S (which is written)
+])
+def test_recurrent_steps_rejects(lib, kw, code):
+    assert steps(lib, **kw) == code
+
+
+def test_recurrent_steps_noop_shapes(lib):
+    assert steps(lib, m=0, q=None, k=None, v=None, g=None, beta=None, S=None, o=None) == OK
+    assert steps(lib, N=0, q=None, k=None, v=None, g=None, beta=None, S=None, o=None) == OK
 
 
 def test_noalloc_rejects_on_the_host(lib):

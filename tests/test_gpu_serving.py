@@ -151,3 +151,62 @@ def test_auto_workspace_is_per_stream():
     torch.cuda.synchronize()
     for (o, S), (ro, rS) in zip(got, ref):
         assert torch.equal(o, ro) and torch.equal(S, rS)
+
+
+@pytest.mark.parametrize("gate", ["channel", "head", "none"])
+@pytest.mark.parametrize("dtype,m", [("float32", 3), ("bfloat16", 1), ("bfloat16", 8)])
+def test_recurrent_steps_all_tokens(gate, dtype, m):
+    """kda_recurrent_steps with every one of the m tokens applied: outputs of
+    all tokens and the final state against the oracle run over the m tokens."""
+    N, H = 5, 6
+    print(f"recurrent_steps gate={gate} dtype={dtype} m={m}", flush=True)
+    inp = inputs.prefill_inputs(N, m, H, dtype=dtype, g_scale=0.1, s0_std=0.03, seed=60 + m, gate=gate)
+    d = {n: (x.to(DEV) if x is not None else None) for n, x in inp.items()}
+    S = d["S0"].clone()
+    o = kda.recurrent_steps(d["q"], d["k"], d["v"], d["g"], d["beta"], S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = kda_ref.recurrent(inp["q"], inp["k"], inp["v"], channel_gate(inp["g"], inp["q"]), inp["beta"],
+                                     inp["S0"])
+    eo, es = max_rel_err(o, o_ref), max_rel_err(S, S_ref)
+    print(f"  o err {eo:.3e}  S err {es:.3e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_speculative_decode_accepted_prefix():
+    """Speculative decoding, three rounds: m = 4 drafted tokens per sequence
+    are verified from the outputs of kda_chunk_fwd run on them without
+    committing the state (S_T = NULL); then kda_recurrent_steps advances each
+    sequence's state by its accepted prefix accept[n] (0 .. 4) in one call.
+    Against the oracle run over the accepted tokens of every round in turn;
+    outputs of tokens past the prefix are left untouched."""
+    N, H, m = 6, 4, 4
+    S = inputs.decode_state(N, H, s_std=0.02, seed=71, device=DEV)
+    S_ref = S.double().cpu().numpy()
+    rng = np.random.default_rng(72)
+    for rnd in range(3):
+        inp = inputs.prefill_inputs(N, m, H, dtype="bfloat16", g_scale=0.1, seed=700 + rnd)
+        d = {n: (x.to(DEV) if x is not None else None) for n, x in inp.items()}
+        # verification pass over all drafted tokens: outputs only
+        o_ver, none = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S, return_state=False,
+                                    workspace=None)
+        assert none is None
+        o_all_ref, _ = kda_ref.recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S_ref)
+        torch.cuda.synchronize()
+        assert max_rel_err(o_ver, o_all_ref) <= TOL["bfloat16"]
+        accept = np.array([0, 1, 2, 3, 4] + [int(rng.integers(0, m + 1))], dtype=np.int32)[:N]
+        out = torch.full_like(d["v"], float("nan"))
+        kda.recurrent_steps(d["q"], d["k"], d["v"], d["g"], d["beta"], S, torch.from_numpy(accept).to(DEV),
+                            out=out)
+        torch.cuda.synchronize()
+        for n in range(N):
+            j = int(accept[n])
+            sl = lambda x: x[n:n + 1, :j]   # noqa: E731
+            if j > 0:
+                o_r, S_n = kda_ref.recurrent(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["g"]),
+                                             sl(inp["beta"]), S_ref[n:n + 1])
+                assert max_rel_err(out[n:n + 1, :j], o_r) <= TOL["bfloat16"]
+                S_ref[n] = S_n[0]
+            assert torch.isnan(out[n, j:].float()).all()
+        es = max_rel_err(S, S_ref)
+        print(f"  round {rnd}: accept {accept.tolist()}  S err {es:.3e}", flush=True)
+        assert es <= TOL["bfloat16"]
