@@ -21,6 +21,9 @@
 //   dbeta_r = sum_j Y[r,j] dZ[r,j] + sum_i dAkk[r,i] (Kh Kb^T)[r,i]
 //   dq = e^G dQt,  dk = e^G dKh + e^-G dKb + e^{G_64-G} dKt
 //   dG = Qt.dQt + Kh.dKh - Kb.dKb - Kt.dKt (elementwise)
+// (the gradient kernel evaluates these with every decay factor referenced to
+// the end of a 16-token sub-chunk rather than to the chunk start, so that no
+// factor grows with the chunk's total decay; see chunk_bwd_grad_kernel)
 //   dG_64 += e^{G_64} sum_j S[c,j] dS'[c,j] + sum_r Kt[r,c] dKt[r,c]
 //   dg = reverse cumulative sum of dG over the chunk's tokens.
 //
@@ -273,7 +276,8 @@ struct GradLds {
     static constexpr int OFF_VN = OFF_DO + T128;
     static constexpr int OFF_BETA = OFF_VN + T128;            // beta [64] fp32
     static constexpr int OFF_DB = OFF_BETA + C * 4;           // dbeta [64] fp32
-    static constexpr int TOTAL = OFF_DB + C * 4;
+    static constexpr int OFF_F = OFF_DB + C * 4;              // F [6 block pairs][128] bf16
+    static constexpr int TOTAL = OFF_F + 6 * DK * 2;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
     static_assert(2 * T128 >= C * DK * 4, "g staging fits in region A");
     static_assert(4 * T64 >= 2 * C * DK * 2, "q, k staging fits in region CR");
@@ -319,6 +323,7 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     bf16_t* sVN = reinterpret_cast<bf16_t*>(smem + L::OFF_VN);
     float* sbeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
     float* sdb = reinterpret_cast<float*>(smem + L::OFF_DB);
+    bf16_t* sF = reinterpret_cast<bf16_t*>(smem + L::OFF_F);
     // staging, unpadded row-major [64][128]
     const float* stG = reinterpret_cast<const float*>(smem + L::OFF_A);
     const bf16_t* stQ = reinterpret_cast<const bf16_t*>(smem + L::OFF_CR);
@@ -418,26 +423,47 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         carry += bs[0] + bs[1] + bs[2] + bs[3];
     }
     const float Gc = carry;
+    // Sub-chunk boundaries of this lane's channel: Bv[j] = G at the end of
+    // sub-chunk j - 1 (16-token blocks; Bv[0] = 0, Bv[4] = G_64).  Every
+    // decay factor below is referenced to one of them, so that none grows
+    // with the chunk's total decay (only with one sub-chunk's).
+    float Bv[5];
+    Bv[0] = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Bv[m + 1] = __shfl(G[m][3], ln + 48);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         *reinterpret_cast<bf16x8*>(sDO + vr * L::P128 + vc + 8 * i) = dov[i];
         *reinterpret_cast<bf16x8*>(sVN + vr * L::P128 + vc + 8 * i) = vnv[i];
     }
     lds_barrier();                                 // staging reads done before A and CR are reused
+    // row r of block m:  Ke = 2^{G_r - B_{m+1}} k (>= 1), Kend = 2^{B_{m+1} - G_r} k (<= 1)
+    // token-major for K K^T; Qs = 2^{G_r - B_m} q, Ks = 2^{G_r - B_m} k (<= 1) and
+    // Kend transposed for the token contractions
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        f32x4 qt, kh, kb;
+        f32x4 qs, ks, kend;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float eg = __builtin_amdgcn_exp2f(G[m][e]), egi = __builtin_amdgcn_exp2f(-G[m][e]);
-            qt[e] = eg * qv[m][e]; kh[e] = eg * kv[m][e]; kb[e] = egi * kv[m][e];
+            const float ea = __builtin_amdgcn_exp2f(G[m][e] - Bv[m + 1]);
+            const float eai = __builtin_amdgcn_exp2f(Bv[m + 1] - G[m][e]);
+            const float esi = __builtin_amdgcn_exp2f(G[m][e] - Bv[m]);
+            qs[e] = esi * qv[m][e]; ks[e] = esi * kv[m][e]; kend[e] = eai * kv[m][e];
             const int r = 16 * m + 4 * lg + e;
-            sKh[r * L::P128 + c] = (bf16_t)kh[e];
-            sKb[r * L::P128 + c] = (bf16_t)kb[e];
+            sKh[r * L::P128 + c] = (bf16_t)(ea * kv[m][e]);
+            sKb[r * L::P128 + c] = (bf16_t)kend[e];
         }
-        store_vec4<bf16_t>(sQtT + c * L::P64 + 16 * m + 4 * lg, qt);
-        store_vec4<bf16_t>(sKhT + c * L::P64 + 16 * m + 4 * lg, kh);
-        store_vec4<bf16_t>(sKbT + c * L::P64 + 16 * m + 4 * lg, kb);
+        store_vec4<bf16_t>(sQtT + c * L::P64 + 16 * m + 4 * lg, qs);
+        store_vec4<bf16_t>(sKhT + c * L::P64 + 16 * m + 4 * lg, ks);
+        store_vec4<bf16_t>(sKbT + c * L::P64 + 16 * m + 4 * lg, kend);
+    }
+    if (lg == 0) {
+        // F[R, I] = 2^{B_{R+1} - B_{I+1}} (<= 1) for block pairs R > I, index R (R - 1) / 2 + I
+#pragma unroll
+        for (int R = 1; R < 4; ++R)
+#pragma unroll
+            for (int I = 0; I < R; ++I)
+                sF[(R * (R - 1) / 2 + I) * DK + c] = (bf16_t)__builtin_amdgcn_exp2f(Bv[R + 1] - Bv[I + 1]);
     }
     if (t < C) {
         const int tok = tok0 + t;
@@ -464,7 +490,14 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         for (int s = 0; s < 4; ++s) {
             const int ko = 32 * s + 8 * lg;
             const bf16x8 vnf = ld8(sVN + rb * L::P128 + ko);
-            kk = mma(ld8(sKh + ra * L::P128 + ko), ld8(sKb + rb * L::P128 + ko), kk);
+            // (K K^T)[r, i] = sum_c Ke_r Kend_i F[mb, nb] over the channels c
+            bf16x8 kbf = ld8(sKb + rb * L::P128 + ko);
+            if (nb < mb) {
+                const bf16x8 f = ld8(sF + (mb * (mb - 1) / 2 + nb) * DK + ko);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) kbf[x] = (bf16_t)((float)kbf[x] * (float)f[x]);
+            }
+            kk = mma(ld8(sKh + ra * L::P128 + ko), kbf, kk);
             m1 = mma(dzf[j][s], vnf, m1);
             m2 = mma(ld8(sDO + ra * L::P128 + ko), vnf, m2);
         }
@@ -527,19 +560,41 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
             aT[m] = mma(ld8(sVN + ar), dsf[s], aT[m]);
         }
     }
+    // dQt and dKh of rows in block m are carried relative to B_{m+1}: the
+    // state terms (dO S^T, -dV S^T, whose own factor is 2^{G_r}) times
+    // 2^{B_{m+1}} (<= 1) here, the in-chunk terms below against keys
+    // referenced to B_{m+1}
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float f = __builtin_amdgcn_exp2f(Bv[m + 1]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { aQ[m][e] *= f; aH[m][e] *= f; }
+    }
+    auto scale8 = [](bf16x8 x, float f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (bf16_t)((float)x[i] * f);
+        return x;
+    };
 #pragma unroll
     for (int s = 0; s < 2; ++s) {                  // contraction over tokens
         const int ko = 32 * s + 8 * lg;
+        const int tb = 2 * s + (lg >> 1);          // 16-token block of this lane's 8 tokens
         const bf16x8 kbt = ld8(sKbT + c * L::P64 + ko);
         const bf16x8 qtt = ld8(sQtT + c * L::P64 + ko);
         const bf16x8 kht = ld8(sKhT + c * L::P64 + ko);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int ar = (16 * m + ln) * L::P64 + ko;
-            aQ[m] = mma(ld8(sdAqk + ar), kbt, aQ[m]);
-            aH[m] = mma(ld8(sdAp + ar), kbt, aH[m]);
-            aB[m] = mma(ld8(sdAqkT + ar), qtt, aB[m]);
-            aB[m] = mma(ld8(sdApT + ar), kht, aB[m]);
+            // rows of block m against keys of block tb <= m: Kend (ref B_{tb+1})
+            // times 2^{B_{m+1} - B_{tb+1}}; blocks tb > m are zero in dAqk, dA'
+            const bf16x8 kq = tb == m ? kbt : scale8(kbt, tb < m ? __builtin_amdgcn_exp2f(Bv[m + 1] - Bv[tb + 1]) : 0.f);
+            aQ[m] = mma(ld8(sdAqk + ar), kq, aQ[m]);
+            aH[m] = mma(ld8(sdAp + ar), kq, aH[m]);
+            // keys of block m against rows of block tb >= m: Qs, Ks (ref B_tb)
+            // times 2^{B_tb - B_m}; blocks tb < m are zero in dAqk^T, dA'^T
+            const float fb = tb == m ? 1.f : (tb > m ? __builtin_amdgcn_exp2f(Bv[tb] - Bv[m]) : 0.f);
+            aB[m] = mma(ld8(sdAqkT + ar), tb == m ? qtt : scale8(qtt, fb), aB[m]);
+            aB[m] = mma(ld8(sdApT + ar), tb == m ? kht : scale8(kht, fb), aB[m]);
         }
     }
 
@@ -552,13 +607,15 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float eg = __builtin_amdgcn_exp2f(G[m][e]), egi = __builtin_amdgcn_exp2f(-G[m][e]);
+            // dQt, dKh relative to B_{m+1}; dKb relative to B_m (keys of block m)
+            const float ea = __builtin_amdgcn_exp2f(G[m][e] - Bv[m + 1]);
+            const float es = __builtin_amdgcn_exp2f(Bv[m] - G[m][e]);
             const float et = __builtin_amdgcn_exp2f(Gc - G[m][e]);
             const float dqt = aQ[m][e], dkh = aH[m][e], dkb = aB[m][e], dkt = aT[m][e];
-            dG[m][e] = qv[m][e] * eg * dqt + kv[m][e] * (eg * dkh - egi * dkb - et * dkt);
+            dG[m][e] = qv[m][e] * ea * dqt + kv[m][e] * (ea * dkh - es * dkb - et * dkt);
             ktp += kv[m][e] * et * dkt;
-            oq[m][e] = eg * dqt;
-            ok_[m][e] = eg * dkh + egi * dkb + et * dkt;
+            oq[m][e] = ea * dqt;
+            ok_[m][e] = ea * dkh + es * dkb + et * dkt;
         }
     }
     ktp += __shfl_xor(ktp, 16);

@@ -39,9 +39,9 @@
  * any other chunk uses the ends of its four 16-token sub-chunks, which only
  * needs every channel's log-decay over each such sub-chunk to stay above -87
  * (chunk totals down to about -350).  Stronger gates are outside the
- * supported range.  The backward pass (kda_chunk_bwd*) recomputes the decay
- * factors from the chunk start and needs every chunk's per-channel log-decay
- * above -80.  The decode step has no limit.
+ * supported range.  The backward pass (kda_chunk_bwd*) references its decay
+ * factors to the same sub-chunk ends and has the same range.  The decode step
+ * has no limit.
  */
 #ifndef KDA_H
 #define KDA_H
