@@ -431,6 +431,15 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     Bv[0] = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) Bv[m + 1] = __shfl(G[m][3], ln + 48);
+    // A wave whose 16 channels all keep their chunk decay within 2^-96 takes
+    // every reference at the chunk start instead (Bv = 0: the factors below
+    // reduce to 2^{G}, 2^{-G} and 1), which skips the per-block rescaling of
+    // the token contractions; the choice is per wave, the formulas the same.
+    const bool fastw = __builtin_amdgcn_ballot_w64(Gc < -96.f) == 0;
+    if (fastw) {
+#pragma unroll
+        for (int j = 0; j < 5; ++j) Bv[j] = 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         *reinterpret_cast<bf16x8*>(sDO + vr * L::P128 + vc + 8 * i) = dov[i];
@@ -564,11 +573,13 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     // state terms (dO S^T, -dV S^T, whose own factor is 2^{G_r}) times
     // 2^{B_{m+1}} (<= 1) here, the in-chunk terms below against keys
     // referenced to B_{m+1}
+    if (!fastw) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const float f = __builtin_amdgcn_exp2f(Bv[m + 1]);
+        for (int m = 0; m < 4; ++m) {
+            const float f = __builtin_amdgcn_exp2f(Bv[m + 1]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { aQ[m][e] *= f; aH[m][e] *= f; }
+            for (int e = 0; e < 4; ++e) { aQ[m][e] *= f; aH[m][e] *= f; }
+        }
     }
     auto scale8 = [](bf16x8 x, float f) {
 #pragma unroll
@@ -587,14 +598,21 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
             const int ar = (16 * m + ln) * L::P64 + ko;
             // rows of block m against keys of block tb <= m: Kend (ref B_{tb+1})
             // times 2^{B_{m+1} - B_{tb+1}}; blocks tb > m are zero in dAqk, dA'
-            const bf16x8 kq = tb == m ? kbt : scale8(kbt, tb < m ? __builtin_amdgcn_exp2f(Bv[m + 1] - Bv[tb + 1]) : 0.f);
+            // (on a fast wave every factor is 1 and nothing is rescaled)
+            bf16x8 kq = kbt;
+            if (!fastw && tb != m) kq = scale8(kbt, tb < m ? __builtin_amdgcn_exp2f(Bv[m + 1] - Bv[tb + 1]) : 0.f);
             aQ[m] = mma(ld8(sdAqk + ar), kq, aQ[m]);
             aH[m] = mma(ld8(sdAp + ar), kq, aH[m]);
             // keys of block m against rows of block tb >= m: Qs, Ks (ref B_tb)
             // times 2^{B_tb - B_m}; blocks tb < m are zero in dAqk^T, dA'^T
-            const float fb = tb == m ? 1.f : (tb > m ? __builtin_amdgcn_exp2f(Bv[tb] - Bv[m]) : 0.f);
-            aB[m] = mma(ld8(sdAqkT + ar), tb == m ? qtt : scale8(qtt, fb), aB[m]);
-            aB[m] = mma(ld8(sdApT + ar), tb == m ? kht : scale8(kht, fb), aB[m]);
+            bf16x8 qq = qtt, kk2 = kht;
+            if (!fastw && tb != m) {
+                const float fb = tb > m ? __builtin_amdgcn_exp2f(Bv[tb] - Bv[m]) : 0.f;
+                qq = scale8(qtt, fb);
+                kk2 = scale8(kht, fb);
+            }
+            aB[m] = mma(ld8(sdAqkT + ar), qq, aB[m]);
+            aB[m] = mma(ld8(sdApT + ar), kk2, aB[m]);
         }
     }
 

@@ -65,6 +65,27 @@ def test_layer_small_shapes(B, T, d_model, H, rank):
     check(inp, y, iv, H)
 
 
+def test_layer_strong_decay():
+    """W_up scaled by 50 (gate pre-activation std about 2.5 on this shape):
+    log alpha = -softplus(.) then sums to below -100 over a 64-token
+    chunk in the strongest channels (sub-chunk path of the KDA step).  y and
+    every intermediate against the oracle."""
+    B, T, dm, H, rank = 1, 300, 256, 2, 64
+    inp = inputs.layer_inputs(B=B, T=T, d_model=dm, H=H, seed=13, gate_rank=rank)
+    inp["W_up"] = (inp["W_up"].float() * 50.0).to(inp["W_up"].dtype)
+    dev = torch.device("cuda", 0)
+    W = {n: inp[n].to(dev) for n in kda.LAYER_WEIGHTS}
+    print("layer strong decay", flush=True)
+    y, iv = kda.layer_fwd(inp["x"].to(dev), W, H, intermediates=True)
+    torch.cuda.synchronize()
+    g = iv["g"].double().cpu().numpy()[0]                          # [T, H, 128]
+    n = T // 64
+    sums = g[:n * 64].reshape(n, 64, H, 128).sum(axis=1)
+    print(f"  most negative chunk log-decay {sums.min():.1f}", flush=True)
+    assert sums.min() < -100
+    check(inp, y.cpu(), {k: v.cpu() for k, v in iv.items()}, H)
+
+
 def test_layer_full_width_short_sequence():
     inp, y, iv = run_layer(1, 1000, 2048, 16, 128, seed=12)
     check(inp, y, iv, 16)
