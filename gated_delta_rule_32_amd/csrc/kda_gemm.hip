@@ -216,13 +216,23 @@ gemm_nt_kernel(const void* A_, const bf16_t* B, OutT* C, int M, int N, int K,
 // step's first-half operands.  Each step's loads have a whole step to land,
 // and no wave waits on LDS right after the barrier.  K must be a multiple of
 // 64 (the layer's feature sizes are).
+//
+// B may be up to four weight matrices stacked along N (rows n of the product
+// come from matrix n / n_split, n_split a multiple of 256, so each tile reads
+// one of them): the layer's q, k, v and gate projections then run as one
+// product over x, whose 16 rounds of tiles amortise the pipeline's fill and
+// drain better than four products of 4 rounds.
 constexpr int LBM = 256, LBN = 256, LBK = 64;
 constexpr int LGT = 512;
 constexpr int LSTAGE = (LBM + LBN) * LBK * 2;      // 64 KiB
 
+struct StackedB {
+    const bf16_t* p[4];
+};
+
 __global__ void __launch_bounds__(LGT)
-gemm_nt_large_kernel(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, int K,
-                     int lda, int ldb, int ldc)
+gemm_nt_large_kernel(const bf16_t* A, StackedB Bs, bf16_t* C, int M, int N, int K,
+                     int lda, int ldb, int ldc, int n_split)
 {
     __shared__ __attribute__((aligned(1024))) char smem[2 * LSTAGE];
     const int t = threadIdx.x, lane = t & 63;
@@ -243,6 +253,10 @@ gemm_nt_large_kernel(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, 
         tn = j % tiles_n;
     }
     const int m0 = tm * LBM, n0 = tn * LBN;
+    // this tile's weight matrix and its rows n0 - seg n_split ..
+    const int seg = n0 / n_split;
+    const bf16_t* B = Bs.p[seg];
+    const int nb0 = n0 - seg * n_split, nseg = min(n_split, N - seg * n_split);
 
     // loads of one K-step: 32 segments of A, 32 of B, 8 per wave
     const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;    // row within segment, chunk fetched
@@ -254,7 +268,7 @@ gemm_nt_large_kernel(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, 
             const bool isA = seg < 32;
             const int row = 8 * (seg & 31) + lrow;
             const bf16_t* src = isA ? A + (size_t)min(m0 + row, M - 1) * lda
-                                    : B + (size_t)min(n0 + row, N - 1) * ldb;
+                                    : B + (size_t)min(nb0 + row, nseg - 1) * ldb;
             __builtin_amdgcn_global_load_lds(src + k0 + 8 * lchunk,
                                              (__attribute__((address_space(3))) void*)(st + seg * 1024), 16, 0, 0);
         }
@@ -334,6 +348,24 @@ gemm_nt_large_kernel(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, 
 
 }  // namespace
 
+bool gemm_stacked_ok(int M, int n_split, int nmat)
+{
+    return M >= LBM && n_split > 0 && n_split % LBN == 0 && nmat >= 1 && nmat <= 4;
+}
+
+hipError_t launch_gemm_nt_stacked(const bf16_t* A, const bf16_t* const* B, int nmat, bf16_t* C, int M,
+                                  int n_split, int K, int lda, int ldb, int ldc, hipStream_t stream)
+{
+    if (!gemm_stacked_ok(M, n_split, nmat)) return hipErrorInvalidValue;
+    StackedB bs;
+    for (int i = 0; i < 4; ++i) bs.p[i] = B[i < nmat ? i : nmat - 1];
+    const int N = nmat * n_split;
+    const unsigned tiles = (unsigned)(((M + LBM - 1) / LBM) * (N / LBN));
+    hipLaunchKernelGGL(gemm_nt_large_kernel, dim3(tiles), dim3(LGT), 0, stream, A, bs, C, M, N, K, lda, ldb,
+                       ldc, n_split);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, bool c_f32,
                           int epilogue, int M, int N, int K, int lda, int ldb, int ldc,
                           hipStream_t stream, const bf16_t* B2, int n_split)
@@ -341,8 +373,9 @@ hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, b
     if (M <= 0 || N <= 0) return hipSuccess;
     if (!B2 && !a_f32 && !c_f32 && epilogue == 0 && M >= LBM && N >= LBN) {
         const unsigned tiles = (unsigned)(((M + LBM - 1) / LBM) * ((N + LBN - 1) / LBN));
+        const StackedB bs = {{B, B, B, B}};
         hipLaunchKernelGGL(gemm_nt_large_kernel, dim3(tiles), dim3(LGT), 0, stream,
-                           (const bf16_t*)A, B, (bf16_t*)C, M, N, K, lda, ldb, ldc);
+                           (const bf16_t*)A, bs, (bf16_t*)C, M, N, K, lda, ldb, ldc, N);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN))), block(GT);

@@ -134,6 +134,13 @@ hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, b
                           int epilogue, int M, int N, int K, int lda, int ldb, int ldc,
                           hipStream_t stream, const bf16_t* B2 = nullptr, int n_split = 0);
 
+// The same product (bf16 A and C) with B made of `nmat` (1 to 4) weight
+// matrices of n_split rows each, stacked along N: C[:, i n_split ..] =
+// A B[i]^T.  Requires gemm_stacked_ok (M >= 256, n_split % 256 == 0).
+bool gemm_stacked_ok(int M, int n_split, int nmat);
+hipError_t launch_gemm_nt_stacked(const bf16_t* A, const bf16_t* const* B, int nmat, bf16_t* C, int M,
+                                  int n_split, int K, int lda, int ldb, int ldc, hipStream_t stream);
+
 // Weights of one KDA token-mixing layer, all bf16, [out_features, in_features]
 // (conv taps [H*128, 4]).
 struct LayerWeights {

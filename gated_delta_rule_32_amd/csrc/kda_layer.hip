@@ -220,11 +220,17 @@ hipError_t launch_layer_fwd(const LayerWeights& W, const bf16_t* x, bf16_t* y, i
     hipError_t e;
     // 1. projections: q, k, v and gate pre-activations in bf16; the low-rank
     //    gate input W_down x and the beta logits in fp32
+    //    (as one product over the four stacked weights when the tiles allow)
     const bf16_t* Win[4] = {W.W_q, W.W_k, W.W_v, W.W_g};
-    for (int i = 0; i < 4; ++i)
-        if ((e = launch_gemm_nt(x, false, Win[i], pre + (size_t)i * HDm, false, 0, R, HDm, d_model,
-                                d_model, d_model, NY, stream)))
+    if (gemm_stacked_ok(R, HDm, 4)) {
+        if ((e = launch_gemm_nt_stacked(x, Win, 4, pre, R, HDm, d_model, d_model, d_model, NY, stream)))
             return e;
+    } else {
+        for (int i = 0; i < 4; ++i)
+            if ((e = launch_gemm_nt(x, false, Win[i], pre + (size_t)i * HDm, false, 0, R, HDm, d_model,
+                                    d_model, d_model, NY, stream)))
+                return e;
+    }
     //    ([W_down; W_beta] stacked: one pass over x writes both)
     if ((e = launch_gemm_nt(x, false, W.W_down, low, true, 0, R, rank + H, d_model, d_model, d_model,
                             ldz, stream, W.W_beta, rank)))
