@@ -186,11 +186,23 @@ __device__ __forceinline__ bf16x8 a_pair(const bf16_t* row, int p, int lg, bool 
     return cat8(a, b);
 }
 
+// The same operand from lower-triangular 16 x 16 tiles (the KDA block's Tm
+// and Aqk): tiles (R, 2p) and, with `hi`, (R, 2p + 1), row ln of each.
+__device__ __forceinline__ bf16x8 a_pair_tiles(const bf16_t* tiles, int R, int p, int ln, int lg, bool hi) {
+    const bf16_t* t0 = tiles + (R * (R + 1) / 2 + 2 * p) * 256 + ln * 16 + 4 * lg;
+    const bf16x4 a = ld4(t0);
+    const bf16x4 b = hi ? ld4(t0 + 256) : bf16x4{};
+    return cat8(a, b);
+}
+
 // ---- forward state scan: per-chunk operand block -------------------------------
 // Workspace block of one chunk, written by a prep kernel and read by
 // chunk_scan_kernel (bf16 only).  It is the image of the scan's LDS stage:
 // rows keep their 16-byte padding and Kt^T its swizzle (kbt_swz), so the scan
-// copies it linearly in 1 KiB pieces.  Byte offsets:
+// copies it linearly in 1 KiB pieces.  The KDA block (WSK_*) keeps only the
+// ten lower 16 x 16 tiles of the triangular Tm Diag(beta) and Aqk, 64,512
+// bytes in all; the general DPLR block (WS_*) keeps them as padded rows
+// (72,704 bytes), since its Tm field also carries the H0 slice.  Byte offsets:
 constexpr int WS_P128 = DK + 8, WS_P64 = C + 8;    // padded row pitches (elements)
 constexpr int WS_QT = 0;                            // Qt   [64][136] bf16, token-major
 constexpr int WS_KH = WS_QT + C * WS_P128 * 2;      // Kh   [64][136] bf16, token-major
@@ -201,6 +213,18 @@ constexpr int WS_QK = WS_TM + C * WS_P64 * 2;       // Aqk  [64][72] bf16
 constexpr int WS_GAM = WS_QK + C * WS_P64 * 2;      // e^{G_64} [128] fp32
 constexpr int WS_USED = WS_GAM + DK * 4;            // 72,192 bytes written
 constexpr int WS_CHUNK = (WS_USED + 1023) / 1024 * 1024;   // 72,704: whole KiB per block
+// KDA block: Qt, Kh, Kt^T as above, then the lower tiles (R, c), c <= R, of
+// Tm Diag(beta) and of Aqk, tile index R (R + 1) / 2 + c, each 16 rows of 32
+// bytes (so that an MFMA A-fragment read of 16 rows x 8 bytes per lane group
+// covers 512 contiguous bytes), then e^{G_64}.
+constexpr int WS_TILE = 16 * 16 * 2, WS_NTILE = 10;
+constexpr int WSK_TM = WS_TM;                               // Tm Diag(beta) tiles
+constexpr int WSK_QK = WSK_TM + WS_NTILE * WS_TILE;         // Aqk tiles
+constexpr int WSK_GAM = WSK_QK + WS_NTILE * WS_TILE;        // e^{G_64} [128] fp32
+constexpr int WSK_USED = WSK_GAM + DK * 4;                  // 64,000 bytes written
+constexpr int WSK_CHUNK = (WSK_USED + 1023) / 1024 * 1024;  // 64,512
+__device__ __forceinline__ constexpr int lt_tile(int R, int c) { return R * (R + 1) / 2 + c; }
+__device__ __forceinline__ constexpr int lt_tile_row(int ti) { return ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3; }
 
 // Element (channel c, token i) of the swizzled Kb^T: the 8-token blocks of a
 // row are XOR-permuted by bits 3..5 of the channel.

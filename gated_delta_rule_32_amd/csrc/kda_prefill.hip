@@ -752,8 +752,9 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
 
         if constexpr (PREP) {
             // ===== export the key-side operands of this chunk =====
-            // (byte copies of the LDS regions: the layouts already match)
-            char* blk = ws + ((size_t)head * nchunks + n) * WS_CHUNK;
+            // (byte copies of the LDS regions, whose layouts already match,
+            // and the lower tiles of Tm and Aqk)
+            char* blk = ws + ((size_t)head * nchunks + n) * WSK_CHUNK;
             typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
             static_assert(L::P128 == WS_P128 && L::P64 == WS_P64, "workspace rows match the LDS rows");
             static_assert(L::OFF_KH == L::OFF_QT + C * WS_P128 * 2, "Qt and Kh are adjacent");
@@ -765,10 +766,18 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
             // nor Aqk from this block, only Kh, Kt^T, Tm and gamma)
             if constexpr (BWD) copy(WS_KH, L::OFF_KH, WS_KBT - WS_KH);
             else copy(WS_QT, L::OFF_QT, WS_KBT - WS_QT);  // Qt and Kh
-            copy(WS_KBT, L::OFF_KBT, WS_TM - WS_KBT);
-            copy(WS_TM, L::OFF_RT, WS_QK - WS_TM);
-            if constexpr (!BWD) copy(WS_QK, L::OFF_QK, WS_GAM - WS_QK);
-            copy(WS_GAM, L::OFF_GAM, WS_USED - WS_GAM);
+            copy(WS_KBT, L::OFF_KBT, WSK_TM - WS_KBT);
+            copy(WSK_GAM, L::OFF_GAM, WSK_USED - WSK_GAM);
+            // the lower 16 x 16 tiles of Tm Diag(beta) and (not for the
+            // backward pass) Aqk: 32 units of 16 bytes per tile
+            for (int u = t; u < (BWD ? 1 : 2) * WS_NTILE * 32; u += NT) {
+                const int mat = u / (WS_NTILE * 32), v2 = u % (WS_NTILE * 32);
+                const int ti = v2 >> 5, r = (v2 >> 1) & 15, hh = v2 & 1;
+                const int R = lt_tile_row(ti), cc = ti - R * (R + 1) / 2;
+                const E* src = (mat ? sQK : RT) + (16 * R + r) * L::P64 + 16 * cc + 8 * hh;
+                *reinterpret_cast<i32x4*>(blk + (mat ? WSK_QK : WSK_TM) + ti * WS_TILE + r * 32 + hh * 16) =
+                    *reinterpret_cast<const i32x4*>(src);
+            }
             if constexpr (BWD) {
                 // operands of the backward state scan: transposes read from LDS
                 // eight strided elements at a time, written 16 bytes at a time
@@ -949,7 +958,6 @@ chunk_fwd_kernel(const E* q, const E* k, const E* v, const float* g, const E* be
 // lane; the consumers feed it two 16-row blocks at once (four values from
 // each), reading the A-operand with the same split, so each product is a
 // plain sum over k.
-constexpr int SC_KIB = WS_CHUNK / 1024;                   // 1 KiB pieces per block
 constexpr int SEG_NONE = 0, SEG_SUMMARY = 1, SEG_OUTPUT = 2;   // chunk_scan_kernel segment modes
 
 template <int NCW, bool SAVE = false> struct ScanCfg {   // NCW consumer waves
@@ -1031,7 +1039,10 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
     const size_t tokstride = (size_t)H * DK;
     const size_t hbase = ((size_t)b * T * H + h) * DK;
     const size_t sbase = (size_t)head * DK * DK;
-    const char* wsh = ws + (size_t)head * nchunks * WS_CHUNK;
+    // block layout: the KDA block with tiled Tm and Aqk, or the DPLR block
+    constexpr int B_TM = DPLR ? WS_TM : WSK_TM, B_QK = DPLR ? WS_QK : WSK_QK, B_GAM = DPLR ? WS_GAM : WSK_GAM;
+    constexpr int B_CHUNK = DPLR ? WS_CHUNK : WSK_CHUNK, B_KIB = B_CHUNK / 1024;
+    const char* wsh = ws + (size_t)head * nchunks * B_CHUNK;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
     // ---- loader side: lane pt moves V / output unit (token ut, columns 8 ug ..)
@@ -1039,19 +1050,19 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
     const bool ulane = t < 256 && ut < C;     // lanes of the first four loader waves
     bf16x8 vrow[SC::VPL], o0row = bf16x8{};   // unit i of a lane: pt + 256 i
     // DPLR: the H0 slice [128][DV] (unpadded) replaces the Tm pages
-    constexpr int TM_P0 = WS_TM / 1024, TM_P1 = WS_QK / 1024;
+    constexpr int TM_P0 = B_TM / 1024, TM_P1 = B_QK / 1024;
     constexpr int HPR = SC::DV / 8;                       // 16-byte pieces per H0 row
     constexpr int HRPP = 64 / HPR;                        // H0 rows per 1 KiB page
     constexpr int HPAGES = DK / HRPP;
-    static_assert(!DPLR || (WS_TM % 1024 == 0 && WS_QK % 1024 == 0 && HPAGES <= TM_P1 - TM_P0),
+    static_assert(!DPLR || (B_TM % 1024 == 0 && B_QK % 1024 == 0 && HPAGES <= TM_P1 - TM_P0),
                   "H0 slice fits the Tm slot");
-    constexpr int QT_P1 = WS_KH / 1024, QK_P0 = WS_QK / 1024, QK_P1 = WS_GAM / 1024;
-    static_assert(WS_QT == 0 && WS_KH % 1024 == 0 && WS_QK % 1024 == 0 && WS_GAM % 1024 == 0,
+    constexpr int QT_P1 = WS_KH / 1024, QK_P0 = B_QK / 1024, QK_P1 = B_GAM / 1024;
+    static_assert(WS_QT == 0 && WS_KH % 1024 == 0 && B_QK % 1024 == 0 && B_GAM % 1024 == 0,
                   "Qt and Aqk occupy whole pages");
     auto load_block = [&](int n) {            // workspace block n -> stage n % 2
-        const char* src = wsh + (size_t)n * WS_CHUNK;
+        const char* src = wsh + (size_t)n * B_CHUNK;
         char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
-        for (int u = wave; u < SC_KIB; u += SC::NLW) {
+        for (int u = wave; u < B_KIB; u += SC::NLW) {
             // without output, the Qt and Aqk pages are not read: not copied
             if (NOOUT && (u < QT_P1 || (u >= QK_P0 && u < QK_P1))) continue;
             const char* from = src + (size_t)u * 1024 + lane * 16;
@@ -1159,9 +1170,14 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             const bf16_t* sQt = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_QT);
             const bf16_t* sKh = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_KH);
             const bf16_t* sKbT = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_KBT);
-            const bf16_t* sTm = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_TM);
-            const bf16_t* sQK = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_QK);
-            const float* sGam = reinterpret_cast<const float*>(st + SC::OFF_BLK + WS_GAM);
+            const bf16_t* sTm = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + B_TM);
+            const bf16_t* sQK = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + B_QK);
+            const float* sGam = reinterpret_cast<const float*>(st + SC::OFF_BLK + B_GAM);
+            // A-operand pair p of row block Rb of Tm or Aqk (lower part only)
+            auto tri_pair = [&](const bf16_t* m, int Rb, int p) {
+                if constexpr (DPLR) return a_pair(m + (16 * Rb + ln) * WS_P64, p, lg, 2 * p + 1 <= Rb);
+                else return a_pair_tiles(m, Rb, p, ln, lg, 2 * p + 1 <= Rb);
+            };
             const bf16_t* sVT = reinterpret_cast<const bf16_t*>(st + SC::OFF_VT);
             bf16_t* sO = reinterpret_cast<bf16_t*>(smem + SC::OFF_O + (n & 1) * C * SC::DV * 2);
             const size_t cidx = (size_t)head * nchunks + n;
@@ -1222,13 +1238,11 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
                     continue;
                 }
                 f32x4 a = z4;
-                const bf16_t* row = sTm + (16 * Rb + ln) * WS_P64;
 #pragma unroll
                 for (int p = 0; p < 2; ++p)
                     if (2 * p <= Rb)
                         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            a_pair(row, p, lg, 2 * p + 1 <= Rb),
-                            cat8(to_bf16x4(zt[2 * p]), to_bf16x4(zt[2 * p + 1])), a, 0, 0, 0);
+                            tri_pair(sTm, Rb, p), cat8(to_bf16x4(zt[2 * p]), to_bf16x4(zt[2 * p + 1])), a, 0, 0, 0);
                 vn[Rb] = a;
             }
             if constexpr (SAVE) {
@@ -1247,13 +1261,11 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
 #pragma unroll
             for (int Rb = 0; Rb < 4; ++Rb) {
                 f32x4 a = qs[Rb];
-                const bf16_t* row = sQK + (16 * Rb + ln) * WS_P64;
 #pragma unroll
                 for (int p = 0; p < 2; ++p)
                     if (2 * p <= Rb)
                         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            a_pair(row, p, lg, 2 * p + 1 <= Rb),
-                            cat8(to_bf16x4(vn[2 * p]), to_bf16x4(vn[2 * p + 1])), a, 0, 0, 0);
+                            tri_pair(sQK, Rb, p), cat8(to_bf16x4(vn[2 * p]), to_bf16x4(vn[2 * p + 1])), a, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sO[(16 * Rb + 4 * lg + e) * SC::DV + jc] = (bf16_t)a[e];
             }
@@ -1519,7 +1531,7 @@ void launch_gate(const void* q, const void* k, const void* v, const float* g, co
 
 size_t chunk_ws_bytes(long long B, long long T, long long H)
 {
-    return (size_t)B * (size_t)H * (size_t)((T + C - 1) / C) * (size_t)WS_CHUNK;
+    return (size_t)B * (size_t)H * (size_t)((T + C - 1) / C) * (size_t)WSK_CHUNK;
 }
 
 int chunk_seg_count(long long B, long long T, long long H)
