@@ -199,10 +199,11 @@ __device__ __forceinline__ bf16x8 a_pair_tiles(const bf16_t* tiles, int R, int p
 // Workspace block of one chunk, written by a prep kernel and read by
 // chunk_scan_kernel (bf16 only).  It is the image of the scan's LDS stage:
 // rows keep their 16-byte padding and Kt^T its swizzle (kbt_swz), so the scan
-// copies it linearly in 1 KiB pieces.  The KDA block (WSK_*) keeps only the
-// ten lower 16 x 16 tiles of the triangular Tm Diag(beta) and Aqk, 64,512
-// bytes in all; the general DPLR block (WS_*) keeps them as padded rows
-// (72,704 bytes), since its Tm field also carries the H0 slice.  Byte offsets:
+// copies it linearly in 1 KiB pieces.  The general DPLR block (WS_*, 72,704
+// bytes) keeps padded rows as below.  The KDA block (WSK_*, 60,416 bytes)
+// drops the padding: its rows are XOR-swizzled in 16-byte units instead, and
+// it keeps only the ten lower 16 x 16 tiles of the triangular Tm Diag(beta)
+// and Aqk.  Byte offsets of the DPLR block:
 constexpr int WS_P128 = DK + 8, WS_P64 = C + 8;    // padded row pitches (elements)
 constexpr int WS_QT = 0;                            // Qt   [64][136] bf16, token-major
 constexpr int WS_KH = WS_QT + C * WS_P128 * 2;      // Kh   [64][136] bf16, token-major
@@ -213,16 +214,32 @@ constexpr int WS_QK = WS_TM + C * WS_P64 * 2;       // Aqk  [64][72] bf16
 constexpr int WS_GAM = WS_QK + C * WS_P64 * 2;      // e^{G_64} [128] fp32
 constexpr int WS_USED = WS_GAM + DK * 4;            // 72,192 bytes written
 constexpr int WS_CHUNK = (WS_USED + 1023) / 1024 * 1024;   // 72,704: whole KiB per block
-// KDA block: Qt, Kh, Kt^T as above, then the lower tiles (R, c), c <= R, of
-// Tm Diag(beta) and of Aqk, tile index R (R + 1) / 2 + c, each 16 rows of 32
-// bytes (so that an MFMA A-fragment read of 16 rows x 8 bytes per lane group
-// covers 512 contiguous bytes), then e^{G_64}.
+// KDA block:
+//   Qt, Kh  [64][128] bf16, token-major rows of 256 B; the 16-byte unit u of
+//           row r sits at unit u ^ (r % 16), so that an MFMA A-fragment read
+//           (16 rows, 8 bytes per lane) touches every bank once per 256 B;
+//   Kt^T    [128][64] bf16, channel-major rows of 128 B; unit u of row c at
+//           u ^ ((c / 2) % 8) (rows two apart share banks);
+//   the lower tiles (R, c), c <= R, of Tm Diag(beta) and of Aqk, tile index
+//           R (R + 1) / 2 + c, each 16 rows of 32 bytes (an A-fragment read of
+//           16 rows x 8 bytes per lane group covers 512 contiguous bytes);
+//   e^{G_64} [128] fp32.
 constexpr int WS_TILE = 16 * 16 * 2, WS_NTILE = 10;
-constexpr int WSK_TM = WS_TM;                               // Tm Diag(beta) tiles
+constexpr int WSK_QT = 0;
+constexpr int WSK_KH = WSK_QT + C * DK * 2;                 // 16 KiB
+constexpr int WSK_KBT = WSK_KH + C * DK * 2;
+constexpr int WSK_TM = WSK_KBT + DK * C * 2;                // Tm Diag(beta) tiles
 constexpr int WSK_QK = WSK_TM + WS_NTILE * WS_TILE;         // Aqk tiles
 constexpr int WSK_GAM = WSK_QK + WS_NTILE * WS_TILE;        // e^{G_64} [128] fp32
-constexpr int WSK_USED = WSK_GAM + DK * 4;                  // 64,000 bytes written
-constexpr int WSK_CHUNK = (WSK_USED + 1023) / 1024 * 1024;  // 64,512
+constexpr int WSK_USED = WSK_GAM + DK * 4;                  // 59,904 bytes written
+constexpr int WSK_CHUNK = (WSK_USED + 1023) / 1024 * 1024;  // 60,416
+// element offsets of the swizzled rows
+__device__ __forceinline__ constexpr int wsk_tok(int r, int e) {      // Qt / Kh (row r, channel e)
+    return r * DK + ((((e >> 3) ^ (r & 15))) << 3) + (e & 7);
+}
+__device__ __forceinline__ constexpr int wsk_kbt(int c, int i) {      // Kt^T (channel c, token i)
+    return c * C + ((((i >> 3) ^ ((c >> 1) & 7))) << 3) + (i & 7);
+}
 __device__ __forceinline__ constexpr int lt_tile(int R, int c) { return R * (R + 1) / 2 + c; }
 __device__ __forceinline__ constexpr int lt_tile_row(int ti) { return ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3; }
 

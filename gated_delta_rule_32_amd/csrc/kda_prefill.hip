@@ -752,22 +752,28 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
 
         if constexpr (PREP) {
             // ===== export the key-side operands of this chunk =====
-            // (byte copies of the LDS regions, whose layouts already match,
-            // and the lower tiles of Tm and Aqk)
+            // (16-byte units from the padded LDS rows into the KDA block's
+            // swizzled rows and lower tiles; for the backward pass, whose
+            // save-mode scan reads neither Qt nor Aqk, only Kh, Kt^T, Tm and
+            // gamma)
             char* blk = ws + ((size_t)head * nchunks + n) * WSK_CHUNK;
             typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-            static_assert(L::P128 == WS_P128 && L::P64 == WS_P64, "workspace rows match the LDS rows");
-            static_assert(L::OFF_KH == L::OFF_QT + C * WS_P128 * 2, "Qt and Kh are adjacent");
-            auto copy = [&](int dst, int src, int bytes) {
-                for (int u = t; u < bytes / 16; u += NT)
-                    reinterpret_cast<i32x4*>(blk + dst)[u] = reinterpret_cast<const i32x4*>(smem + src)[u];
-            };
-            // (for the backward pass, whose save-mode scan reads neither Qt
-            // nor Aqk from this block, only Kh, Kt^T, Tm and gamma)
-            if constexpr (BWD) copy(WS_KH, L::OFF_KH, WS_KBT - WS_KH);
-            else copy(WS_QT, L::OFF_QT, WS_KBT - WS_QT);  // Qt and Kh
-            copy(WS_KBT, L::OFF_KBT, WSK_TM - WS_KBT);
-            copy(WSK_GAM, L::OFF_GAM, WSK_USED - WSK_GAM);
+            static_assert(L::P128 == WS_P128 && L::P64 == WS_P64, "LDS rows are padded as the DPLR block's");
+            // Qt, Kh: 64 rows of 16 units each
+            for (int u = BWD ? C * 16 + t : t; u < 2 * C * 16; u += NT) {
+                const int mat = u / (C * 16), r = (u >> 4) & (C - 1), uu = u & 15;
+                const E* src = (mat ? sKh : sQt) + r * L::P128 + 8 * uu;
+                *reinterpret_cast<i32x4*>(blk + (mat ? WSK_KH : WSK_QT) + 2 * wsk_tok(r, 8 * uu)) =
+                    *reinterpret_cast<const i32x4*>(src);
+            }
+            // Kt^T: 128 rows of 8 units each
+            for (int u = t; u < DK * 8; u += NT) {
+                const int c = u >> 3, uu = u & 7;
+                *reinterpret_cast<i32x4*>(blk + WSK_KBT + 2 * wsk_kbt(c, 8 * uu)) =
+                    *reinterpret_cast<const i32x4*>(sKbT + L::kbt(c, 8 * uu));
+            }
+            if (t < DK / 4)
+                reinterpret_cast<f32x4*>(blk + WSK_GAM)[t] = reinterpret_cast<const f32x4*>(s_gam)[t];
             // the lower 16 x 16 tiles of Tm Diag(beta) and (not for the
             // backward pass) Aqk: 32 units of 16 bytes per tile
             for (int u = t; u < (BWD ? 1 : 2) * WS_NTILE * 32; u += NT) {
@@ -1039,7 +1045,9 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
     const size_t tokstride = (size_t)H * DK;
     const size_t hbase = ((size_t)b * T * H + h) * DK;
     const size_t sbase = (size_t)head * DK * DK;
-    // block layout: the KDA block with tiled Tm and Aqk, or the DPLR block
+    // block layout: the KDA block (swizzled rows, tiled Tm and Aqk) or the
+    // DPLR block (padded rows)
+    constexpr int B_QT = DPLR ? WS_QT : WSK_QT, B_KH = DPLR ? WS_KH : WSK_KH, B_KBT = DPLR ? WS_KBT : WSK_KBT;
     constexpr int B_TM = DPLR ? WS_TM : WSK_TM, B_QK = DPLR ? WS_QK : WSK_QK, B_GAM = DPLR ? WS_GAM : WSK_GAM;
     constexpr int B_CHUNK = DPLR ? WS_CHUNK : WSK_CHUNK, B_KIB = B_CHUNK / 1024;
     const char* wsh = ws + (size_t)head * nchunks * B_CHUNK;
@@ -1056,8 +1064,8 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
     constexpr int HPAGES = DK / HRPP;
     static_assert(!DPLR || (B_TM % 1024 == 0 && B_QK % 1024 == 0 && HPAGES <= TM_P1 - TM_P0),
                   "H0 slice fits the Tm slot");
-    constexpr int QT_P1 = WS_KH / 1024, QK_P0 = B_QK / 1024, QK_P1 = B_GAM / 1024;
-    static_assert(WS_QT == 0 && WS_KH % 1024 == 0 && B_QK % 1024 == 0 && B_GAM % 1024 == 0,
+    constexpr int QT_P1 = B_KH / 1024, QK_P0 = B_QK / 1024, QK_P1 = B_GAM / 1024;
+    static_assert(B_QT == 0 && B_KH % 1024 == 0 && B_QK % 1024 == 0 && B_GAM % 1024 == 0,
                   "Qt and Aqk occupy whole pages");
     auto load_block = [&](int n) {            // workspace block n -> stage n % 2
         const char* src = wsh + (size_t)n * B_CHUNK;
@@ -1167,9 +1175,9 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             if (n + 1 < c1) write_vt(n + 1);
         } else {
             const char* st = smem + (n & 1) * SC::STAGE;
-            const bf16_t* sQt = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_QT);
-            const bf16_t* sKh = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_KH);
-            const bf16_t* sKbT = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + WS_KBT);
+            const bf16_t* sQt = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + B_QT);
+            const bf16_t* sKh = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + B_KH);
+            const bf16_t* sKbT = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + B_KBT);
             const bf16_t* sTm = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + B_TM);
             const bf16_t* sQK = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + B_QK);
             const float* sGam = reinterpret_cast<const float*>(st + SC::OFF_BLK + B_GAM);
@@ -1196,13 +1204,21 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             for (int p = 0; p < 4; ++p) sb[p] = cat8(to_bf16x4(acc_s[2 * p]), to_bf16x4(acc_s[2 * p + 1]));
             constexpr int NF = NOOUT ? 4 : 8;         // Kh (and Qt) fragments per block
             bf16x8 fa[2][NF];
+            // A-operand pair p of rows 16 Rb + ln of Kh or Qt: padded rows
+            // (DPLR), or swizzled rows (KDA: row 16 Rb + ln has swizzle ln)
+            auto tok_pair = [&](const bf16_t* m, int Rb, int p) {
+                if constexpr (DPLR) return a_pair(m + (16 * Rb + ln) * WS_P128, p, lg, true);
+                else {
+                    const bf16_t* row = m + (16 * Rb + ln) * DK + 4 * (lg & 1);
+                    return cat8(ld4(row + (((4 * p + (lg >> 1)) ^ ln) << 3)),
+                                ld4(row + (((4 * p + 2 + (lg >> 1)) ^ ln) << 3)));
+                }
+            };
             auto frags = [&](int Rb, bf16x8 (&f)[NF]) {
-                const bf16_t* kr = sKh + (16 * Rb + ln) * WS_P128;
-                const bf16_t* qr = sQt + (16 * Rb + ln) * WS_P128;
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    f[p] = a_pair(kr, p, lg, true);
-                    if constexpr (!NOOUT) f[4 + p] = a_pair(qr, p, lg, true);
+                    f[p] = tok_pair(sKh, Rb, p);
+                    if constexpr (!NOOUT) f[4 + p] = tok_pair(sQt, Rb, p);
                 }
             };
             f32x4 pk[4], qs[4];
@@ -1278,9 +1294,16 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             bf16x8 vb[2];
 #pragma unroll
             for (int p = 0; p < 2; ++p) vb[p] = cat8(to_bf16x4(vn[2 * p]), to_bf16x4(vn[2 * p + 1]));
-            const bf16_t* kl = sKbT + ln * WS_P64 + ((((lg >> 1) ^ (ln >> 3)) & 1) << 3) + 4 * (lg & 1);
+            // DPLR block: rows of 72 with the 8-token blocks XOR-permuted by
+            // bits 3..5 of the channel; KDA block: rows of 64, units permuted
+            // by bits 1..3 of the channel (= bits 1..3 of ln)
+            const bf16_t* kl = DPLR ? sKbT + ln * WS_P64 + ((((lg >> 1) ^ (ln >> 3)) & 1) << 3) + 4 * (lg & 1)
+                                    : sKbT + ln * C + 4 * (lg & 1);
             auto kbt_at = [&](int cb, int p, int hh) {
-                return kl + 16 * cb * WS_P64 + ((p ^ ((cb >> 1) & 1)) << 5) + ((hh ^ (cb & 1)) << 4);
+                if constexpr (DPLR)
+                    return kl + 16 * cb * WS_P64 + ((p ^ ((cb >> 1) & 1)) << 5) + ((hh ^ (cb & 1)) << 4);
+                else
+                    return kl + 16 * cb * C + (((4 * p + 2 * hh + (lg >> 1)) ^ ((ln >> 1) & 7)) << 3);
             };
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {

@@ -245,7 +245,7 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
  *   workspace  device scratch of at least kda_chunk_bwd_workspace_size(...)
  *              bytes, 256-byte aligned, owned by the caller; contents on entry
  *              and exit unspecified.  It holds the recomputed forward pass:
- *              per (batch, head, 64-token chunk) 252,928 bytes -- the key-side
+ *              per (batch, head, 64-token chunk) 248,832 bytes -- the key-side
  *              operand blocks of both scans and, in bf16, the state entering
  *              the chunk, its gradient on leaving it, V - Kh S, Vn and
  *              Tm^T dVn.
@@ -281,7 +281,7 @@ int kda_chunk_bwd_gated(const void* q, const void* k, const void* v,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes kda_chunk_bwd needs: B * H * ceil(T / 64) * 252928 for
+ * Workspace bytes kda_chunk_bwd needs: B * H * ceil(T / 64) * 248832 for
  * dtype == KDA_BF16 and d_k = d_v = 128; 0 for invalid or unsupported
  * arguments.
  */

@@ -74,11 +74,11 @@ def step(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S=P + 
     (dict(ST=P + 2**26 + 64), INVALID),         # S_T overlaps g
     (dict(S0=P + 2**30, ST=P + 2**30 + 16), INVALID),  # partial S0/S_T overlap
     (dict(B=2**30, H=2**30), UNSUP),            # size overflow
-    (dict(ws=P + 2**31 + 16, wsb=64512), ALIGN),           # workspace needs 256-byte alignment
-    (dict(ws=P + 2**24, wsb=64512), INVALID),               # workspace overlaps k
-    (dict(ws=P + 2**31, wsb=64511), WSERR),                 # bf16 workspace below one block
+    (dict(ws=P + 2**31 + 16, wsb=60416), ALIGN),           # workspace needs 256-byte alignment
+    (dict(ws=P + 2**24, wsb=60416), INVALID),               # workspace overlaps k
+    (dict(ws=P + 2**31, wsb=60415), WSERR),                 # bf16 workspace below one block
     (dict(ws=P + 2**31, wsb=0), WSERR),                     # a non-NULL workspace of zero bytes
-    (dict(ws=P + 2**31, wsb=64512, T=65), WSERR),           # two chunks need two blocks
+    (dict(ws=P + 2**31, wsb=60416, T=65), WSERR),           # two chunks need two blocks
 ])
 def test_chunk_fwd_rejects(lib, kw, code):
     assert chunk(lib, **kw) == code
@@ -107,10 +107,10 @@ def test_recurrent_step_rejects(lib, kw, code):
 
 
 def test_block_and_scan_workspace_queries(lib):
-    assert lib.kda_chunk_fwd_block_bytes() == 64512
+    assert lib.kda_chunk_fwd_block_bytes() == 60416
     f = lib.kda_chunk_fwd_scan_workspace_size
-    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 64512
-    assert f(2, 65, 3, 128, 128, BF16) == 6 * 2 * 64512
+    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 60416
+    assert f(2, 65, 3, 128, 128, BF16) == 6 * 2 * 60416
     assert f(1, 64, 1, 128, 128, F32) == 0            # fp32 uses no workspace
     assert f(1, 0, 1, 128, 128, BF16) == 0 and f(1, 64, 1, 64, 128, BF16) == 0
 
@@ -157,21 +157,21 @@ def test_fp32_ignores_a_small_workspace(lib):
 
 def test_workspace_size_query(lib):
     f = lib.kda_chunk_fwd_workspace_size
-    # few heads, bf16: two-kernel schedule, one 64,512-byte block per chunk
+    # few heads, bf16: two-kernel schedule, one 60,416-byte block per chunk
     # 24 to 48 heads (a multiple of 8): prep and scan pipelined in one launch,
     # one int32 ready flag per block and 8 arrival counters after the blocks
-    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 64512 + (32 * 1024 + 8) * 4
-    assert f(2, 1000, 20, 128, 128, BF16) == 40 * 16 * 64512 + (40 * 16 + 8) * 4
-    assert f(1, 1000, 36, 128, 128, BF16) == 36 * 16 * 64512            # not a multiple of 8: one pass
+    assert f(1, 65536, 32, 128, 128, BF16) == 32 * 1024 * 60416 + (32 * 1024 + 8) * 4
+    assert f(2, 1000, 20, 128, 128, BF16) == 40 * 16 * 60416 + (40 * 16 + 8) * 4
+    assert f(1, 1000, 36, 128, 128, BF16) == 36 * 16 * 60416            # not a multiple of 8: one pass
     assert f(1, 64, 32, 128, 128, BF16) == 0                            # one chunk: fused kernel
-    assert f(1, 100, 3, 128, 128, BF16) == 3 * 2 * 64512
+    assert f(1, 100, 3, 128, 128, BF16) == 3 * 2 * 60416
     # 16 heads or fewer over enough chunks: the state scan runs in nseg
     # segments: fp32 summaries [nseg - 1][128][256], entry states [nseg][128][128]
     SEG = lambda n: (3 * (n - 1) + 1) * 128 * 128 * 4
-    assert f(1, 32768, 16, 128, 128, BF16) == 16 * 512 * 64512 + 16 * SEG(4)      # 4 segments
-    assert f(1, 4096, 1, 128, 128, BF16) == 64 * 64512 + SEG(16)                  # 16 segments
-    assert f(2, 1300, 4, 128, 128, BF16) == 8 * 21 * 64512 + 8 * SEG(7)           # 7 segments of 3 chunks
-    assert f(1, 256, 16, 128, 128, BF16) == 16 * 4 * 64512 + 16 * SEG(2)          # 2 segments of 2 chunks
+    assert f(1, 32768, 16, 128, 128, BF16) == 16 * 512 * 60416 + 16 * SEG(4)      # 4 segments
+    assert f(1, 4096, 1, 128, 128, BF16) == 64 * 60416 + SEG(16)                  # 16 segments
+    assert f(2, 1300, 4, 128, 128, BF16) == 8 * 21 * 60416 + 8 * SEG(7)           # 7 segments of 3 chunks
+    assert f(1, 256, 16, 128, 128, BF16) == 16 * 4 * 60416 + 16 * SEG(2)          # 2 segments of 2 chunks
     # many heads, fp32, tiny T or bad arguments: fused kernel, no workspace
     assert f(8, 4096, 16, 128, 128, BF16) == 0
     assert f(1, 256, 1, 128, 128, F32) == 0
@@ -210,7 +210,7 @@ def test_layer_workspace_layout(lib):
     total = lib.kda_layer_workspace_layout(B, T, dm, H, r, offs)
     R, hd = B * T, H * 128
     sizes = [R * 4 * hd * 2, R * 144 * 4, R * hd * 2, R * hd * 2, R * hd * 2, R * hd * 4,
-             R * H * 2, R * hd * 2, R * hd * 2, H * 512 * 64512 + H * 10 * 128 * 128 * 4]
+             R * H * 2, R * hd * 2, R * hd * 2, H * 512 * 60416 + H * 10 * 128 * 128 * 4]
     assert list(offs)[0] == 0
     for i in range(9):
         assert offs[i + 1] - offs[i] == (sizes[i] + 255) // 256 * 256
@@ -245,7 +245,7 @@ def test_layer_fwd_empty_is_noop(lib):
 
 
 # ------------------------------------------------------------ backward pass
-BWD_UNIT = 252928   # workspace bytes per (batch, head, 64-token chunk)
+BWD_UNIT = 248832   # workspace bytes per (batch, head, 64-token chunk)
 
 
 def bwd(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S0=None,
