@@ -186,15 +186,6 @@ __device__ __forceinline__ bf16x8 a_pair(const bf16_t* row, int p, int lg, bool 
     return cat8(a, b);
 }
 
-// The same operand from lower-triangular 16 x 16 tiles (the KDA block's Tm
-// and Aqk): tiles (R, 2p) and, with `hi`, (R, 2p + 1), row ln of each.
-__device__ __forceinline__ bf16x8 a_pair_tiles(const bf16_t* tiles, int R, int p, int ln, int lg, bool hi) {
-    const bf16_t* t0 = tiles + (R * (R + 1) / 2 + 2 * p) * 256 + ln * 16 + 4 * lg;
-    const bf16x4 a = ld4(t0);
-    const bf16x4 b = hi ? ld4(t0 + 256) : bf16x4{};
-    return cat8(a, b);
-}
-
 // ---- forward state scan: per-chunk operand block -------------------------------
 // Workspace block of one chunk, written by a prep kernel and read by
 // chunk_scan_kernel (bf16 only).  It is the image of the scan's LDS stage:
@@ -214,34 +205,39 @@ constexpr int WS_QK = WS_TM + C * WS_P64 * 2;       // Aqk  [64][72] bf16
 constexpr int WS_GAM = WS_QK + C * WS_P64 * 2;      // e^{G_64} [128] fp32
 constexpr int WS_USED = WS_GAM + DK * 4;            // 72,192 bytes written
 constexpr int WS_CHUNK = (WS_USED + 1023) / 1024 * 1024;   // 72,704: whole KiB per block
-// KDA block:
-//   Qt, Kh  [64][128] bf16, token-major rows of 256 B; the 16-byte unit u of
-//           row r sits at unit u ^ (r % 16), so that an MFMA A-fragment read
-//           (16 rows, 8 bytes per lane) touches every bank once per 256 B;
-//   Kt^T    [128][64] bf16, channel-major rows of 128 B; unit u of row c at
+// KDA block.  Every MFMA A-operand the scan reads is one contiguous 16-byte
+// unit: for a row (token of Qt / Kh, channel of Kt^T) and a pair p of
+// 16-column blocks, lane group lg (lane / 16) takes columns 32p + 4lg .. +3
+// and 32p + 16 + 4lg .. +3 (see a_pair), stored together as unit 4p + lg.
+//   Qt, Kh  [64 tokens][16 units] bf16, rows of 256 B; unit u of row r at
+//           u ^ (r % 16), so the 16 lanes of a lane group read 16 distinct
+//           units (every bank once);
+//   Kt^T    [128 channels][8 units], rows of 128 B; unit u of row c at
 //           u ^ ((c / 2) % 8) (rows two apart share banks);
-//   the lower tiles (R, c), c <= R, of Tm Diag(beta) and of Aqk, tile index
-//           R (R + 1) / 2 + c, each 16 rows of 32 bytes (an A-fragment read of
-//           16 rows x 8 bytes per lane group covers 512 contiguous bytes);
+//   Tm Diag(beta), Aqk: the lower part only, as the six operand pairs
+//           (Rb, p), 2p <= Rb, in the order (0,0) (1,0) (2,0) (2,1) (3,0)
+//           (3,1) (wsk_pair_off): a pair whose second block lies above the
+//           diagonal holds 8-byte units (the first block's four columns),
+//           the others 16-byte units, each [16 rows][4 lane groups];
 //   e^{G_64} [128] fp32.
-constexpr int WS_TILE = 16 * 16 * 2, WS_NTILE = 10;
+constexpr int WS_TRI = 5 * 1024;                            // bytes of one triangular matrix
 constexpr int WSK_QT = 0;
 constexpr int WSK_KH = WSK_QT + C * DK * 2;                 // 16 KiB
 constexpr int WSK_KBT = WSK_KH + C * DK * 2;
-constexpr int WSK_TM = WSK_KBT + DK * C * 2;                // Tm Diag(beta) tiles
-constexpr int WSK_QK = WSK_TM + WS_NTILE * WS_TILE;         // Aqk tiles
-constexpr int WSK_GAM = WSK_QK + WS_NTILE * WS_TILE;        // e^{G_64} [128] fp32
+constexpr int WSK_TM = WSK_KBT + DK * C * 2;                // Tm Diag(beta) pairs
+constexpr int WSK_QK = WSK_TM + WS_TRI;                     // Aqk pairs
+constexpr int WSK_GAM = WSK_QK + WS_TRI;                    // e^{G_64} [128] fp32
 constexpr int WSK_USED = WSK_GAM + DK * 4;                  // 59,904 bytes written
 constexpr int WSK_CHUNK = (WSK_USED + 1023) / 1024 * 1024;  // 60,416
-// element offsets of the swizzled rows
-__device__ __forceinline__ constexpr int wsk_tok(int r, int e) {      // Qt / Kh (row r, channel e)
-    return r * DK + ((((e >> 3) ^ (r & 15))) << 3) + (e & 7);
+// element offset of unit (row r, logical unit u) of Qt / Kh, and of Kt^T
+__device__ __forceinline__ constexpr int wsk_tok_unit(int r, int u) { return r * DK + ((u ^ (r & 15)) << 3); }
+__device__ __forceinline__ constexpr int wsk_kbt_unit(int c, int u) { return c * C + ((u ^ ((c >> 1) & 7)) << 3); }
+// byte offset of operand pair (Rb, p) of a triangular matrix, and whether it
+// holds both blocks
+__device__ __forceinline__ constexpr int wsk_pair_off(int Rb, int p) {
+    return Rb == 0 ? 0 : Rb == 1 ? 512 : Rb == 2 ? (p == 0 ? 1536 : 2560) : (p == 0 ? 3072 : 4096);
 }
-__device__ __forceinline__ constexpr int wsk_kbt(int c, int i) {      // Kt^T (channel c, token i)
-    return c * C + ((((i >> 3) ^ ((c >> 1) & 7))) << 3) + (i & 7);
-}
-__device__ __forceinline__ constexpr int lt_tile(int R, int c) { return R * (R + 1) / 2 + c; }
-__device__ __forceinline__ constexpr int lt_tile_row(int ti) { return ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3; }
+__device__ __forceinline__ constexpr bool wsk_pair_full(int Rb, int p) { return 2 * p + 1 <= Rb; }
 
 // Element (channel c, token i) of the swizzled Kb^T: the 8-token blocks of a
 // row are XOR-permuted by bits 3..5 of the channel.

@@ -752,37 +752,39 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
 
         if constexpr (PREP) {
             // ===== export the key-side operands of this chunk =====
-            // (16-byte units from the padded LDS rows into the KDA block's
-            // swizzled rows and lower tiles; for the backward pass, whose
-            // save-mode scan reads neither Qt nor Aqk, only Kh, Kt^T, Tm and
-            // gamma)
+            // (gathered from the padded LDS rows into the KDA block's
+            // operand units, two 8-byte halves per 16-byte unit; for the
+            // backward pass, whose save-mode scan reads neither Qt nor Aqk,
+            // only Kh, Kt^T, Tm and gamma)
             char* blk = ws + ((size_t)head * nchunks + n) * WSK_CHUNK;
             typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-            static_assert(L::P128 == WS_P128 && L::P64 == WS_P64, "LDS rows are padded as the DPLR block's");
-            // Qt, Kh: 64 rows of 16 units each
+            typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+            auto put = [&](int dst, const E* lo, const E* hi) {      // 16-byte unit from two 8-byte halves
+                const i32x2 a = *reinterpret_cast<const i32x2*>(lo), c2 = *reinterpret_cast<const i32x2*>(hi);
+                *reinterpret_cast<i32x4*>(blk + dst) = i32x4{a[0], a[1], c2[0], c2[1]};
+            };
+            // Qt, Kh: 64 rows of 16 units; unit u = 4p + lg of row r
             for (int u = BWD ? C * 16 + t : t; u < 2 * C * 16; u += NT) {
                 const int mat = u / (C * 16), r = (u >> 4) & (C - 1), uu = u & 15;
-                const E* src = (mat ? sKh : sQt) + r * L::P128 + 8 * uu;
-                *reinterpret_cast<i32x4*>(blk + (mat ? WSK_KH : WSK_QT) + 2 * wsk_tok(r, 8 * uu)) =
-                    *reinterpret_cast<const i32x4*>(src);
+                const E* row = (mat ? sKh : sQt) + r * L::P128 + 32 * (uu >> 2) + 4 * (uu & 3);
+                put((mat ? WSK_KH : WSK_QT) + 2 * wsk_tok_unit(r, uu), row, row + 16);
             }
-            // Kt^T: 128 rows of 8 units each
+            // Kt^T: 128 rows of 8 units (tokens from the swizzled LDS tile)
             for (int u = t; u < DK * 8; u += NT) {
-                const int c = u >> 3, uu = u & 7;
-                *reinterpret_cast<i32x4*>(blk + WSK_KBT + 2 * wsk_kbt(c, 8 * uu)) =
-                    *reinterpret_cast<const i32x4*>(sKbT + L::kbt(c, 8 * uu));
+                const int c = u >> 3, uu = u & 7, i0 = 32 * (uu >> 2) + 4 * (uu & 3);
+                put(WSK_KBT + 2 * wsk_kbt_unit(c, uu), sKbT + L::kbt(c, i0), sKbT + L::kbt(c, i0 + 16));
             }
             if (t < DK / 4)
                 reinterpret_cast<f32x4*>(blk + WSK_GAM)[t] = reinterpret_cast<const f32x4*>(s_gam)[t];
-            // the lower 16 x 16 tiles of Tm Diag(beta) and (not for the
-            // backward pass) Aqk: 32 units of 16 bytes per tile
-            for (int u = t; u < (BWD ? 1 : 2) * WS_NTILE * 32; u += NT) {
-                const int mat = u / (WS_NTILE * 32), v2 = u % (WS_NTILE * 32);
-                const int ti = v2 >> 5, r = (v2 >> 1) & 15, hh = v2 & 1;
-                const int R = lt_tile_row(ti), cc = ti - R * (R + 1) / 2;
-                const E* src = (mat ? sQK : RT) + (16 * R + r) * L::P64 + 16 * cc + 8 * hh;
-                *reinterpret_cast<i32x4*>(blk + (mat ? WSK_QK : WSK_TM) + ti * WS_TILE + r * 32 + hh * 16) =
-                    *reinterpret_cast<const i32x4*>(src);
+            // Tm Diag(beta) and (not for the backward pass) Aqk: six operand
+            // pairs of 64 units each (8-byte units for the two half pairs)
+            for (int u = t; u < (BWD ? 1 : 2) * 6 * 64; u += NT) {
+                const int mat = u / (6 * 64), k6 = (u >> 6) % 6, l = u & 63;
+                const int Rb = k6 < 1 ? 0 : k6 < 2 ? 1 : k6 < 4 ? 2 : 3, pp = (k6 == 3 || k6 == 5) ? 1 : 0;
+                const E* row = (mat ? sQK : RT) + (16 * Rb + (l >> 2)) * L::P64 + 32 * pp + 4 * (l & 3);
+                const int off = (mat ? WSK_QK : WSK_TM) + wsk_pair_off(Rb, pp);
+                if (wsk_pair_full(Rb, pp)) put(off + 16 * l, row, row + 16);
+                else *reinterpret_cast<i32x2*>(blk + off + 8 * l) = *reinterpret_cast<const i32x2*>(row);
             }
             if constexpr (BWD) {
                 // operands of the backward state scan: transposes read from LDS
@@ -1184,7 +1186,11 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             // A-operand pair p of row block Rb of Tm or Aqk (lower part only)
             auto tri_pair = [&](const bf16_t* m, int Rb, int p) {
                 if constexpr (DPLR) return a_pair(m + (16 * Rb + ln) * WS_P64, p, lg, 2 * p + 1 <= Rb);
-                else return a_pair_tiles(m, Rb, p, ln, lg, 2 * p + 1 <= Rb);
+                else {
+                    const char* q = reinterpret_cast<const char*>(m) + wsk_pair_off(Rb, p);
+                    if (wsk_pair_full(Rb, p)) return *reinterpret_cast<const bf16x8*>(q + 16 * (4 * ln + lg));
+                    return cat8(*reinterpret_cast<const bf16x4*>(q + 8 * (4 * ln + lg)), bf16x4{});
+                }
             };
             const bf16_t* sVT = reinterpret_cast<const bf16_t*>(st + SC::OFF_VT);
             bf16_t* sO = reinterpret_cast<bf16_t*>(smem + SC::OFF_O + (n & 1) * C * SC::DV * 2);
@@ -1205,14 +1211,10 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             constexpr int NF = NOOUT ? 4 : 8;         // Kh (and Qt) fragments per block
             bf16x8 fa[2][NF];
             // A-operand pair p of rows 16 Rb + ln of Kh or Qt: padded rows
-            // (DPLR), or swizzled rows (KDA: row 16 Rb + ln has swizzle ln)
+            // (DPLR), or one 16-byte unit (KDA)
             auto tok_pair = [&](const bf16_t* m, int Rb, int p) {
                 if constexpr (DPLR) return a_pair(m + (16 * Rb + ln) * WS_P128, p, lg, true);
-                else {
-                    const bf16_t* row = m + (16 * Rb + ln) * DK + 4 * (lg & 1);
-                    return cat8(ld4(row + (((4 * p + (lg >> 1)) ^ ln) << 3)),
-                                ld4(row + (((4 * p + 2 + (lg >> 1)) ^ ln) << 3)));
-                }
+                else return *reinterpret_cast<const bf16x8*>(m + wsk_tok_unit(16 * Rb + ln, 4 * p + lg));
             };
             auto frags = [&](int Rb, bf16x8 (&f)[NF]) {
 #pragma unroll
@@ -1295,15 +1297,15 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
 #pragma unroll
             for (int p = 0; p < 2; ++p) vb[p] = cat8(to_bf16x4(vn[2 * p]), to_bf16x4(vn[2 * p + 1]));
             // DPLR block: rows of 72 with the 8-token blocks XOR-permuted by
-            // bits 3..5 of the channel; KDA block: rows of 64, units permuted
-            // by bits 1..3 of the channel (= bits 1..3 of ln)
-            const bf16_t* kl = DPLR ? sKbT + ln * WS_P64 + ((((lg >> 1) ^ (ln >> 3)) & 1) << 3) + 4 * (lg & 1)
-                                    : sKbT + ln * C + 4 * (lg & 1);
+            // bits 3..5 of the channel (two 8-byte halves per operand); KDA
+            // block: one 16-byte unit per operand
+            const bf16_t* kl = sKbT + ln * WS_P64 + ((((lg >> 1) ^ (ln >> 3)) & 1) << 3) + 4 * (lg & 1);
             auto kbt_at = [&](int cb, int p, int hh) {
-                if constexpr (DPLR)
-                    return kl + 16 * cb * WS_P64 + ((p ^ ((cb >> 1) & 1)) << 5) + ((hh ^ (cb & 1)) << 4);
-                else
-                    return kl + 16 * cb * C + (((4 * p + 2 * hh + (lg >> 1)) ^ ((ln >> 1) & 7)) << 3);
+                return kl + 16 * cb * WS_P64 + ((p ^ ((cb >> 1) & 1)) << 5) + ((hh ^ (cb & 1)) << 4);
+            };
+            auto kbt_pair = [&](int cb, int p) {
+                if constexpr (DPLR) return cat8(ld4(kbt_at(cb, p, 0)), ld4(kbt_at(cb, p, 1)));
+                else return *reinterpret_cast<const bf16x8*>(sKbT + wsk_kbt_unit(16 * cb + ln, 4 * p + lg));
             };
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
@@ -1314,7 +1316,7 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
                 }
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    const bf16x8 a = cat8(ld4(kbt_at(cb, p, 0)), ld4(kbt_at(cb, p, 1)));
+                    const bf16x8 a = kbt_pair(cb, p);
                     acc_s[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vb[p], acc_s[cb], 0, 0, 0);
                 }
                 if constexpr (DPLR) {
