@@ -1069,12 +1069,30 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
     constexpr int QT_P1 = B_KH / 1024, QK_P0 = B_QK / 1024, QK_P1 = B_GAM / 1024;
     static_assert(B_QT == 0 && B_KH % 1024 == 0 && B_QK % 1024 == 0 && B_GAM % 1024 == 0,
                   "Qt and Aqk occupy whole pages");
-    auto load_block = [&](int n) {            // workspace block n -> stage n % 2
+    // The block is copied in two groups: G1, the pages of Qt and Kh, which the
+    // consumers read first, and G2, the rest.  In step n the loaders issue G2
+    // of block n + 1 (and its V rows) at the start; once the consumers have
+    // passed their first phase (a second barrier per step) they wait for
+    // those, write V^T, store the previous output tile and then issue G1 of
+    // block n + 2 into the G1 pages of this step's stage, which stays in
+    // flight until the middle of step n + 1.  (Every LDS access of a loader
+    // comes after that wait, so no wait for the DMA in flight falls into the
+    // part of a step before the middle barrier.)
+    constexpr int G1_P0 = NOOUT ? QT_P1 : 0, G1_P1 = B_KBT / 1024;      // G1 pages [G1_P0, G1_P1)
+    static_assert(B_KBT % 1024 == 0, "G1 pages");
+    auto load_g1 = [&](int n) {               // G1 of block n -> stage n % 2
         const char* src = wsh + (size_t)n * B_CHUNK;
         char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
-        for (int u = wave; u < B_KIB; u += SC::NLW) {
-            // without output, the Qt and Aqk pages are not read: not copied
-            if (NOOUT && (u < QT_P1 || (u >= QK_P0 && u < QK_P1))) continue;
+        for (int u = G1_P0 + wave; u < G1_P1; u += SC::NLW)
+            __builtin_amdgcn_global_load_lds(src + (size_t)u * 1024 + lane * 16,
+                                             (__attribute__((address_space(3))) void*)(dst + u * 1024), 16, 0, 0);
+    };
+    auto load_block = [&](int n) {            // G2 of workspace block n -> stage n % 2
+        const char* src = wsh + (size_t)n * B_CHUNK;
+        char* dst = smem + (n & 1) * SC::STAGE + SC::OFF_BLK;
+        for (int u = G1_P1 + wave; u < B_KIB; u += SC::NLW) {
+            // without output, the Aqk pages are not read: not copied
+            if (NOOUT && u >= QK_P0 && u < QK_P1) continue;
             const char* from = src + (size_t)u * 1024 + lane * 16;
             if constexpr (DPLR) {
                 if (u >= TM_P0 && u < TM_P1) {
@@ -1093,13 +1111,17 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
     // The producers never wait, so every wait ends; the spin budget (shared
     // by all waits of the wave, about a second in all) only guards against a
     // launch that cannot make progress: once spent, the wave stops waiting.
+    // The flag is read with a scalar load that bypasses the scalar cache
+    // (glc), waited for in the same statement: it does not count against the
+    // vector-memory counter, so a poll does not wait for the copies in flight.
     int spin_budget = 1 << 20;
     auto wait_ready = [&](int n) {
         if (!flags) return;
         const int* f = flags + (size_t)head * nchunks + n;
         while (spin_budget > 0) {
-            if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
-                break;
+            int fv;
+            asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(fv) : "s"(f) : "memory");
+            if (fv != 0) break;
             __builtin_amdgcn_s_sleep(1);
             --spin_budget;
         }
@@ -1161,20 +1183,34 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             }
     } else {
         wait_ready(c0);
+        load_g1(c0);
         load_block(c0);
         load_v(c0);
         __builtin_amdgcn_s_waitcnt(0);        // vmcnt, lgkmcnt and expcnt all zero
         write_vt(c0);
+        if (c0 + 1 < c1) { wait_ready(c0 + 1); load_g1(c0 + 1); }   // lands during step c0
     }
     lds_barrier();
 
     for (int n = c0; n < c1; ++n) {
         if (loader) {
-            if (n + 1 < c1) { wait_ready(n + 1); load_block(n + 1); load_v(n + 1); }
-            if (!NOOUT && n > c0) store_out(n - 1);
-            if constexpr (DPLR) load_o0(n);
-            __builtin_amdgcn_s_waitcnt(0);    // the stage must be complete at the barrier
+            // the ready flag of block n + 2, read early (a vector load that
+            // lands with the copies below); polled only if it was not set
+            int ready2 = 1;
+            if (flags && n + 2 < c1)
+                ready2 = __hip_atomic_load(flags + (size_t)head * nchunks + n + 2, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            // G2 (and V) of block n + 1; its G1 is in flight since step n - 1
+            if (n + 1 < c1) { load_block(n + 1); load_v(n + 1); }
+            lds_barrier();                    // the consumers are done with G1 of block n
+            __builtin_amdgcn_s_waitcnt(0);    // block n + 1 complete (G1, G2), V rows in registers
             if (n + 1 < c1) write_vt(n + 1);
+            if (!NOOUT && n > c0) store_out(n - 1);
+            if constexpr (DPLR) load_o0(n);   // (after the store of chunk n - 1, which adds O0 of n - 1)
+            if (n + 2 < c1) {
+                if (__builtin_amdgcn_readfirstlane(ready2) == 0) wait_ready(n + 2);
+                load_g1(n + 2);               // into the G1 pages of this step's stage
+            }
         } else {
             const char* st = smem + (n & 1) * SC::STAGE;
             const bf16_t* sQt = reinterpret_cast<const bf16_t*>(st + SC::OFF_BLK + B_QT);
@@ -1240,6 +1276,9 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
                 if (Rb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
             }
+            // the G1 pages of this stage (Qt, Kh) are read: the loaders may
+            // refill them with block n + 2
+            lds_barrier();
 
             // Z = V - P (V^T read in the B layout), Vn = Tm Z (lower blocks only)
             f32x4 zt[4], vn[4];
