@@ -374,6 +374,31 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
     for (int n = n_first; n < n_end; ++n) {
         const bool full = (n + 1) * C <= T;     // uniform: no row of this chunk is past T
 
+        // PREP: this chunk's operand block.  Its units are gathered from the
+        // padded LDS rows, two 8-byte halves per 16-byte unit.  Qt, Kh and
+        // Kt^T (not Qt for the backward pass, whose save-mode scan does not
+        // read it) are exported by threads u0, u0 + du, ...
+        char* blk = PREP ? ws + ((size_t)head * nchunks + n) * WSK_CHUNK : nullptr;
+        typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+        typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+        auto put = [&](int dst, const E* lo, const E* hi) {
+            const i32x2 a = *reinterpret_cast<const i32x2*>(lo), c2 = *reinterpret_cast<const i32x2*>(hi);
+            *reinterpret_cast<i32x4*>(blk + dst) = i32x4{a[0], a[1], c2[0], c2[1]};
+        };
+        auto export_tok = [&](int u0, int du) {
+            // Qt, Kh: 64 rows of 16 units; unit u = 4p + lg of row r
+            for (int u = (BWD ? C * 16 : 0) + u0; u < 2 * C * 16; u += du) {
+                const int mat = u / (C * 16), r = (u >> 4) & (C - 1), uu = u & 15;
+                const E* row = (mat ? sKh : sQt) + r * L::P128 + 32 * (uu >> 2) + 4 * (uu & 3);
+                put((mat ? WSK_KH : WSK_QT) + 2 * wsk_tok_unit(r, uu), row, row + 16);
+            }
+            // Kt^T: 128 rows of 8 units (tokens from the swizzled LDS tile)
+            for (int u = u0; u < DK * 8; u += du) {
+                const int c = u >> 3, uu = u & 7, i0 = 32 * (uu >> 2) + 4 * (uu & 3);
+                put(WSK_KBT + 2 * wsk_kbt_unit(c, uu), sKbT + L::kbt(c, i0), sKbT + L::kbt(c, i0 + 16));
+            }
+        };
+
         // ===== E: cumulative log2-decay and the decay-scaled operands =====
         // G is kept in log2 units so that 2^G = e^{sum g}.  Each lane owns
         // 8 channels x 2 consecutive rows; the prefix over rows is local, then
@@ -622,6 +647,9 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
                     }
                 }
                 if (!PREP && wave >= 4) p_block(wave - 4);
+                // prep: Qt, Kh and Kt^T are final after E on this path; the
+                // waves without tiles export them while the tiles are formed
+                if (PREP && wave >= 4) export_tok(t - 256, NT - 256);
             } else {
                 m1_subchunk<E, DV>(smem, t);
                 if (!PREP && wave >= 4) p_block(wave - 4);
@@ -751,29 +779,10 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
         }
 
         if constexpr (PREP) {
-            // ===== export the key-side operands of this chunk =====
-            // (gathered from the padded LDS rows into the KDA block's
-            // operand units, two 8-byte halves per 16-byte unit; for the
-            // backward pass, whose save-mode scan reads neither Qt nor Aqk,
-            // only Kh, Kt^T, Tm and gamma)
-            char* blk = ws + ((size_t)head * nchunks + n) * WSK_CHUNK;
-            typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-            typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
-            auto put = [&](int dst, const E* lo, const E* hi) {      // 16-byte unit from two 8-byte halves
-                const i32x2 a = *reinterpret_cast<const i32x2*>(lo), c2 = *reinterpret_cast<const i32x2*>(hi);
-                *reinterpret_cast<i32x4*>(blk + dst) = i32x4{a[0], a[1], c2[0], c2[1]};
-            };
-            // Qt, Kh: 64 rows of 16 units; unit u = 4p + lg of row r
-            for (int u = BWD ? C * 16 + t : t; u < 2 * C * 16; u += NT) {
-                const int mat = u / (C * 16), r = (u >> 4) & (C - 1), uu = u & 15;
-                const E* row = (mat ? sKh : sQt) + r * L::P128 + 32 * (uu >> 2) + 4 * (uu & 3);
-                put((mat ? WSK_KH : WSK_QT) + 2 * wsk_tok_unit(r, uu), row, row + 16);
-            }
-            // Kt^T: 128 rows of 8 units (tokens from the swizzled LDS tile)
-            for (int u = t; u < DK * 8; u += NT) {
-                const int c = u >> 3, uu = u & 7, i0 = 32 * (uu >> 2) + 4 * (uu & 3);
-                put(WSK_KBT + 2 * wsk_kbt_unit(c, uu), sKbT + L::kbt(c, i0), sKbT + L::kbt(c, i0 + 16));
-            }
+            // ===== export the rest of this chunk's operand block =====
+            // (Qt, Kh and Kt^T here only on the sub-chunk path, which rebases
+            // Qt and Kh after the intra-chunk products)
+            if (slow) export_tok(t, NT);
             if (t < DK / 4)
                 reinterpret_cast<f32x4*>(blk + WSK_GAM)[t] = reinterpret_cast<const f32x4*>(s_gam)[t];
             // Tm Diag(beta) and (not for the backward pass) Aqk: six operand
