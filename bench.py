@@ -436,7 +436,8 @@ def layer_line(steps, warmup):
             "model_flops": gemm_flops + kda_flops,
             "achieved_tflops": round((gemm_flops + kda_flops) / t_layer / 1e12, 1),
             "frac_of_bf16_peak": round((gemm_flops + kda_flops) / t_layer / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "projection_gemm_counters": measured_counters(["kda_layer_gemm_large"], GEMM_KERNEL_SRC)}
+            "projection_gemm_counters": measured_counters(["kda_layer_gemm_qkvg", "kda_layer_gemm_o"],
+                                                          GEMM_KERNEL_SRC)}
 
 
 def backward_line(steps, warmup, with_cpu=False, wl="c2"):

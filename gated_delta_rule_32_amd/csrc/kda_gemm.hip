@@ -230,6 +230,7 @@ struct StackedB {
     const bf16_t* p[4];
 };
 
+template <int NB>    // weight matrices stacked along N (1: one matrix)
 __global__ void __launch_bounds__(LGT)
 gemm_nt_large_kernel(const bf16_t* A, StackedB Bs, bf16_t* C, int M, int N, int K,
                      int lda, int ldb, int ldc, int n_split)
@@ -254,7 +255,7 @@ gemm_nt_large_kernel(const bf16_t* A, StackedB Bs, bf16_t* C, int M, int N, int 
     }
     const int m0 = tm * LBM, n0 = tn * LBN;
     // this tile's weight matrix and its rows n0 - seg n_split ..
-    const int seg = n0 / n_split;
+    const int seg = NB == 1 ? 0 : n0 / n_split;
     const bf16_t* B = Bs.p[seg];
     const int nb0 = n0 - seg * n_split, nseg = min(n_split, N - seg * n_split);
 
@@ -361,8 +362,13 @@ hipError_t launch_gemm_nt_stacked(const bf16_t* A, const bf16_t* const* B, int n
     for (int i = 0; i < 4; ++i) bs.p[i] = B[i < nmat ? i : nmat - 1];
     const int N = nmat * n_split;
     const unsigned tiles = (unsigned)(((M + LBM - 1) / LBM) * (N / LBN));
-    hipLaunchKernelGGL(gemm_nt_large_kernel, dim3(tiles), dim3(LGT), 0, stream, A, bs, C, M, N, K, lda, ldb,
-                       ldc, n_split);
+#define KDA_LARGE(NB) hipLaunchKernelGGL(gemm_nt_large_kernel<NB>, dim3(tiles), dim3(LGT), 0, stream, A, bs, C, M, N, \
+                                         K, lda, ldb, ldc, n_split)
+    if (nmat == 4) KDA_LARGE(4);
+    else if (nmat == 3) KDA_LARGE(3);
+    else if (nmat == 2) KDA_LARGE(2);
+    else KDA_LARGE(1);
+#undef KDA_LARGE
     return hipGetLastError();
 }
 
@@ -374,7 +380,7 @@ hipError_t launch_gemm_nt(const void* A, bool a_f32, const bf16_t* B, void* C, b
     if (!B2 && !a_f32 && !c_f32 && epilogue == 0 && M >= LBM && N >= LBN) {
         const unsigned tiles = (unsigned)(((M + LBM - 1) / LBM) * ((N + LBN - 1) / LBN));
         const StackedB bs = {{B, B, B, B}};
-        hipLaunchKernelGGL(gemm_nt_large_kernel, dim3(tiles), dim3(LGT), 0, stream,
+        hipLaunchKernelGGL(gemm_nt_large_kernel<1>, dim3(tiles), dim3(LGT), 0, stream,
                            (const bf16_t*)A, bs, (bf16_t*)C, M, N, K, lda, ldb, ldc, N);
         return hipGetLastError();
     }
