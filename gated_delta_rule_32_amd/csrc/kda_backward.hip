@@ -166,7 +166,7 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
             for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    svdS[(cidx * DK + 16 * cb + 4 * lg + e) * DK + j0 + jc] = (bf16_t)acc_s[cb][e];
+                    svdS[sv_at(cidx, DK, 16 * cb + 4 * lg + e, j0 + jc)] = (bf16_t)acc_s[cb][e];
 
             bf16x8 sb[4], dob[2];
 #pragma unroll
@@ -208,7 +208,7 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * Rb + 4 * lg + e, tok = n * C + r;
                     dvv[Rb][e] = sBeta[r] * a[e];
-                    svdZ[(cidx * C + r) * DK + j0 + jc] = (bf16_t)a[e];
+                    svdZ[sv_at(cidx, C, r, j0 + jc)] = (bf16_t)a[e];
                     if (tok < T) dv[hbase + (size_t)tok * tokstride + j0 + jc] = (bf16_t)dvv[Rb][e];
                 }
             }
@@ -366,31 +366,32 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     }
     bf16x8 sf[4], dsf[4];                          // S, dS' rows c as B fragments
     {
-        const bf16_t* pS = svS + (cidx * DK + c) * DK + 8 * lg;
-        const bf16_t* pdS = svdS + (cidx * DK + c) * DK + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) { sf[s] = ld8(pS + 32 * s); dsf[s] = ld8(pdS + 32 * s); }
+        for (int s = 0; s < 4; ++s) {
+            sf[s] = ld8(svS + sv_at(cidx, DK, c, 32 * s + 8 * lg));
+            dsf[s] = ld8(svdS + sv_at(cidx, DK, c, 32 * s + 8 * lg));
+        }
     }
     // C x C tiles tt = wave, wave + 8 as (mb, nb); those above the diagonal are zero
     bf16x8 dzf[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int tt = wave + 8 * j, mb = tt >> 2;
-        const bf16_t* p = svdZ + (cidx * C + 16 * mb + ln) * DK + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) dzf[j][s] = ((tt & 3) <= mb) ? ld8(p + 32 * s) : bf16x8{};
+        for (int s = 0; s < 4; ++s)
+            dzf[j][s] = ((tt & 3) <= mb) ? ld8(svdZ + sv_at(cidx, C, 16 * mb + ln, 32 * s + 8 * lg)) : bf16x8{};
     }
     // row r = t / 8, columns 16 (t % 8) .. +15 of the 64 x 128 value-side tiles
     const int vr = t >> 3, vc = 16 * (t & 7);
     const bool vok = tok0 + vr < T;
     const size_t vat = hbase + (size_t)min(tok0 + vr, T - 1) * tokstride + vc;
-    const size_t wat = (cidx * C + vr) * DK + vc;
     bf16x8 yv[2], zv[2], dov[2], vnv[2], dvv[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        yv[i] = ld8(svY + wat + 8 * i);
-        zv[i] = ld8(svdZ + wat + 8 * i);
-        vnv[i] = ld8(svVn + wat + 8 * i);
+        const size_t wat = sv_at(cidx, C, vr, vc + 8 * i);
+        yv[i] = ld8(svY + wat);
+        zv[i] = ld8(svdZ + wat);
+        vnv[i] = ld8(svVn + wat);
         dov[i] = vok ? ld8(dO + vat + 8 * i) : bf16x8{};
         dvv[i] = vok ? ld8(dV + vat + 8 * i) : bf16x8{};
     }

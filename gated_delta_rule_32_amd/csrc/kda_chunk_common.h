@@ -245,6 +245,22 @@ __device__ __forceinline__ constexpr int kbt_swz(int c, int i) {
     return c * WS_P64 + ((((i >> 3) ^ ((c >> 3) & 7)) << 3) | (i & 7));
 }
 
+// ---- backward pass: saved per-chunk tensors -----------------------------------
+// S_n and dS' ([128 channels][128 value columns] per chunk) and Y, Vn, dZ
+// ([64 tokens][128 columns]) are written by the scans' consumer waves, whose
+// lane (ln, lg) holds rows 4 lg + e (e < 4) of column ln of a 16 x 16 tile,
+// and read by the gradient kernel as 8 consecutive columns of one row.  They
+// are stored as 16 x 16 tiles, [chunk][16-column slice][16-row block][256],
+// the rows of a tile in the order 4 e + lg and each row's 16 columns
+// contiguous: a consumer store of one e covers 128 contiguous bytes (a whole
+// line, instead of four 32-byte pieces), and a row's 8 columns stay 16
+// contiguous bytes for the reader.  Element offset of (row r, column c) of a
+// chunk with `rows` rows:
+__device__ __forceinline__ size_t sv_at(size_t cidx, int rows, int r, int c) {
+    return ((cidx * (DK / 16) + (c >> 4)) * (rows >> 4) + (r >> 4)) * 256 + (((r & 3) << 2) | ((r >> 2) & 3)) * 16 +
+           (c & 15);
+}
+
 // ---- backward pass: per-chunk operand block of the reverse state scan --------
 // Written by the prep kernel next to the forward block, read by
 // chunk_bwd_scan_kernel.  All bf16 except the two vectors; rows padded to

@@ -1245,7 +1245,7 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
                 for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        svS[(cidx * DK + 16 * cb + 4 * lg + e) * DK + j0 + jc] = (bf16_t)acc_s[cb][e];
+                        svS[sv_at(cidx, DK, 16 * cb + 4 * lg + e, j0 + jc)] = (bf16_t)acc_s[cb][e];
             }
 
             // P = Kh S and Qt S; a block's eight operand loads go out before its
@@ -1316,7 +1316,7 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
                 for (int Rb = 0; Rb < 4; ++Rb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const size_t at = (cidx * C + 16 * Rb + 4 * lg + e) * DK + j0 + jc;
+                        const size_t at = sv_at(cidx, C, 16 * Rb + 4 * lg + e, j0 + jc);
                         svY[at] = (bf16_t)zt[Rb][e];
                         svVn[at] = (bf16_t)vn[Rb][e];
                     }
