@@ -162,11 +162,16 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
 
             // dS' of this chunk (gradient of the state it hands on), for the
             // gradient kernel
+            // (neighbouring lanes pair up so that each store is a 4-byte column
+            // pair, see pair_rows_bf16)
+            const int prow = 4 * lg + 2 * (ln & 1), pcol = j0 + 16 * cw + (ln & ~1);
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    svdS[sv_at(cidx, DK, 16 * cb + 4 * lg + e, j0 + jc)] = (bf16_t)acc_s[cb][e];
+            for (int cb = 0; cb < 8; ++cb) {
+                bf16x2 p0, p1;
+                pair_rows_bf16(acc_s[cb], lane, p0, p1);
+                *reinterpret_cast<bf16x2*>(svdS + sv_at(cidx, DK, 16 * cb + prow, pcol)) = p0;
+                *reinterpret_cast<bf16x2*>(svdS + sv_at(cidx, DK, 16 * cb + prow + 1, pcol)) = p1;
+            }
 
             bf16x8 sb[4], dob[2];
 #pragma unroll
@@ -205,12 +210,15 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
                 for (int p = 0; p < 2; ++p)
                     a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rt, p, lg, true), vb[p], a, 0, 0, 0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * Rb + 4 * lg + e, tok = n * C + r;
-                    dvv[Rb][e] = sBeta[r] * a[e];
-                    svdZ[sv_at(cidx, C, r, j0 + jc)] = (bf16_t)a[e];
-                    if (tok < T) dv[hbase + (size_t)tok * tokstride + j0 + jc] = (bf16_t)dvv[Rb][e];
-                }
+                for (int e = 0; e < 4; ++e) dvv[Rb][e] = sBeta[16 * Rb + 4 * lg + e] * a[e];
+                bf16x2 z0, z1, d0, d1;
+                pair_rows_bf16(a, lane, z0, z1);
+                pair_rows_bf16(dvv[Rb], lane, d0, d1);
+                const int r0 = 16 * Rb + prow, tok = n * C + r0;
+                *reinterpret_cast<bf16x2*>(svdZ + sv_at(cidx, C, r0, pcol)) = z0;
+                *reinterpret_cast<bf16x2*>(svdZ + sv_at(cidx, C, r0 + 1, pcol)) = z1;
+                if (tok < T) *reinterpret_cast<bf16x2*>(dv + hbase + (size_t)tok * tokstride + pcol) = d0;
+                if (tok + 1 < T) *reinterpret_cast<bf16x2*>(dv + hbase + (size_t)(tok + 1) * tokstride + pcol) = d1;
             }
 
             // dS <- Diag(gamma) dS' + Qt^T dO - Kh^T dV

@@ -261,6 +261,26 @@ __device__ __forceinline__ size_t sv_at(size_t cidx, int rows, int r, int c) {
            (c & 15);
 }
 
+// Pair exchange for stores of an accumulator tile (lane (ln, lg) holds rows
+// 4 lg + e of column ln): neighbouring lanes swap halves (DPP quad_perm
+// [1,0,3,2]) so that an even lane holds rows 4 lg, 4 lg + 1 and an odd lane
+// rows 4 lg + 2, 4 lg + 3, each at the column pair (ln & ~1, ln | 1).
+// Returns the two 4-byte pieces of the lane: piece i is row
+// 4 lg + 2 (ln & 1) + i, columns (ln & ~1, ln | 1).
+__device__ __forceinline__ void pair_rows_bf16(const f32x4& x, int lane, bf16x2& p0, bf16x2& p1) {
+    const bool odd = lane & 1;
+    const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0xB1, 0xF, 0xF, false));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s1), 0xB1, 0xF, 0xF, false));
+    if (odd) {
+        p0[0] = (bf16_t)r0; p0[1] = (bf16_t)x[2];
+        p1[0] = (bf16_t)r1; p1[1] = (bf16_t)x[3];
+    } else {
+        p0[0] = (bf16_t)x[0]; p0[1] = (bf16_t)r0;
+        p1[0] = (bf16_t)x[1]; p1[1] = (bf16_t)r1;
+    }
+}
+
 // ---- backward pass: per-chunk operand block of the reverse state scan --------
 // Written by the prep kernel next to the forward block, read by
 // chunk_bwd_scan_kernel.  All bf16 except the two vectors; rows padded to

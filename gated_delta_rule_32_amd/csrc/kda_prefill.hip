@@ -1240,12 +1240,17 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             const bf16_t* sVT = reinterpret_cast<const bf16_t*>(st + SC::OFF_VT);
             bf16_t* sO = reinterpret_cast<bf16_t*>(smem + SC::OFF_O + (n & 1) * C * SC::DV * 2);
             const size_t cidx = (size_t)head * nchunks + n;
+            // saved tiles: neighbouring lanes pair up so that each store is a
+            // 4-byte column pair (see pair_rows_bf16)
+            const int prow = 4 * lg + 2 * (ln & 1), pcol = j0 + 16 * cw + (ln & ~1);
             if constexpr (SAVE) {
 #pragma unroll
-                for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        svS[sv_at(cidx, DK, 16 * cb + 4 * lg + e, j0 + jc)] = (bf16_t)acc_s[cb][e];
+                for (int cb = 0; cb < 8; ++cb) {
+                    bf16x2 p0, p1;
+                    pair_rows_bf16(acc_s[cb], lane, p0, p1);
+                    *reinterpret_cast<bf16x2*>(svS + sv_at(cidx, DK, 16 * cb + prow, pcol)) = p0;
+                    *reinterpret_cast<bf16x2*>(svS + sv_at(cidx, DK, 16 * cb + prow + 1, pcol)) = p1;
+                }
             }
 
             // P = Kh S and Qt S; a block's eight operand loads go out before its
@@ -1313,13 +1318,16 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             }
             if constexpr (SAVE) {
 #pragma unroll
-                for (int Rb = 0; Rb < 4; ++Rb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const size_t at = sv_at(cidx, C, 16 * Rb + 4 * lg + e, j0 + jc);
-                        svY[at] = (bf16_t)zt[Rb][e];
-                        svVn[at] = (bf16_t)vn[Rb][e];
-                    }
+                for (int Rb = 0; Rb < 4; ++Rb) {
+                    bf16x2 y0, y1, w0, w1;
+                    pair_rows_bf16(zt[Rb], lane, y0, y1);
+                    pair_rows_bf16(vn[Rb], lane, w0, w1);
+                    const size_t a0 = sv_at(cidx, C, 16 * Rb + prow, pcol), a1 = sv_at(cidx, C, 16 * Rb + prow + 1, pcol);
+                    *reinterpret_cast<bf16x2*>(svY + a0) = y0;
+                    *reinterpret_cast<bf16x2*>(svY + a1) = y1;
+                    *reinterpret_cast<bf16x2*>(svVn + a0) = w0;
+                    *reinterpret_cast<bf16x2*>(svVn + a1) = w1;
+                }
             }
 
             // O = Qt S + Aqk Vn -> LDS staging (stored to HBM by the loaders)
