@@ -101,7 +101,7 @@ enum {
  *                                           any other overlap is rejected.
  *   workspace                 device scratch, owned by the caller, or NULL.
  *                             With dtype == KDA_BF16 and workspace_bytes >=
- *                             B * H * ceil(T / 64) * 72704, the call runs two
+ *                             B * H * ceil(T / 64) * 60416, the call runs two
  *                             kernels: the key-side operands of every chunk
  *                             are computed in parallel into the workspace,
  *                             then a serial scan applies them to the state.
@@ -180,12 +180,14 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
 
 /*
  * Workspace bytes that kda_chunk_fwd should be given for the fastest schedule
- * on this shape: B * H * ceil(T / 64) * 72704 when the two-kernel schedule is
+ * on this shape: B * H * ceil(T / 64) * 60416 when the two-kernel schedule is
  * expected to win (bf16 with fewer than 128 heads in total), plus, when its
  * scan runs in nseg > 1 segments (16 heads or fewer, at least two chunks per
  * segment), B * H * (3 * (nseg - 1) + 1) * 65536 for the segment summaries
- * and entry states; else 0 (the fused kernel is used and no workspace is
- * needed).
+ * and entry states, or, when prep and scan run pipelined in one launch (24
+ * to 48 heads, a multiple of 8, at least two chunks), (B * H * ceil(T / 64)
+ * + 8) * 4 for the per-block ready flags and per-XCD arrival counters; else 0
+ * (the fused kernel is used and no workspace is needed).
  * Invalid arguments return 0.
  */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
