@@ -259,10 +259,12 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
 // registers.
 //
 // Every global read is issued at the start: q, k and g go global -> LDS with
-// 16-byte LDS-destination loads, the rest into registers (the S and dS' rows
-// of the wave's channel block as B fragments, the dZ rows of its C x C tiles
-// as A fragments, and the dO, Vn, dV tiles that are then parked in LDS).  LDS
-// regions are reused phase by phase:
+// 16-byte LDS-destination loads, the rest into registers (the dO and Vn tiles
+// that are then parked in LDS, the dZ rows of the wave's C x C tiles as A
+// fragments, the Y and dZ values of the first dbeta term, the S and dS' rows
+// of its channel block as B fragments), in the order the phases consume them;
+// -dV = -Diag(beta) dZ is formed from the dZ values.  LDS regions are reused
+// phase by phase:
 //   A  : g staging (fp32) -> Kh, Kb -> dV -> dq, dk staging
 //   B  : Qt^T, Kh^T, Kb^T -> dg staging (fp32)
 //   CR : q, k staging -> dAqk, dAqk^T, dA', dA'^T
@@ -293,11 +295,6 @@ struct GradLds {
 };
 
 __device__ __forceinline__ bf16x8 ld8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ bf16x8 neg8(bf16x8 x) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = -x[i];
-    return x;
-}
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -311,7 +308,7 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 template <int GATE>
 __global__ void __launch_bounds__(512)
 chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf16_t* beta,
-                      const bf16_t* dO, const bf16_t* dV, const bf16_t* svS, const bf16_t* svdS,
+                      const bf16_t* dO, const bf16_t* svS, const bf16_t* svdS,
                       const bf16_t* svY, const bf16_t* svVn, const bf16_t* svdZ,
                       bf16_t* dq, bf16_t* dk, float* dg, bf16_t* dbeta, int T, int H)
 {
@@ -372,38 +369,48 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
             for (int e = 0; e < 4; ++e)
                 gh[m][e] = g[((size_t)b * T + min(tok0 + 16 * m + 4 * lg + e, T - 1)) * H + h];
     }
-    bf16x8 sf[4], dsf[4];                          // S, dS' rows c as B fragments
-    {
+    // row r = t / 8, columns 16 (t % 8) .. +15 of the 64 x 128 value-side tiles
+    const int vr = t >> 3, vc = 16 * (t & 7);
+    const bool vok = tok0 + vr < T;
+    const size_t vat = hbase + (size_t)min(tok0 + vr, T - 1) * tokstride + vc;
+    // Register loads in the order they are consumed (dO and Vn are parked in
+    // LDS after the decay phase, dZ and Y feed the C x C products, S and dS'
+    // the C x d_k products); dV is not read: it is Diag(beta) dZ.
+    __builtin_amdgcn_sched_barrier(0);            // keep them behind the LDS-destination loads
+    bf16x8 yv[2], zv[2], dov[2], vnv[2];
+    const bf16_t betr = beta[((size_t)b * T + min(tok0 + (t & 63), T - 1)) * H + h];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            sf[s] = ld8(svS + sv_at(cidx, DK, c, 32 * s + 8 * lg));
-            dsf[s] = ld8(svdS + sv_at(cidx, DK, c, 32 * s + 8 * lg));
-        }
+    for (int i = 0; i < 2; ++i) {
+        dov[i] = ld8(dO + vat + 8 * i);
+        vnv[i] = ld8(svVn + sv_at(cidx, C, vr, vc + 8 * i));
     }
-    // C x C tiles tt = wave, wave + 8 as (mb, nb); those above the diagonal are zero
+    // C x C tiles tt = wave, wave + 8 as (mb, nb); those above the diagonal are
+    // zero and skipped (their loads are issued anyway, so the count is fixed)
     bf16x8 dzf[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int tt = wave + 8 * j, mb = tt >> 2;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            dzf[j][s] = ((tt & 3) <= mb) ? ld8(svdZ + sv_at(cidx, C, 16 * mb + ln, 32 * s + 8 * lg)) : bf16x8{};
+        for (int s = 0; s < 4; ++s) dzf[j][s] = ld8(svdZ + sv_at(cidx, C, 16 * mb + ln, 32 * s + 8 * lg));
     }
-    // row r = t / 8, columns 16 (t % 8) .. +15 of the 64 x 128 value-side tiles
-    const int vr = t >> 3, vc = 16 * (t & 7);
-    const bool vok = tok0 + vr < T;
-    const size_t vat = hbase + (size_t)min(tok0 + vr, T - 1) * tokstride + vc;
-    bf16x8 yv[2], zv[2], dov[2], vnv[2], dvv[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const size_t wat = sv_at(cidx, C, vr, vc + 8 * i);
         yv[i] = ld8(svY + wat);
         zv[i] = ld8(svdZ + wat);
-        vnv[i] = ld8(svVn + wat);
-        dov[i] = vok ? ld8(dO + vat + 8 * i) : bf16x8{};
-        dvv[i] = vok ? ld8(dV + vat + 8 * i) : bf16x8{};
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    bf16x8 sf[4], dsf[4];                          // S, dS' rows c as B fragments
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        sf[s] = ld8(svS + sv_at(cidx, DK, c, 32 * s + 8 * lg));
+        dsf[s] = ld8(svdS + sv_at(cidx, DK, c, 32 * s + 8 * lg));
+    }
+    if (!vok) { dov[0] = bf16x8{}; dov[1] = bf16x8{}; }
+    // The loads return in issue order: once at most the 20 register loads
+    // issued after beta, dO and Vn are outstanding, the LDS-destination loads
+    // are complete (vmcnt 20, no wait on the other counters).  The rest
+    // arrive while the decay phase and the C x C products run.
+    __builtin_amdgcn_s_waitcnt((20 & 15) | ((20 >> 4) << 14) | (7 << 4) | (15 << 8));
     lds_barrier();
 
     // ===== decay and the decay-scaled keys / queries =====
@@ -416,11 +423,14 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * m + 4 * lg + e;
             const bool ok = tok0 + r < T;
+            // (the staged rows past T hold the clamped last token: read, then mask)
             float gl = 0.f;
-            if constexpr (GATE == GATE_CHANNEL) gl = ok ? stG[r * DK + c] * LOG2E : 0.f;
-            else if constexpr (GATE == GATE_HEAD) gl = ok ? gh[m][e] * LOG2E : 0.f;
-            qv[m][e] = ok ? (float)stQ[r * DK + c] : 0.f;
-            kv[m][e] = ok ? (float)stK[r * DK + c] : 0.f;
+            if constexpr (GATE == GATE_CHANNEL) gl = stG[r * DK + c] * LOG2E;
+            else if constexpr (GATE == GATE_HEAD) gl = gh[m][e] * LOG2E;
+            const float qr = (float)stQ[r * DK + c], kr = (float)stK[r * DK + c];
+            gl = ok ? gl : 0.f;
+            qv[m][e] = ok ? qr : 0.f;
+            kv[m][e] = ok ? kr : 0.f;
             s4[e] = (e ? s4[e - 1] : 0.f) + gl;
         }
         float bs[4];
@@ -485,7 +495,7 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     }
     if (t < C) {
         const int tok = tok0 + t;
-        sbeta[t] = tok < T ? (float)beta[((size_t)b * T + tok) * H + h] : 0.f;
+        sbeta[t] = tok < T ? (float)betr : 0.f;
         sdb[t] = 0.f;
     }
     lds_barrier();
@@ -557,7 +567,13 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     lds_barrier();                                 // Kh, Kb dead; dA tiles and dbeta complete
     if (t < C && tok0 + t < T) dbeta[((size_t)b * T + tok0 + t) * H + h] = (bf16_t)sdb[t];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<bf16x8*>(sDV + vr * L::P128 + vc + 8 * i) = neg8(dvv[i]);
+    for (int i = 0; i < 2; ++i) {                  // -dV = -Diag(beta) dZ
+        bf16x8 dvn;
+        const float nb = -sbeta[vr];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) dvn[x] = (bf16_t)(nb * (float)zv[i][x]);
+        *reinterpret_cast<bf16x8*>(sDV + vr * L::P128 + vc + 8 * i) = dvn;
+    }
     lds_barrier();
 
     // ===== C x d_k products: wave w -> channel block w, token blocks m = 0..3 =====
@@ -755,7 +771,7 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const f
 
 #define KDA_GRAD(GT) hipLaunchKernelGGL(chunk_bwd_grad_kernel<GT>, dim3((unsigned)(heads * nchunks)), dim3(512), 0, \
                                       stream, (const bf16_t*)q, (const bf16_t*)k, g, (const bf16_t*)beta,       \
-                                      (const bf16_t*)dO, (const bf16_t*)dv, svS, svdS, svY, svVn, svdZ,          \
+                                      (const bf16_t*)dO, svS, svdS, svY, svVn, svdZ,                             \
                                       (bf16_t*)dq, (bf16_t*)dk, dg, (bf16_t*)dbeta, T, H)
     if (gate == GATE_HEAD) KDA_GRAD(GATE_HEAD);
     else if (gate == GATE_NONE) KDA_GRAD(GATE_NONE);
