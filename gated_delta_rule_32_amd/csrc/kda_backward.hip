@@ -384,15 +384,14 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         dov[i] = ld8(dO + vat + 8 * i);
         vnv[i] = ld8(svVn + sv_at(cidx, C, vr, vc + 8 * i));
     }
-    // C x C tiles tt = wave, wave + 8 as (mb, nb); those above the diagonal are
-    // zero and skipped (their loads are issued anyway, so the count is fixed)
-    bf16x8 dzf[2][4];
+    // C x C tiles (mb, nb) = (wave / 2, 2 (wave % 2) + j), j = 0, 1: both of a
+    // wave's tiles in one row block, so its dZ rows are loaded once (the tiles
+    // above the diagonal are zero and skipped; their wave still loads the rows,
+    // so the count is fixed)
+    const int mbw = wave >> 1;
+    bf16x8 dzf[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int tt = wave + 8 * j, mb = tt >> 2;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) dzf[j][s] = ld8(svdZ + sv_at(cidx, C, 16 * mb + ln, 32 * s + 8 * lg));
-    }
+    for (int s = 0; s < 4; ++s) dzf[s] = ld8(svdZ + sv_at(cidx, C, 16 * mbw + ln, 32 * s + 8 * lg));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const size_t wat = sv_at(cidx, C, vr, vc + 8 * i);
@@ -406,11 +405,11 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
         dsf[s] = ld8(svdS + sv_at(cidx, DK, c, 32 * s + 8 * lg));
     }
     if (!vok) { dov[0] = bf16x8{}; dov[1] = bf16x8{}; }
-    // The loads return in issue order: once at most the 20 register loads
+    // The loads return in issue order: once at most the 16 register loads
     // issued after beta, dO and Vn are outstanding, the LDS-destination loads
-    // are complete (vmcnt 20, no wait on the other counters).  The rest
+    // are complete (vmcnt 16, no wait on the other counters).  The rest
     // arrive while the decay phase and the C x C products run.
-    __builtin_amdgcn_s_waitcnt((20 & 15) | ((20 >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8));
     lds_barrier();
 
     // ===== decay and the decay-scaled keys / queries =====
@@ -503,7 +502,7 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     // ===== C x C products: KK = Kh Kb^T, M1 = dZ Vn^T, M2 = dO Vn^T =====
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int tt = wave + 8 * j, mb = tt >> 2, nb = tt & 3;
+        const int mb = mbw, nb = 2 * (wave & 1) + j;
         const int r0 = 16 * mb + 4 * lg, i = 16 * nb + ln;
         if (nb > mb) {
 #pragma unroll
@@ -526,7 +525,7 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
                 for (int x = 0; x < 8; ++x) kbf[x] = (bf16_t)((float)kbf[x] * (float)f[x]);
             }
             kk = mma(ld8(sKh + ra * L::P128 + ko), kbf, kk);
-            m1 = mma(dzf[j][s], vnf, m1);
+            m1 = mma(dzf[s], vnf, m1);
             m2 = mma(ld8(sDO + ra * L::P128 + ko), vnf, m2);
         }
         f32x4 aq, ap;

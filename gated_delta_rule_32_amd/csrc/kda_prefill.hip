@@ -468,8 +468,10 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
             // referenced to the ends of the four 16-token sub-chunks (slow
             // path below), which needs only each sub-chunk's decay in range.
             bool slow_chunk = false;
-            if constexpr (GATE != GATE_NONE)
-                slow_chunk = __builtin_amdgcn_ballot_w64(s_gtot[lane] < -FAST_LIM || s_gtot[lane + 64] < -FAST_LIM) != 0;
+            if constexpr (GATE != GATE_NONE) {
+                const float ga = s_gtot[lane], gb = s_gtot[lane + 64];   // both read, no branch
+                slow_chunk = __builtin_amdgcn_ballot_w64((ga < -FAST_LIM) | (gb < -FAST_LIM)) != 0;
+            }
             {
                 if constexpr (NG == 8) {
                     const f32x4 o0 = *reinterpret_cast<const f32x4*>(s_tot + wave * DK + 8 * cg);
