@@ -160,18 +160,13 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
             const float* sBeta = reinterpret_cast<const float*>(blk + WSB_BETA);
             const size_t cidx = (size_t)head * nchunks + n;
 
-            // dS' of this chunk (gradient of the state it hands on), for the
-            // gradient kernel
-            // (neighbouring lanes pair up so that each store is a 4-byte column
-            // pair, see pair_rows_bf16)
+            // Outputs of this step: dS' (the gradient of the state the chunk
+            // hands on, i.e. acc_s before the update), dZ and dV.  Neighbouring
+            // lanes pair up so that each store is a 4-byte column pair (see
+            // pair_rows_bf16).  The stores are issued at the end of the step:
+            // issued at its start they queue behind the loader waves' block
+            // copy and hold up the dependent MFMA chain.
             const int prow = 4 * lg + 2 * (ln & 1), pcol = j0 + 16 * cw + (ln & ~1);
-#pragma unroll
-            for (int cb = 0; cb < 8; ++cb) {
-                bf16x2 p0, p1;
-                pair_rows_bf16(acc_s[cb], lane, p0, p1);
-                *reinterpret_cast<bf16x2*>(svdS + sv_at(cidx, DK, 16 * cb + prow, pcol)) = p0;
-                *reinterpret_cast<bf16x2*>(svdS + sv_at(cidx, DK, 16 * cb + prow + 1, pcol)) = p1;
-            }
 
             bf16x8 sb[4], dob[2];
 #pragma unroll
@@ -202,6 +197,7 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
 #pragma unroll
             for (int p = 0; p < 2; ++p) vb[p] = cat8(to_bf16x4(dvn[2 * p]), to_bf16x4(dvn[2 * p + 1]));
             f32x4 dvv[4];
+            bf16x2 zp[4][2], dp[4][2];
 #pragma unroll
             for (int Rb = 0; Rb < 4; ++Rb) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
@@ -211,16 +207,13 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
                     a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rt, p, lg, true), vb[p], a, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dvv[Rb][e] = sBeta[16 * Rb + 4 * lg + e] * a[e];
-                bf16x2 z0, z1, d0, d1;
-                pair_rows_bf16(a, lane, z0, z1);
-                pair_rows_bf16(dvv[Rb], lane, d0, d1);
-                const int r0 = 16 * Rb + prow, tok = n * C + r0;
-                *reinterpret_cast<bf16x2*>(svdZ + sv_at(cidx, C, r0, pcol)) = z0;
-                *reinterpret_cast<bf16x2*>(svdZ + sv_at(cidx, C, r0 + 1, pcol)) = z1;
-                if (tok < T) *reinterpret_cast<bf16x2*>(dv + hbase + (size_t)tok * tokstride + pcol) = d0;
-                if (tok + 1 < T) *reinterpret_cast<bf16x2*>(dv + hbase + (size_t)(tok + 1) * tokstride + pcol) = d1;
+                pair_rows_bf16(a, lane, zp[Rb][0], zp[Rb][1]);
+                pair_rows_bf16(dvv[Rb], lane, dp[Rb][0], dp[Rb][1]);
             }
 
+            bf16x2 sp[8][2];                     // dS', stored after the update
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) pair_rows_bf16(acc_s[cb], lane, sp[cb][0], sp[cb][1]);
             // dS <- Diag(gamma) dS' + Qt^T dO - Kh^T dV
             bf16x8 nb[2];
 #pragma unroll
@@ -237,6 +230,19 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
                     a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rh, p, lg, true), nb[p], a, 0, 0, 0);
                 }
                 acc_s[cb] = a;
+            }
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+                *reinterpret_cast<bf16x2*>(svdS + sv_at(cidx, DK, 16 * cb + prow, pcol)) = sp[cb][0];
+                *reinterpret_cast<bf16x2*>(svdS + sv_at(cidx, DK, 16 * cb + prow + 1, pcol)) = sp[cb][1];
+            }
+#pragma unroll
+            for (int Rb = 0; Rb < 4; ++Rb) {
+                const int r0 = 16 * Rb + prow, tok = n * C + r0;
+                *reinterpret_cast<bf16x2*>(svdZ + sv_at(cidx, C, r0, pcol)) = zp[Rb][0];
+                *reinterpret_cast<bf16x2*>(svdZ + sv_at(cidx, C, r0 + 1, pcol)) = zp[Rb][1];
+                if (tok < T) *reinterpret_cast<bf16x2*>(dv + hbase + (size_t)tok * tokstride + pcol) = dp[Rb][0];
+                if (tok + 1 < T) *reinterpret_cast<bf16x2*>(dv + hbase + (size_t)(tok + 1) * tokstride + pcol) = dp[Rb][1];
             }
         }
         lds_barrier();

@@ -1242,17 +1242,16 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             const bf16_t* sVT = reinterpret_cast<const bf16_t*>(st + SC::OFF_VT);
             bf16_t* sO = reinterpret_cast<bf16_t*>(smem + SC::OFF_O + (n & 1) * C * SC::DV * 2);
             const size_t cidx = (size_t)head * nchunks + n;
-            // saved tiles: neighbouring lanes pair up so that each store is a
-            // 4-byte column pair (see pair_rows_bf16)
+            // saved tiles (SAVE): neighbouring lanes pair up so that each store
+            // is a 4-byte column pair (see pair_rows_bf16).  S (the state
+            // entering the chunk), Y and Vn are stored at the end of the step:
+            // issued earlier they queue behind the loader waves' block copy and
+            // hold up the dependent MFMA chain.
             const int prow = 4 * lg + 2 * (ln & 1), pcol = j0 + 16 * cw + (ln & ~1);
+            bf16x2 s_pr[SAVE ? 8 : 1][2], y_pr[SAVE ? 4 : 1][2], w_pr[SAVE ? 4 : 1][2];
             if constexpr (SAVE) {
 #pragma unroll
-                for (int cb = 0; cb < 8; ++cb) {
-                    bf16x2 p0, p1;
-                    pair_rows_bf16(acc_s[cb], lane, p0, p1);
-                    *reinterpret_cast<bf16x2*>(svS + sv_at(cidx, DK, 16 * cb + prow, pcol)) = p0;
-                    *reinterpret_cast<bf16x2*>(svS + sv_at(cidx, DK, 16 * cb + prow + 1, pcol)) = p1;
-                }
+                for (int cb = 0; cb < 8; ++cb) pair_rows_bf16(acc_s[cb], lane, s_pr[cb][0], s_pr[cb][1]);
             }
 
             // P = Kh S and Qt S; a block's eight operand loads go out before its
@@ -1321,14 +1320,8 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
             if constexpr (SAVE) {
 #pragma unroll
                 for (int Rb = 0; Rb < 4; ++Rb) {
-                    bf16x2 y0, y1, w0, w1;
-                    pair_rows_bf16(zt[Rb], lane, y0, y1);
-                    pair_rows_bf16(vn[Rb], lane, w0, w1);
-                    const size_t a0 = sv_at(cidx, C, 16 * Rb + prow, pcol), a1 = sv_at(cidx, C, 16 * Rb + prow + 1, pcol);
-                    *reinterpret_cast<bf16x2*>(svY + a0) = y0;
-                    *reinterpret_cast<bf16x2*>(svY + a1) = y1;
-                    *reinterpret_cast<bf16x2*>(svVn + a0) = w0;
-                    *reinterpret_cast<bf16x2*>(svVn + a1) = w1;
+                    pair_rows_bf16(zt[Rb], lane, y_pr[Rb][0], y_pr[Rb][1]);
+                    pair_rows_bf16(vn[Rb], lane, w_pr[Rb][0], w_pr[Rb][1]);
                 }
             }
 
@@ -1385,6 +1378,21 @@ chunk_scan_body(const char* ws, const bf16_t* v, const float* S0, bf16_t* o, flo
                     const bf16_t* sH0 = sTm;          // [128][DV] in the Tm slot
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc_s[cb][e] += (float)sH0[(16 * cb + 4 * lg + e) * SC::DV + jc];
+                }
+            }
+            if constexpr (SAVE) {
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb) {
+                    *reinterpret_cast<bf16x2*>(svS + sv_at(cidx, DK, 16 * cb + prow, pcol)) = s_pr[cb][0];
+                    *reinterpret_cast<bf16x2*>(svS + sv_at(cidx, DK, 16 * cb + prow + 1, pcol)) = s_pr[cb][1];
+                }
+#pragma unroll
+                for (int Rb = 0; Rb < 4; ++Rb) {
+                    const size_t a0 = sv_at(cidx, C, 16 * Rb + prow, pcol), a1 = sv_at(cidx, C, 16 * Rb + prow + 1, pcol);
+                    *reinterpret_cast<bf16x2*>(svY + a0) = y_pr[Rb][0];
+                    *reinterpret_cast<bf16x2*>(svY + a1) = y_pr[Rb][1];
+                    *reinterpret_cast<bf16x2*>(svVn + a0) = w_pr[Rb][0];
+                    *reinterpret_cast<bf16x2*>(svVn + a1) = w_pr[Rb][1];
                 }
             }
         }
