@@ -659,7 +659,8 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
         }
         lds_barrier();
 
-        // ===== UT diagonal blocks (wave 0) | inter-chunk output Qt S (waves 1-7) =====
+        // ===== UT diagonal blocks (wave 0) | inter-chunk output Qt S (waves 1-7;
+        // backward prep: the transposed operands of the backward state scan) =====
         if (wave == 0) {
             // column m of X = (I + A_bb)^{-1} for block bb, right-looking substitution
             const int bb = lane >> 4, m = lane & 15;
@@ -696,6 +697,40 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) A[i * L::PA + m] = x[i];
+        } else if constexpr (PREP && BWD) {
+            // Aqk^T, Qt^T, Kh^T and Kt (final since the intra-chunk products)
+            // for the backward state scan, by the seven waves that have no
+            // substitution chain, transposed 16 x 16 blocks at a time on the
+            // matrix cores: the A operand is 16 rows of the source (4
+            // consecutive columns per lane, one 8-byte LDS read), B the
+            // identity, so accumulator lane (ln, lg) holds source rows 4lg ..
+            // 4lg+3 of column ln, i.e. 4 consecutive elements of row ln of the
+            // transpose (bf16 times one, summed in fp32: exact).
+            char* bb = wsb + ((size_t)head * nchunks + n) * WSB_CHUNK;
+            bf16x4 ident;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ident[e] = (bf16_t)(4 * lg + e == ln ? 1.f : 0.f);
+            // blocks 0-31 Qt^T, 32-63 Kh^T ([128][64] from [64][128]), 64-95
+            // Kt ([64][128] from the swizzled Kt^T tile, 4 consecutive tokens
+            // contiguous), 96-111 Aqk^T ([64][64])
+            for (int bk = wave - 1; bk < 112; bk += NW - 1) {
+                const int m = bk >> 5, b5 = bk & 31, r0 = 16 * (b5 & 3), c0 = 16 * (b5 >> 2);
+                bf16x4 a;
+                char* dst;
+                int row, col, dpitch;
+                if (m < 2) {
+                    a = *reinterpret_cast<const bf16x4*>((m ? sKh : sQt) + (r0 + ln) * L::P128 + c0 + 4 * lg);
+                    dst = bb + (m ? WSB_KHT : WSB_QTT); row = c0; col = r0; dpitch = WSB_P64;
+                } else if (m == 2) {
+                    a = *reinterpret_cast<const bf16x4*>(sKbT + L::kbt(c0 + ln, r0 + 4 * lg));
+                    dst = bb + WSB_KT; row = r0; col = c0; dpitch = WSB_P128;
+                } else {
+                    a = *reinterpret_cast<const bf16x4*>(sQK + (r0 + ln) * L::P64 + c0 + 4 * lg);
+                    dst = bb + WSB_AQKT; row = c0; col = r0; dpitch = WSB_P64;
+                }
+                const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, z4, 0, 0, 0);
+                *reinterpret_cast<bf16x4*>(dst + ((size_t)(row + ln) * dpitch + col + 4 * lg) * 2) = to_bf16x4(d);
+            }
         } else if constexpr (!PREP) {
             // output tiles t = (wave - 1) + (NW - 1) m: (jb = t / 4, R = t % 4)
 #pragma unroll
@@ -798,30 +833,11 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
                 else *reinterpret_cast<i32x2*>(blk + off + 8 * l) = *reinterpret_cast<const i32x2*>(row);
             }
             if constexpr (BWD) {
-                // operands of the backward state scan: transposes read from LDS
-                // eight strided elements at a time, written 16 bytes at a time
+                // the rest of the backward state scan's operands (Aqk^T, Qt^T,
+                // Kh^T and Kt went out during the diagonal UT step)
                 char* bb = wsb + ((size_t)head * nchunks + n) * WSB_CHUNK;
-                auto transpose = [&](bf16_t* dst, const E* src, int src_pitch, int rows) {
-                    for (int u = t; u < rows * (C / 8); u += NT) {     // dst row, 8-column group
-                        const int row = u >> 3, c8 = 8 * (u & 7);
-                        bf16x8 x;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) x[i] = src[(c8 + i) * src_pitch + row];
-                        *reinterpret_cast<bf16x8*>(dst + row * WSB_P64 + c8) = x;
-                    }
-                };
-                transpose(reinterpret_cast<bf16_t*>(bb + WSB_AQKT), sQK, L::P64, C);
-                transpose(reinterpret_cast<bf16_t*>(bb + WSB_QTT), sQt, L::P128, DK);
-                transpose(reinterpret_cast<bf16_t*>(bb + WSB_KHT), sKh, L::P128, DK);
                 for (int u = t; u < C * WSB_P64 * 2 / 16; u += NT)
                     reinterpret_cast<i32x4*>(bb + WSB_TMT)[u] = reinterpret_cast<const i32x4*>(sTmT)[u];
-                for (int u = t; u < C * (DK / 8); u += NT) {           // Kt, token-major, from Kt^T
-                    const int r = u >> 4, c8 = 8 * (u & 15);
-                    bf16x8 x;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] = sKbT[L::kbt(c8 + i, r)];
-                    *reinterpret_cast<bf16x8*>(bb + WSB_KT + (r * WSB_P128 + c8) * 2) = x;
-                }
                 if (t < DK) reinterpret_cast<float*>(bb + WSB_GAM)[t] = s_gam[t];
                 if (t < C) reinterpret_cast<float*>(bb + WSB_BETA)[t] = s_beta[t];
                 // the next chunk's first LDS writes (beta, column totals) come
