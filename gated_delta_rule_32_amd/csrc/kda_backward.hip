@@ -47,7 +47,9 @@ namespace {
 // LDS-destination loads and write dO^T of the value slice next to it; NCW
 // consumer waves each hold a 128 x 16 slice of dS in accumulators.  The
 // contraction operands that are products of the previous step stay in
-// registers (accumulator tiles packed in pairs as B operands, a_pair A reads).
+// registers (accumulator tiles packed in pairs as B operands); the block's
+// operands are read as 16-byte A units (WSB_* in kda_chunk_common.h), and the
+// zero pairs of the upper triangular Aqk^T and Tm^T are skipped.
 template <int NCW> struct BScanCfg {
     static constexpr int DV = 16 * NCW;
     static constexpr int NLW = 8 - NCW;
@@ -151,8 +153,14 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
             const char* st = smem + (n & 1) * SC::STAGE;
             const char* blk = st + SC::OFF_BLK;
             const bf16_t* sdOT = reinterpret_cast<const bf16_t*>(st + SC::OFF_DOT);
-            const bf16_t* sAqkT = reinterpret_cast<const bf16_t*>(blk + WSB_AQKT);
-            const bf16_t* sTmT = reinterpret_cast<const bf16_t*>(blk + WSB_TMT);
+            // A operands from the block (layout WSB_* in kda_chunk_common.h):
+            // pair p of row block Rb of the upper triangular Aqk^T, Tm^T, and
+            // unit 4p + lg of a row of Qt^T, Kh^T, Kt
+            auto tri_up = [&](int mat, int Rb, int p) {
+                const char* q = blk + mat + wsb_pair_off(Rb, p);
+                if (wsb_pair_full(Rb, p)) return *reinterpret_cast<const bf16x8*>(q + 16 * (4 * ln + lg));
+                return cat8(bf16x4{}, *reinterpret_cast<const bf16x4*>(q + 8 * (4 * ln + lg)));
+            };
             const bf16_t* sQtT = reinterpret_cast<const bf16_t*>(blk + WSB_QTT);
             const bf16_t* sKhT = reinterpret_cast<const bf16_t*>(blk + WSB_KHT);
             const bf16_t* sKt = reinterpret_cast<const bf16_t*>(blk + WSB_KT);
@@ -181,14 +189,15 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
 #pragma unroll
             for (int Rb = 0; Rb < 4; ++Rb) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
-                const bf16_t* ra = sAqkT + (16 * Rb + ln) * WSB_P64;
-                const bf16_t* rk = sKt + (16 * Rb + ln) * WSB_P128;
 #pragma unroll
                 for (int p = 0; p < 2; ++p)
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(ra, p, lg, true), dob[p], a, 0, 0, 0);
+                    if (!wsb_pair_zero(Rb, p))
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tri_up(WSB_AQKT, Rb, p), dob[p], a, 0, 0, 0);
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rk, p, lg, true), sb[p], a, 0, 0, 0);
+                for (int p = 0; p < 4; ++p) {
+                    const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(sKt + wsk_tok_unit(16 * Rb + ln, 4 * p + lg));
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, sb[p], a, 0, 0, 0);
+                }
                 dvn[Rb] = a;
             }
 
@@ -201,10 +210,10 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
 #pragma unroll
             for (int Rb = 0; Rb < 4; ++Rb) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
-                const bf16_t* rt = sTmT + (16 * Rb + ln) * WSB_P64;
 #pragma unroll
                 for (int p = 0; p < 2; ++p)
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rt, p, lg, true), vb[p], a, 0, 0, 0);
+                    if (!wsb_pair_zero(Rb, p))
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tri_up(WSB_TMT, Rb, p), vb[p], a, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dvv[Rb][e] = sBeta[16 * Rb + 4 * lg + e] * a[e];
                 pair_rows_bf16(a, lane, zp[Rb][0], zp[Rb][1]);
@@ -222,12 +231,11 @@ chunk_bwd_scan_kernel(const char* wsb, const bf16_t* dO, const float* dST, bf16_
             for (int cb = 0; cb < 8; ++cb) {
                 const f32x4 gv = *reinterpret_cast<const f32x4*>(sGam + 16 * cb + 4 * lg);
                 f32x4 a = acc_s[cb] * gv;
-                const bf16_t* rq = sQtT + (16 * cb + ln) * WSB_P64;
-                const bf16_t* rh = sKhT + (16 * cb + ln) * WSB_P64;
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rq, p, lg, true), dob[p], a, 0, 0, 0);
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pair(rh, p, lg, true), nb[p], a, 0, 0, 0);
+                    const int u = wsk_kbt_unit(16 * cb + ln, 4 * p + lg);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(sQtT + u), dob[p], a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(sKhT + u), nb[p], a, 0, 0, 0);
                 }
                 acc_s[cb] = a;
             }

@@ -283,18 +283,36 @@ __device__ __forceinline__ void pair_rows_bf16(const f32x4& x, int lane, bf16x2&
 
 // ---- backward pass: per-chunk operand block of the reverse state scan --------
 // Written by the prep kernel next to the forward block, read by
-// chunk_bwd_scan_kernel.  All bf16 except the two vectors; rows padded to
-// 72 / 136 elements as in the forward block.
-constexpr int WSB_P64 = C + 8, WSB_P128 = DK + 8;
-constexpr int WSB_AQKT = 0;                              // Aqk^T [64][72]
-constexpr int WSB_TMT = WSB_AQKT + C * WSB_P64 * 2;      // Tm^T  [64][72] (no beta)
-constexpr int WSB_QTT = WSB_TMT + C * WSB_P64 * 2;       // Qt^T  [128][72]
-constexpr int WSB_KHT = WSB_QTT + DK * WSB_P64 * 2;      // Kh^T  [128][72]
-constexpr int WSB_KT = WSB_KHT + DK * WSB_P64 * 2;       // Kt = e^{G_64 - G} k [64][136]
-constexpr int WSB_GAM = WSB_KT + C * WSB_P128 * 2;       // e^{G_64} [128] fp32
-constexpr int WSB_BETA = WSB_GAM + DK * 4;               // beta [64] fp32 (0 past T)
-constexpr int WSB_USED = WSB_BETA + C * 4;               // 73,472 bytes
-constexpr int WSB_CHUNK = (WSB_USED + 1023) / 1024 * 1024;   // 73,728
+// chunk_bwd_scan_kernel (copied linearly into LDS and read there as MFMA A
+// operands).  bf16 except the two vectors, no row padding:
+//   Aqk^T, Tm^T (no beta): upper triangular, as the operand pairs (Rb, p) of
+//           their nonzero blocks (wsb_pair_off): row block Rb, pair p of
+//           columns 32p + 4lg .. +3 and 32p + 16 + 4lg .. +3 for lane group
+//           lg; a pair whose first block lies below the diagonal holds 8-byte
+//           units (the second block's four columns), the others 16-byte
+//           units, each [16 rows][4 lane groups];
+//   Qt^T, Kh^T [128][64]: the unit layout of the forward block's Kt^T
+//           (wsk_kbt_unit);
+//   Kt = e^{G_64 - G} k [64][128]: the unit layout of its Qt (wsk_tok_unit);
+//   e^{G_64} [128] and beta [64] (0 past T), fp32.
+constexpr int WSB_AQKT = 0;
+constexpr int WSB_TMT = WSB_AQKT + WS_TRI;
+constexpr int WSB_QTT = WSB_TMT + WS_TRI;                // 16 KiB each
+constexpr int WSB_KHT = WSB_QTT + DK * C * 2;
+constexpr int WSB_KT = WSB_KHT + DK * C * 2;
+constexpr int WSB_GAM = WSB_KT + C * DK * 2;
+constexpr int WSB_BETA = WSB_GAM + DK * 4;
+constexpr int WSB_USED = WSB_BETA + C * 4;               // 60,160 bytes
+constexpr int WSB_CHUNK = (WSB_USED + 1023) / 1024 * 1024;   // 60,416
+// byte offset of operand pair (Rb, p) of an upper triangular matrix (pairs
+// with 2p + 1 < Rb are zero and not stored), and whether it holds both blocks
+__device__ __forceinline__ constexpr int wsb_pair_off(int Rb, int p) {
+    return Rb == 0 ? 1024 * p : Rb == 1 ? (p == 0 ? 2048 : 2560) : Rb == 2 ? 3584 : 4608;
+}
+__device__ __forceinline__ constexpr bool wsb_pair_full(int Rb, int p) { return 2 * p >= Rb; }
+__device__ __forceinline__ constexpr bool wsb_pair_zero(int Rb, int p) { return 2 * p + 1 < Rb; }
+// row pitch (elements) of the prep's Tm^T staging tile in LDS
+constexpr int TMT_P = C + 8;
 
 // Eight consecutive elements (one 16-byte load for bf16, two for fp32).
 template <typename E> struct Raw8;

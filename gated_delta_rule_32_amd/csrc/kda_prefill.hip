@@ -294,7 +294,8 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
     float* s_gtot = reinterpret_cast<float*>(smem + L::OFF_GTOT);
     // prep for the backward pass: Tm^T, unscaled, in the (unused) value-side
     // buffers; null otherwise
-    static_assert(!BWD || (PREP && L::OFF_VN - L::OFF_V >= C * WSB_P64 * 2), "Tm^T fits in the value-side buffers");
+    static_assert(!BWD || (PREP && L::OFF_VN - L::OFF_V >= C * TMT_P * 2 && L::P64 == TMT_P),
+                  "Tm^T fits in the value-side buffers");
     bf16_t* sTmT = BWD ? reinterpret_cast<bf16_t*>(smem + L::OFF_V) : nullptr;
 
     const int t = threadIdx.x, lane = t & 63;
@@ -710,26 +711,35 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
             bf16x4 ident;
 #pragma unroll
             for (int e = 0; e < 4; ++e) ident[e] = (bf16_t)(4 * lg + e == ln ? 1.f : 0.f);
-            // blocks 0-31 Qt^T, 32-63 Kh^T ([128][64] from [64][128]), 64-95
+            // Blocks 0-31 Qt^T, 32-63 Kh^T ([128][64] from [64][128]), 64-95
             // Kt ([64][128] from the swizzled Kt^T tile, 4 consecutive tokens
-            // contiguous), 96-111 Aqk^T ([64][64])
-            for (int bk = wave - 1; bk < 112; bk += NW - 1) {
-                const int m = bk >> 5, b5 = bk & 31, r0 = 16 * (b5 & 3), c0 = 16 * (b5 >> 2);
-                bf16x4 a;
-                char* dst;
-                int row, col, dpitch;
-                if (m < 2) {
-                    a = *reinterpret_cast<const bf16x4*>((m ? sKh : sQt) + (r0 + ln) * L::P128 + c0 + 4 * lg);
-                    dst = bb + (m ? WSB_KHT : WSB_QTT); row = c0; col = r0; dpitch = WSB_P64;
-                } else if (m == 2) {
-                    a = *reinterpret_cast<const bf16x4*>(sKbT + L::kbt(c0 + ln, r0 + 4 * lg));
-                    dst = bb + WSB_KT; row = r0; col = c0; dpitch = WSB_P128;
-                } else {
-                    a = *reinterpret_cast<const bf16x4*>(sQK + (r0 + ln) * L::P64 + c0 + 4 * lg);
-                    dst = bb + WSB_AQKT; row = c0; col = r0; dpitch = WSB_P64;
+            // contiguous), 96-105 the nonzero blocks of Aqk^T.  A lane's four
+            // elements (row `row`, columns 32p + 16h + 4lg .. +3) are half h
+            // of unit 4p + lg of that row in the block's layout.
+            for (int bk = wave - 1; bk < 106; bk += NW - 1) {
+                const int m = bk >> 5, b5 = bk & 31;
+                int r0 = 16 * (b5 & 3), c0 = 16 * (b5 >> 2);
+                if (m == 3) {                 // upper block (Ib, Rr), Rr >= Ib, of Aqk^T
+                    const int Ib = b5 < 4 ? 0 : b5 < 7 ? 1 : b5 < 9 ? 2 : 3;
+                    const int Rr = Ib + b5 - (Ib == 0 ? 0 : Ib == 1 ? 4 : Ib == 2 ? 7 : 9);
+                    r0 = 16 * Rr; c0 = 16 * Ib;   // Aqk rows r0.., columns c0..
                 }
-                const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, z4, 0, 0, 0);
-                *reinterpret_cast<bf16x4*>(dst + ((size_t)(row + ln) * dpitch + col + 4 * lg) * 2) = to_bf16x4(d);
+                bf16x4 a;
+                if (m < 2) a = *reinterpret_cast<const bf16x4*>((m ? sKh : sQt) + (r0 + ln) * L::P128 + c0 + 4 * lg);
+                else if (m == 2) a = *reinterpret_cast<const bf16x4*>(sKbT + L::kbt(c0 + ln, r0 + 4 * lg));
+                else a = *reinterpret_cast<const bf16x4*>(sQK + (r0 + ln) * L::P64 + c0 + 4 * lg);
+                const bf16x4 d = to_bf16x4(__builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, z4, 0, 0, 0));
+                // transpose row, and its columns' pair p and half h
+                const int row = (m == 2 ? r0 : c0) + ln, cc = m == 2 ? c0 : r0, p = cc >> 5, h = (cc >> 4) & 1;
+                size_t off;
+                if (m < 2) off = (m ? WSB_KHT : WSB_QTT) + 2 * wsk_kbt_unit(row, 4 * p + lg) + 8 * h;
+                else if (m == 2) off = WSB_KT + 2 * wsk_tok_unit(row, 4 * p + lg) + 8 * h;
+                else {
+                    const int Ib = c0 >> 4;
+                    off = WSB_AQKT + wsb_pair_off(Ib, p) +
+                          (wsb_pair_full(Ib, p) ? 16 * (4 * ln + lg) + 8 * h : 8 * (4 * ln + lg));
+                }
+                *reinterpret_cast<bf16x4*>(bb + off) = d;
             }
         } else if constexpr (!PREP) {
             // output tiles t = (wave - 1) + (NW - 1) m: (jb = t / 4, R = t % 4)
@@ -771,14 +781,14 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
                         x[e] = RA[(r + e) * L::PA + 16 * bb + ln];
                         RT[(r + e) * L::P64 + 16 * bb + ln] = (E)(bcol * x[e]);
                     }
-                    if (sTmT) store_vec4<bf16_t>(sTmT + (16 * bb + ln) * WSB_P64 + r, x);
+                    if (sTmT) store_vec4<bf16_t>(sTmT + (16 * bb + ln) * TMT_P + r, x);
                 }
             } else {
                 for (int u = wave - 4; u < 6; u += 4) {   // zero upper blocks of RT (lower of Tm^T)
                     const int I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
                     const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
                     store_vec4<E>(RT + (16 * R + ln) * L::P64 + 16 * I + 4 * lg, z4);
-                    if (sTmT) store_vec4<bf16_t>(sTmT + (16 * I + ln) * WSB_P64 + 16 * R + 4 * lg, z4);
+                    if (sTmT) store_vec4<bf16_t>(sTmT + (16 * I + ln) * TMT_P + 16 * R + 4 * lg, z4);
                 }
             }
             if (wave < 3 && n + 1 < n_end) load_chunk(n + 1, in);
@@ -836,8 +846,21 @@ chunk_fwd_body(const E* q, const E* k, const E* v, const float* g, const E* beta
                 // the rest of the backward state scan's operands (Aqk^T, Qt^T,
                 // Kh^T and Kt went out during the diagonal UT step)
                 char* bb = wsb + ((size_t)head * nchunks + n) * WSB_CHUNK;
-                for (int u = t; u < C * WSB_P64 * 2 / 16; u += NT)
-                    reinterpret_cast<i32x4*>(bb + WSB_TMT)[u] = reinterpret_cast<const i32x4*>(sTmT)[u];
+                // Tm^T as the operand pairs of its nonzero blocks: 4 full pairs
+                // of 64 units, then the two half pairs (second block only)
+                for (int u = t; u < 6 * 64; u += NT) {
+                    const int k6 = u >> 6, l = u & 63;
+                    const int Rb = k6 < 2 ? 0 : k6 < 4 ? 1 : k6 < 5 ? 2 : 3, p = (k6 == 0 || k6 == 2) ? 0 : 1;
+                    const bf16_t* row = sTmT + (16 * Rb + (l >> 2)) * TMT_P + 32 * p + 4 * (l & 3);
+                    const int off = WSB_TMT + wsb_pair_off(Rb, p);
+                    const i32x2 hi = *reinterpret_cast<const i32x2*>(row + 16);
+                    if (wsb_pair_full(Rb, p)) {
+                        const i32x2 lo = *reinterpret_cast<const i32x2*>(row);
+                        *reinterpret_cast<i32x4*>(bb + off + 16 * l) = i32x4{lo[0], lo[1], hi[0], hi[1]};
+                    } else {
+                        *reinterpret_cast<i32x2*>(bb + off + 8 * l) = hi;
+                    }
+                }
                 if (t < DK) reinterpret_cast<float*>(bb + WSB_GAM)[t] = s_gam[t];
                 if (t < C) reinterpret_cast<float*>(bb + WSB_BETA)[t] = s_beta[t];
                 // the next chunk's first LDS writes (beta, column totals) come

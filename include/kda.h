@@ -283,7 +283,7 @@ int kda_chunk_bwd_gated(const void* q, const void* k, const void* v,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes kda_chunk_bwd needs: B * H * ceil(T / 64) * 248832 for
+ * Workspace bytes kda_chunk_bwd needs: B * H * ceil(T / 64) * 235520 for
  * dtype == KDA_BF16 and d_k = d_v = 128; 0 for invalid or unsupported
  * arguments.
  */

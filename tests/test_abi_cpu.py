@@ -245,7 +245,7 @@ def test_layer_fwd_empty_is_noop(lib):
 
 
 # ------------------------------------------------------------ backward pass
-BWD_UNIT = 248832   # workspace bytes per (batch, head, 64-token chunk)
+BWD_UNIT = 235520   # workspace bytes per (batch, head, 64-token chunk)
 
 
 def bwd(lib, q=P, k=P + 2**24, v=P + 2**25, g=P + 2**26, beta=P + 2**27, S0=None,
