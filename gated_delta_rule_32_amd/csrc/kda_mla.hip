@@ -16,8 +16,9 @@
 // avoid bank conflicts).  Scores S^T = C Q^T on MFMA with the query heads'
 // fragments held in registers (wave w: 16 tokens x 16 heads); an online
 // softmax per head (running maximum and sum in LDS, double-buffered); then
-// O += P C on MFMA (wave w: 64 latent columns of every head), C read
-// transposed from the same LDS tile.  A second kernel merges the splits.
+// O += P C on MFMA (wave w: 64 latent columns of every head), with the C^T
+// fragments formed from the same LDS tile on the matrix cores (identity
+// products, 8-byte reads).  A second kernel merges the splits.
 #include "kda_chunk_common.h"
 #include "kda_internal.h"
 
@@ -159,22 +160,35 @@ mqa_split_kernel(const bf16_t* q, const bf16_t* cache, float* part, float* ml, i
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[h2][j] *= al;
         }
+        // C^T fragments (tokens along k) from the row-major tile on the matrix
+        // cores: A = 16 tile rows x 4 latent columns per lane (one 8-byte read),
+        // B = identity, so accumulator lane (ln, lg) holds tokens 4lg .. 4lg+3
+        // of latent column ln (bf16 times one summed in fp32: exact).  Two such
+        // blocks give the k order {32s + 4lg .., 32s + 16 + 4lg ..}; P is read in
+        // the same order.
+        bf16x4 ident;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ident[e] = (bf16_t)(4 * lg + e == ln ? 1.f : 0.f);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             bf16x8 pa[HB];
 #pragma unroll
-            for (int h2 = 0; h2 < HB; ++h2)
-                pa[h2] = *reinterpret_cast<const bf16x8*>(sP + (16 * h2 + ln) * L::PP + 32 * s + 8 * lg);
+            for (int h2 = 0; h2 < HB; ++h2) {
+                const bf16_t* pr = sP + (16 * h2 + ln) * L::PP + 32 * s + 4 * lg;
+                pa[h2] = cat8(*reinterpret_cast<const bf16x4*>(pr), *reinterpret_cast<const bf16x4*>(pr + 16));
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int d = 64 * wave + 16 * j + ln;
+                const int d = 64 * wave + 16 * j + 4 * lg;            // this lane's 4 latent columns of the A read
                 const int unit = d >> 3, el = d & 7;
-                bf16x8 cfr;
+                bf16x4 half[2];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = 32 * s + 8 * lg + i;
-                    cfr[i] = *reinterpret_cast<const bf16_t*>(ct + r * 1024 + swz(r, unit) * 16 + el * 2);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int r = 32 * s + 16 * hh + ln;
+                    const bf16x4 a = *reinterpret_cast<const bf16x4*>(ct + r * 1024 + swz(r, unit) * 16 + el * 2);
+                    half[hh] = to_bf16x4(__builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0));
                 }
+                const bf16x8 cfr = cat8(half[0], half[1]);
 #pragma unroll
                 for (int h2 = 0; h2 < HB; ++h2)
                     acc[h2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h2], cfr, acc[h2][j], 0, 0, 0);
