@@ -423,7 +423,7 @@ chunk_bwd_grad_kernel(const bf16_t* q, const bf16_t* k, const float* g, const bf
     // issued after beta, dO and Vn are outstanding, the LDS-destination loads
     // are complete (vmcnt 16, no wait on the other counters).  The rest
     // arrive while the decay phase and the C x C products run.
-    __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8));
+    wait_vmcnt<16>();
     lds_barrier();
 
     // ===== decay and the decay-scaled keys / queries =====

@@ -19,6 +19,15 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// s_waitcnt on the vector-memory counter only: at most N vector memory
+// operations of this wave outstanding (vmcnt is bits 3:0 and 15:14 of the
+// immediate; expcnt and lgkmcnt at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---- MFMA wrappers -------------------------------------------------------
 // A 16 x 16 output tile D = A B.  `frag_kc` fetches an operand from a row-major
 // LDS matrix whose rows are the tile's M (or N) index and whose columns are the
