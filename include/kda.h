@@ -247,7 +247,7 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
  *   workspace  device scratch of at least kda_chunk_bwd_workspace_size(...)
  *              bytes, 256-byte aligned, owned by the caller; contents on entry
  *              and exit unspecified.  It holds the recomputed forward pass:
- *              per (batch, head, 64-token chunk) 248,832 bytes -- the key-side
+ *              per (batch, head, 64-token chunk) 235,520 bytes -- the key-side
  *              operand blocks of both scans and, in bf16, the state entering
  *              the chunk, its gradient on leaving it, V - Kh S, Vn and
  *              Tm^T dVn.
