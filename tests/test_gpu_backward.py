@@ -212,3 +212,14 @@ def test_one_round_slices_with_ragged_tail():
     inp = inputs.prefill_inputs(2, 150, 64, dtype="bfloat16", g_scale=0.1, s0_std=0.05, seed=77)
     gr = inputs.grad_inputs(2, 150, 64, ds_std=0.05, seed=77)
     check(run_bwd(inp, gr), oracle_grads(inp, gr))
+
+
+@pytest.mark.parametrize("B,H", [(1, 64), (3, 30)])
+def test_32_column_slices_with_ragged_tail(B, H):
+    """64 to 127 heads select 32-column slices (two consumer waves) in both
+    state scans; T = 150 leaves a ragged last chunk, with S0, dS_T and strong
+    decay.  Every gradient of every head against the oracle."""
+    print(f"backward {B * H} heads (32-column scan slices), T=150", flush=True)
+    inp = inputs.prefill_inputs(B, 150, H, dtype="bfloat16", g_scale=1.0, s0_std=0.05, seed=78 + H)
+    gr = inputs.grad_inputs(B, 150, H, ds_std=0.05, seed=78 + H)
+    check(run_bwd(inp, gr), oracle_grads(inp, gr))
